@@ -1,0 +1,308 @@
+"""Plain CPU oracle for the MXFP4 quantize-then-contract path.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package.  The product
+library (``mxfp4_precision_numerics_amd``) never imports, loads or calls it,
+and the two share no code: the arithmetic here lives in ``mx_oracle.c`` (plain
+C99 loops, built with ``-O2 -ffp-contract=off``, no fast-math).
+
+This module only marshals numpy arrays to the C functions and splits
+independent output rows over threads (ctypes releases the GIL during a foreign
+call, so the plain single-threaded C runs on several cores at once).  Every
+function documents which definition it follows; the C file cites the sources.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "mx_oracle.c")
+_LIB = os.path.join(_HERE, "libmxoracle.so")
+
+RNE = 0
+SR = 1
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (plain C99, no contraction, no fast-math)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call([
+            "gcc", "-std=c99", "-O2", "-ffp-contract=off", "-fno-fast-math",
+            "-fPIC", "-shared", "-Wall", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        L = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        i64, u64, u32, i32 = ctypes.c_int64, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_int32
+        L.oracle_philox4x32_10.argtypes = [P, P, P]
+        L.oracle_rht_sign_mask.argtypes = [u64]
+        L.oracle_rht_sign_mask.restype = u32
+        L.oracle_sr_bits.argtypes = [u64, u32, u64]
+        L.oracle_sr_bits.restype = u32
+        L.oracle_rht_block.argtypes = [P, P, u32, ctypes.c_int]
+        L.oracle_scale_byte.argtypes = [ctypes.c_double]
+        L.oracle_scale_byte.restype = ctypes.c_uint8
+        L.oracle_rtne_mag.argtypes = [ctypes.c_double]
+        L.oracle_sr_mag.argtypes = [ctypes.c_double, u32]
+        L.oracle_quantize_1d.argtypes = [P, ctypes.c_int, i64, i64, ctypes.c_int, P, i32, i64,
+                                         ctypes.c_int, u32, ctypes.c_int, u64, u32, u64,
+                                         P, P, i64, i64]
+        L.oracle_quantize_2d.argtypes = [P, ctypes.c_int, i64, i64, i64, P, P, P, P, i64, i64]
+        L.oracle_decode.argtypes = [ctypes.c_uint8, ctypes.c_uint8]
+        L.oracle_decode.restype = ctypes.c_double
+        L.oracle_dequantize.argtypes = [P, P, i64, i64, i64, ctypes.c_int, P, i64, i64]
+        L.oracle_round_bf16.argtypes = [ctypes.c_double]
+        L.oracle_round_bf16.restype = ctypes.c_uint16
+        L.oracle_grouped_gemm.argtypes = [P, P, P, P, P, ctypes.c_int, P, i32, ctypes.c_int,
+                                          i64, i64, i64, ctypes.c_double, P, P, i64, P]
+        _lib = L
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def default_threads() -> int:
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def _split(n, parts):
+    parts = max(1, min(parts, n)) if n > 0 else 1
+    step = (n + parts - 1) // parts if n > 0 else 0
+    return [(i, min(n, i + step)) for i in range(0, n, step)] if n > 0 else []
+
+
+def _run(jobs, threads):
+    if threads <= 1 or len(jobs) <= 1:
+        rc = [j() for j in jobs]
+    else:
+        with ThreadPoolExecutor(max_workers=threads) as ex:
+            rc = list(ex.map(lambda j: j(), jobs))
+    if any(r != 0 for r in rc):
+        raise ValueError("oracle rejected arguments (rc=%s)" % rc)
+
+
+# --------------------------------------------------------------------------
+# Philox and the sign mask (Salmon et al., SC'11)
+# --------------------------------------------------------------------------
+def philox4x32_10(ctr, key):
+    c = np.asarray(ctr, dtype=np.uint32).copy()
+    k = np.asarray(key, dtype=np.uint32).copy()
+    out = np.zeros(4, dtype=np.uint32)
+    lib().oracle_philox4x32_10(_ptr(c), _ptr(k), _ptr(out))
+    return out
+
+
+def rht_sign_mask(seed: int) -> int:
+    return int(lib().oracle_rht_sign_mask(seed))
+
+
+def sr_bits(seed: int, stream: int, index: int) -> int:
+    return int(lib().oracle_sr_bits(seed, stream, index))
+
+
+# --------------------------------------------------------------------------
+# RHT
+# --------------------------------------------------------------------------
+def rht(x, sign_mask: int, inverse: bool = False):
+    """fp32 RHT of every 32-block along the last axis.  x is fp32 or bf16
+    (as uint16 bits) numpy; returns fp32 of the same shape."""
+    x = _widen(x)
+    flat = np.ascontiguousarray(x.reshape(-1, 32))
+    out = np.empty_like(flat)
+    L = lib()
+    for i in range(flat.shape[0]):
+        L.oracle_rht_block(flat[i].ctypes.data, out[i].ctypes.data, sign_mask, int(inverse))
+    return out.reshape(x.shape)
+
+
+def _widen(x):
+    """bf16 bits (uint16) -> fp32 by the 16-bit shift; fp32 unchanged."""
+    if x.dtype == np.uint16:
+        return (x.astype(np.uint32) << 16).view(np.float32)
+    if x.dtype == np.float32:
+        return x
+    raise TypeError("oracle inputs are fp32 or bf16 bits (uint16)")
+
+
+def _dtype_code(x):
+    if x.dtype == np.float32:
+        return 0
+    if x.dtype == np.uint16:
+        return 1
+    raise TypeError("oracle inputs are fp32 or bf16 bits (uint16)")
+
+
+# --------------------------------------------------------------------------
+# Quantizers
+# --------------------------------------------------------------------------
+def padded_total(group_offsets) -> int:
+    off = np.asarray(group_offsets, dtype=np.int64)
+    n = np.diff(off)
+    return int(np.sum((n + 31) // 32 * 32))
+
+
+def quantize_1d(x, block_axis: int = 1, group_offsets=None, kp: int | None = None,
+                use_rht: bool = False, sign_mask: int = 0, rnd: int = RNE,
+                seed: int = 0, stream: int = 0, index_base: int = 0,
+                threads: int | None = None):
+    """1x32 quantization (see mx_oracle.c, oracle_quantize_1d).
+
+    Returns (codes uint8, scales uint8).  For block_axis=0 the outputs are the
+    transposed, per-group padded layout [cols x kp/2] and [cols x kp/32];
+    entries beyond the padded total stay 0 here."""
+    x = np.ascontiguousarray(x)
+    rows, cols = x.shape
+    threads = threads or default_threads()
+    if block_axis == 1:
+        qr, qc = rows, cols
+        off = None
+        ng = 0
+        kp_ = 0
+    else:
+        off = np.ascontiguousarray(
+            np.asarray(group_offsets if group_offsets is not None else [0, rows], dtype=np.int32))
+        ng = len(off) - 1
+        kp_ = padded_total(off) if kp is None else int(kp)
+        qr, qc = cols, kp_
+    codes = np.zeros((qr, qc // 2), dtype=np.uint8)
+    scales = np.zeros((qr, qc // 32), dtype=np.uint8)
+    L = lib()
+    dt = _dtype_code(x)
+
+    def job(a, b):
+        return lambda: L.oracle_quantize_1d(
+            _ptr(x), dt, rows, cols, block_axis, _ptr(off), ng, kp_, int(use_rht),
+            sign_mask, rnd, seed, stream, index_base, _ptr(codes), _ptr(scales), a, b)
+
+    _run([job(a, b) for a, b in _split(qr, threads * 4)], threads)
+    return codes, scales
+
+
+def quantize_2d(w, threads: int | None = None):
+    """32x32 RTNE quantization of w [batch x rows x cols] (or [rows x cols]).
+    Returns (codes, scales, codes_t, scales_t)."""
+    w = np.ascontiguousarray(w)
+    squeeze = w.ndim == 2
+    if squeeze:
+        w = w[None]
+    batch, rows, cols = w.shape
+    codes = np.zeros((batch, rows, cols // 2), dtype=np.uint8)
+    scales = np.zeros((batch, rows // 32, cols // 32), dtype=np.uint8)
+    codes_t = np.zeros((batch, cols, rows // 2), dtype=np.uint8)
+    scales_t = np.zeros((batch, cols // 32, rows // 32), dtype=np.uint8)
+    L = lib()
+    dt = _dtype_code(w)
+    threads = threads or default_threads()
+
+    def job(a, b):
+        return lambda: L.oracle_quantize_2d(_ptr(w), dt, batch, rows, cols, _ptr(codes),
+                                            _ptr(scales), _ptr(codes_t), _ptr(scales_t), a, b)
+
+    _run([job(a, b) for a, b in _split(rows // 32, threads * 4)], threads)
+    if squeeze:
+        return codes[0], scales[0], codes_t[0], scales_t[0]
+    return codes, scales, codes_t, scales_t
+
+
+def dequantize(codes, scales, block_rows: int = 1, threads: int | None = None):
+    """Exact decode to float64: (-1)^s * E2M1[m] * 2^(byte-127)."""
+    codes = np.ascontiguousarray(codes)
+    scales = np.ascontiguousarray(scales)
+    squeeze = codes.ndim == 2
+    if squeeze:
+        codes = codes[None]
+        scales = scales[None]
+    batch, rows, half = codes.shape
+    cols = half * 2
+    y = np.zeros((batch, rows, cols), dtype=np.float64)
+    L = lib()
+    threads = threads or default_threads()
+
+    def job(a, b):
+        return lambda: L.oracle_dequantize(_ptr(codes), _ptr(scales), batch, rows, cols,
+                                           block_rows, _ptr(y), a, b)
+
+    _run([job(a, b) for a, b in _split(rows, threads * 4)], threads)
+    return y[0] if squeeze else y
+
+
+def decode(code: int, scale_byte: int) -> float:
+    return float(lib().oracle_decode(code, scale_byte))
+
+
+def round_bf16_bits(values):
+    L = lib()
+    v = np.asarray(values, dtype=np.float64).ravel()
+    return np.array([L.oracle_round_bf16(float(t)) for t in v], dtype=np.uint16).reshape(
+        np.shape(values))
+
+
+def scale_byte(amax: float) -> int:
+    return int(lib().oracle_scale_byte(float(amax)))
+
+
+def rtne_mag(a: float) -> int:
+    return int(lib().oracle_rtne_mag(float(a)))
+
+
+def sr_mag(a: float, r16: int) -> int:
+    return int(lib().oracle_sr_mag(float(a), int(r16)))
+
+
+# --------------------------------------------------------------------------
+# Grouped GEMM (FP64)
+# --------------------------------------------------------------------------
+def grouped_gemm(a_codes, a_scales, b_codes, b_scales, group_offsets, M, N, K,
+                 a_row_index=None, b_scale_2d=False, group_dim_k=False, alpha=1.0,
+                 rows=None, threads: int | None = None):
+    """FP64 C = alpha * deq(A) deq(B)^T per group (see oracle_grouped_gemm).
+
+    rows: optional list of (group, m) pairs to compute; default all rows.
+    Returns (row_pairs, C[n_rows x N]) where row_pairs is the int array of
+    (group, m) used."""
+    off = np.ascontiguousarray(np.asarray(group_offsets, dtype=np.int32))
+    G = len(off) - 1
+    if rows is None:
+        if not group_dim_k:
+            rows = [(g, m) for g in range(G) for m in range(int(off[g]), int(off[g + 1]))]
+        else:
+            rows = [(g, m) for g in range(G) for m in range(M)]
+    rows = np.asarray(rows, dtype=np.int64).reshape(-1, 2)
+    rg = np.ascontiguousarray(rows[:, 0].astype(np.int32))
+    rm = np.ascontiguousarray(rows[:, 1].astype(np.int64))
+    out = np.zeros((len(rows), N), dtype=np.float64)
+    idx = None if a_row_index is None else np.ascontiguousarray(
+        np.asarray(a_row_index, dtype=np.int32))
+    arrs = [np.ascontiguousarray(a) for a in (a_codes, a_scales, b_codes, b_scales)]
+    L = lib()
+    threads = threads or default_threads()
+
+    def job(a, b):
+        return lambda: L.oracle_grouped_gemm(
+            _ptr(arrs[0]), _ptr(arrs[1]), _ptr(idx), _ptr(arrs[2]), _ptr(arrs[3]),
+            int(bool(b_scale_2d)), _ptr(off), G, int(bool(group_dim_k)), M, N, K, float(alpha),
+            _ptr(rg[a:b]), _ptr(rm[a:b]), b - a, out[a:b].ctypes.data)
+
+    _run([job(a, b) for a, b in _split(len(rows), threads * 4)], threads)
+    return rows, out
