@@ -1,0 +1,168 @@
+/*
+ * mx.h -- C ABI of libmx355, the MXFP4 quantize-then-contract path on AMD
+ * MI355X (gfx950).
+ *
+ * The path is the one the pages train a mixture-of-experts LLM with
+ * ("Training an MoE LLM in MXFP4: How We Closed the Gap to BF16", Abstract):
+ * hybrid 1D/2D block quantization to MXFP4 -- E2M1 elements with one UE8M0
+ * power-of-two scale per block ("AMD's ALTO Gets 4-Bit MoE Training to
+ * Within 0.007 of BF16", section "What ALTO Actually Does") -- an optional
+ * randomized Hadamard transform (RHT) along the reduction dimension,
+ * round-to-nearest-even or stochastic rounding, and the expert GEMM that only
+ * ever sees the quantized operands, accumulated in FP32.
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  The library
+ *     never allocates, never frees, never synchronises and keeps no state; it
+ *     is safe to call from several host threads on different streams.
+ *   - Every call validates its arguments on the host first.  On any status
+ *     other than MX_OK nothing was launched.  Kernels run asynchronously on
+ *     `stream` (0 = the null stream); a device fault surfaces at the caller's
+ *     next synchronisation.
+ *   - Element code nibble (OCP MX v1.0, FP4 E2M1): bit 3 sign, bits 2..1
+ *     exponent, bit 0 mantissa; magnitudes {0, .5, 1, 1.5, 2, 3, 4, 6}.  Two
+ *     codes per byte, the even element in the low nibble.
+ *   - Scale byte (UE8M0): value 2^(byte - 127); 0xFF marks a block whose amax
+ *     is NaN or Inf (after the RHT, when one is applied); such a block's codes
+ *     are all 0.
+ *   - Block scale: X = floor(log2(amax)) - 2, clamped to [-127, 127], so amax
+ *     maps into [4, 8) and values in (6, 8) * 2^X saturate to 6 (OCP MX v1.0).
+ *   - Round to nearest: ties go to the even code; |v| > 6 saturates to 6; the
+ *     sign bit is kept when the magnitude rounds to 0.
+ *   - Stochastic rounding (SR): with v = x / 2^X, lo <= |v| < hi neighbours on
+ *     the E2M1 grid and D = floor(2^16 (|v| - lo) / (hi - lo)), the magnitude
+ *     rounds up iff r16 < D, where r16 is 16 random bits of Philox4x32-10
+ *     (Salmon et al., SC'11): for element index i, counter
+ *     (g lo, g hi, stream_id, 0) with g = i >> 3, key (seed lo, seed hi),
+ *     output word (i & 7) >> 1, its low half for even i, high half for odd i.
+ *     The element index is index_base + the element's position in the
+ *     quantized logical matrix (row-major, blocks along its last axis), so a
+ *     tensor quantized in row slices, each with its own index_base, gives
+ *     bit-identical results to the whole tensor.
+ *   - RHT of a 32-block: y = c * H32 * (s .* x), H32 the Sylvester Hadamard
+ *     matrix (H[i][j] = (-1)^popcount(i & j)), s_j = -1 where bit j of
+ *     sign_mask is set, c = fp32(2^-2.5); computed in fp32 as butterfly stages
+ *     h = 1, 2, 4, 8, 16 (pairs (i, i+h) -> (a+b, a-b)) then one multiply by
+ *     c.  The stage order is part of the contract.  Inverse: butterflies,
+ *     times c, then the sign flips.
+ */
+#ifndef MX355_MX_H
+#define MX355_MX_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MX_OK = 0,
+    MX_ERR_NULL = 1,         /* a required pointer is NULL                  */
+    MX_ERR_SHAPE = 2,        /* a size is negative / not a multiple of 32 / inconsistent */
+    MX_ERR_ALIGN = 3,        /* a pointer is not 16-byte aligned             */
+    MX_ERR_DTYPE = 4,        /* unsupported element type                     */
+    MX_ERR_UNSUPPORTED = 5,  /* a valid but unimplemented option combination */
+    MX_ERR_LAUNCH = 6        /* the HIP runtime rejected a kernel launch     */
+} mx_status;
+
+typedef enum { MX_F32 = 0, MX_BF16 = 1 } mx_dtype;
+typedef enum { MX_RNE = 0, MX_SR = 1 } mx_round;
+
+/* HIP stream handle (hipStream_t) passed as an opaque pointer. */
+typedef void* mx_stream;
+
+/* Library version (monotone integer). */
+int mx_version(void);
+
+/* Human-readable name of a status code (static storage). */
+const char* mx_status_str(mx_status s);
+
+/* The RHT sign mask for a seed: word 0 of Philox4x32-10 at counter 0 under
+ * key (seed lo, seed hi).  Host function; no device work. */
+uint32_t mx_rht_sign_mask(uint64_t seed);
+
+/* Randomized Hadamard transform of every 32-block along the last axis.
+ * x: [rows x cols] row-major, type xt (fp32 or bf16); y: [rows x cols] fp32.
+ * cols % 32 == 0; rows >= 0 (0 launches nothing).  x and y may not overlap.
+ * inverse != 0 applies the inverse transform.
+ * Pages: the RHT the recipe layers on the quantizer (Abstract of "Training an
+ * MoE LLM in MXFP4"). */
+mx_status mx_rht(const void* x, mx_dtype xt, float* y, int64_t rows, int64_t cols,
+                 uint32_t sign_mask, int inverse, mx_stream stream);
+
+/* 1x32 MXFP4 quantization (the "1D" half of the hybrid scheme, used for
+ * activations and gradients).
+ *
+ * block_axis = 1 (row-wise): x [rows x cols], cols % 32 == 0.  Blocks of 32
+ *   run along cols.  codes [rows x cols/2], scales [rows x cols/32].
+ *   group_offsets must be NULL, num_groups 0, kp 0.
+ * block_axis = 0 (column-wise, grouped): the rows of x (tokens) are split
+ *   into num_groups groups by group_offsets (DEVICE int32[num_groups+1],
+ *   non-decreasing, [0] = 0, [num_groups] = rows; produced on the device by
+ *   routing).  Each group is zero-padded to a multiple of 32 tokens and the
+ *   result is written transposed, so the token axis is contiguous:
+ *   Q [cols x kp] with Q[c][P_g + r] = x[off_g + r][c], P_g the padded start
+ *   of group g.  codes [cols x kp/2], scales [cols x kp/32].  kp (a multiple
+ *   of 32) is the capacity of that axis; the caller guarantees
+ *   kp >= sum_g ceil32(n_g) (rows + 31 * num_groups always suffices).
+ *   Positions beyond the padded total are not written.
+ * use_rht != 0 applies the RHT (sign_mask) to each block before quantizing.
+ * rnd: MX_RNE or MX_SR (seed, stream_id, index_base as above; index_base %
+ *   32 == 0).
+ * x may be fp32 or bf16; pointers 16-byte aligned except scales (any).
+ * Pages: hybrid 1D/2D quantization, RHT and SR (Abstract of "Training an MoE
+ * LLM in MXFP4"); E2M1 + UE8M0 ("What ALTO Actually Does"). */
+mx_status mx_quantize_1d(const void* x, mx_dtype xt, int64_t rows, int64_t cols,
+                         int block_axis, const int32_t* group_offsets, int32_t num_groups,
+                         int64_t kp, int use_rht, uint32_t sign_mask, mx_round rnd,
+                         uint64_t seed, uint32_t stream_id, uint64_t index_base,
+                         uint8_t* codes, uint8_t* scales, mx_stream stream);
+
+/* 32x32 MXFP4 quantization, round to nearest even (the "2D" half of the
+ * hybrid scheme, used for weights).  w: batch x [rows x cols], rows % 32 ==
+ * 0, cols % 32 == 0.  One pass writes the as-given layout (codes
+ * [batch x rows x cols/2], scales [batch x rows/32 x cols/32]) and/or the
+ * transposed layout (codes_t [batch x cols x rows/2], scales_t
+ * [batch x cols/32 x rows/32]); a 32x32 block has the same scale and codes in
+ * both, so the transposed pair is exactly the quantization of w^T.  Either
+ * pair may be NULL (not both).  Pages: "What ALTO Actually Does" (UE8M0 per
+ * block), Abstract (hybrid 1D/2D). */
+mx_status mx_quantize_2d(const void* w, mx_dtype wt, int64_t batch, int64_t rows, int64_t cols,
+                         uint8_t* codes, uint8_t* scales, uint8_t* codes_t, uint8_t* scales_t,
+                         mx_stream stream);
+
+/* Exact decode: y = (-1)^s * E2M1[m] * 2^(byte - 127).
+ * codes batch x [rows x cols/2]; block_rows = 1 (scales [rows x cols/32]) or
+ * 32 (scales [rows/32 x cols/32], rows % 32 == 0); y batch x [rows x cols],
+ * yt fp32 or bf16 (every decoded value is exact in both, except 6*2^(>=127)
+ * which overflows to Inf).  cols % 32 == 0. */
+mx_status mx_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t batch, int64_t rows,
+                        int64_t cols, int block_rows, void* y, mx_dtype yt, mx_stream stream);
+
+/* Grouped MXFP4 GEMM with FP32 accumulation: per group,
+ *   C = alpha * deq(A) . deq(B)^T,
+ * both operands K-contiguous (codes [. x K/2], scales [. x K/32]).
+ * The GEMM only ever sees the quantized operands ("What ALTO Actually Does").
+ *
+ * group_dim_k = 0 (forward / data gradient): groups split the M rows of C by
+ *   group_offsets (DEVICE int32[num_groups+1], [0] = 0, [num_groups] = M).
+ *   Row m of group g reads A row a_row_index[m] (DEVICE int32[M]; NULL = m)
+ *   and multiplies B_g = b_codes + g*N*K/2 ([N x K]); b_scale_2d selects 2D
+ *   scales [N/32 x K/32] per group (else 1D [N x K/32]).  C [M x N].
+ * group_dim_k = 1 (weight gradient): groups split K by group_offsets (DEVICE,
+ *   multiples of 32, [num_groups] <= K); A [M x K], B [N x K], 1D scales;
+ *   C [num_groups x M x N]; a group with an empty K range writes zeros.
+ * K % 32 == 0, N % 32 == 0, M >= 0; ct = MX_BF16 (round to nearest even) or
+ * MX_F32.  Code and C pointers 16-byte aligned. */
+mx_status mx_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
+                          const int32_t* a_row_index,
+                          const uint8_t* b_codes, const uint8_t* b_scales, int b_scale_2d,
+                          const int32_t* group_offsets, int32_t num_groups, int group_dim_k,
+                          int64_t M, int64_t N, int64_t K, float alpha,
+                          void* c, mx_dtype ct, mx_stream stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MX355_MX_H */

@@ -1,0 +1,598 @@
+// mx_quant.hip -- RHT, 1x32 / 32x32 MXFP4 quantization and dequantization
+// kernels for gfx950, and their C-ABI entry points (include/mx.h).
+//
+// The kernels are HBM-bound streams.  Lane mappings are chosen so that every
+// global load and store of a wave is a contiguous run:
+//   row-wise 1D / RHT: a quad of lanes owns one 32-block (8 elements per
+//     lane, one 16-byte bf16 load), a wave covers 16 consecutive blocks; the
+//     RHT's stages 8 and 16 cross lanes through DPP quad permutes; the lane's
+//     8 elements take exactly one Philox call when rounding stochastically.
+//   column-wise 1D: a lane owns two adjacent columns and 32 consecutive
+//     tokens; a wave reads 256 contiguous bytes of each token row, the RHT
+//     and the block amax along tokens stay in-lane, and the lane writes the
+//     two 16-byte code runs of the transposed (token-contiguous) layout.
+//   2D: a workgroup owns a 32-row strip of 8 tiles; lanes read 64 contiguous
+//     bytes of one tile row, the tile amax is reduced across lanes and waves,
+//     and the transposed codes are regrouped through LDS.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/mx.h"
+#include "mx_device.h"
+
+using namespace mx;
+
+// ===========================================================================
+// Row-wise 1x32 quantization (optionally with the RHT).
+// ===========================================================================
+constexpr int ROW_UNROLL = 4;   // blocks per quad per loop trip (loads in flight)
+
+template <bool BF16, bool RHT, bool SR>
+__global__ __launch_bounds__(256) void q1d_row_kernel(const void* __restrict__ x, int64_t nblocks,
+                                                      uint32_t mask, uint32_t k0, uint32_t k1,
+                                                      uint32_t stream_id, uint64_t index_base,
+                                                      uint8_t* __restrict__ codes,
+                                                      uint8_t* __restrict__ scales) {
+    const int lane = threadIdx.x & 63;
+    const int q = lane & 3;
+    const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x >> 6);
+    // per-lane sign words for the RHT: lane q holds block elements 8q..8q+7
+    const uint32_t m8 = (mask >> (8 * q)) & 0xFFu;
+    uint32_t sgn[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sgn[e] = ((m8 >> e) & 1u) << 31;
+
+    for (int64_t base = wave * 16 * ROW_UNROLL; base < nblocks; base += nwaves * 16 * ROW_UNROLL) {
+        float v[ROW_UNROLL][8];
+#pragma unroll
+        for (int u = 0; u < ROW_UNROLL; ++u) {
+            const int64_t blk = base + u * 16 + (lane >> 2);
+            if (blk < nblocks) {
+                if (BF16) {
+                    const uint4 w = *((const uint4*)((const uint8_t*)x + blk * 64) + q);
+                    v[u][0] = bf16lo(w.x); v[u][1] = bf16hi(w.x);
+                    v[u][2] = bf16lo(w.y); v[u][3] = bf16hi(w.y);
+                    v[u][4] = bf16lo(w.z); v[u][5] = bf16hi(w.z);
+                    v[u][6] = bf16lo(w.w); v[u][7] = bf16hi(w.w);
+                } else {
+                    const uint4* p = (const uint4*)((const uint8_t*)x + blk * 128) + 2 * q;
+                    const uint4 a = p[0], b = p[1];
+                    v[u][0] = __uint_as_float(a.x); v[u][1] = __uint_as_float(a.y);
+                    v[u][2] = __uint_as_float(a.z); v[u][3] = __uint_as_float(a.w);
+                    v[u][4] = __uint_as_float(b.x); v[u][5] = __uint_as_float(b.y);
+                    v[u][6] = __uint_as_float(b.z); v[u][7] = __uint_as_float(b.w);
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[u][e] = 0.0f;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < ROW_UNROLL; ++u) {
+            const int64_t blk = base + u * 16 + (lane >> 2);
+            float* t = v[u];
+            if (RHT) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) t[e] = __uint_as_float(__float_as_uint(t[e]) ^ sgn[e]);
+                rht32_quad(t, q);
+            }
+            uint32_t am = 0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) am = max(am, __float_as_uint(t[e]) & 0x7FFFFFFFu);
+            am = quad_max_u(am);
+            const uint32_t byte = scale_byte_from_amax_bits(am);
+            const float sc = scale_operand(byte);
+            uint32_t packed;
+            if (SR) {
+                const uint64_t g = (index_base + (uint64_t)blk * 32 + (uint64_t)q * 8) >> 3;
+                const u32x4 r = philox4x32_10((uint32_t)g, (uint32_t)(g >> 32), stream_id, 0u, k0, k1);
+                packed = cvt8_sr(t, sc, r);
+            } else {
+                packed = cvt8_rne(t, sc);
+            }
+            if (byte == 0xFFu) packed = 0;   // non-finite block: codes are 0
+            if (blk < nblocks) {
+                *((uint32_t*)(codes + blk * 16) + q) = packed;
+                if (q == 0) scales[blk] = (uint8_t)byte;
+            }
+        }
+    }
+}
+
+// ===========================================================================
+// Stand-alone RHT (fp32 output), same quad mapping.
+// ===========================================================================
+template <bool BF16, bool INV>
+__global__ __launch_bounds__(256) void rht_kernel(const void* __restrict__ x, int64_t nblocks, uint32_t mask,
+                                                  float* __restrict__ y) {
+    const int lane = threadIdx.x & 63;
+    const int q = lane & 3;
+    const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x >> 6);
+    const uint32_t m8 = (mask >> (8 * q)) & 0xFFu;
+    for (int64_t base = wave * 16; base < nblocks; base += nwaves * 16) {
+        const int64_t blk = base + (lane >> 2);
+        float t[8];
+        if (blk < nblocks) {
+            if (BF16) {
+                const uint4 w = *((const uint4*)((const uint8_t*)x + blk * 64) + q);
+                t[0] = bf16lo(w.x); t[1] = bf16hi(w.x); t[2] = bf16lo(w.y); t[3] = bf16hi(w.y);
+                t[4] = bf16lo(w.z); t[5] = bf16hi(w.z); t[6] = bf16lo(w.w); t[7] = bf16hi(w.w);
+            } else {
+                const uint4* p = (const uint4*)((const uint8_t*)x + blk * 128) + 2 * q;
+                const uint4 a = p[0], b = p[1];
+                t[0] = __uint_as_float(a.x); t[1] = __uint_as_float(a.y);
+                t[2] = __uint_as_float(a.z); t[3] = __uint_as_float(a.w);
+                t[4] = __uint_as_float(b.x); t[5] = __uint_as_float(b.y);
+                t[6] = __uint_as_float(b.z); t[7] = __uint_as_float(b.w);
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) t[e] = 0.0f;
+        }
+        if (!INV) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) t[e] = __uint_as_float(__float_as_uint(t[e]) ^ (((m8 >> e) & 1u) << 31));
+        }
+        rht32_quad(t, q);
+        if (INV) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) t[e] = __uint_as_float(__float_as_uint(t[e]) ^ (((m8 >> e) & 1u) << 31));
+        }
+        if (blk < nblocks) {
+            uint4* o = (uint4*)(y + blk * 32) + 2 * q;
+            o[0] = make_uint4(__float_as_uint(t[0]), __float_as_uint(t[1]), __float_as_uint(t[2]), __float_as_uint(t[3]));
+            o[1] = make_uint4(__float_as_uint(t[4]), __float_as_uint(t[5]), __float_as_uint(t[6]), __float_as_uint(t[7]));
+        }
+    }
+}
+
+// ===========================================================================
+// Column-wise, grouped 1x32 quantization (blocks run down the token axis of
+// one group; output transposed so tokens are contiguous).
+// ===========================================================================
+constexpr int COL_MAX_GROUPS = 4096;
+
+template <bool BF16, bool RHT, bool SR>
+__global__ __launch_bounds__(256) void q1d_col_kernel(const void* __restrict__ x, int64_t rows, int64_t cols,
+                                                      const int32_t* __restrict__ off, int num_groups,
+                                                      int64_t kp, int64_t col_pairs_per_row,
+                                                      uint32_t mask, uint32_t k0, uint32_t k1,
+                                                      uint32_t stream_id, uint64_t index_base,
+                                                      uint8_t* __restrict__ codes,
+                                                      uint8_t* __restrict__ scales) {
+    // padded start (in 32-token blocks) of every group, and its token offset
+    __shared__ int32_t pstart[COL_MAX_GROUPS + 1];
+    for (int g = threadIdx.x; g <= num_groups; g += blockDim.x) pstart[g] = 0;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int32_t acc = 0;
+        for (int g = 0; g < num_groups; ++g) {
+            pstart[g] = acc;
+            const int32_t n = off[g + 1] - off[g];
+            acc += (n + 31) >> 5;
+        }
+        pstart[num_groups] = acc;
+    }
+    __syncthreads();
+    const int64_t nblk_total = (int64_t)pstart[num_groups];
+    const int64_t kp_blocks = kp >> 5;
+
+    const int64_t items = col_pairs_per_row * kp_blocks;   // (padded block, column pair)
+    for (int64_t it = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; it < items;
+         it += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t pb = it / col_pairs_per_row;
+        const int64_t cp = it - pb * col_pairs_per_row;
+        if (pb >= nblk_total) continue;
+        // group of padded block pb (binary search over pstart)
+        int lo = 0, hi = num_groups - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (pstart[mid] <= pb) lo = mid; else hi = mid - 1;
+        }
+        // skip empty groups that share the same pstart
+        const int g = lo;
+        const int64_t tok0 = (int64_t)off[g] + (pb - pstart[g]) * 32;
+        const int64_t tok_end = off[g + 1];
+        const int64_t c0 = cp * 2;
+        const bool two = (c0 + 1) < cols;
+        const bool paired = two && ((cols & 1) == 0);   // pair loads stay aligned
+        float a[32], b[32];
+#pragma unroll
+        for (int j = 0; j < 32; ++j) {
+            const int64_t r = tok0 + j;
+            if (r < tok_end) {
+                if (BF16) {
+                    const uint16_t* row = (const uint16_t*)x + r * cols + c0;
+                    if (paired) {
+                        const uint32_t w = *(const uint32_t*)row;
+                        a[j] = bf16lo(w);
+                        b[j] = bf16hi(w);
+                    } else {
+                        a[j] = __uint_as_float((uint32_t)row[0] << 16);
+                        b[j] = two ? __uint_as_float((uint32_t)row[1] << 16) : 0.0f;
+                    }
+                } else {
+                    const float* row = (const float*)x + r * cols + c0;
+                    if (paired) {
+                        const float2 w = *(const float2*)row;
+                        a[j] = w.x;
+                        b[j] = w.y;
+                    } else {
+                        a[j] = row[0];
+                        b[j] = two ? row[1] : 0.0f;
+                    }
+                }
+            } else {
+                a[j] = 0.0f;
+                b[j] = 0.0f;
+            }
+        }
+#pragma unroll
+        for (int side = 0; side < 2; ++side) {
+            if (side == 1 && !two) break;
+            float* t = side ? b : a;
+            const int64_t c = c0 + side;
+            if (RHT) {
+#pragma unroll
+                for (int j = 0; j < 32; ++j) t[j] = __uint_as_float(__float_as_uint(t[j]) ^ (((mask >> j) & 1u) << 31));
+                fwht_inlane<32>(t);
+                const float cc = __uint_as_float(0x3E3504F3u);
+#pragma unroll
+                for (int j = 0; j < 32; ++j) t[j] = t[j] * cc;
+            }
+            uint32_t am = 0;
+#pragma unroll
+            for (int j = 0; j < 32; ++j) am = max(am, __float_as_uint(t[j]) & 0x7FFFFFFFu);
+            const uint32_t byte = scale_byte_from_amax_bits(am);
+            const float sc = scale_operand(byte);
+            uint32_t w[4];
+            const uint64_t ebase = index_base + (uint64_t)c * (uint64_t)kp + (uint64_t)pb * 32;
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+                if (SR) {
+                    const uint64_t g8 = (ebase + qq * 8) >> 3;
+                    const u32x4 r = philox4x32_10((uint32_t)g8, (uint32_t)(g8 >> 32), stream_id, 0u, k0, k1);
+                    w[qq] = cvt8_sr(t + 8 * qq, sc, r);
+                } else {
+                    w[qq] = cvt8_rne(t + 8 * qq, sc);
+                }
+            }
+            if (byte == 0xFFu) w[0] = w[1] = w[2] = w[3] = 0;   // non-finite block: codes are 0
+            *(uint4*)(codes + c * (kp >> 1) + pb * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+            scales[c * kp_blocks + pb] = (uint8_t)byte;
+        }
+    }
+}
+
+// ===========================================================================
+// 32x32 quantization (RTNE), both layouts in one pass.
+// Workgroup: 256 threads, a strip of 32 rows x 8 tiles (256 columns).
+// Thread t: strip row r = t / 8, tile j = t % 8, 32 contiguous elements.
+// ===========================================================================
+template <bool BF16>
+__global__ __launch_bounds__(256) void q2d_kernel(const void* __restrict__ w, int64_t rows, int64_t cols,
+                                                  int64_t strips_per_row, int64_t nstrips,
+                                                  uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+                                                  uint8_t* __restrict__ codes_t, uint8_t* __restrict__ scales_t) {
+    __shared__ uint32_t wave_amax[4][8];
+    __shared__ uint32_t tile_scale[8];
+    __shared__ uint4 tcodes[8][32];   // [tile][row] 16 bytes of row codes
+    const int t = threadIdx.x;
+    const int r = t >> 3;          // 0..31
+    const int j = t & 7;           // tile within the strip
+    const int lane = t & 63;
+    const int wv = t >> 6;
+    const int64_t tiles_per_row = cols >> 5;
+    const int64_t row_tiles = rows >> 5;
+    for (int64_t s = blockIdx.x; s < nstrips; s += gridDim.x) {
+        const int64_t bt_tr = s / strips_per_row;         // batch * row_tiles + tile row
+        const int64_t sc_ = s - bt_tr * strips_per_row;   // strip along columns
+        const int64_t bt = bt_tr / row_tiles;
+        const int64_t tr = bt_tr - bt * row_tiles;
+        const int64_t tile = sc_ * 8 + j;
+        const bool valid = tile < tiles_per_row;
+        const int64_t grow = bt * rows + tr * 32 + r;      // global row in the batch stack
+        float v[32];
+        if (valid) {
+            if (BF16) {
+                const uint4* p = (const uint4*)((const uint16_t*)w + grow * cols + tile * 32);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const uint4 q = p[k];
+                    v[8 * k + 0] = bf16lo(q.x); v[8 * k + 1] = bf16hi(q.x);
+                    v[8 * k + 2] = bf16lo(q.y); v[8 * k + 3] = bf16hi(q.y);
+                    v[8 * k + 4] = bf16lo(q.z); v[8 * k + 5] = bf16hi(q.z);
+                    v[8 * k + 6] = bf16lo(q.w); v[8 * k + 7] = bf16hi(q.w);
+                }
+            } else {
+                const uint4* p = (const uint4*)((const float*)w + grow * cols + tile * 32);
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const uint4 q = p[k];
+                    v[4 * k + 0] = __uint_as_float(q.x); v[4 * k + 1] = __uint_as_float(q.y);
+                    v[4 * k + 2] = __uint_as_float(q.z); v[4 * k + 3] = __uint_as_float(q.w);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < 32; ++k) v[k] = 0.0f;
+        }
+        uint32_t am = 0;
+#pragma unroll
+        for (int k = 0; k < 32; ++k) am = max(am, __float_as_uint(v[k]) & 0x7FFFFFFFu);
+        // lanes with the same j within the wave: xor 8, 16, 32
+        am = max(am, (uint32_t)__shfl_xor((int)am, 8));
+        am = max(am, (uint32_t)__shfl_xor((int)am, 16));
+        am = max(am, (uint32_t)__shfl_xor((int)am, 32));
+        if (lane < 8) wave_amax[wv][lane] = am;
+        __syncthreads();
+        if (t < 8) {
+            const uint32_t m = max(max(wave_amax[0][t], wave_amax[1][t]), max(wave_amax[2][t], wave_amax[3][t]));
+            tile_scale[t] = scale_byte_from_amax_bits(m);
+        }
+        __syncthreads();
+        const uint32_t byte = tile_scale[j];
+        const float sc = scale_operand(byte);
+        uint32_t cw[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) cw[k] = byte == 0xFFu ? 0u : cvt8_rne(v + 8 * k, sc);
+        if (valid && codes) *(uint4*)(codes + grow * (cols >> 1) + tile * 16) = make_uint4(cw[0], cw[1], cw[2], cw[3]);
+        if (valid && r == 0) {
+            if (scales) scales[(bt * row_tiles + tr) * tiles_per_row + tile] = (uint8_t)byte;
+            if (scales_t) scales_t[(bt * tiles_per_row + tile) * row_tiles + tr] = (uint8_t)byte;
+        }
+        if (codes_t) {
+            tcodes[j][r] = make_uint4(cw[0], cw[1], cw[2], cw[3]);
+            __syncthreads();
+            // thread t: tile jj = t / 32, column cc = t % 32 of that tile
+            const int jj = t >> 5;
+            const int cc = t & 31;
+            const int64_t tile2 = sc_ * 8 + jj;
+            if (tile2 < tiles_per_row) {
+                const int word = cc >> 3;            // dword holding column cc in a row
+                const int sh = (cc & 7) * 4;
+                uint32_t o[4] = {0, 0, 0, 0};
+#pragma unroll
+                for (int rr = 0; rr < 32; ++rr) {
+                    const uint4 q = tcodes[jj][rr];
+                    const uint32_t wd = word == 0 ? q.x : word == 1 ? q.y : word == 2 ? q.z : q.w;
+                    const uint32_t nib = (wd >> sh) & 0xFu;
+                    o[rr >> 3] |= nib << ((rr & 7) * 4);
+                }
+                const int64_t col = tile2 * 32 + cc;
+                *(uint4*)(codes_t + (bt * cols + col) * (rows >> 1) + tr * 16) = make_uint4(o[0], o[1], o[2], o[3]);
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// ===========================================================================
+// Dequantize: a lane decodes 8 elements (one dword of codes).
+// ===========================================================================
+template <bool OUT_BF16, int BLOCK_ROWS>
+__global__ __launch_bounds__(256) void deq_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
+                                                  int64_t rows, int64_t cols, int64_t nunits,
+                                                  void* __restrict__ y) {
+    const int64_t units_per_row = cols >> 3;
+    const int64_t srows = rows / BLOCK_ROWS;
+    for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < nunits;
+         u += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t grow = u / units_per_row;                 // global row over the batch
+        const int64_t cu = u - grow * units_per_row;
+        const int64_t bt = grow / rows;
+        const int64_t r = grow - bt * rows;
+        const uint32_t cw = *((const uint32_t*)codes + u);
+        const uint8_t sb = scales[(bt * srows + r / BLOCK_ROWS) * (cols >> 5) + (cu >> 2)];
+        const float sc = scale_operand(sb);
+        float f[8];
+        decode8(cw, sc, f);
+        if (sb == 0xFF) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) f[k] = __uint_as_float(0x7FC00000u);
+        }
+        if (OUT_BF16) {
+            // every decoded value is exact in bf16: the high half is the value
+            uint32_t o[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                o[k] = (__float_as_uint(f[2 * k]) >> 16) | (__float_as_uint(f[2 * k + 1]) & 0xFFFF0000u);
+            *((uint4*)y + u) = make_uint4(o[0], o[1], o[2], o[3]);
+        } else {
+            uint4* p = (uint4*)y + 2 * u;
+            p[0] = make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]), __float_as_uint(f[3]));
+            p[1] = make_uint4(__float_as_uint(f[4]), __float_as_uint(f[5]), __float_as_uint(f[6]), __float_as_uint(f[7]));
+        }
+    }
+}
+
+// ===========================================================================
+// Host side
+// ===========================================================================
+namespace {
+
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+inline int grid_for(int64_t work_items, int items_per_block) {
+    int64_t g = (work_items + items_per_block - 1) / items_per_block;
+    const int64_t cap = 256 * 32;   // enough resident waves; loops cover the rest
+    if (g > cap) g = cap;
+    if (g < 1) g = 1;
+    return (int)g;
+}
+
+inline mx_status launched() {
+    return hipGetLastError() == hipSuccess ? MX_OK : MX_ERR_LAUNCH;
+}
+
+uint32_t host_philox_word0(uint32_t k0, uint32_t k1) {
+    uint32_t c0 = 0, c1 = 0, c2 = 0, c3 = 0;
+    for (int round = 0; round < 10; ++round) {
+        const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+        const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+        const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+        const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+        c1 = (uint32_t)p1;
+        c3 = (uint32_t)p0;
+        c0 = n0;
+        c2 = n2;
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
+    }
+    return c0;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mx_version(void) { return 1; }
+
+const char* mx_status_str(mx_status s) {
+    switch (s) {
+        case MX_OK: return "MX_OK";
+        case MX_ERR_NULL: return "MX_ERR_NULL";
+        case MX_ERR_SHAPE: return "MX_ERR_SHAPE";
+        case MX_ERR_ALIGN: return "MX_ERR_ALIGN";
+        case MX_ERR_DTYPE: return "MX_ERR_DTYPE";
+        case MX_ERR_UNSUPPORTED: return "MX_ERR_UNSUPPORTED";
+        case MX_ERR_LAUNCH: return "MX_ERR_LAUNCH";
+    }
+    return "MX_ERR_UNKNOWN";
+}
+
+uint32_t mx_rht_sign_mask(uint64_t seed) { return host_philox_word0((uint32_t)seed, (uint32_t)(seed >> 32)); }
+
+mx_status mx_rht(const void* x, mx_dtype xt, float* y, int64_t rows, int64_t cols, uint32_t sign_mask,
+                 int inverse, mx_stream stream) {
+    if (rows < 0 || cols <= 0 || cols % 32) return MX_ERR_SHAPE;
+    if (xt != MX_F32 && xt != MX_BF16) return MX_ERR_DTYPE;
+    if (rows == 0) return MX_OK;
+    if (!x || !y) return MX_ERR_NULL;
+    if (!aligned16(x) || !aligned16(y)) return MX_ERR_ALIGN;
+    const int64_t nblocks = rows * (cols / 32);
+    const int grid = grid_for(nblocks, 4 * 16);
+    hipStream_t s = (hipStream_t)stream;
+    (void)hipGetLastError();
+    if (xt == MX_BF16) {
+        if (inverse) hipLaunchKernelGGL((rht_kernel<true, true>), dim3(grid), dim3(256), 0, s, x, nblocks, sign_mask, y);
+        else hipLaunchKernelGGL((rht_kernel<true, false>), dim3(grid), dim3(256), 0, s, x, nblocks, sign_mask, y);
+    } else {
+        if (inverse) hipLaunchKernelGGL((rht_kernel<false, true>), dim3(grid), dim3(256), 0, s, x, nblocks, sign_mask, y);
+        else hipLaunchKernelGGL((rht_kernel<false, false>), dim3(grid), dim3(256), 0, s, x, nblocks, sign_mask, y);
+    }
+    return launched();
+}
+
+#define MX_DISPATCH3(KERNEL, B, R, S, GRID, STREAM, ...)                                              \
+    do {                                                                                            \
+        if (B) {                                                                                    \
+            if (R) {                                                                                \
+                if (S) hipLaunchKernelGGL((KERNEL<true, true, true>), GRID, dim3(256), 0, STREAM, __VA_ARGS__);   \
+                else hipLaunchKernelGGL((KERNEL<true, true, false>), GRID, dim3(256), 0, STREAM, __VA_ARGS__);    \
+            } else {                                                                                \
+                if (S) hipLaunchKernelGGL((KERNEL<true, false, true>), GRID, dim3(256), 0, STREAM, __VA_ARGS__);  \
+                else hipLaunchKernelGGL((KERNEL<true, false, false>), GRID, dim3(256), 0, STREAM, __VA_ARGS__);   \
+            }                                                                                       \
+        } else {                                                                                    \
+            if (R) {                                                                                \
+                if (S) hipLaunchKernelGGL((KERNEL<false, true, true>), GRID, dim3(256), 0, STREAM, __VA_ARGS__);  \
+                else hipLaunchKernelGGL((KERNEL<false, true, false>), GRID, dim3(256), 0, STREAM, __VA_ARGS__);   \
+            } else {                                                                                \
+                if (S) hipLaunchKernelGGL((KERNEL<false, false, true>), GRID, dim3(256), 0, STREAM, __VA_ARGS__); \
+                else hipLaunchKernelGGL((KERNEL<false, false, false>), GRID, dim3(256), 0, STREAM, __VA_ARGS__);  \
+            }                                                                                       \
+        }                                                                                           \
+    } while (0)
+
+mx_status mx_quantize_1d(const void* x, mx_dtype xt, int64_t rows, int64_t cols, int block_axis,
+                         const int32_t* group_offsets, int32_t num_groups, int64_t kp, int use_rht,
+                         uint32_t sign_mask, mx_round rnd, uint64_t seed, uint32_t stream_id,
+                         uint64_t index_base, uint8_t* codes, uint8_t* scales, mx_stream stream) {
+    if (xt != MX_F32 && xt != MX_BF16) return MX_ERR_DTYPE;
+    if (rnd != MX_RNE && rnd != MX_SR) return MX_ERR_UNSUPPORTED;
+    if (rows < 0 || cols <= 0) return MX_ERR_SHAPE;
+    if (index_base % 32) return MX_ERR_SHAPE;
+    const bool bf = xt == MX_BF16, rh = use_rht != 0, sr = rnd == MX_SR;
+    const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+    hipStream_t s = (hipStream_t)stream;
+    if (block_axis == 1) {
+        if (cols % 32) return MX_ERR_SHAPE;
+        if (group_offsets || num_groups || kp) return MX_ERR_SHAPE;
+        if (rows == 0) return MX_OK;
+        if (!x || !codes || !scales) return MX_ERR_NULL;
+        if (!aligned16(x) || !aligned16(codes)) return MX_ERR_ALIGN;
+        const int64_t nblocks = rows * (cols / 32);
+        const int grid = grid_for(nblocks, 4 * 16 * ROW_UNROLL);
+        (void)hipGetLastError();
+        MX_DISPATCH3(q1d_row_kernel, bf, rh, sr, dim3(grid), s, x, nblocks, sign_mask, k0, k1, stream_id,
+                     index_base, codes, scales);
+        return launched();
+    }
+    if (block_axis != 0) return MX_ERR_SHAPE;
+    if (num_groups < 1 || num_groups > COL_MAX_GROUPS) return MX_ERR_SHAPE;
+    if (kp < 0 || kp % 32) return MX_ERR_SHAPE;
+    if (!group_offsets) return MX_ERR_NULL;
+    if (kp == 0 || rows == 0) return MX_OK;
+    if (!x || !codes || !scales) return MX_ERR_NULL;
+    if (!aligned16(x) || !aligned16(codes)) return MX_ERR_ALIGN;
+    const int64_t cpairs = (cols + 1) / 2;
+    const int64_t items = cpairs * (kp / 32);
+    const int grid = grid_for(items, 256);
+    (void)hipGetLastError();
+    MX_DISPATCH3(q1d_col_kernel, bf, rh, sr, dim3(grid), s, x, rows, cols, group_offsets, (int)num_groups, kp,
+                 cpairs, sign_mask, k0, k1, stream_id, index_base, codes, scales);
+    return launched();
+}
+
+mx_status mx_quantize_2d(const void* w, mx_dtype wt, int64_t batch, int64_t rows, int64_t cols, uint8_t* codes,
+                         uint8_t* scales, uint8_t* codes_t, uint8_t* scales_t, mx_stream stream) {
+    if (wt != MX_F32 && wt != MX_BF16) return MX_ERR_DTYPE;
+    if (batch < 0 || rows < 0 || cols < 0 || rows % 32 || cols % 32) return MX_ERR_SHAPE;
+    if ((codes == nullptr) != (scales == nullptr)) return MX_ERR_NULL;
+    if ((codes_t == nullptr) != (scales_t == nullptr)) return MX_ERR_NULL;
+    if (!codes && !codes_t) return MX_ERR_NULL;
+    if (batch == 0 || rows == 0 || cols == 0) return MX_OK;
+    if (!w) return MX_ERR_NULL;
+    if (!aligned16(w) || (codes && !aligned16(codes)) || (codes_t && !aligned16(codes_t))) return MX_ERR_ALIGN;
+    const int64_t strips_per_row = (cols / 32 + 7) / 8;
+    const int64_t nstrips = batch * (rows / 32) * strips_per_row;
+    const int grid = grid_for(nstrips, 1);
+    hipStream_t s = (hipStream_t)stream;
+    (void)hipGetLastError();
+    if (wt == MX_BF16)
+        hipLaunchKernelGGL((q2d_kernel<true>), dim3(grid), dim3(256), 0, s, w, rows, cols, strips_per_row, nstrips,
+                           codes, scales, codes_t, scales_t);
+    else
+        hipLaunchKernelGGL((q2d_kernel<false>), dim3(grid), dim3(256), 0, s, w, rows, cols, strips_per_row, nstrips,
+                           codes, scales, codes_t, scales_t);
+    return launched();
+}
+
+mx_status mx_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t batch, int64_t rows, int64_t cols,
+                        int block_rows, void* y, mx_dtype yt, mx_stream stream) {
+    if (yt != MX_F32 && yt != MX_BF16) return MX_ERR_DTYPE;
+    if (batch < 0 || rows < 0 || cols < 0 || cols % 32) return MX_ERR_SHAPE;
+    if (block_rows != 1 && block_rows != 32) return MX_ERR_SHAPE;
+    if (block_rows == 32 && rows % 32) return MX_ERR_SHAPE;
+    if (batch == 0 || rows == 0 || cols == 0) return MX_OK;
+    if (!codes || !scales || !y) return MX_ERR_NULL;
+    if (!aligned16(codes) || !aligned16(y)) return MX_ERR_ALIGN;
+    const int64_t nunits = batch * rows * (cols / 8);
+    const int grid = grid_for(nunits, 256);
+    hipStream_t s = (hipStream_t)stream;
+    (void)hipGetLastError();
+    if (yt == MX_BF16) {
+        if (block_rows == 1) hipLaunchKernelGGL((deq_kernel<true, 1>), dim3(grid), dim3(256), 0, s, codes, scales, rows, cols, nunits, y);
+        else hipLaunchKernelGGL((deq_kernel<true, 32>), dim3(grid), dim3(256), 0, s, codes, scales, rows, cols, nunits, y);
+    } else {
+        if (block_rows == 1) hipLaunchKernelGGL((deq_kernel<false, 1>), dim3(grid), dim3(256), 0, s, codes, scales, rows, cols, nunits, y);
+        else hipLaunchKernelGGL((deq_kernel<false, 32>), dim3(grid), dim3(256), 0, s, codes, scales, rows, cols, nunits, y);
+    }
+    return launched();
+}
+
+}  // extern "C"

@@ -1,0 +1,210 @@
+"""Thin Python binding over libmx355 (C ABI in include/mx.h).
+
+Argument marshalling only: every step of the path runs in the HIP kernels of
+libmx355.so.  PyTorch supplies device memory (tensors are passed as raw device
+pointers) and the current HIP stream.  There is no fallback: if the library
+or a GPU is missing, calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmx355.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "mx.h")
+
+MX_F32, MX_BF16 = 0, 1
+RNE, SR = 0, 1
+STATUS = {0: "MX_OK", 1: "MX_ERR_NULL", 2: "MX_ERR_SHAPE", 3: "MX_ERR_ALIGN",
+          4: "MX_ERR_DTYPE", 5: "MX_ERR_UNSUPPORTED", 6: "MX_ERR_LAUNCH"}
+
+
+class MXError(RuntimeError):
+    def __init__(self, fn, code):
+        super().__init__("%s returned %s" % (fn, STATUS.get(code, code)))
+        self.code = code
+
+
+_lib = None
+
+
+def lib():
+    """Load libmx355.so (built in-tree by __graft_entry__.build())."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libmx355.so is not built; run "
+                               "python -m mxfp4_precision_numerics_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        P, i64, u64, u32, i32, c_int = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint64,
+                                        ctypes.c_uint32, ctypes.c_int32, ctypes.c_int)
+        L.mx_version.restype = c_int
+        L.mx_status_str.argtypes = [c_int]
+        L.mx_status_str.restype = ctypes.c_char_p
+        L.mx_rht_sign_mask.argtypes = [u64]
+        L.mx_rht_sign_mask.restype = u32
+        L.mx_rht.argtypes = [P, c_int, P, i64, i64, u32, c_int, P]
+        L.mx_quantize_1d.argtypes = [P, c_int, i64, i64, c_int, P, i32, i64, c_int, u32, c_int,
+                                     u64, u32, u64, P, P, P]
+        L.mx_quantize_2d.argtypes = [P, c_int, i64, i64, i64, P, P, P, P, P]
+        L.mx_dequantize.argtypes = [P, P, i64, i64, i64, c_int, P, c_int, P]
+        L.mx_grouped_gemm.argtypes = [P, P, P, P, P, c_int, P, i32, c_int, i64, i64, i64,
+                                      ctypes.c_float, P, c_int, P]
+        for name in ("mx_rht", "mx_quantize_1d", "mx_quantize_2d", "mx_dequantize",
+                     "mx_grouped_gemm"):
+            getattr(L, name).restype = c_int
+        _lib = L
+    return _lib
+
+
+def declared_functions():
+    """Function names declared in include/mx.h."""
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*[A-Za-z_][\w\s\*]*?\b(mx_\w+)\s*\(", text, re.M)))
+
+
+def _check(fn, code):
+    if code != 0:
+        raise MXError(fn, code)
+
+
+# ---------------------------------------------------------------------------
+# torch plumbing
+# ---------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream():
+    return _torch().cuda.current_stream().cuda_stream
+
+
+def _dtype_code(t):
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return MX_F32
+    if t.dtype == torch.bfloat16:
+        return MX_BF16
+    raise TypeError("expected float32 or bfloat16, got %s" % t.dtype)
+
+
+def _dev(t, name):
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t
+
+
+def rht_sign_mask(seed: int) -> int:
+    return int(lib().mx_rht_sign_mask(seed))
+
+
+def rht(x, sign_mask: int, inverse: bool = False, out=None):
+    torch = _torch()
+    _dev(x, "x")
+    rows, cols = x.shape
+    if out is None:
+        out = torch.empty((rows, cols), dtype=torch.float32, device=x.device)
+    _check("mx_rht", lib().mx_rht(_ptr(x), _dtype_code(x), _ptr(out), rows, cols, sign_mask,
+                                  int(inverse), _stream()))
+    return out
+
+
+def padded_capacity(rows: int, num_groups: int) -> int:
+    """A token capacity that holds any grouping of `rows` tokens into
+    `num_groups` groups each padded to a multiple of 32."""
+    return (rows + 31 * num_groups + 31) // 32 * 32
+
+
+def quantize_1d(x, block_axis: int = 1, group_offsets=None, kp: int = 0, use_rht: bool = False,
+                sign_mask: int = 0, rnd: int = RNE, seed: int = 0, stream_id: int = 0,
+                index_base: int = 0, codes=None, scales=None):
+    """Returns (codes, scales) uint8 device tensors; see mx_quantize_1d."""
+    torch = _torch()
+    _dev(x, "x")
+    rows, cols = x.shape
+    ng = 0
+    if block_axis == 1:
+        shape_c, shape_s = (rows, cols // 2), (rows, cols // 32)
+    else:
+        _dev(group_offsets, "group_offsets")
+        ng = group_offsets.numel() - 1
+        if not kp:
+            kp = padded_capacity(rows, ng)
+        shape_c, shape_s = (cols, kp // 2), (cols, kp // 32)
+    if codes is None:
+        codes = torch.empty(shape_c, dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(shape_s, dtype=torch.uint8, device=x.device)
+    _check("mx_quantize_1d", lib().mx_quantize_1d(
+        _ptr(x), _dtype_code(x), rows, cols, block_axis, _ptr(group_offsets), ng, kp,
+        int(use_rht), sign_mask, rnd, seed, stream_id, index_base, _ptr(codes), _ptr(scales),
+        _stream()))
+    return codes, scales
+
+
+def quantize_2d(w, layout=True, transposed=True):
+    """w [batch x rows x cols] or [rows x cols]; returns (codes, scales,
+    codes_t, scales_t), None for a layout not asked for."""
+    torch = _torch()
+    _dev(w, "w")
+    squeeze = w.dim() == 2
+    w3 = w.unsqueeze(0) if squeeze else w
+    b, r, c = w3.shape
+    dev = w.device
+    codes = torch.empty((b, r, c // 2), dtype=torch.uint8, device=dev) if layout else None
+    scales = torch.empty((b, r // 32, c // 32), dtype=torch.uint8, device=dev) if layout else None
+    codes_t = torch.empty((b, c, r // 2), dtype=torch.uint8, device=dev) if transposed else None
+    scales_t = torch.empty((b, c // 32, r // 32), dtype=torch.uint8, device=dev) if transposed else None
+    _check("mx_quantize_2d", lib().mx_quantize_2d(
+        _ptr(w3), _dtype_code(w3), b, r, c, _ptr(codes), _ptr(scales), _ptr(codes_t),
+        _ptr(scales_t), _stream()))
+    out = [codes, scales, codes_t, scales_t]
+    if squeeze:
+        out = [None if t is None else t[0] for t in out]
+    return tuple(out)
+
+
+def dequantize(codes, scales, block_rows: int = 1, out_dtype=None, out=None):
+    torch = _torch()
+    _dev(codes, "codes")
+    _dev(scales, "scales")
+    out_dtype = out_dtype or torch.float32
+    squeeze = codes.dim() == 2
+    c3 = codes.unsqueeze(0) if squeeze else codes
+    b, r, half = c3.shape
+    if out is None:
+        out = torch.empty((b, r, half * 2), dtype=out_dtype, device=codes.device)
+    _check("mx_dequantize", lib().mx_dequantize(
+        _ptr(c3), _ptr(scales), b, r, half * 2, block_rows, _ptr(out), _dtype_code(out),
+        _stream()))
+    return out[0] if squeeze else out
+
+
+def grouped_gemm(a_codes, a_scales, b_codes, b_scales, group_offsets, M, N, K,
+                 a_row_index=None, b_scale_2d=False, group_dim_k=False, alpha=1.0,
+                 out_dtype=None, out=None):
+    torch = _torch()
+    for t, nm in ((a_codes, "a_codes"), (a_scales, "a_scales"), (b_codes, "b_codes"),
+                  (b_scales, "b_scales"), (group_offsets, "group_offsets")):
+        _dev(t, nm)
+    if a_row_index is not None:
+        _dev(a_row_index, "a_row_index")
+    G = group_offsets.numel() - 1
+    out_dtype = out_dtype or torch.bfloat16
+    if out is None:
+        shape = (G, M, N) if group_dim_k else (M, N)
+        out = torch.empty(shape, dtype=out_dtype, device=a_codes.device)
+    _check("mx_grouped_gemm", lib().mx_grouped_gemm(
+        _ptr(a_codes), _ptr(a_scales), _ptr(a_row_index), _ptr(b_codes), _ptr(b_scales),
+        int(bool(b_scale_2d)), _ptr(group_offsets), G, int(bool(group_dim_k)), M, N, K,
+        float(alpha), _ptr(out), _dtype_code(out), _stream()))
+    return out

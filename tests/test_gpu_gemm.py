@@ -1,0 +1,168 @@
+"""GPU parity of the grouped MXFP4 GEMM against the FP64 oracle.
+
+Operands are produced on the CPU (oracle quantizers or random bytes) and the
+same bytes are handed to both sides.  The bar: relative Frobenius error
+<= 1e-5 of the fp32 output against the FP64 oracle, per group; a bf16 output
+within half a bf16 ulp of the oracle value plus the fp32 accumulation error.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from mxfp4_precision_numerics_amd import mx, synth
+from tests.gpu_util import dev, host, rel_fro
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-5
+
+
+def _q1d(rng, rows, k, scale=1.0):
+    x = (rng.standard_normal((rows, k)) * scale).astype(np.float32)
+    return oracle.quantize_1d(x)
+
+
+def _bf16_ulp(v):
+    """Spacing of bf16 values (8 significant bits) at magnitude v."""
+    a = np.maximum(np.abs(v), 2.0 ** -126)
+    return np.exp2(np.floor(np.log2(a)) - 7)
+
+
+def _check_bf16(got_bits, want):
+    """A bf16 output is the round-to-nearest-even of the fp32 accumulation:
+    within half a bf16 ulp of a value that is itself within the fp32
+    accumulation tolerance of the FP64 oracle."""
+    got = (got_bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    ulp = _bf16_ulp(np.maximum(np.abs(want), np.abs(got)))
+    err = np.abs(got - want)
+    bound = 0.5 * ulp + 2 * TOL * np.abs(want) + 1e-30
+    assert np.all(err <= bound), float(np.max(err / bound))
+
+
+def _run_fprop(counts, K, N, a_rows, b_2d, seed, out_dtype="f32", gather=True):
+    import torch
+    rng = np.random.default_rng(seed)
+    off = synth.offsets_from_counts(counts)
+    M, G = int(off[-1]), len(counts)
+    ac, asc = _q1d(rng, a_rows, K)
+    idx = rng.integers(0, a_rows, max(M, 1)).astype(np.int32)[:M] if gather else None
+    if b_2d:
+        w = (rng.standard_normal((G, N, K)) * 0.02).astype(np.float32)
+        bc, bs, _, _ = oracle.quantize_2d(w)
+    else:
+        pairs = [_q1d(rng, N, K) for _ in range(G)]
+        bc = np.stack([p[0] for p in pairs])
+        bs = np.stack([p[1] for p in pairs])
+    dt = torch.float32 if out_dtype == "f32" else torch.bfloat16
+    c = mx.grouped_gemm(dev(ac), dev(asc), dev(bc), dev(bs), dev(off), M, N, K,
+                        a_row_index=None if idx is None else dev(idx), b_scale_2d=b_2d,
+                        out_dtype=dt)
+    rows, want = oracle.grouped_gemm(ac, asc, bc, bs, off, M, N, K, a_row_index=idx,
+                                     b_scale_2d=b_2d)
+    got = host(c)
+    return off, rows, got, want
+
+
+@pytest.mark.parametrize("counts,K,N", [
+    ([5, 0, 33, 130], 2880, 160),
+    ([1], 64, 32),
+    ([0, 257, 0], 96, 96),
+    ([128, 128], 256, 256),
+])
+@pytest.mark.parametrize("b_2d", [False, True])
+def test_fprop_grouped_fp32(counts, K, N, b_2d):
+    off, rows, got, want = _run_fprop(counts, K, N, a_rows=150, b_2d=b_2d, seed=sum(counts) + K)
+    for g in range(len(counts)):
+        sel = rows[:, 0] == g
+        if not np.any(sel):
+            continue
+        ms = rows[sel, 1]
+        assert rel_fro(got[ms], want[sel]) <= TOL, g
+
+
+def test_fprop_bf16_output():
+    off, rows, got, want = _run_fprop([40, 90], 2880, 192, a_rows=64, b_2d=True, seed=4,
+                                      out_dtype="bf16")
+    _check_bf16(got[rows[:, 1]], want)
+
+
+def test_one_hot_rows_reproduce_b_exactly():
+    import torch
+    rng = np.random.default_rng(17)
+    K, N = 128, 64
+    a_codes = np.zeros((K, K // 2), dtype=np.uint8)
+    for k in range(K):
+        a_codes[k, k // 2] = 0x2 if k % 2 == 0 else 0x20
+    a_scales = np.full((K, K // 32), 127, dtype=np.uint8)
+    bc, bs = _q1d(rng, N, K)
+    off = np.array([0, K], dtype=np.int32)
+    c = host(mx.grouped_gemm(dev(a_codes), dev(a_scales), dev(bc[None]), dev(bs[None]), dev(off),
+                             K, N, K, out_dtype=torch.float32))
+    B = oracle.dequantize(bc, bs)
+    assert np.array_equal(c.astype(np.float64), B.T)
+
+
+@pytest.mark.parametrize("counts", [[32, 0, 64, 96, 448], [2048], [0, 32]])
+def test_wgrad_split_k_fp32(counts):
+    import torch
+    rng = np.random.default_rng(len(counts))
+    M, N = 96, 160
+    off = synth.offsets_from_counts(counts)
+    Kt = int(off[-1])
+    ac, asc = _q1d(rng, M, Kt)
+    bc, bs = _q1d(rng, N, Kt)
+    c = host(mx.grouped_gemm(dev(ac), dev(asc), dev(bc), dev(bs), dev(off), M, N, Kt,
+                             group_dim_k=True, out_dtype=torch.float32))
+    rows, want = oracle.grouped_gemm(ac, asc, bc, bs, off, M, N, Kt, group_dim_k=True)
+    for g in range(len(counts)):
+        sel = rows[:, 0] == g
+        if counts[g] == 0:
+            assert np.all(c[g] == 0)
+        else:
+            assert rel_fro(c[g][rows[sel, 1]], want[sel]) <= TOL
+
+
+def test_alpha_scales_output():
+    import torch
+    rng = np.random.default_rng(2)
+    ac, asc = _q1d(rng, 64, 128)
+    bc, bs = _q1d(rng, 32, 128)
+    off = np.array([0, 64], dtype=np.int32)
+    c1 = host(mx.grouped_gemm(dev(ac), dev(asc), dev(bc[None]), dev(bs[None]), dev(off), 64, 32, 128,
+                              out_dtype=torch.float32))
+    c2 = host(mx.grouped_gemm(dev(ac), dev(asc), dev(bc[None]), dev(bs[None]), dev(off), 64, 32, 128,
+                              alpha=0.25, out_dtype=torch.float32))
+    assert np.array_equal(c2, c1 * np.float32(0.25))
+
+
+def test_config4_full_size_fprop_sampled_rows():
+    """Grouped expert forward at full size: 32 experts, Zipf(1.1) routing of
+    16384 tokens x top-4 (65536 rows), K = 2880, N = 5760.  A = 1x32 RTNE
+    activations gathered by routing; B = 32x32-quantized weights, Wt layout.
+    The GPU computes every row; the oracle checks 4 rows per expert (first,
+    last and two seeded) over all N columns."""
+    import torch
+    x = synth.channel_scaled_activations()
+    ac, asc = oracle.quantize_1d(x)
+    w = synth.normal_bf16((32, 2880, 5760), 0.02, seed=3)
+    _, _, bct, bst = oracle.quantize_2d(w)        # Wt layout: [e][5760][2880/2]
+    counts = synth.zipf_counts()
+    off = synth.offsets_from_counts(counts)
+    idx = synth.routing_row_index(counts)
+    M, N, K = 65536, 5760, 2880
+    c = mx.grouped_gemm(dev(ac), dev(asc), dev(bct), dev(bst), dev(off), M, N, K,
+                        a_row_index=dev(idx), b_scale_2d=True, out_dtype=torch.float32)
+    rng = np.random.default_rng(40)
+    sample = []
+    for g in range(32):
+        a, b = int(off[g]), int(off[g + 1])
+        if b > a:
+            sample += [(g, a), (g, b - 1)] + [(g, int(m)) for m in rng.integers(a, b, 2)]
+    rows, want = oracle.grouped_gemm(ac, asc, bct, bst, off, M, N, K, a_row_index=idx,
+                                     b_scale_2d=True, rows=sample)
+    got = host(c[torch.as_tensor(rows[:, 1], device=c.device)])
+    for g in range(32):
+        sel = rows[:, 0] == g
+        assert rel_fro(got[sel], want[sel]) <= TOL, g
+    cb = mx.grouped_gemm(dev(ac), dev(asc), dev(bct), dev(bst), dev(off), M, N, K,
+                         a_row_index=dev(idx), b_scale_2d=True, out_dtype=torch.bfloat16)
+    _check_bf16(host(cb[torch.as_tensor(rows[:, 1], device=cb.device)]), want)
