@@ -156,14 +156,21 @@ def quantize_2d(w, layout=True, transposed=True):
     codes_t, scales_t), None for a layout not asked for."""
     torch = _torch()
     _dev(w, "w")
-    squeeze = w.dim() == 2
-    w3 = w.unsqueeze(0) if squeeze else w
-    b, r, c = w3.shape
+    b, r, c = (1,) + tuple(w.shape) if w.dim() == 2 else tuple(w.shape)
     dev = w.device
     codes = torch.empty((b, r, c // 2), dtype=torch.uint8, device=dev) if layout else None
     scales = torch.empty((b, r // 32, c // 32), dtype=torch.uint8, device=dev) if layout else None
     codes_t = torch.empty((b, c, r // 2), dtype=torch.uint8, device=dev) if transposed else None
     scales_t = torch.empty((b, c // 32, r // 32), dtype=torch.uint8, device=dev) if transposed else None
+    return quantize_2d_into(w, codes, scales, codes_t, scales_t)
+
+
+def quantize_2d_into(w, codes, scales, codes_t, scales_t):
+    """As quantize_2d, into caller-provided buffers (either pair may be None)."""
+    _dev(w, "w")
+    squeeze = w.dim() == 2
+    w3 = w.unsqueeze(0) if squeeze else w
+    b, r, c = w3.shape
     _check("mx_quantize_2d", lib().mx_quantize_2d(
         _ptr(w3), _dtype_code(w3), b, r, c, _ptr(codes), _ptr(scales), _ptr(codes_t),
         _ptr(scales_t), _stream()))
