@@ -32,6 +32,8 @@ sys.path.insert(0, ROOT)
 import numpy as np  # noqa: E402
 
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic.txt")
+ROLE_KERNEL = {"gemm": "gemm_kernel<true>", "gemm_wgrad": "gemm_kernel<false>"}
 PEAK_FP4_TFLOPS = 10100.0      # MI355X dense FP4 MFMA, TFLOP/s
 E, D, F2, T, TOPK = 32, 2880, 5760, 16384, 4
 ROWS = T * TOPK
@@ -145,48 +147,81 @@ def work_model():
     }
 
 
-def cpu_baseline(inputs_np_seconds=None):
+def kernel_source_hash():
+    """sha256 over the sources the GEMM kernel is compiled from."""
+    import hashlib
+    h = hashlib.sha256()
+    for rel in ("mxfp4_precision_numerics_amd/csrc/mx_gemm.hip",
+                "mxfp4_precision_numerics_amd/csrc/mx_device.h", "include/mx.h"):
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(role):
+    """HBM bytes per launch (scaled FETCH_SIZE + WRITE_SIZE) recorded for this
+    role's kernel, or None when no record exists or the kernel's sources have
+    changed since the counters were taken."""
+    if role not in ROLE_KERNEL or not os.path.exists(TRAFFIC_FILE):
+        return None
+    src, rec = None, {}
+    for line in open(TRAFFIC_FILE):
+        f = line.split()
+        if len(f) >= 2 and f[0] == "source_sha256":
+            src = f[1]
+        elif len(f) >= 6 and f[0] == "kernel":
+            rec[f[1]] = (float(f[3]), float(f[5]))
+    if src != kernel_source_hash() or ROLE_KERNEL[role] not in rec:
+        return None
+    rd, wr = rec[ROLE_KERNEL[role]]
+    return {"read_bytes": rd, "write_bytes": wr, "bytes": rd + wr}
+
+
+def cpu_baseline(gemm_seconds=8.0):
     """The oracle, untuned, on a bounded sample of the same step; its rate per
-    role is extrapolated to the full step."""
+    role is extrapolated to the full step.  The quantizers run on fixed
+    slices; the FP64 GEMM runs batches of sampled output rows (full N, full K)
+    until about `gemm_seconds` have passed."""
     import oracle
     from mxfp4_precision_numerics_amd import synth
     threads = oracle.default_threads()
-    t_total = 0.0
     rng = np.random.default_rng(0)
-    rows = 256
+    rows = 4096
     xs = synth.channel_scaled_activations(rows=rows, cols=D, seed=1)
     gs = synth.normal_bf16((rows, F2), 1e-3, seed=5)
+    w = work_model()
+    per_el = 2 + 0.5 + 1 / 32
     timings = {}
     # row-wise RTNE and SR quantize: time per element
     t0 = time.perf_counter()
     oracle.quantize_1d(xs)
     oracle.quantize_1d(gs, rnd=oracle.SR, seed=5)
     dt = time.perf_counter() - t0
-    el = rows * (D + F2)
-    w = work_model()
-    timings["q1d_row"] = dt / el * (w["q1d_row"]["bytes"] / (2 + 0.5 + 1 / 32))
-    # column-wise RHT + SR
-    off = np.array([0, 100, 256], dtype=np.int32)
+    timings["q1d_row"] = dt / (rows * (D + F2)) * (w["q1d_row"]["bytes"] / per_el)
+    # column-wise RHT + SR over two ragged expert segments
+    off = np.array([0, 1500, rows], dtype=np.int32)
     t0 = time.perf_counter()
     oracle.quantize_1d(gs, block_axis=0, group_offsets=off, use_rht=True, sign_mask=1, rnd=oracle.SR, seed=5)
     dt = time.perf_counter() - t0
-    timings["q1d_col"] = dt / (rows * F2) * (w["q1d_col"]["bytes"] / (2 + 0.5 + 1 / 32))
-    # 2D on one expert slice
-    wsl = synth.normal_bf16((1, 320, F2), 0.02, seed=5)
+    timings["q1d_col"] = dt / (rows * F2) * (w["q1d_col"]["bytes"] / per_el)
+    # 2D, both layouts, on one full gate_up expert matrix
+    wsl = synth.normal_bf16((1, D, F2), 0.02, seed=5)
     t0 = time.perf_counter()
     oracle.quantize_2d(wsl)
     dt = time.perf_counter() - t0
     timings["q2d"] = dt / wsl.size * (E * D * F2 + E * D * D)
     # GEMM: MAC rate on sampled output rows (full N, full K)
-    ac, asc = oracle.quantize_1d(synth.channel_scaled_activations(rows=64, cols=D, seed=1))
+    ac, asc = oracle.quantize_1d(synth.channel_scaled_activations(rows=256, cols=D, seed=1))
     wb = synth.normal_bf16((1, F2, D), 0.02, seed=5)
     bc, bs, _, _ = oracle.quantize_2d(wb)
-    sample_rows = [(0, int(m)) for m in rng.integers(0, 64, 2 * threads)]
-    t0 = time.perf_counter()
-    oracle.grouped_gemm(ac, asc, bc, bs, [0, 64], 64, F2, D, b_scale_2d=True, rows=sample_rows)
-    dt = time.perf_counter() - t0
-    macs = len(sample_rows) * F2 * D
-    mac_s = macs / dt
+    done, dt = 0, 0.0
+    while dt < gemm_seconds and done < 4096:
+        sample_rows = [(0, int(m)) for m in rng.integers(0, 256, 2 * threads)]
+        t0 = time.perf_counter()
+        oracle.grouped_gemm(ac, asc, bc, bs, [0, 256], 256, F2, D, b_scale_2d=True, rows=sample_rows)
+        dt += time.perf_counter() - t0
+        done += len(sample_rows)
+    mac_s = done * F2 * D / dt
     timings["gemm"] = w["gemm"]["flops"] / 2 / mac_s
     timings["gemm_wgrad"] = w["gemm_wgrad"]["flops"] / 2 / mac_s
     t_total = sum(timings.values())
@@ -196,9 +231,10 @@ def cpu_baseline(inputs_np_seconds=None):
         "unit": "TFLOP/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": ("row-wise quantize of 256 rows (2880 and 5760 wide), column-wise RHT+SR of 256x5760, "
-                   "2D of a 320x5760 slice, FP64 GEMM of %d output rows x 5760 x 2880; per-role rates "
-                   "extrapolated to the full step (%.0f s extrapolated)" % (len(sample_rows), t_total)),
+        "sample": ("row-wise quantize of 4096x2880 (RTNE) and 4096x5760 (SR), column-wise RHT+SR of "
+                   "4096x5760 in two ragged segments, 2D (both layouts) of one 2880x5760 expert, FP64 "
+                   "GEMM of %d sampled output rows x 5760 x 2880; per-role rates extrapolated to the "
+                   "full step (%.0f s extrapolated)" % (done, t_total)),
         "extrapolated_step_s": t_total,
     }
 
@@ -270,12 +306,15 @@ def main():
     value = total_flops / (ms_step / 1e3) / 1e12
     dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
     dk = kernels[dom]
+    tr = measured_traffic(dom)
     if "TFLOP/s" in dk:
         roof = {"kernel": dom, "bound": "mfma", "achieved": dk["TFLOP/s"], "peak": PEAK_FP4_TFLOPS,
-                "unit": "TFLOP/s", "frac": dk["TFLOP/s"] / PEAK_FP4_TFLOPS, "traffic": None}
+                "unit": "TFLOP/s", "frac": dk["TFLOP/s"] / PEAK_FP4_TFLOPS, "traffic": tr and tr["bytes"]}
     else:
         roof = {"kernel": dom, "bound": "hbm", "achieved": dk["GB/s"], "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": dk["GB/s"] / PEAK_HBM_GBS, "traffic": None}
+                "unit": "GB/s", "frac": dk["GB/s"] / PEAK_HBM_GBS, "traffic": tr and tr["bytes"]}
+    if tr:
+        roof["traffic_read_write"] = [tr["read_bytes"], tr["write_bytes"]]
     quant_bytes = sum(w[k]["bytes"] for k in ("q1d_row", "q1d_col", "q2d"))
     quant_ms = sum(kernels[k]["ms_per_step"] for k in ("q1d_row", "q1d_col", "q2d"))
     gemm_ms = kernels["gemm"]["ms_per_step"] + kernels["gemm_wgrad"]["ms_per_step"]

@@ -2,18 +2,42 @@
 // (v_mfma_scale_f32_32x32x64_f8f6f4, both operands E2M1, FP32 accumulation).
 //
 // Operand layout the MFMA reads (one wave, 32x32 output, K = 64): lane l
-// supplies row (l % 32) of A and K elements [32 (l / 32), +32) as 16 bytes
-// (even element in the low nibble) plus that 32-block's UE8M0 scale byte;
-// B likewise per output column.  A 32-element MX block is therefore exactly
-// one lane's 16-byte operand and one scale byte, so the row-major code and
-// scale layouts produced by the quantizers are consumed as they are.
-// Accumulator: lane l, register r holds C[8 (r / 4) + 4 (l / 32) + r % 4][l % 32].
+// supplies row (l % 32) of its operand and K elements [32 (l / 32), +32) as
+// 16 bytes (even element in the low nibble) plus that 32-block's UE8M0 scale
+// byte.  A 32-element MX block is exactly one lane's 16-byte operand and one
+// scale byte, so the row-major code and scale layouts written by the
+// quantizers are consumed as they are.  Accumulator: lane l, register e holds
+// D[8 (e / 4) + 4 (l / 32) + e % 4][l % 32].
 //
-// Tiling: a workgroup (4 waves, 2 x 2) computes a BM x BN tile of one group;
-// each wave owns (BM/2) x (BN/2) as 32x32 MFMA blocks.  K advances 128 at a
-// time (64 code bytes per row); A/B code tiles and their scale bytes are
-// staged through double-buffered LDS with an XOR swizzle of the 16-byte
-// chunks so the MFMA operand reads are bank-conflict free.
+// The MFMA's first operand is the weight tile (rows = output columns n) and
+// its second the activation tile (rows = output rows m), so D = C^T per
+// 32x32 block and each lane ends up holding 4 consecutive output columns of
+// one output row: the epilogue stores 8-byte (bf16) or 16-byte (fp32) runs.
+//
+// Tiling: a workgroup of 4 waves (2 x 2) computes a 256 x 256 tile of one
+// group; each wave owns 128 x 128 (16 MFMA blocks, 256 accumulators held in
+// AGPRs).  K advances 128 per stage.  Every operand byte moves global -> LDS
+// by the CDNA LDS-DMA loads (global_load_lds_dwordx4 for 16-byte code
+// chunks, global_load_lds_ubyte for scale bytes, each landing as a dword), so
+// no staging registers are needed: a 3-buffer LDS ring keeps two stages in
+// flight while one is multiplied.  The DMA is issued from register-only
+// inline assembly and its completion is awaited explicitly (s_waitcnt
+// vmcnt + s_barrier), which lets a stage land while the two before it are
+// still outstanding.  Operand fragments are double-buffered in registers:
+// the second K-half of a stage is read while the first multiplies, and the
+// next stage's first half is read while the second multiplies.
+//
+// LDS code tiles use an XOR swizzle of 16-byte chunks; each row's 4 scale
+// dwords are stored in the order (s0, s2, s1, s3), so one 8-byte read gives a
+// lane the scales of both K-halves.  A chunk at or past the end of the K
+// range is loaded from a clamped (valid) address and its scale is forced to
+// 2^-127 on both operands, so its products (at most 36 * 2^-254) vanish in
+// the fp32 accumulation.
+//
+// Tile order: 32 consecutive tile ids cover 4 M-tiles x 8 N-tiles of one
+// group, and blocks of 32 ids are dealt round-robin to the 8 XCDs (work-
+// groups are dispatched to XCDs round-robin), so the workgroups resident on
+// one XCD share A rows and B columns in its L2.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -41,59 +65,122 @@ struct GemmArgs {
     float alpha;
 };
 
+constexpr int BM = 256, BN = 256;
 constexpr int BK = 128;            // K elements per stage
-constexpr int BKB = BK / 2;        // code bytes per row per stage
-constexpr int CHUNKS = BKB / 16;   // 16-byte chunks per row per stage (4)
+constexpr int NST = 3;             // LDS ring depth
+constexpr int GROUP_M = 4;         // M-tiles per tile-order group
+constexpr int XCDS = 8;
+constexpr int XCD_BLOCK = 32;      // consecutive tile ids per XCD turn
+// one stage in LDS: A codes, B codes (256 rows x 64 bytes each), A and B
+// scales (256 rows x 4 dwords each)
+constexpr int OFF_A = 0, OFF_B = 16384, OFF_AS = 32768, OFF_BS = 36864;
+constexpr int STAGE_BYTES = 40960;
+constexpr int DMA_PER_STAGE = 16;  // DMA ops per thread per stage
 
-__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 1) & 3); }
+// 16-byte chunk swizzle: the 32 rows an MFMA operand read touches at one
+// chunk index land in distinct bank groups whether the LDS serves 8 lanes
+// (32 banks) or 16 lanes (64 banks) of a ds_read_b128 per cycle.
+__device__ __forceinline__ int swz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+// scale dword slot p of a row holds chunk (0, 2, 1, 3)[p] (an involution)
+__device__ __forceinline__ int sperm(int p) { return ((p & 1) << 1) | ((p >> 1) & 1); }
 
-template <int BM, int BN, bool OUT_BF16>
-__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
-    constexpr int WM = BM / 2, WN = BN / 2;
-    constexpr int FM = WM / 32, FN = WN / 32;
-    constexpr int A_CH = BM * CHUNKS / 256;   // A chunks per thread per stage
-    constexpr int B_CH = BN * CHUNKS / 256;
-    static_assert(A_CH >= 1 && B_CH >= 1, "tile too small");
+// LDS-DMA: every lane moves 16 bytes (or 1 byte, zero-extended to a dword)
+// from base + voff to LDS byte address lds + 16 lane (or + 4 lane).  M0
+// carries the wave's LDS base.  Register operands only; completion is
+// awaited with an explicit s_waitcnt vmcnt.
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :: "v"(voff), "s"(base), "s"(lds) : "memory");
+}
+__device__ __forceinline__ void dma1(const void* base, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_ubyte %0, %1"
+                 :: "v"(voff), "s"(base), "s"(lds) : "memory");
+}
 
-    __shared__ uint4 lds_a[2][BM * CHUNKS];
-    __shared__ uint4 lds_b[2][BN * CHUNKS];
-    __shared__ uint32_t lds_as[2][BM];
-    __shared__ uint32_t lds_bs[2][BN];
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    const __bf16 x = (__bf16)a, y = (__bf16)b;   // v_cvt_pk_bf16_f32: round to nearest even
+    return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+}
+
+template <bool OUT_BF16>
+__global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
+    constexpr int WM = 128, WN = 128, FM = 4, FN = 4;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[NST * STAGE_BYTES];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
 
+    // ---------------- tile id: XCD-aware remap of the workgroup id ----------
+    const int64_t wg = blockIdx.x;
+    const int64_t xcd = wg % XCDS, j = wg / XCDS;
+    int64_t id = (j / XCD_BLOCK) * (XCDS * XCD_BLOCK) + xcd * XCD_BLOCK + (j % XCD_BLOCK);
+
     // ---------------- tile decode ----------------
+    // Groups split M: wave 0 reads all group offsets at once, scans the tile
+    // counts ceil(n_g / BM) * tiles_n across its lanes and publishes the
+    // group holding tile `id` (one round trip to memory instead of one per
+    // group).
+    __shared__ int32_t tile_group[2];
     int g = 0;
-    int64_t m_begin = 0, m_end = 0, k_begin = 0, k_end = p.K;
-    const int nt = (int)(blockIdx.x % (uint32_t)p.tiles_n);
-    int64_t mlin = blockIdx.x / (uint32_t)p.tiles_n;
+    int64_t m_begin = 0, m_end = 0, k_begin = 0, k_end = p.K, mtiles = 0;
     if (p.group_dim_k == 0) {
-        bool found = false;
-        for (g = 0; g < p.G; ++g) {
-            const int64_t gb = p.off[g], ge = p.off[g + 1];
-            const int64_t mt = (ge - gb + BM - 1) / BM;
-            if (mlin < mt) {
-                m_begin = gb + mlin * BM;
-                m_end = min(ge, m_begin + BM);
-                found = true;
-                break;
+        if (wave == 0) {
+            if (lane == 0) tile_group[0] = -1;
+            int64_t running = 0;
+            for (int base = 0; base < p.G; base += 64) {
+                const int gg = base + lane;
+                int64_t t = 0, gb = 0, ge = 0;
+                if (gg < p.G) {
+                    gb = p.off[gg];
+                    ge = p.off[gg + 1];
+                    t = (ge - gb + BM - 1) / BM * p.tiles_n;
+                }
+                int64_t incl = t;
+#pragma unroll
+                for (int d = 1; d < 64; d <<= 1) {
+                    const int64_t v = __shfl_up(incl, d);
+                    if (lane >= d) incl += v;
+                }
+                const int64_t start = running + incl - t;
+                if (gg < p.G && id >= start && id < start + t) {
+                    tile_group[0] = gg;
+                    tile_group[1] = (int32_t)(id - start);
+                }
+                running += __shfl(incl, 63);
             }
-            mlin -= mt;
         }
-        if (!found) return;
+        __syncthreads();
+        g = tile_group[0];
+        if (g < 0) return;                      // past the last tile (uniform)
+        id = tile_group[1];
+        m_begin = p.off[g];
+        m_end = p.off[g + 1];
+        mtiles = (m_end - m_begin + BM - 1) / BM;
     } else {
-        g = (int)(mlin / p.tiles_m);
+        const int64_t per = (int64_t)p.tiles_m * p.tiles_n;
+        g = (int)(id / per);
         if (g >= p.G) return;
-        const int64_t mt = mlin - (int64_t)g * p.tiles_m;
-        m_begin = mt * BM;
-        m_end = min(p.M, m_begin + BM);
+        id -= (int64_t)g * per;
+        mtiles = p.tiles_m;
+        m_begin = 0;
+        m_end = p.M;
         k_begin = p.off[g];
         k_end = p.off[g + 1];
     }
-    const int64_t n_begin = (int64_t)nt * BN;
+    // grouped order inside the group: GROUP_M M-tiles x all N-tiles, m fastest
+    const int64_t span = (int64_t)GROUP_M * p.tiles_n;
+    const int64_t sgrp = id / span;
+    const int64_t rem = id - sgrp * span;
+    const int64_t gm = min((int64_t)GROUP_M, mtiles - sgrp * GROUP_M);
+    const int64_t nt = rem / gm;
+    const int64_t mt = sgrp * GROUP_M + (rem - nt * gm);
+    const int64_t grp_end = m_end;
+    m_begin = m_begin + mt * BM;
+    m_end = min(grp_end, m_begin + BM);
+    const int64_t n_begin = nt * BN;
+
     const int64_t KB = p.K / 2;      // code bytes per operand row
     const int64_t KS = p.K / 32;     // scale bytes per operand row
 
@@ -104,157 +191,189 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
         bscales += (int64_t)g * (p.b_scale_2d ? (p.N / 32) * KS : p.N * KS);
     }
 
-    // ---------------- per-thread load assignments ----------------
-    // chunk id = tid + 256 * i -> tile row id / CHUNKS, chunk id % CHUNKS
-    const uint8_t* a_row_ptr[A_CH];
-    const uint8_t* a_srow_ptr[A_CH];
-    int a_lds_idx[A_CH];
-    int a_chunk[A_CH];
+    // ---------------- per-thread DMA assignments ----------------
+    // DMA j of thread t fills LDS slot t + 256 j of each operand: row
+    // r = t/4 + 64 j, slot position pc = t % 4 within the row.
+    const int pc = tid & 3;
+    uint32_t a_off[4], b_off[4], as_off[4], bs_off[4];
+    int a_chunk[4], s_chunk;
+    s_chunk = sperm(pc);
 #pragma unroll
-    for (int i = 0; i < A_CH; ++i) {
-        const int id = tid + 256 * i;
-        const int r = id / CHUNKS, c = id % CHUNKS;
+    for (int jj = 0; jj < 4; ++jj) {
+        const int r = (tid >> 2) + 64 * jj;
+        a_chunk[jj] = pc ^ swz(r);            // code chunk this lane fetches
         int64_t m = m_begin + r;
-        if (m >= m_end) m = m_end - 1;            // clamp: rows past the tile end are never stored
+        if (m >= m_end) m = m_end - 1;        // rows past the tile end are never stored
         const int64_t arow = p.a_row_index ? (int64_t)p.a_row_index[m] : m;
-        a_row_ptr[i] = p.a_codes + arow * KB;
-        a_srow_ptr[i] = p.a_scales + arow * KS;
-        a_lds_idx[i] = r * CHUNKS + swz(r, c);
-        a_chunk[i] = c;
-    }
-    const uint8_t* b_row_ptr[B_CH];
-    const uint8_t* b_srow_ptr[B_CH];
-    int b_lds_idx[B_CH];
-    int b_chunk[B_CH];
-#pragma unroll
-    for (int i = 0; i < B_CH; ++i) {
-        const int id = tid + 256 * i;
-        const int r = id / CHUNKS, c = id % CHUNKS;
+        a_off[jj] = (uint32_t)(arow * KB);
+        as_off[jj] = (uint32_t)(arow * KS);
         int64_t n = n_begin + r;
         if (n >= p.N) n = p.N - 1;
-        b_row_ptr[i] = bcodes + n * KB;
-        b_srow_ptr[i] = bscales + (p.b_scale_2d ? (n / 32) * KS : n * KS);
-        b_lds_idx[i] = r * CHUNKS + swz(r, c);
-        b_chunk[i] = c;
+        b_off[jj] = (uint32_t)(n * KB);
+        bs_off[jj] = (uint32_t)(p.b_scale_2d ? (n / 32) * KS : n * KS);
     }
-
-    v16f acc[FM][FN];
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+    const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
 
     const int64_t klen = k_end - k_begin;
     const int nkt = (int)((klen + BK - 1) / BK);
+    const int64_t kc0 = k_begin / 32;        // first K-chunk of the range
+    const int64_t kc_end = k_end / 32;
 
-    uint4 ra[A_CH], rb[B_CH];
-    uint32_t ras[A_CH], rbs[B_CH];
-
-    auto load_stage = [&](int kt) {
-        const int64_t kbase = k_begin + (int64_t)kt * BK;
+    // stage kt -> LDS buffer `buf`; chunks past the end are clamped in range
+    auto issue = [&](int kt, int buf) {
+        const uint32_t sb = lds_base + (uint32_t)buf * STAGE_BYTES;
+        const int64_t kcs = kc0 + (int64_t)kt * 4;
 #pragma unroll
-        for (int i = 0; i < A_CH; ++i) {
-            const int64_t k = kbase + a_chunk[i] * 32;
-            if (k < k_end) {
-                ra[i] = *(const uint4*)(a_row_ptr[i] + k / 2);
-                ras[i] = a_srow_ptr[i][k / 32];
-            } else {
-                ra[i] = make_uint4(0, 0, 0, 0);
-                ras[i] = 0;
-            }
+        for (int jj = 0; jj < 4; ++jj) {
+            const int64_t kc = min(kcs + a_chunk[jj], kc_end - 1);
+            dma16(p.a_codes, a_off[jj] + (uint32_t)(kc * 16), sb + OFF_A + jj * 4096 + wave * 1024);
+            dma16(bcodes, b_off[jj] + (uint32_t)(kc * 16), sb + OFF_B + jj * 4096 + wave * 1024);
         }
+        const int64_t kcsc = min(kcs + s_chunk, kc_end - 1);
 #pragma unroll
-        for (int i = 0; i < B_CH; ++i) {
-            const int64_t k = kbase + b_chunk[i] * 32;
-            if (k < k_end) {
-                rb[i] = *(const uint4*)(b_row_ptr[i] + k / 2);
-                rbs[i] = b_srow_ptr[i][k / 32];
-            } else {
-                rb[i] = make_uint4(0, 0, 0, 0);
-                rbs[i] = 0;
-            }
+        for (int jj = 0; jj < 4; ++jj) {
+            dma1(p.a_scales, as_off[jj] + (uint32_t)kcsc, sb + OFF_AS + jj * 1024 + wave * 256);
+            dma1(bscales, bs_off[jj] + (uint32_t)kcsc, sb + OFF_BS + jj * 1024 + wave * 256);
         }
     };
-    auto store_stage = [&](int buf) {
+
+    v16f acc[FN][FM];
 #pragma unroll
-        for (int i = 0; i < A_CH; ++i) {
-            lds_a[buf][a_lds_idx[i]] = ra[i];
-            ((uint8_t*)lds_as[buf])[(tid + 256 * i) / CHUNKS * 4 + a_chunk[i]] = (uint8_t)ras[i];
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int jj = 0; jj < FM; ++jj)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][jj][e] = 0.0f;
+
+    const int lr = lane & 31;      // operand row within a 32-row MFMA block
+    const int lh = lane >> 5;      // which 32-element half of K = 64
+
+    struct Frag { v8i b[FN]; v8i a[FM]; };
+    struct Scl { uint2 b[FN]; uint2 a[FM]; };
+    auto read_frag = [&](Frag& f, int buf, int ks) {
+        const uint8_t* sb = lds + buf * STAGE_BYTES;
+        const int ch = ks * 2 + lh;
+#pragma unroll
+        for (int i = 0; i < FN; ++i) {
+            const int r = wn * WN + i * 32 + lr;
+            const uint4 v = *(const uint4*)(sb + OFF_B + (r * 4 + (ch ^ swz(r))) * 16);
+            f.b[i] = (v8i){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
         }
 #pragma unroll
-        for (int i = 0; i < B_CH; ++i) {
-            lds_b[buf][b_lds_idx[i]] = rb[i];
-            ((uint8_t*)lds_bs[buf])[(tid + 256 * i) / CHUNKS * 4 + b_chunk[i]] = (uint8_t)rbs[i];
+        for (int i = 0; i < FM; ++i) {
+            const int r = wm * WM + i * 32 + lr;
+            const uint4 v = *(const uint4*)(sb + OFF_A + (r * 4 + (ch ^ swz(r))) * 16);
+            f.a[i] = (v8i){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+        }
+    };
+    auto read_scl = [&](Scl& s, int buf) {
+        const uint8_t* sb = lds + buf * STAGE_BYTES;
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+            s.b[i] = *(const uint2*)(sb + OFF_BS + (wn * WN + i * 32 + lr) * 16 + lh * 8);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+            s.a[i] = *(const uint2*)(sb + OFF_AS + (wm * WM + i * 32 + lr) * 16 + lh * 8);
+    };
+    auto mma = [&](const Frag& f, const Scl& s, int ks, bool tail) {
+#pragma unroll
+        for (int i = 0; i < FN; ++i) {
+            const int sb = tail ? 0 : (int)(ks ? s.b[i].y : s.b[i].x);
+#pragma unroll
+            for (int jj = 0; jj < FM; ++jj) {
+                const int sa = tail ? 0 : (int)(ks ? s.a[jj].y : s.a[jj].x);
+                acc[i][jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                    f.b[i], f.a[jj], acc[i][jj], 4, 4, 0, sb, 0, sa);
+            }
         }
     };
 
     if (nkt > 0) {
-        load_stage(0);
-        store_stage(0);
-    }
-    __syncthreads();
-
-    const int lr = lane & 31;      // row within a 32-row MFMA block
-    const int lh = lane >> 5;      // which 32-element half of K = 64
-
-    for (int kt = 0; kt < nkt; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < nkt) load_stage(kt + 1);
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const int ch = ks * 2 + lh;
-            v8i af[FM], bfr[FN];
-            int as_[FM], bs_[FN];
-#pragma unroll
-            for (int i = 0; i < FM; ++i) {
-                const int r = wm * WM + i * 32 + lr;
-                const uint4 v = lds_a[buf][r * CHUNKS + swz(r, ch)];
-                af[i] = (v8i){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-                as_[i] = ((const uint8_t*)lds_as[buf])[r * 4 + ch];
-            }
-#pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                const int r = wn * WN + j * 32 + lr;
-                const uint4 v = lds_b[buf][r * CHUNKS + swz(r, ch)];
-                bfr[j] = (v8i){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-                bs_[j] = ((const uint8_t*)lds_bs[buf])[r * 4 + ch];
-            }
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                        af[i], bfr[j], acc[i][j], 4, 4, 0, as_[i], 0, bs_[j]);
+        Frag f0, f1;
+        Scl sc, nsc;
+        // Two stages are in flight at every wait; a thread issues exactly
+        // DMA_PER_STAGE ops per stage (past-the-end stages are clamped loads
+        // into a buffer nobody reads), so vmcnt(16) means "all but the
+        // newest stage have landed".
+        issue(0, 0);
+        issue(1, 1);
+        asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        read_frag(f0, 0, 0);
+        read_scl(sc, 0);
+        for (int kt = 0; kt < nkt; ++kt) {
+            const int buf = kt % NST;
+            // buffer (kt+2)%3 held stage kt-1, whose reads all finished
+            // before the previous barrier
+            issue(kt + 2, (kt + 2) % NST);
+            read_frag(f1, buf, 1);
+            const int64_t kcl = kc0 + (int64_t)kt * 4 + lh;   // this lane's chunk in K-half 0
+            mma(f0, sc, 0, kcl >= kc_end);
+            // stage kt+1 has landed (own DMA) and every wave is done with
+            // its reads of this stage's first half
+            asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            read_frag(f0, (kt + 1) % NST, 0);
+            read_scl(nsc, (kt + 1) % NST);
+            mma(f1, sc, 1, kcl + 2 >= kc_end);
+            sc = nsc;
         }
-        if (kt + 1 < nkt) store_stage(buf ^ 1);
-        __syncthreads();
+        // drain the DMA of the two past-the-end stages before the workgroup
+        // can finish (their LDS writes must not outlive it)
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
 
     // ---------------- epilogue ----------------
+    // Each wave stages its 128 x 128 result through LDS one 32-row slab at a
+    // time (row pitch padded by 16 bytes against bank conflicts) and stores
+    // whole 16-byte runs, so a store instruction covers 4 full row segments
+    // of 256 (bf16) or 2 of 512 (fp32) bytes instead of 32 scattered pieces.
+    constexpr int EB = OUT_BF16 ? 2 : 4;              // output element bytes
+    constexpr int PITCH = WN * EB + 16;                // LDS bytes per staged row
+    constexpr int SEGS = WN * EB / 16;                 // 16-byte runs per row
+    static_assert(4 * 32 * PITCH <= NST * STAGE_BYTES, "epilogue staging fits the ring");
+    __syncthreads();                                   // every wave is done with the ring
+    uint8_t* stage_c = lds + wave * 32 * PITCH;
     const int64_t rows_here = m_end - m_begin;
-    int64_t c_row0 = m_begin;
     uint8_t* cbase = (uint8_t*)p.c;
-    if (p.group_dim_k == 1) cbase += (int64_t)g * p.M * p.N * (OUT_BF16 ? 2 : 4);
+    if (p.group_dim_k == 1) cbase += (int64_t)g * p.M * p.N * EB;
+    const float alpha = p.alpha;
+    const int64_t col0 = n_begin + wn * WN;            // first output column of this wave
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int jj = 0; jj < FM; ++jj) {
+        // lane (lr, lh) holds row lr of the slab, columns i*32 + 8q + 4lh + (0..3)
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-            const int64_t col = n_begin + wn * WN + j * 32 + lr;
-            if (col >= p.N) continue;
+        for (int i = 0; i < FN; ++i) {
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int rl = wm * WM + i * 32 + (e >> 2) * 8 + lh * 4 + (e & 3);
-                if (rl >= rows_here) continue;
-                const int64_t row = c_row0 + rl;
-                const float v = acc[i][j][e] * p.alpha;
+            for (int q = 0; q < 4; ++q) {
+                const int cl = i * 32 + 8 * q + 4 * lh;
+                const float v0 = acc[i][jj][4 * q + 0] * alpha;
+                const float v1 = acc[i][jj][4 * q + 1] * alpha;
+                const float v2 = acc[i][jj][4 * q + 2] * alpha;
+                const float v3 = acc[i][jj][4 * q + 3] * alpha;
+                uint8_t* dst = stage_c + lr * PITCH + cl * EB;
                 if (OUT_BF16)
-                    ((uint16_t*)cbase)[row * p.N + col] = (uint16_t)f32_to_bf16_rne(v);
+                    *(uint2*)dst = make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
                 else
-                    ((float*)cbase)[row * p.N + col] = v;
+                    *(uint4*)dst = make_uint4(__float_as_uint(v0), __float_as_uint(v1),
+                                              __float_as_uint(v2), __float_as_uint(v3));
             }
         }
+        __builtin_amdgcn_s_waitcnt(0xC07F);            // lgkmcnt(0): the slab is in LDS
+        __builtin_amdgcn_wave_barrier();
+        const int64_t row_base = m_begin + wm * WM + jj * 32;
+#pragma unroll
+        for (int k = 0; k < 32 * SEGS / 64; ++k) {
+            const int sidx = lane + 64 * k;
+            const int r = sidx / SEGS, sg = sidx % SEGS;
+            const uint4 v = *(const uint4*)(stage_c + r * PITCH + sg * 16);
+            const int64_t col = col0 + sg * (16 / EB);
+            if (wm * WM + jj * 32 + r < rows_here && col < p.N)
+                *(uint4*)(cbase + ((row_base + r) * p.N + col) * EB) = v;
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);            // reads done before the slab is reused
+        __builtin_amdgcn_wave_barrier();
+    }
 }
 
 inline bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
@@ -274,8 +393,12 @@ extern "C" mx_status mx_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_sc
     if (M == 0) return MX_OK;
     if (!a_codes || !a_scales || !b_codes || !b_scales || !c) return MX_ERR_NULL;
     if (!aligned16(a_codes) || !aligned16(b_codes) || !aligned16(c)) return MX_ERR_ALIGN;
+    // operand rows are addressed by 32-bit byte offsets: each B group and the
+    // A rows (wherever a row index can point) must lie within 4 GiB
+    if (group_dim_k == 0 && N * (K / 2) > 0xFFFFFFFFLL) return MX_ERR_SHAPE;
+    if (group_dim_k == 1 && (M > 0 && (M - 1) * (K / 2) > 0xFFFFFFFFLL || (N - 1) * (K / 2) > 0xFFFFFFFFLL))
+        return MX_ERR_SHAPE;
 
-    constexpr int BM = 128, BN = 128;
     GemmArgs p;
     p.a_codes = a_codes;
     p.a_scales = a_scales;
@@ -298,12 +421,15 @@ extern "C" mx_status mx_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_sc
         tiles = ((M + BM - 1) / BM + num_groups) * p.tiles_n;   // upper bound on sum_g ceil(n_g / BM)
     else
         tiles = (int64_t)num_groups * p.tiles_m * p.tiles_n;
+    // the XCD remap is a bijection on multiples of XCDS * XCD_BLOCK
+    const int64_t quantum = XCDS * XCD_BLOCK;
+    tiles = (tiles + quantum - 1) / quantum * quantum;
     if (tiles > 0x7FFFFFFF) return MX_ERR_SHAPE;
     hipStream_t s = (hipStream_t)stream;
     (void)hipGetLastError();
     if (ct == MX_BF16)
-        hipLaunchKernelGGL((gemm_kernel<BM, BN, true>), dim3((unsigned)tiles), dim3(256), 0, s, p);
+        hipLaunchKernelGGL((gemm_kernel<true>), dim3((unsigned)tiles), dim3(256), 0, s, p);
     else
-        hipLaunchKernelGGL((gemm_kernel<BM, BN, false>), dim3((unsigned)tiles), dim3(256), 0, s, p);
+        hipLaunchKernelGGL((gemm_kernel<false>), dim3((unsigned)tiles), dim3(256), 0, s, p);
     return hipGetLastError() == hipSuccess ? MX_OK : MX_ERR_LAUNCH;
 }
