@@ -75,7 +75,10 @@ constexpr int XCD_BLOCK = 32;      // consecutive tile ids per XCD turn
 // scales (256 rows x 4 dwords each)
 constexpr int OFF_A = 0, OFF_B = 16384, OFF_AS = 32768, OFF_BS = 36864;
 constexpr int STAGE_BYTES = 40960;
-constexpr int DMA_PER_STAGE = 16;  // DMA ops per thread per stage
+// DMA ops per thread per stage: 8 code moves, 4 A-scale moves, and 4 B-scale
+// moves (1D B scales) or 1 (2D B scales: 8 row groups of 32 per tile).
+template <bool B2D>
+constexpr int dma_per_stage() { return B2D ? 13 : 16; }
 
 // 16-byte chunk swizzle: the 32 rows an MFMA operand read touches at one
 // chunk index land in distinct bank groups whether the LDS serves 8 lanes
@@ -102,7 +105,7 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
 }
 
-template <bool OUT_BF16>
+template <bool OUT_BF16, bool B2D>
 __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
     constexpr int WM = 128, WN = 128, FM = 4, FN = 4;
     __shared__ __attribute__((aligned(16))) uint8_t lds[NST * STAGE_BYTES];
@@ -152,9 +155,9 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
             }
         }
         __syncthreads();
-        g = tile_group[0];
+        g = __builtin_amdgcn_readfirstlane(tile_group[0]);   // uniform: the DMA takes scalar bases
         if (g < 0) return;                      // past the last tile (uniform)
-        id = tile_group[1];
+        id = __builtin_amdgcn_readfirstlane(tile_group[1]);
         m_begin = p.off[g];
         m_end = p.off[g + 1];
         mtiles = (m_end - m_begin + BM - 1) / BM;
@@ -188,7 +191,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
     const uint8_t* bscales = p.b_scales;
     if (p.group_dim_k == 0) {
         bcodes += (int64_t)g * p.N * KB;
-        bscales += (int64_t)g * (p.b_scale_2d ? (p.N / 32) * KS : p.N * KS);
+        bscales += (int64_t)g * (B2D ? (p.N / 32) * KS : p.N * KS);
     }
 
     // ---------------- per-thread DMA assignments ----------------
@@ -210,7 +213,16 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
         int64_t n = n_begin + r;
         if (n >= p.N) n = p.N - 1;
         b_off[jj] = (uint32_t)(n * KB);
-        bs_off[jj] = (uint32_t)(p.b_scale_2d ? (n / 32) * KS : n * KS);
+        bs_off[jj] = (uint32_t)(n * KS);
+    }
+    // 2D B scales: lane l of every wave fetches row group (l / 4) % 8 of the
+    // tile at slot position l % 4 (lanes 32..63 repeat lanes 0..31), into its
+    // wave's own 256-byte copy
+    uint32_t bs2_off = 0;
+    if (B2D) {
+        int64_t grp = n_begin / 32 + ((lane >> 2) & 7);
+        if (grp > p.N / 32 - 1) grp = p.N / 32 - 1;    // groups past N are never stored
+        bs2_off = (uint32_t)(grp * KS);
     }
     const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
 
@@ -233,8 +245,9 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
             dma1(p.a_scales, as_off[jj] + (uint32_t)kcsc, sb + OFF_AS + jj * 1024 + wave * 256);
-            dma1(bscales, bs_off[jj] + (uint32_t)kcsc, sb + OFF_BS + jj * 1024 + wave * 256);
+            if (!B2D) dma1(bscales, bs_off[jj] + (uint32_t)kcsc, sb + OFF_BS + jj * 1024 + wave * 256);
         }
+        if (B2D) dma1(bscales, bs2_off + (uint32_t)kcsc, sb + OFF_BS + wave * 256);
     };
 
     v16f acc[FN][FM];
@@ -270,7 +283,8 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
         const uint8_t* sb = lds + buf * STAGE_BYTES;
 #pragma unroll
         for (int i = 0; i < FN; ++i)
-            s.b[i] = *(const uint2*)(sb + OFF_BS + (wn * WN + i * 32 + lr) * 16 + lh * 8);
+            s.b[i] = B2D ? *(const uint2*)(sb + OFF_BS + wave * 256 + (wn * 4 + i) * 16 + lh * 8)
+                         : *(const uint2*)(sb + OFF_BS + (wn * WN + i * 32 + lr) * 16 + lh * 8);
 #pragma unroll
         for (int i = 0; i < FM; ++i)
             s.a[i] = *(const uint2*)(sb + OFF_AS + (wm * WM + i * 32 + lr) * 16 + lh * 8);
@@ -288,16 +302,22 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
         }
     };
 
+    // "every DMA but the newest stage's has landed"
+    auto wait_all_but_one_stage = [] {
+        if (B2D) asm volatile("s_waitcnt vmcnt(13)" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    };
+    static_assert(dma_per_stage<true>() == 13 && dma_per_stage<false>() == 16, "wait counts");
     if (nkt > 0) {
         Frag f0, f1;
         Scl sc, nsc;
         // Two stages are in flight at every wait; a thread issues exactly
-        // DMA_PER_STAGE ops per stage (past-the-end stages are clamped loads
-        // into a buffer nobody reads), so vmcnt(16) means "all but the
-        // newest stage have landed".
+        // dma_per_stage ops per stage (past-the-end stages are clamped loads
+        // into a buffer nobody reads), so a vmcnt of that count means "all
+        // but the newest stage have landed".
         issue(0, 0);
         issue(1, 1);
-        asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+        wait_all_but_one_stage();
         __builtin_amdgcn_s_barrier();
         read_frag(f0, 0, 0);
         read_scl(sc, 0);
@@ -311,7 +331,8 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
             mma(f0, sc, 0, kcl >= kc_end);
             // stage kt+1 has landed (own DMA) and every wave is done with
             // its reads of this stage's first half
-            asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)" ::: "memory");
+            wait_all_but_one_stage();
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             __builtin_amdgcn_s_barrier();
             read_frag(f0, (kt + 1) % NST, 0);
             read_scl(nsc, (kt + 1) % NST);
@@ -428,8 +449,10 @@ extern "C" mx_status mx_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_sc
     hipStream_t s = (hipStream_t)stream;
     (void)hipGetLastError();
     if (ct == MX_BF16)
-        hipLaunchKernelGGL((gemm_kernel<true>), dim3((unsigned)tiles), dim3(256), 0, s, p);
+        if (b_scale_2d) hipLaunchKernelGGL((gemm_kernel<true, true>), dim3((unsigned)tiles), dim3(256), 0, s, p);
+        else hipLaunchKernelGGL((gemm_kernel<true, false>), dim3((unsigned)tiles), dim3(256), 0, s, p);
     else
-        hipLaunchKernelGGL((gemm_kernel<false>), dim3((unsigned)tiles), dim3(256), 0, s, p);
+        if (b_scale_2d) hipLaunchKernelGGL((gemm_kernel<false, true>), dim3((unsigned)tiles), dim3(256), 0, s, p);
+        else hipLaunchKernelGGL((gemm_kernel<false, false>), dim3((unsigned)tiles), dim3(256), 0, s, p);
     return hipGetLastError() == hipSuccess ? MX_OK : MX_ERR_LAUNCH;
 }

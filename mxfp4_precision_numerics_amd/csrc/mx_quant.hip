@@ -7,10 +7,12 @@
 //     lane, one 16-byte bf16 load), a wave covers 16 consecutive blocks; the
 //     RHT's stages 8 and 16 cross lanes through DPP quad permutes; the lane's
 //     8 elements take exactly one Philox call when rounding stochastically.
-//   column-wise 1D: a lane owns two adjacent columns and 32 consecutive
-//     tokens; a wave reads 256 contiguous bytes of each token row, the RHT
-//     and the block amax along tokens stay in-lane, and the lane writes the
-//     two 16-byte code runs of the transposed (token-contiguous) layout.
+//   column-wise 1D: a persistent workgroup streams tiles of 256 padded
+//     tokens x 64 columns through LDS (128-byte row reads, the next tile
+//     prefetched into registers while the current one is quantized); a
+//     thread takes 32 tokens of one column from LDS so the RHT and the block
+//     amax stay in-lane, and codes are regrouped in LDS so each column's
+//     tile leaves as one 128-byte run of the token-contiguous layout.
 //   2D: a workgroup owns a 32-row strip of 8 tiles; lanes read 64 contiguous
 //     bytes of one tile row, the tile amax is reduced across lanes and waves,
 //     and the transposed codes are regrouped through LDS.
@@ -152,89 +154,170 @@ __global__ __launch_bounds__(256) void rht_kernel(const void* __restrict__ x, in
 // ===========================================================================
 // Column-wise, grouped 1x32 quantization (blocks run down the token axis of
 // one group; output transposed so tokens are contiguous).
+//
+// A workgroup quantizes tiles of 8 consecutive padded 32-token blocks x 64
+// columns.  The tile's token rows are read with coalesced 16-byte loads into
+// LDS; each thread then takes two adjacent columns of one block from LDS
+// (32 tokens each, so the RHT and the amax stay in-lane); the codes are
+// regrouped in LDS so that every column's 8 blocks leave as one contiguous
+// 128-byte run of the token-contiguous output.
 // ===========================================================================
 constexpr int COL_MAX_GROUPS = 4096;
+constexpr int CT_BLOCKS = 8;                 // padded 32-token blocks per tile
+constexpr int CT_COLS = 64;                  // columns per tile
+constexpr int CT_OUT_PITCH = CT_BLOCKS * 16 + 16;   // LDS bytes per column of staged codes
+
+template <bool BF16>
+struct ColTile {
+    static constexpr int EB = BF16 ? 2 : 4;
+    static constexpr int ROWB = CT_COLS * EB;                 // bytes of one token row of the tile
+    static constexpr int BSTRIDE = 32 * ROWB + 128;           // LDS bytes per block (+128: next block
+                                                              // starts in the other half of the banks)
+    static constexpr int TILE = CT_BLOCKS * BSTRIDE;
+};
 
 template <bool BF16, bool RHT, bool SR>
-__global__ __launch_bounds__(256) void q1d_col_kernel(const void* __restrict__ x, int64_t rows, int64_t cols,
+__global__ __launch_bounds__(256) void q1d_col_kernel(const void* __restrict__ x, int64_t cols,
                                                       const int32_t* __restrict__ off, int num_groups,
-                                                      int64_t kp, int64_t col_pairs_per_row,
+                                                      int64_t kp, int64_t col_tiles, int64_t tiles, int vec,
                                                       uint32_t mask, uint32_t k0, uint32_t k1,
                                                       uint32_t stream_id, uint64_t index_base,
                                                       uint8_t* __restrict__ codes,
                                                       uint8_t* __restrict__ scales) {
-    // padded start (in 32-token blocks) of every group, and its token offset
-    __shared__ int32_t pstart[COL_MAX_GROUPS + 1];
-    for (int g = threadIdx.x; g <= num_groups; g += blockDim.x) pstart[g] = 0;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        int32_t acc = 0;
-        for (int g = 0; g < num_groups; ++g) {
-            pstart[g] = acc;
-            const int32_t n = off[g + 1] - off[g];
-            acc += (n + 31) >> 5;
+    using TL = ColTile<BF16>;
+    constexpr int CH = TL::ROWB / 16;                       // 16-byte chunks per tile row
+    constexpr int NLD = CT_BLOCKS * 32 * CH / 256;           // chunks per thread per tile
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    uint8_t* tile = smem;                                          // TL::TILE bytes
+    int32_t* pstart = (int32_t*)(smem + TL::TILE);                 // num_groups + 1
+    __shared__ int32_t wave_sum[4];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+    // padded start (in 32-token blocks) of every group: block-wide scan of
+    // ceil32(n_g) / 32, each thread summing a contiguous chunk of groups
+    {
+        const int chunk = (num_groups + 255) / 256;
+        const int g0 = min(num_groups, tid * chunk), g1 = min(num_groups, g0 + chunk);
+        int32_t local = 0;
+        for (int g = g0; g < g1; ++g) local += (off[g + 1] - off[g] + 31) >> 5;
+        int32_t incl = local;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int32_t v = __shfl_up(incl, d);
+            if (lane >= d) incl += v;
         }
-        pstart[num_groups] = acc;
+        if (lane == 63) wave_sum[wave] = incl;
+        __syncthreads();
+        int32_t run = incl - local;
+        for (int w = 0; w < wave; ++w) run += wave_sum[w];
+        for (int g = g0; g < g1; ++g) {
+            pstart[g] = run;
+            run += (off[g + 1] - off[g] + 31) >> 5;
+        }
+        if (tid == 255) pstart[num_groups] = run;
+        __syncthreads();
     }
-    __syncthreads();
-    const int64_t nblk_total = (int64_t)pstart[num_groups];
+    const int64_t nblk_total = pstart[num_groups];
     const int64_t kp_blocks = kp >> 5;
 
-    const int64_t items = col_pairs_per_row * kp_blocks;   // (padded block, column pair)
-    for (int64_t it = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; it < items;
-         it += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t pb = it / col_pairs_per_row;
-        const int64_t cp = it - pb * col_pairs_per_row;
-        if (pb >= nblk_total) continue;
-        // group of padded block pb (binary search over pstart)
-        int lo = 0, hi = num_groups - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (pstart[mid] <= pb) lo = mid; else hi = mid - 1;
+    // Token range of the tile's 8 blocks: lane b < 8 of every wave resolves
+    // block b (its group by binary search over pstart); n = -1 marks a block
+    // past the padded total.
+    auto block_info = [&](int64_t pb0, int64_t& t0, int32_t& n) {
+        t0 = 0;
+        n = -1;
+        const int64_t pb = pb0 + lane;
+        if (lane < CT_BLOCKS && pb < nblk_total) {
+            int lo = 0, hi = num_groups - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (pstart[mid] <= pb) lo = mid; else hi = mid - 1;
+            }
+            t0 = (int64_t)off[lo] + (pb - pstart[lo]) * 32;
+            n = (int32_t)min((int64_t)32, (int64_t)off[lo + 1] - t0);
         }
-        // skip empty groups that share the same pstart
-        const int g = lo;
-        const int64_t tok0 = (int64_t)off[g] + (pb - pstart[g]) * 32;
-        const int64_t tok_end = off[g + 1];
-        const int64_t c0 = cp * 2;
-        const bool two = (c0 + 1) < cols;
-        const bool paired = two && ((cols & 1) == 0);   // pair loads stay aligned
-        float a[32], b[32];
+    };
+    auto bcast64 = [](int64_t v, int src) {
+        const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, src);
+        const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)((uint64_t)v >> 32), src);
+        return (int64_t)(((uint64_t)hi << 32) | lo);
+    };
+    // chunk k of this thread: block, row in block, 16-byte chunk in the row
+    auto chunk_b = [&](int k) { return BF16 ? k : (k >> 1); };
+    auto chunk_j = [&](int k) { return BF16 ? (tid >> 3) : ((tid >> 4) + 16 * (k & 1)); };
+    const int chunk_c = tid & (CH - 1);
+    // vector path: the tile's rows into registers (zeros outside the data)
+    auto load_regs = [&](uint4* v, int64_t pb0, int64_t c0) {
+        int64_t t0;
+        int32_t n;
+        block_info(pb0, t0, n);
+        const int64_t col = c0 + chunk_c * (16 / TL::EB);
 #pragma unroll
-        for (int j = 0; j < 32; ++j) {
-            const int64_t r = tok0 + j;
-            if (r < tok_end) {
-                if (BF16) {
-                    const uint16_t* row = (const uint16_t*)x + r * cols + c0;
-                    if (paired) {
-                        const uint32_t w = *(const uint32_t*)row;
-                        a[j] = bf16lo(w);
-                        b[j] = bf16hi(w);
-                    } else {
-                        a[j] = __uint_as_float((uint32_t)row[0] << 16);
-                        b[j] = two ? __uint_as_float((uint32_t)row[1] << 16) : 0.0f;
-                    }
-                } else {
-                    const float* row = (const float*)x + r * cols + c0;
-                    if (paired) {
-                        const float2 w = *(const float2*)row;
-                        a[j] = w.x;
-                        b[j] = w.y;
-                    } else {
-                        a[j] = row[0];
-                        b[j] = two ? row[1] : 0.0f;
-                    }
-                }
-            } else {
-                a[j] = 0.0f;
-                b[j] = 0.0f;
+        for (int k = 0; k < NLD; ++k) {
+            const int b = chunk_b(k), j = chunk_j(k);
+            const int64_t tb = bcast64(t0, b);
+            const int32_t nb = __builtin_amdgcn_readlane(n, b);
+            v[k] = make_uint4(0, 0, 0, 0);
+            if (j < nb && col < cols)
+                v[k] = *(const uint4*)((const uint8_t*)x + ((tb + j) * cols + col) * TL::EB);
+        }
+    };
+
+    const int64_t stride = gridDim.x;
+    int64_t tl = blockIdx.x;
+    uint4 pre[NLD];
+    if (vec && tl < tiles) load_regs(pre, (tl / col_tiles) * CT_BLOCKS, (tl % col_tiles) * CT_COLS);
+    for (; tl < tiles; tl += stride) {
+        const int64_t ct = tl % col_tiles;
+        const int64_t pb0 = (tl / col_tiles) * CT_BLOCKS;
+        // tiles run block-row-major, so once a tile is past the padded total
+        // every later tile of this workgroup is too (uniform exit)
+        if (pb0 >= nblk_total) break;
+        const int64_t c0 = ct * CT_COLS;
+
+        // ---- the tile into LDS (rows past a group's end, columns past cols: 0)
+        if (vec) {
+#pragma unroll
+            for (int k = 0; k < NLD; ++k)
+                *(uint4*)(tile + chunk_b(k) * TL::BSTRIDE + chunk_j(k) * TL::ROWB + chunk_c * 16) = pre[k];
+        } else {
+            int64_t t0;
+            int32_t n;
+            block_info(pb0, t0, n);
+            for (int k = 0; k < CT_BLOCKS * 32 * CT_COLS / 256; ++k) {
+                const int b = k >> 3, j = (tid >> 6) + 4 * (k & 7), cc = tid & 63;
+                const int64_t tb = bcast64(t0, b);
+                const int32_t nb = __builtin_amdgcn_readlane(n, b);
+                const int64_t col = c0 + cc;
+                uint8_t* dst = tile + b * TL::BSTRIDE + j * TL::ROWB + cc * TL::EB;
+                const bool ok = j < nb && col < cols;
+                const int64_t src = (tb + j) * cols + col;
+                if (BF16) *(uint16_t*)dst = ok ? ((const uint16_t*)x)[src] : (uint16_t)0;
+                else *(float*)dst = ok ? ((const float*)x)[src] : 0.0f;
             }
         }
+        __syncthreads();
+        // ---- prefetch the next tile while this one is quantized
+        if (vec) {
+            const int64_t nx = tl + stride;
+            if (nx < tiles && (nx / col_tiles) * CT_BLOCKS < nblk_total)
+                load_regs(pre, (nx / col_tiles) * CT_BLOCKS, (nx % col_tiles) * CT_COLS);
+        }
+
+        // ---- quantize: thread = (block b, column pair cp), one column at a time
+        const int b = tid >> 5, cp = tid & 31;
+        uint4 outc[2];
+        uint32_t outs[2];
 #pragma unroll
         for (int side = 0; side < 2; ++side) {
-            if (side == 1 && !two) break;
-            float* t = side ? b : a;
-            const int64_t c = c0 + side;
+            float t[32];
+#pragma unroll
+            for (int j = 0; j < 32; ++j) {
+                const uint8_t* src = tile + b * TL::BSTRIDE + j * TL::ROWB + (cp * 2 + side) * TL::EB;
+                if (BF16) t[j] = __uint_as_float((uint32_t)(*(const uint16_t*)src) << 16);
+                else t[j] = *(const float*)src;
+            }
+            const int64_t c = c0 + 2 * cp + side;
             if (RHT) {
 #pragma unroll
                 for (int j = 0; j < 32; ++j) t[j] = __uint_as_float(__float_as_uint(t[j]) ^ (((mask >> j) & 1u) << 31));
@@ -249,7 +332,7 @@ __global__ __launch_bounds__(256) void q1d_col_kernel(const void* __restrict__ x
             const uint32_t byte = scale_byte_from_amax_bits(am);
             const float sc = scale_operand(byte);
             uint32_t w[4];
-            const uint64_t ebase = index_base + (uint64_t)c * (uint64_t)kp + (uint64_t)pb * 32;
+            const uint64_t ebase = index_base + (uint64_t)c * (uint64_t)kp + (uint64_t)(pb0 + b) * 32;
 #pragma unroll
             for (int qq = 0; qq < 4; ++qq) {
                 if (SR) {
@@ -261,9 +344,33 @@ __global__ __launch_bounds__(256) void q1d_col_kernel(const void* __restrict__ x
                 }
             }
             if (byte == 0xFFu) w[0] = w[1] = w[2] = w[3] = 0;   // non-finite block: codes are 0
-            *(uint4*)(codes + c * (kp >> 1) + pb * 16) = make_uint4(w[0], w[1], w[2], w[3]);
-            scales[c * kp_blocks + pb] = (uint8_t)byte;
+            outc[side] = make_uint4(w[0], w[1], w[2], w[3]);
+            outs[side] = byte;
         }
+        __syncthreads();                                     // every thread is done reading the tile
+        // ---- regroup: column-major codes [64][8 x 16 B], then scales [64][8]
+        uint8_t* oc = tile;
+        uint8_t* os = tile + CT_COLS * CT_OUT_PITCH;
+#pragma unroll
+        for (int side = 0; side < 2; ++side) {
+            const int col = 2 * cp + side;
+            *(uint4*)(oc + col * CT_OUT_PITCH + b * 16) = outc[side];
+            os[col * CT_BLOCKS + b] = (uint8_t)outs[side];
+        }
+        __syncthreads();
+        // ---- store: 8 lanes write one column's 8 blocks (128 contiguous bytes)
+        const int64_t nv = min((int64_t)CT_BLOCKS, nblk_total - pb0);
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int q = tid + 256 * k;
+            const int col = q >> 3, ch = q & 7;
+            if (c0 + col < cols && ch < nv) {
+                *(uint4*)(codes + (c0 + col) * (kp >> 1) + (pb0 + ch) * 16) =
+                    *(const uint4*)(oc + col * CT_OUT_PITCH + ch * 16);
+                scales[(c0 + col) * kp_blocks + pb0 + ch] = os[col * CT_BLOCKS + ch];
+            }
+        }
+        __syncthreads();                                     // LDS is reused by the next tile
     }
 }
 
@@ -416,6 +523,16 @@ namespace {
 
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Workgroups that fit on the current device at `per_cu` per compute unit.
+inline int resident_blocks(int per_cu) {
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
+    }
+    return cus * per_cu;
+}
+
 inline int grid_for(int64_t work_items, int items_per_block) {
     int64_t g = (work_items + items_per_block - 1) / items_per_block;
     const int64_t cap = 256 * 32;   // enough resident waves; loops cover the rest
@@ -487,26 +604,27 @@ mx_status mx_rht(const void* x, mx_dtype xt, float* y, int64_t rows, int64_t col
     return launched();
 }
 
-#define MX_DISPATCH3(KERNEL, B, R, S, GRID, STREAM, ...)                                              \
+#define MX_DISPATCH3_LDS(KERNEL, B, R, S, GRID, LDS, STREAM, ...)                                              \
     do {                                                                                            \
         if (B) {                                                                                    \
             if (R) {                                                                                \
-                if (S) hipLaunchKernelGGL((KERNEL<true, true, true>), GRID, dim3(256), 0, STREAM, __VA_ARGS__);   \
-                else hipLaunchKernelGGL((KERNEL<true, true, false>), GRID, dim3(256), 0, STREAM, __VA_ARGS__);    \
+                if (S) hipLaunchKernelGGL((KERNEL<true, true, true>), GRID, dim3(256), LDS, STREAM, __VA_ARGS__);   \
+                else hipLaunchKernelGGL((KERNEL<true, true, false>), GRID, dim3(256), LDS, STREAM, __VA_ARGS__);    \
             } else {                                                                                \
-                if (S) hipLaunchKernelGGL((KERNEL<true, false, true>), GRID, dim3(256), 0, STREAM, __VA_ARGS__);  \
-                else hipLaunchKernelGGL((KERNEL<true, false, false>), GRID, dim3(256), 0, STREAM, __VA_ARGS__);   \
+                if (S) hipLaunchKernelGGL((KERNEL<true, false, true>), GRID, dim3(256), LDS, STREAM, __VA_ARGS__);  \
+                else hipLaunchKernelGGL((KERNEL<true, false, false>), GRID, dim3(256), LDS, STREAM, __VA_ARGS__);   \
             }                                                                                       \
         } else {                                                                                    \
             if (R) {                                                                                \
-                if (S) hipLaunchKernelGGL((KERNEL<false, true, true>), GRID, dim3(256), 0, STREAM, __VA_ARGS__);  \
-                else hipLaunchKernelGGL((KERNEL<false, true, false>), GRID, dim3(256), 0, STREAM, __VA_ARGS__);   \
+                if (S) hipLaunchKernelGGL((KERNEL<false, true, true>), GRID, dim3(256), LDS, STREAM, __VA_ARGS__);  \
+                else hipLaunchKernelGGL((KERNEL<false, true, false>), GRID, dim3(256), LDS, STREAM, __VA_ARGS__);   \
             } else {                                                                                \
-                if (S) hipLaunchKernelGGL((KERNEL<false, false, true>), GRID, dim3(256), 0, STREAM, __VA_ARGS__); \
-                else hipLaunchKernelGGL((KERNEL<false, false, false>), GRID, dim3(256), 0, STREAM, __VA_ARGS__);  \
+                if (S) hipLaunchKernelGGL((KERNEL<false, false, true>), GRID, dim3(256), LDS, STREAM, __VA_ARGS__); \
+                else hipLaunchKernelGGL((KERNEL<false, false, false>), GRID, dim3(256), LDS, STREAM, __VA_ARGS__);  \
             }                                                                                       \
         }                                                                                           \
     } while (0)
+#define MX_DISPATCH3(KERNEL, B, R, S, GRID, STREAM, ...) MX_DISPATCH3_LDS(KERNEL, B, R, S, GRID, 0, STREAM, __VA_ARGS__)
 
 mx_status mx_quantize_1d(const void* x, mx_dtype xt, int64_t rows, int64_t cols, int block_axis,
                          const int32_t* group_offsets, int32_t num_groups, int64_t kp, int use_rht,
@@ -539,12 +657,28 @@ mx_status mx_quantize_1d(const void* x, mx_dtype xt, int64_t rows, int64_t cols,
     if (kp == 0 || rows == 0) return MX_OK;
     if (!x || !codes || !scales) return MX_ERR_NULL;
     if (!aligned16(x) || !aligned16(codes)) return MX_ERR_ALIGN;
-    const int64_t cpairs = (cols + 1) / 2;
-    const int64_t items = cpairs * (kp / 32);
-    const int grid = grid_for(items, 256);
+    const int64_t col_tiles = (cols + CT_COLS - 1) / CT_COLS;
+    const int64_t tiles = col_tiles * ((kp / 32 + CT_BLOCKS - 1) / CT_BLOCKS);
+    // persistent grid, sized to residency: the bf16 RHT+SR variant needs
+    // ~150 VGPRs (3 workgroups per CU); fp32 tiles take 66 KiB of LDS and
+    // up to ~240 VGPRs (2 per CU)
+    const int grid = (int)min(tiles, (int64_t)resident_blocks(bf ? 3 : 2));
+    const int vec = (cols % (bf ? 8 : 4)) == 0;
+    const size_t lds = (size_t)(bf ? ColTile<true>::TILE : ColTile<false>::TILE) + 4 * (size_t)(num_groups + 1);
+    if (!bf) {
+        static bool attr_set = false;
+        if (!attr_set) {
+            const int mx_lds = ColTile<false>::TILE + 4 * (COL_MAX_GROUPS + 1);
+            (void)hipFuncSetAttribute((const void*)q1d_col_kernel<false, false, false>, hipFuncAttributeMaxDynamicSharedMemorySize, mx_lds);
+            (void)hipFuncSetAttribute((const void*)q1d_col_kernel<false, false, true>, hipFuncAttributeMaxDynamicSharedMemorySize, mx_lds);
+            (void)hipFuncSetAttribute((const void*)q1d_col_kernel<false, true, false>, hipFuncAttributeMaxDynamicSharedMemorySize, mx_lds);
+            (void)hipFuncSetAttribute((const void*)q1d_col_kernel<false, true, true>, hipFuncAttributeMaxDynamicSharedMemorySize, mx_lds);
+            attr_set = true;
+        }
+    }
     (void)hipGetLastError();
-    MX_DISPATCH3(q1d_col_kernel, bf, rh, sr, dim3(grid), s, x, rows, cols, group_offsets, (int)num_groups, kp,
-                 cpairs, sign_mask, k0, k1, stream_id, index_base, codes, scales);
+    MX_DISPATCH3_LDS(q1d_col_kernel, bf, rh, sr, dim3(grid), lds, s, x, cols, group_offsets, (int)num_groups, kp,
+                     col_tiles, tiles, vec, sign_mask, k0, k1, stream_id, index_base, codes, scales);
     return launched();
 }
 
