@@ -13,9 +13,10 @@
 //     thread takes 32 tokens of one column from LDS so the RHT and the block
 //     amax stay in-lane, and codes are regrouped in LDS so each column's
 //     tile leaves as one 128-byte run of the token-contiguous layout.
-//   2D: a workgroup owns a 32-row strip of 8 tiles; lanes read 64 contiguous
-//     bytes of one tile row, the tile amax is reduced across lanes and waves,
-//     and the transposed codes are regrouped through LDS.
+//   2D: a workgroup owns up to 8 x 8 tiles (256 x 256) and walks its tile
+//     rows; lanes read 64 contiguous bytes of one tile row, the tile amax is
+//     reduced across lanes and waves, and the transposed codes are regrouped
+//     through LDS so each column leaves as one contiguous run.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <string.h>
@@ -376,17 +377,26 @@ __global__ __launch_bounds__(256) void q1d_col_kernel(const void* __restrict__ x
 
 // ===========================================================================
 // 32x32 quantization (RTNE), both layouts in one pass.
-// Workgroup: 256 threads, a strip of 32 rows x 8 tiles (256 columns).
-// Thread t: strip row r = t / 8, tile j = t % 8, 32 contiguous elements.
+// A workgroup owns a super-strip of up to 8 tile rows x 8 tiles (256 x 256
+// elements) and walks its tile rows one at a time.  Per tile row, thread t
+// takes row r = t / 8 of tile j = t % 8 (32 contiguous elements); the tile
+// amax is reduced across lanes and waves, the row's 16 code bytes go straight
+// to the as-given layout (8 threads cover a row's 128 contiguous bytes), and
+// are kept in LDS.  After the last tile row the codes are regrouped by
+// column, so every column of W leaves as up to 128 contiguous bytes of the
+// transposed layout written by one workgroup (full lines, no partial lines
+// merged across XCDs).
 // ===========================================================================
+constexpr int Q2_TR = 8;   // tile rows per super-strip
+
 template <bool BF16>
 __global__ __launch_bounds__(256) void q2d_kernel(const void* __restrict__ w, int64_t rows, int64_t cols,
-                                                  int64_t strips_per_row, int64_t nstrips,
+                                                  int64_t col_strips, int64_t row_strips, int64_t nsuper,
                                                   uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
                                                   uint8_t* __restrict__ codes_t, uint8_t* __restrict__ scales_t) {
     __shared__ uint32_t wave_amax[4][8];
-    __shared__ uint32_t tile_scale[8];
-    __shared__ uint4 tcodes[8][32];   // [tile][row] 16 bytes of row codes
+    __shared__ uint8_t tile_scale[Q2_TR][8];
+    __shared__ uint4 tcodes[Q2_TR][8][32];   // [tile row][tile][row] 16 bytes of row codes
     const int t = threadIdx.x;
     const int r = t >> 3;          // 0..31
     const int j = t & 7;           // tile within the strip
@@ -394,86 +404,98 @@ __global__ __launch_bounds__(256) void q2d_kernel(const void* __restrict__ w, in
     const int wv = t >> 6;
     const int64_t tiles_per_row = cols >> 5;
     const int64_t row_tiles = rows >> 5;
-    for (int64_t s = blockIdx.x; s < nstrips; s += gridDim.x) {
-        const int64_t bt_tr = s / strips_per_row;         // batch * row_tiles + tile row
-        const int64_t sc_ = s - bt_tr * strips_per_row;   // strip along columns
-        const int64_t bt = bt_tr / row_tiles;
-        const int64_t tr = bt_tr - bt * row_tiles;
-        const int64_t tile = sc_ * 8 + j;
+    for (int64_t s = blockIdx.x; s < nsuper; s += gridDim.x) {
+        const int64_t bt = s / (row_strips * col_strips);
+        const int64_t rem = s - bt * row_strips * col_strips;
+        const int64_t rs = rem / col_strips;
+        const int64_t cs = rem - rs * col_strips;
+        const int64_t tr0 = rs * Q2_TR;
+        const int ntr = (int)min((int64_t)Q2_TR, row_tiles - tr0);
+        const int64_t tile = cs * 8 + j;
         const bool valid = tile < tiles_per_row;
-        const int64_t grow = bt * rows + tr * 32 + r;      // global row in the batch stack
-        float v[32];
-        if (valid) {
-            if (BF16) {
-                const uint4* p = (const uint4*)((const uint16_t*)w + grow * cols + tile * 32);
+        for (int ts = 0; ts < ntr; ++ts) {
+            const int64_t tr = tr0 + ts;
+            const int64_t grow = bt * rows + tr * 32 + r;      // global row in the batch stack
+            float v[32];
+            if (valid) {
+                if (BF16) {
+                    const uint4* p = (const uint4*)((const uint16_t*)w + grow * cols + tile * 32);
 #pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const uint4 q = p[k];
-                    v[8 * k + 0] = bf16lo(q.x); v[8 * k + 1] = bf16hi(q.x);
-                    v[8 * k + 2] = bf16lo(q.y); v[8 * k + 3] = bf16hi(q.y);
-                    v[8 * k + 4] = bf16lo(q.z); v[8 * k + 5] = bf16hi(q.z);
-                    v[8 * k + 6] = bf16lo(q.w); v[8 * k + 7] = bf16hi(q.w);
+                    for (int k = 0; k < 4; ++k) {
+                        const uint4 q = p[k];
+                        v[8 * k + 0] = bf16lo(q.x); v[8 * k + 1] = bf16hi(q.x);
+                        v[8 * k + 2] = bf16lo(q.y); v[8 * k + 3] = bf16hi(q.y);
+                        v[8 * k + 4] = bf16lo(q.z); v[8 * k + 5] = bf16hi(q.z);
+                        v[8 * k + 6] = bf16lo(q.w); v[8 * k + 7] = bf16hi(q.w);
+                    }
+                } else {
+                    const uint4* p = (const uint4*)((const float*)w + grow * cols + tile * 32);
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) {
+                        const uint4 q = p[k];
+                        v[4 * k + 0] = __uint_as_float(q.x); v[4 * k + 1] = __uint_as_float(q.y);
+                        v[4 * k + 2] = __uint_as_float(q.z); v[4 * k + 3] = __uint_as_float(q.w);
+                    }
                 }
             } else {
-                const uint4* p = (const uint4*)((const float*)w + grow * cols + tile * 32);
 #pragma unroll
-                for (int k = 0; k < 8; ++k) {
-                    const uint4 q = p[k];
-                    v[4 * k + 0] = __uint_as_float(q.x); v[4 * k + 1] = __uint_as_float(q.y);
-                    v[4 * k + 2] = __uint_as_float(q.z); v[4 * k + 3] = __uint_as_float(q.w);
-                }
+                for (int k = 0; k < 32; ++k) v[k] = 0.0f;
             }
-        } else {
+            uint32_t am = 0;
 #pragma unroll
-            for (int k = 0; k < 32; ++k) v[k] = 0.0f;
-        }
-        uint32_t am = 0;
-#pragma unroll
-        for (int k = 0; k < 32; ++k) am = max(am, __float_as_uint(v[k]) & 0x7FFFFFFFu);
-        // lanes with the same j within the wave: xor 8, 16, 32
-        am = max(am, (uint32_t)__shfl_xor((int)am, 8));
-        am = max(am, (uint32_t)__shfl_xor((int)am, 16));
-        am = max(am, (uint32_t)__shfl_xor((int)am, 32));
-        if (lane < 8) wave_amax[wv][lane] = am;
-        __syncthreads();
-        if (t < 8) {
-            const uint32_t m = max(max(wave_amax[0][t], wave_amax[1][t]), max(wave_amax[2][t], wave_amax[3][t]));
-            tile_scale[t] = scale_byte_from_amax_bits(m);
-        }
-        __syncthreads();
-        const uint32_t byte = tile_scale[j];
-        const float sc = scale_operand(byte);
-        uint32_t cw[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) cw[k] = byte == 0xFFu ? 0u : cvt8_rne(v + 8 * k, sc);
-        if (valid && codes) *(uint4*)(codes + grow * (cols >> 1) + tile * 16) = make_uint4(cw[0], cw[1], cw[2], cw[3]);
-        if (valid && r == 0) {
-            if (scales) scales[(bt * row_tiles + tr) * tiles_per_row + tile] = (uint8_t)byte;
-            if (scales_t) scales_t[(bt * tiles_per_row + tile) * row_tiles + tr] = (uint8_t)byte;
-        }
-        if (codes_t) {
-            tcodes[j][r] = make_uint4(cw[0], cw[1], cw[2], cw[3]);
+            for (int k = 0; k < 32; ++k) am = max(am, __float_as_uint(v[k]) & 0x7FFFFFFFu);
+            // lanes with the same j within the wave: xor 8, 16, 32
+            am = max(am, (uint32_t)__shfl_xor((int)am, 8));
+            am = max(am, (uint32_t)__shfl_xor((int)am, 16));
+            am = max(am, (uint32_t)__shfl_xor((int)am, 32));
+            if (lane < 8) wave_amax[wv][lane] = am;
             __syncthreads();
-            // thread t: tile jj = t / 32, column cc = t % 32 of that tile
+            if (t < 8) {
+                const uint32_t m = max(max(wave_amax[0][t], wave_amax[1][t]), max(wave_amax[2][t], wave_amax[3][t]));
+                tile_scale[ts][t] = (uint8_t)scale_byte_from_amax_bits(m);
+            }
+            __syncthreads();
+            const uint32_t byte = tile_scale[ts][j];
+            const float sc = scale_operand(byte);
+            uint32_t cw[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) cw[k] = byte == 0xFFu ? 0u : cvt8_rne(v + 8 * k, sc);
+            if (valid && codes) *(uint4*)(codes + grow * (cols >> 1) + tile * 16) = make_uint4(cw[0], cw[1], cw[2], cw[3]);
+            if (valid && r == 0 && scales) scales[(bt * row_tiles + tr) * tiles_per_row + tile] = (uint8_t)byte;
+            tcodes[ts][j][r] = make_uint4(cw[0], cw[1], cw[2], cw[3]);
+        }
+        __syncthreads();
+        if (codes_t) {
+            // thread t: tile jj = t / 32, column cc = t % 32 of that tile; one
+            // 16-byte run per tile row, the runs of a column contiguous
             const int jj = t >> 5;
             const int cc = t & 31;
-            const int64_t tile2 = sc_ * 8 + jj;
+            const int64_t tile2 = cs * 8 + jj;
             if (tile2 < tiles_per_row) {
                 const int word = cc >> 3;            // dword holding column cc in a row
                 const int sh = (cc & 7) * 4;
-                uint32_t o[4] = {0, 0, 0, 0};
-#pragma unroll
-                for (int rr = 0; rr < 32; ++rr) {
-                    const uint4 q = tcodes[jj][rr];
-                    const uint32_t wd = word == 0 ? q.x : word == 1 ? q.y : word == 2 ? q.z : q.w;
-                    const uint32_t nib = (wd >> sh) & 0xFu;
-                    o[rr >> 3] |= nib << ((rr & 7) * 4);
-                }
                 const int64_t col = tile2 * 32 + cc;
-                *(uint4*)(codes_t + (bt * cols + col) * (rows >> 1) + tr * 16) = make_uint4(o[0], o[1], o[2], o[3]);
+                uint8_t* dst = codes_t + (bt * cols + col) * (rows >> 1) + tr0 * 16;
+                for (int ts = 0; ts < ntr; ++ts) {
+                    uint32_t o[4] = {0, 0, 0, 0};
+#pragma unroll
+                    for (int rr = 0; rr < 32; ++rr) {
+                        const uint32_t wd = ((const uint32_t*)&tcodes[ts][jj][rr])[word];
+                        o[rr >> 3] |= ((wd >> sh) & 0xFu) << ((rr & 7) * 4);
+                    }
+                    *(uint4*)(dst + ts * 16) = make_uint4(o[0], o[1], o[2], o[3]);
+                }
+            }
+            // transposed scales: lanes 8 jj .. 8 jj + 7 write one tile column's
+            // consecutive tile-row bytes
+            if (scales_t && t < 64) {
+                const int jt = t >> 3, ts = t & 7;
+                const int64_t tile3 = cs * 8 + jt;
+                if (tile3 < tiles_per_row && ts < ntr)
+                    scales_t[(bt * tiles_per_row + tile3) * row_tiles + tr0 + ts] = tile_scale[ts][jt];
             }
         }
-        __syncthreads();
+        __syncthreads();                       // LDS is reused by the next super-strip
     }
 }
 
@@ -692,17 +714,18 @@ mx_status mx_quantize_2d(const void* w, mx_dtype wt, int64_t batch, int64_t rows
     if (batch == 0 || rows == 0 || cols == 0) return MX_OK;
     if (!w) return MX_ERR_NULL;
     if (!aligned16(w) || (codes && !aligned16(codes)) || (codes_t && !aligned16(codes_t))) return MX_ERR_ALIGN;
-    const int64_t strips_per_row = (cols / 32 + 7) / 8;
-    const int64_t nstrips = batch * (rows / 32) * strips_per_row;
-    const int grid = grid_for(nstrips, 1);
+    const int64_t col_strips = (cols / 32 + 7) / 8;
+    const int64_t row_strips = (rows / 32 + Q2_TR - 1) / Q2_TR;
+    const int64_t nsuper = batch * row_strips * col_strips;
+    const int grid = grid_for(nsuper, 1);
     hipStream_t s = (hipStream_t)stream;
     (void)hipGetLastError();
     if (wt == MX_BF16)
-        hipLaunchKernelGGL((q2d_kernel<true>), dim3(grid), dim3(256), 0, s, w, rows, cols, strips_per_row, nstrips,
-                           codes, scales, codes_t, scales_t);
+        hipLaunchKernelGGL((q2d_kernel<true>), dim3(grid), dim3(256), 0, s, w, rows, cols, col_strips, row_strips,
+                           nsuper, codes, scales, codes_t, scales_t);
     else
-        hipLaunchKernelGGL((q2d_kernel<false>), dim3(grid), dim3(256), 0, s, w, rows, cols, strips_per_row, nstrips,
-                           codes, scales, codes_t, scales_t);
+        hipLaunchKernelGGL((q2d_kernel<false>), dim3(grid), dim3(256), 0, s, w, rows, cols, col_strips, row_strips,
+                           nsuper, codes, scales, codes_t, scales_t);
     return launched();
 }
 
