@@ -168,10 +168,76 @@ def test_colwise_odd_columns_fp32():
     _assert_same(host(c)[:, :48], oc[:, :48], "codes")
 
 
+@pytest.mark.parametrize("dt,cols", [("f32", 100), ("bf16", 70), ("bf16", 136)])
+def test_colwise_vector_and_ragged_column_paths(dt, cols):
+    # fp32 with 16-byte row loads (cols % 4 == 0), bf16 with a column count
+    # that is not a multiple of 8 (element loads), and a bf16 width whose last
+    # 64-column tile is partly outside the matrix
+    counts = [300, 17, 0, 5, 64]
+    off = synth.offsets_from_counts(counts)
+    rows = int(off[-1])
+    rng = np.random.default_rng(cols)
+    x = (rng.standard_normal((rows, cols)) * np.exp2(rng.integers(-6, 6, (1, cols)))).astype(np.float32)
+    if dt == "bf16":
+        x = synth.f32_to_bf16_bits(x)
+        xd = dev_bf16(x)
+    else:
+        xd = dev(x)
+    kp = mx.padded_capacity(rows, len(counts))
+    mask = mx.rht_sign_mask(11)
+    c, s = mx.quantize_1d(xd, block_axis=0, group_offsets=dev(off), kp=kp, use_rht=True, sign_mask=mask,
+                          rnd=1, seed=13, stream_id=3)
+    oc, os_ = oracle.quantize_1d(x, block_axis=0, group_offsets=off, kp=kp, use_rht=True, sign_mask=mask,
+                                 rnd=1, seed=13, stream=3)
+    total = oracle.padded_total(off)
+    _assert_same(host(s)[:, :total // 32], os_[:, :total // 32], "scales")
+    _assert_same(host(c)[:, :total // 2], oc[:, :total // 2], "codes")
+
+
+def test_colwise_many_groups():
+    # more groups than threads in a workgroup: the padded-start scan sums
+    # several groups per thread; many groups are empty or under 32 tokens
+    rng = np.random.default_rng(21)
+    counts = rng.integers(0, 40, 300)
+    counts[rng.integers(0, 300, 60)] = 0
+    off = synth.offsets_from_counts(counts)
+    rows, cols = int(off[-1]), 64
+    x = synth.f32_to_bf16_bits(rng.standard_normal((rows, cols)).astype(np.float32))
+    kp = mx.padded_capacity(rows, len(counts))
+    c, s = mx.quantize_1d(dev_bf16(x), block_axis=0, group_offsets=dev(off), kp=kp, rnd=1, seed=4, stream_id=1)
+    oc, os_ = oracle.quantize_1d(x, block_axis=0, group_offsets=off, kp=kp, rnd=1, seed=4, stream=1)
+    total = oracle.padded_total(off)
+    _assert_same(host(s)[:, :total // 32], os_[:, :total // 32], "scales")
+    _assert_same(host(c)[:, :total // 2], oc[:, :total // 2], "codes")
+
+
+def test_colwise_full_size_sampled_columns():
+    # the weight-gradient operand at its real shape: 65,536 routed token rows
+    # x 2880, 32 Zipf-sized expert segments, RHT + SR.  The GPU quantizes the
+    # whole matrix; the oracle checks sampled columns, each run on its own
+    # with the column's element-index offset (c * kp) as index_base.
+    counts = synth.zipf_counts()
+    off = synth.offsets_from_counts(counts)
+    rows, cols = int(off[-1]), 2880
+    x = synth.normal_bf16((rows, cols), 1e-3, seed=5)
+    kp = mx.padded_capacity(rows, len(counts))
+    mask = mx.rht_sign_mask(5)
+    c, s = mx.quantize_1d(dev_bf16(x), block_axis=0, group_offsets=dev(off), kp=kp, use_rht=True,
+                          sign_mask=mask, rnd=1, seed=5, stream_id=5)
+    ch, sh = host(c), host(s)
+    total = oracle.padded_total(off)
+    for col in (0, 1, 63, 64, 1407, 2879):
+        oc, os_ = oracle.quantize_1d(np.ascontiguousarray(x[:, col:col + 1]), block_axis=0, group_offsets=off,
+                                     kp=kp, use_rht=True, sign_mask=mask, rnd=1, seed=5, stream=5,
+                                     index_base=col * kp)
+        _assert_same(sh[col:col + 1, :total // 32], os_[:, :total // 32], "scales col %d" % col)
+        _assert_same(ch[col:col + 1, :total // 2], oc[:, :total // 2], "codes col %d" % col)
+
+
 # ---------------------------------------------------------------------------
 # 2D 32x32
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("batch,rows,cols", [(1, 32, 32), (2, 64, 288), (3, 96, 544)])
+@pytest.mark.parametrize("batch,rows,cols", [(1, 32, 32), (2, 64, 288), (3, 96, 544), (1, 320, 96)])
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
 def test_2d_parity_both_layouts(batch, rows, cols, dt):
     rng = np.random.default_rng(rows + cols)
