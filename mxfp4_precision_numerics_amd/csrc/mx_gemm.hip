@@ -16,23 +16,27 @@
 //
 // Tiling: a workgroup of 4 waves (2 x 2) computes a 256 x 256 tile of one
 // group; each wave owns 128 x 128 (16 MFMA blocks, 256 accumulators held in
-// AGPRs).  K advances 128 per stage.  Every operand byte moves global -> LDS
-// by the CDNA LDS-DMA loads (global_load_lds_dwordx4 for 16-byte code
-// chunks, global_load_lds_ubyte for scale bytes, each landing as a dword), so
-// no staging registers are needed: a 3-buffer LDS ring keeps two stages in
-// flight while one is multiplied.  The DMA is issued from register-only
-// inline assembly and its completion is awaited explicitly (s_waitcnt
-// vmcnt + s_barrier), which lets a stage land while the two before it are
-// still outstanding.  Operand fragments are double-buffered in registers:
-// the second K-half of a stage is read while the first multiplies, and the
-// next stage's first half is read while the second multiplies.
+// AGPRs).  K advances 256 per stage, so every operand row contributes one
+// 128-byte line per stage (half-line requests cost nearly as much as full
+// ones at the L2).  Every operand byte moves global -> LDS by the CDNA
+// LDS-DMA loads (global_load_lds_dwordx4 for 16-byte code chunks, 8 lanes per
+// row line; global_load_lds_ubyte for scale bytes, each landing as a dword),
+// so no staging registers are needed.  The ring has two 80 KiB buffers (all
+// of a CU's LDS): stage kt+2 is issued at stage kt's barrier into the buffer
+// stage kt has just finished reading, which leaves it a full stage to land.
+// The DMA is issued from register-only inline assembly and its completion is
+// awaited explicitly (s_waitcnt vmcnt + s_barrier).  A stage runs as four
+// K-quarters of 64; operand fragments are double-buffered in registers and
+// the next quarter's eight fragment reads are interleaved one per MFMA with
+// the current quarter's sixteen MFMAs.
 //
-// LDS code tiles use an XOR swizzle of 16-byte chunks; each row's 4 scale
-// dwords are stored in the order (s0, s2, s1, s3), so one 8-byte read gives a
-// lane the scales of both K-halves.  A chunk at or past the end of the K
-// range is loaded from a clamped (valid) address and its scale is forced to
-// 2^-127 on both operands, so its products (at most 36 * 2^-254) vanish in
-// the fp32 accumulation.
+// LDS code tiles use an XOR swizzle of the eight 16-byte chunks of a row;
+// each row's 8 scale dwords are stored in the order (s0, s2, s4, s6, s1, s3,
+// s5, s7), so one 16-byte read gives a lane the scales of its four
+// K-quarters.  A chunk at or past the end of the K range is loaded from a
+// clamped (valid) address and its scale is forced to 2^-127 on both
+// operands, so its products (at most 36 * 2^-254) vanish in the fp32
+// accumulation.
 //
 // Tile order: 32 consecutive tile ids cover 4 M-tiles x 8 N-tiles of one
 // group, and blocks of 32 ids are dealt round-robin to the 8 XCDs (work-
@@ -66,26 +70,28 @@ struct GemmArgs {
 };
 
 constexpr int BM = 256, BN = 256;
-constexpr int BK = 128;            // K elements per stage
-constexpr int NST = 3;             // LDS ring depth
+constexpr int BK = 256;            // K elements per stage: 128 code bytes per row
+constexpr int NST = 2;             // LDS ring depth (2 x 80 KiB: all of a CU's LDS)
 constexpr int GROUP_M = 4;         // M-tiles per tile-order group
 constexpr int XCDS = 8;
 constexpr int XCD_BLOCK = 32;      // consecutive tile ids per XCD turn
-// one stage in LDS: A codes, B codes (256 rows x 64 bytes each), A and B
-// scales (256 rows x 4 dwords each)
-constexpr int OFF_A = 0, OFF_B = 16384, OFF_AS = 32768, OFF_BS = 36864;
-constexpr int STAGE_BYTES = 40960;
-// DMA ops per thread per stage: 8 code moves, 4 A-scale moves, and 4 B-scale
+// one stage in LDS: A codes, B codes (256 rows x 128 bytes each), A and B
+// scales (256 rows x 8 dwords each)
+constexpr int OFF_A = 0, OFF_B = 32768, OFF_AS = 65536, OFF_BS = 73728;
+constexpr int STAGE_BYTES = 81920;
+// DMA ops per thread per stage: 16 code moves, 8 A-scale moves, and 8 B-scale
 // moves (1D B scales) or 1 (2D B scales: 8 row groups of 32 per tile).
 template <bool B2D>
-constexpr int dma_per_stage() { return B2D ? 13 : 16; }
+constexpr int dma_per_stage() { return B2D ? 25 : 32; }
 
-// 16-byte chunk swizzle: the 32 rows an MFMA operand read touches at one
-// chunk index land in distinct bank groups whether the LDS serves 8 lanes
-// (32 banks) or 16 lanes (64 banks) of a ds_read_b128 per cycle.
-__device__ __forceinline__ int swz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
-// scale dword slot p of a row holds chunk (0, 2, 1, 3)[p] (an involution)
-__device__ __forceinline__ int sperm(int p) { return ((p & 1) << 1) | ((p >> 1) & 1); }
+// 16-byte chunk swizzle of a 128-byte row: the rows an MFMA operand read
+// touches at one chunk index land in distinct 16-byte bank groups whether
+// the LDS serves 8 lanes (32 banks: rows r..r+7) or 16 lanes (64 banks: the
+// even and the odd rows of r..r+15) of a ds_read_b128 per cycle.
+__device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+// scale dword slot p of a row holds chunk (0, 2, 4, 6, 1, 3, 5, 7)[p], so
+// lane half h reads the chunks of its four K-quarters (2 q + h) in one go
+__device__ __forceinline__ int sperm(int p) { return p < 4 ? 2 * p : 2 * (p - 4) + 1; }
 
 // LDS-DMA: every lane moves 16 bytes (or 1 byte, zero-extended to a dword)
 // from base + voff to LDS byte address lds + 16 lane (or + 4 lane).  M0
@@ -125,7 +131,9 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
     // counts ceil(n_g / BM) * tiles_n across its lanes and publishes the
     // group holding tile `id` (one round trip to memory instead of one per
     // group).
-    __shared__ int32_t tile_group[2];
+    // the tile decode's result lives in the first ring bytes until every
+    // thread has read it (the ring fills all 160 KiB of LDS)
+    int32_t* tile_group = (int32_t*)lds;
     int g = 0;
     int64_t m_begin = 0, m_end = 0, k_begin = 0, k_end = p.K, mtiles = 0;
     if (p.group_dim_k == 0) {
@@ -158,6 +166,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
         g = __builtin_amdgcn_readfirstlane(tile_group[0]);   // uniform: the DMA takes scalar bases
         if (g < 0) return;                      // past the last tile (uniform)
         id = __builtin_amdgcn_readfirstlane(tile_group[1]);
+        __syncthreads();                        // read by all before the ring's first DMA
         m_begin = p.off[g];
         m_end = p.off[g + 1];
         mtiles = (m_end - m_begin + BM - 1) / BM;
@@ -195,16 +204,17 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
     }
 
     // ---------------- per-thread DMA assignments ----------------
-    // DMA j of thread t fills LDS slot t + 256 j of each operand: row
-    // r = t/4 + 64 j, slot position pc = t % 4 within the row.
-    const int pc = tid & 3;
-    uint32_t a_off[4], b_off[4], as_off[4], bs_off[4];
-    int a_chunk[4], s_chunk;
-    s_chunk = sperm(pc);
+    // Code DMA j of thread t fills 16-byte slot t + 256 j of an operand tile:
+    // row r = t/8 + 32 j, slot position pc = t % 8 of the row's 128 bytes, so
+    // 8 lanes move one full 128-byte line.  Scale DMA j fills dword slot
+    // t + 256 j: the same row, scale position pc.
+    const int pc = tid & 7;
+    const int a_chunk = pc ^ swz(tid >> 3);    // swz(t/8 + 32 j) is the same for every j
+    const int s_chunk = sperm(pc);
+    uint32_t a_off[8], b_off[8], as_off[8], bs_off[8];
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-        const int r = (tid >> 2) + 64 * jj;
-        a_chunk[jj] = pc ^ swz(r);            // code chunk this lane fetches
+    for (int jj = 0; jj < 8; ++jj) {
+        const int r = (tid >> 3) + 32 * jj;
         int64_t m = m_begin + r;
         if (m >= m_end) m = m_end - 1;        // rows past the tile end are never stored
         const int64_t arow = p.a_row_index ? (int64_t)p.a_row_index[m] : m;
@@ -215,12 +225,11 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
         b_off[jj] = (uint32_t)(n * KB);
         bs_off[jj] = (uint32_t)(n * KS);
     }
-    // 2D B scales: lane l of every wave fetches row group (l / 4) % 8 of the
-    // tile at slot position l % 4 (lanes 32..63 repeat lanes 0..31), into its
-    // wave's own 256-byte copy
+    // 2D B scales: lane l of every wave fetches row group l / 8 of the tile at
+    // scale position l % 8, into its wave's own 256-byte copy
     uint32_t bs2_off = 0;
     if (B2D) {
-        int64_t grp = n_begin / 32 + ((lane >> 2) & 7);
+        int64_t grp = n_begin / 32 + (lane >> 3);
         if (grp > p.N / 32 - 1) grp = p.N / 32 - 1;    // groups past N are never stored
         bs2_off = (uint32_t)(grp * KS);
     }
@@ -230,24 +239,33 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
     const int nkt = (int)((klen + BK - 1) / BK);
     const int64_t kc0 = k_begin / 32;        // first K-chunk of the range
     const int64_t kc_end = k_end / 32;
+    // K chunks relative to kc0 (32-bit: the host bounds an operand row to 4 GiB)
+    const int kc_last = (int)(kc_end - kc0) - 1;
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+        a_off[jj] += (uint32_t)(kc0 * 16);
+        b_off[jj] += (uint32_t)(kc0 * 16);
+        as_off[jj] += (uint32_t)kc0;
+        bs_off[jj] += (uint32_t)kc0;
+    }
+    bs2_off += (uint32_t)kc0;
 
     // stage kt -> LDS buffer `buf`; chunks past the end are clamped in range
     auto issue = [&](int kt, int buf) {
         const uint32_t sb = lds_base + (uint32_t)buf * STAGE_BYTES;
-        const int64_t kcs = kc0 + (int64_t)kt * 4;
+        const int kc = min(kt * 8 + a_chunk, kc_last);
+        const int ks = min(kt * 8 + s_chunk, kc_last);
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-            const int64_t kc = min(kcs + a_chunk[jj], kc_end - 1);
+        for (int jj = 0; jj < 8; ++jj) {
             dma16(p.a_codes, a_off[jj] + (uint32_t)(kc * 16), sb + OFF_A + jj * 4096 + wave * 1024);
             dma16(bcodes, b_off[jj] + (uint32_t)(kc * 16), sb + OFF_B + jj * 4096 + wave * 1024);
         }
-        const int64_t kcsc = min(kcs + s_chunk, kc_end - 1);
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-            dma1(p.a_scales, as_off[jj] + (uint32_t)kcsc, sb + OFF_AS + jj * 1024 + wave * 256);
-            if (!B2D) dma1(bscales, bs_off[jj] + (uint32_t)kcsc, sb + OFF_BS + jj * 1024 + wave * 256);
+        for (int jj = 0; jj < 8; ++jj) {
+            dma1(p.a_scales, as_off[jj] + (uint32_t)ks, sb + OFF_AS + jj * 1024 + wave * 256);
+            if (!B2D) dma1(bscales, bs_off[jj] + (uint32_t)ks, sb + OFF_BS + jj * 1024 + wave * 256);
         }
-        if (B2D) dma1(bscales, bs2_off + (uint32_t)kcsc, sb + OFF_BS + wave * 256);
+        if (B2D) dma1(bscales, bs2_off + (uint32_t)ks, sb + OFF_BS + wave * 256);
     };
 
     v16f acc[FN][FM];
@@ -259,23 +277,25 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
             for (int e = 0; e < 16; ++e) acc[i][jj][e] = 0.0f;
 
     const int lr = lane & 31;      // operand row within a 32-row MFMA block
-    const int lh = lane >> 5;      // which 32-element half of K = 64
+    const int lh = lane >> 5;      // which 32-element half of a K-quarter (64)
+    // operand rows w*128 + i*32 + lr share swz(lr) for every i, so a fragment
+    // read is one per-lane base plus an immediate i * 4096
+    const int sw = swz(lr);
+    const uint32_t fb_b = OFF_B + (uint32_t)(wn * WN + lr) * 128;
+    const uint32_t fb_a = OFF_A + (uint32_t)(wm * WM + lr) * 128;
 
     struct Frag { v8i b[FN]; v8i a[FM]; };
-    struct Scl { uint2 b[FN]; uint2 a[FM]; };
-    auto read_frag = [&](Frag& f, int buf, int ks) {
-        const uint8_t* sb = lds + buf * STAGE_BYTES;
-        const int ch = ks * 2 + lh;
+    struct Scl { uint4 b[FN]; uint4 a[FM]; };   // component q: K-quarter q
+    auto read_frag = [&](Frag& f, int buf, int q) {
+        const uint8_t* sb = lds + buf * STAGE_BYTES + (((2 * q + lh) ^ sw) * 16);
 #pragma unroll
         for (int i = 0; i < FN; ++i) {
-            const int r = wn * WN + i * 32 + lr;
-            const uint4 v = *(const uint4*)(sb + OFF_B + (r * 4 + (ch ^ swz(r))) * 16);
+            const uint4 v = *(const uint4*)(sb + fb_b + i * 4096);
             f.b[i] = (v8i){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
         }
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
-            const int r = wm * WM + i * 32 + lr;
-            const uint4 v = *(const uint4*)(sb + OFF_A + (r * 4 + (ch ^ swz(r))) * 16);
+            const uint4 v = *(const uint4*)(sb + fb_a + i * 4096);
             f.a[i] = (v8i){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
         }
     };
@@ -283,19 +303,20 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
         const uint8_t* sb = lds + buf * STAGE_BYTES;
 #pragma unroll
         for (int i = 0; i < FN; ++i)
-            s.b[i] = B2D ? *(const uint2*)(sb + OFF_BS + wave * 256 + (wn * 4 + i) * 16 + lh * 8)
-                         : *(const uint2*)(sb + OFF_BS + (wn * WN + i * 32 + lr) * 16 + lh * 8);
+            s.b[i] = B2D ? *(const uint4*)(sb + OFF_BS + wave * 256 + (wn * 4 + i) * 32 + lh * 16)
+                         : *(const uint4*)(sb + OFF_BS + (wn * WN + i * 32 + lr) * 32 + lh * 16);
 #pragma unroll
         for (int i = 0; i < FM; ++i)
-            s.a[i] = *(const uint2*)(sb + OFF_AS + (wm * WM + i * 32 + lr) * 16 + lh * 8);
+            s.a[i] = *(const uint4*)(sb + OFF_AS + (wm * WM + i * 32 + lr) * 32 + lh * 16);
     };
-    auto mma = [&](const Frag& f, const Scl& s, int ks, bool tail) {
+    auto qsel = [](const uint4& v, int q) { return q == 0 ? v.x : q == 1 ? v.y : q == 2 ? v.z : v.w; };
+    auto mma = [&](const Frag& f, const Scl& s, int q, bool tail) {
 #pragma unroll
         for (int i = 0; i < FN; ++i) {
-            const int sb = tail ? 0 : (int)(ks ? s.b[i].y : s.b[i].x);
+            const int sb = tail ? 0 : (int)qsel(s.b[i], q);
 #pragma unroll
             for (int jj = 0; jj < FM; ++jj) {
-                const int sa = tail ? 0 : (int)(ks ? s.a[jj].y : s.a[jj].x);
+                const int sa = tail ? 0 : (int)qsel(s.a[jj], q);
                 acc[i][jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                     f.b[i], f.a[jj], acc[i][jj], 4, 4, 0, sb, 0, sa);
             }
@@ -304,17 +325,37 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
 
     // "every DMA but the newest stage's has landed"
     auto wait_all_but_one_stage = [] {
-        if (B2D) asm volatile("s_waitcnt vmcnt(13)" ::: "memory");
-        else asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+        if (B2D) asm volatile("s_waitcnt vmcnt(25)" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(32)" ::: "memory");
     };
-    static_assert(dma_per_stage<true>() == 13 && dma_per_stage<false>() == 16, "wait counts");
+    static_assert(dma_per_stage<true>() == 25 && dma_per_stage<false>() == 32, "wait counts");
+    // one MFMA block, optionally followed by one piece of the next read
+    auto mma1 = [&](const Frag& f, const Scl& s, int q, bool tail, int m) {
+        const int i = m >> 2, jj = m & 3;
+        const int sb = tail ? 0 : (int)qsel(s.b[i], q);
+        const int sa = tail ? 0 : (int)qsel(s.a[jj], q);
+        acc[i][jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[i], f.a[jj], acc[i][jj], 4, 4, 0, sb, 0, sa);
+    };
+    auto read_piece = [&](Frag& f, int buf, int q, int k) {
+        const uint8_t* sb = lds + buf * STAGE_BYTES + (((2 * q + lh) ^ sw) * 16);
+        const uint4 v = k < 4 ? *(const uint4*)(sb + fb_b + k * 4096) : *(const uint4*)(sb + fb_a + (k - 4) * 4096);
+        v8i& d = k < 4 ? f.b[k] : f.a[k - 4];
+        d = (v8i){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+    };
+    auto mma_rd = [&](const Frag& f, const Scl& s, int q, bool tail, Frag& nf, int nbuf, int nq) {
+#pragma unroll
+        for (int m = 0; m < 16; ++m) {
+            mma1(f, s, q, tail, m);
+            if (m < 8) read_piece(nf, nbuf, nq, m);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
     if (nkt > 0) {
         Frag f0, f1;
         Scl sc, nsc;
-        // Two stages are in flight at every wait; a thread issues exactly
-        // dma_per_stage ops per stage (past-the-end stages are clamped loads
-        // into a buffer nobody reads), so a vmcnt of that count means "all
-        // but the newest stage have landed".
+        // Stage kt+1's DMA is issued at stage kt-1's barrier, into the buffer
+        // stage kt-1 has finished reading; at stage kt's barrier it is the
+        // only DMA outstanding, so vmcnt(0) means it has landed.
         issue(0, 0);
         issue(1, 1);
         wait_all_but_one_stage();
@@ -322,25 +363,19 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
         read_frag(f0, 0, 0);
         read_scl(sc, 0);
         for (int kt = 0; kt < nkt; ++kt) {
-            const int buf = kt % NST;
-            // buffer (kt+2)%3 held stage kt-1, whose reads all finished
-            // before the previous barrier
-            issue(kt + 2, (kt + 2) % NST);
-            read_frag(f1, buf, 1);
-            const int64_t kcl = kc0 + (int64_t)kt * 4 + lh;   // this lane's chunk in K-half 0
-            mma(f0, sc, 0, kcl >= kc_end);
-            // stage kt+1 has landed (own DMA) and every wave is done with
-            // its reads of this stage's first half
-            wait_all_but_one_stage();
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            const int buf = kt & 1;
+            const int kcl = kt * 8 + lh;              // this lane's chunk in K-quarter 0
+            mma_rd(f0, sc, 0, kcl > kc_last, f1, buf, 1);
+            mma_rd(f1, sc, 1, kcl + 2 > kc_last, f0, buf, 2);
+            mma_rd(f0, sc, 2, kcl + 4 > kc_last, f1, buf, 3);
+            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
             __builtin_amdgcn_s_barrier();
-            read_frag(f0, (kt + 1) % NST, 0);
-            read_scl(nsc, (kt + 1) % NST);
-            mma(f1, sc, 1, kcl + 2 >= kc_end);
+            issue(kt + 2, buf);
+            read_scl(nsc, buf ^ 1);
+            mma_rd(f1, sc, 3, kcl + 6 > kc_last, f0, buf ^ 1, 0);
             sc = nsc;
         }
-        // drain the DMA of the two past-the-end stages before the workgroup
-        // can finish (their LDS writes must not outlive it)
+        // drain the DMA of the two past-the-end stages before the LDS is reused
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
 
