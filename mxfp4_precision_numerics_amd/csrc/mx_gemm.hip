@@ -14,9 +14,11 @@
 // 32x32 block and each lane ends up holding 4 consecutive output columns of
 // one output row: the epilogue stores 8-byte (bf16) or 16-byte (fp32) runs.
 //
-// Tiling: a workgroup of 4 waves (2 x 2) computes a 256 x 256 tile of one
-// group; each wave owns 128 x 128 (16 MFMA blocks, 256 accumulators held in
-// AGPRs).  K advances 256 per stage, so every operand row contributes one
+// Tiling: a workgroup of 8 waves (2 x 4) computes a 256 x 256 tile of one
+// group; each wave owns 128 x 64 (8 MFMA blocks, 128 accumulators), two waves
+// per SIMD so that one wave's LDS and DMA waits are covered by the other's
+// MFMAs.  (A 4-wave form, 2 x 2 waves of 128 x 128 with 256 accumulators in
+// AGPRs and one wave per SIMD, is the same template with NW = 4.)  K advances 256 per stage, so every operand row contributes one
 // 128-byte line per stage (half-line requests cost nearly as much as full
 // ones at the L2).  Every operand byte moves global -> LDS by the CDNA
 // LDS-DMA loads (global_load_lds_dwordx4 for 16-byte code chunks, 8 lanes per
@@ -27,8 +29,8 @@
 // The DMA is issued from register-only inline assembly and its completion is
 // awaited explicitly (s_waitcnt vmcnt + s_barrier).  A stage runs as four
 // K-quarters of 64; operand fragments are double-buffered in registers and
-// the next quarter's eight fragment reads are interleaved one per MFMA with
-// the current quarter's sixteen MFMAs.
+// the next quarter's fragment reads are interleaved one per MFMA with the
+// current quarter's MFMAs.
 //
 // LDS code tiles use an XOR swizzle of the eight 16-byte chunks of a row;
 // each row's 8 scale dwords are stored in the order (s0, s2, s4, s6, s1, s3,
@@ -70,6 +72,9 @@ struct GemmArgs {
 };
 
 constexpr int BM = 256, BN = 256;
+// waves per workgroup: 8 (two per SIMD) measured 8-9% faster than 4 on the
+// expert-step shapes; the kernel is written for both
+constexpr int GEMM_NW = 8;
 constexpr int BK = 256;            // K elements per stage: 128 code bytes per row
 constexpr int NST = 2;             // LDS ring depth (2 x 80 KiB: all of a CU's LDS)
 constexpr int GROUP_M = 4;         // M-tiles per tile-order group
@@ -81,8 +86,8 @@ constexpr int OFF_A = 0, OFF_B = 32768, OFF_AS = 65536, OFF_BS = 73728;
 constexpr int STAGE_BYTES = 81920;
 // DMA ops per thread per stage: 16 code moves, 8 A-scale moves, and 8 B-scale
 // moves (1D B scales) or 1 (2D B scales: 8 row groups of 32 per tile).
-template <bool B2D>
-constexpr int dma_per_stage() { return B2D ? 25 : 32; }
+template <bool B2D, int NW>
+constexpr int dma_per_stage() { return NW == 4 ? (B2D ? 25 : 32) : (B2D ? 13 : 16); }
 
 // 16-byte chunk swizzle of a 128-byte row: the rows an MFMA operand read
 // touches at one chunk index land in distinct 16-byte bank groups whether
@@ -111,15 +116,18 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
 }
 
-template <bool OUT_BF16, bool B2D>
-__global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
-    constexpr int WM = 128, WN = 128, FM = 4, FN = 4;
+template <bool OUT_BF16, bool B2D, int NW>
+__global__ __launch_bounds__(NW * 64, 1) void gemm_kernel(GemmArgs p) {
+    // NW = 4: 2 x 2 waves of 128 x 128; NW = 8: 2 x 4 waves of 128 x 64 (two
+    // waves per SIMD, so one wave's waits are covered by the other's MFMAs)
+    constexpr int NT = NW * 64;
+    constexpr int WM = 128, WN = NW == 4 ? 128 : 64, FM = 4, FN = WN / 32;
     __shared__ __attribute__((aligned(16))) uint8_t lds[NST * STAGE_BYTES];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = NW == 4 ? wave >> 1 : wave >> 2, wn = NW == 4 ? wave & 1 : wave & 3;
 
     // ---------------- tile id: XCD-aware remap of the workgroup id ----------
     const int64_t wg = blockIdx.x;
@@ -211,10 +219,11 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
     const int pc = tid & 7;
     const int a_chunk = pc ^ swz(tid >> 3);    // swz(t/8 + 32 j) is the same for every j
     const int s_chunk = sperm(pc);
-    uint32_t a_off[8], b_off[8], as_off[8], bs_off[8];
+    constexpr int NJ = 2048 / NT;               // code (and scale) moves per operand per thread
+    uint32_t a_off[NJ], b_off[NJ], as_off[NJ], bs_off[NJ];
 #pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
-        const int r = (tid >> 3) + 32 * jj;
+    for (int jj = 0; jj < NJ; ++jj) {
+        const int r = (tid >> 3) + (NT / 8) * jj;
         int64_t m = m_begin + r;
         if (m >= m_end) m = m_end - 1;        // rows past the tile end are never stored
         const int64_t arow = p.a_row_index ? (int64_t)p.a_row_index[m] : m;
@@ -242,7 +251,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
     // K chunks relative to kc0 (32-bit: the host bounds an operand row to 4 GiB)
     const int kc_last = (int)(kc_end - kc0) - 1;
 #pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
+    for (int jj = 0; jj < NJ; ++jj) {
         a_off[jj] += (uint32_t)(kc0 * 16);
         b_off[jj] += (uint32_t)(kc0 * 16);
         as_off[jj] += (uint32_t)kc0;
@@ -256,14 +265,14 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
         const int kc = min(kt * 8 + a_chunk, kc_last);
         const int ks = min(kt * 8 + s_chunk, kc_last);
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-            dma16(p.a_codes, a_off[jj] + (uint32_t)(kc * 16), sb + OFF_A + jj * 4096 + wave * 1024);
-            dma16(bcodes, b_off[jj] + (uint32_t)(kc * 16), sb + OFF_B + jj * 4096 + wave * 1024);
+        for (int jj = 0; jj < NJ; ++jj) {
+            dma16(p.a_codes, a_off[jj] + (uint32_t)(kc * 16), sb + OFF_A + jj * NT * 16 + wave * 1024);
+            dma16(bcodes, b_off[jj] + (uint32_t)(kc * 16), sb + OFF_B + jj * NT * 16 + wave * 1024);
         }
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-            dma1(p.a_scales, as_off[jj] + (uint32_t)ks, sb + OFF_AS + jj * 1024 + wave * 256);
-            if (!B2D) dma1(bscales, bs_off[jj] + (uint32_t)ks, sb + OFF_BS + jj * 1024 + wave * 256);
+        for (int jj = 0; jj < NJ; ++jj) {
+            dma1(p.a_scales, as_off[jj] + (uint32_t)ks, sb + OFF_AS + jj * NT * 4 + wave * 256);
+            if (!B2D) dma1(bscales, bs_off[jj] + (uint32_t)ks, sb + OFF_BS + jj * NT * 4 + wave * 256);
         }
         if (B2D) dma1(bscales, bs2_off + (uint32_t)ks, sb + OFF_BS + wave * 256);
     };
@@ -303,7 +312,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
         const uint8_t* sb = lds + buf * STAGE_BYTES;
 #pragma unroll
         for (int i = 0; i < FN; ++i)
-            s.b[i] = B2D ? *(const uint4*)(sb + OFF_BS + wave * 256 + (wn * 4 + i) * 32 + lh * 16)
+            s.b[i] = B2D ? *(const uint4*)(sb + OFF_BS + wave * 256 + (wn * FN + i) * 32 + lh * 16)
                          : *(const uint4*)(sb + OFF_BS + (wn * WN + i * 32 + lr) * 32 + lh * 16);
 #pragma unroll
         for (int i = 0; i < FM; ++i)
@@ -325,28 +334,34 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
 
     // "every DMA but the newest stage's has landed"
     auto wait_all_but_one_stage = [] {
-        if (B2D) asm volatile("s_waitcnt vmcnt(25)" ::: "memory");
-        else asm volatile("s_waitcnt vmcnt(32)" ::: "memory");
+        if (NW == 4) {
+            if (B2D) asm volatile("s_waitcnt vmcnt(25)" ::: "memory");
+            else asm volatile("s_waitcnt vmcnt(32)" ::: "memory");
+        } else {
+            if (B2D) asm volatile("s_waitcnt vmcnt(13)" ::: "memory");
+            else asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+        }
     };
-    static_assert(dma_per_stage<true>() == 25 && dma_per_stage<false>() == 32, "wait counts");
+    static_assert(dma_per_stage<true, 4>() == 25 && dma_per_stage<false, 4>() == 32 &&
+                  dma_per_stage<true, 8>() == 13 && dma_per_stage<false, 8>() == 16, "wait counts");
     // one MFMA block, optionally followed by one piece of the next read
     auto mma1 = [&](const Frag& f, const Scl& s, int q, bool tail, int m) {
-        const int i = m >> 2, jj = m & 3;
+        const int i = m / FM, jj = m % FM;
         const int sb = tail ? 0 : (int)qsel(s.b[i], q);
         const int sa = tail ? 0 : (int)qsel(s.a[jj], q);
         acc[i][jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[i], f.a[jj], acc[i][jj], 4, 4, 0, sb, 0, sa);
     };
     auto read_piece = [&](Frag& f, int buf, int q, int k) {
         const uint8_t* sb = lds + buf * STAGE_BYTES + (((2 * q + lh) ^ sw) * 16);
-        const uint4 v = k < 4 ? *(const uint4*)(sb + fb_b + k * 4096) : *(const uint4*)(sb + fb_a + (k - 4) * 4096);
-        v8i& d = k < 4 ? f.b[k] : f.a[k - 4];
+        const uint4 v = k < FN ? *(const uint4*)(sb + fb_b + k * 4096) : *(const uint4*)(sb + fb_a + (k - FN) * 4096);
+        v8i& d = k < FN ? f.b[k] : f.a[k - FN];
         d = (v8i){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
     };
     auto mma_rd = [&](const Frag& f, const Scl& s, int q, bool tail, Frag& nf, int nbuf, int nq) {
 #pragma unroll
-        for (int m = 0; m < 16; ++m) {
+        for (int m = 0; m < FN * FM; ++m) {
             mma1(f, s, q, tail, m);
-            if (m < 8) read_piece(nf, nbuf, nq, m);
+            if (m < FN + FM) read_piece(nf, nbuf, nq, m);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
@@ -387,7 +402,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
     constexpr int EB = OUT_BF16 ? 2 : 4;              // output element bytes
     constexpr int PITCH = WN * EB + 16;                // LDS bytes per staged row
     constexpr int SEGS = WN * EB / 16;                 // 16-byte runs per row
-    static_assert(4 * 32 * PITCH <= NST * STAGE_BYTES, "epilogue staging fits the ring");
+    static_assert(NW * 32 * PITCH <= NST * STAGE_BYTES, "epilogue staging fits the ring");
     __syncthreads();                                   // every wave is done with the ring
     uint8_t* stage_c = lds + wave * 32 * PITCH;
     const int64_t rows_here = m_end - m_begin;
@@ -484,10 +499,10 @@ extern "C" mx_status mx_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_sc
     hipStream_t s = (hipStream_t)stream;
     (void)hipGetLastError();
     if (ct == MX_BF16)
-        if (b_scale_2d) hipLaunchKernelGGL((gemm_kernel<true, true>), dim3((unsigned)tiles), dim3(256), 0, s, p);
-        else hipLaunchKernelGGL((gemm_kernel<true, false>), dim3((unsigned)tiles), dim3(256), 0, s, p);
+        if (b_scale_2d) hipLaunchKernelGGL((gemm_kernel<true, true, GEMM_NW>), dim3((unsigned)tiles), dim3(GEMM_NW * 64), 0, s, p);
+        else hipLaunchKernelGGL((gemm_kernel<true, false, GEMM_NW>), dim3((unsigned)tiles), dim3(GEMM_NW * 64), 0, s, p);
     else
-        if (b_scale_2d) hipLaunchKernelGGL((gemm_kernel<false, true>), dim3((unsigned)tiles), dim3(256), 0, s, p);
-        else hipLaunchKernelGGL((gemm_kernel<false, false>), dim3((unsigned)tiles), dim3(256), 0, s, p);
+        if (b_scale_2d) hipLaunchKernelGGL((gemm_kernel<false, true, GEMM_NW>), dim3((unsigned)tiles), dim3(GEMM_NW * 64), 0, s, p);
+        else hipLaunchKernelGGL((gemm_kernel<false, false, GEMM_NW>), dim3((unsigned)tiles), dim3(GEMM_NW * 64), 0, s, p);
     return hipGetLastError() == hipSuccess ? MX_OK : MX_ERR_LAUNCH;
 }
