@@ -33,7 +33,9 @@ import numpy as np  # noqa: E402
 
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic.txt")
-ROLE_KERNEL = {"gemm": "gemm_kernel<true,true>", "gemm_wgrad": "gemm_kernel<false,false>"}
+# kernel-name prefix (template arguments without spaces) of each GEMM role:
+# bf16 output with 2D weight scales, fp32 output with 1D scales
+ROLE_KERNEL = {"gemm": "gemm_kernel<true,true,", "gemm_wgrad": "gemm_kernel<false,false,"}
 PEAK_FP4_TFLOPS = 10100.0      # MI355X dense FP4 MFMA, TFLOP/s
 E, D, F2, T, TOPK = 32, 2880, 5760, 16384, 4
 ROWS = T * TOPK
@@ -171,9 +173,10 @@ def measured_traffic(role):
             src = f[1]
         elif len(f) >= 6 and f[0] == "kernel":
             rec[f[1]] = (float(f[3]), float(f[5]))
-    if src != kernel_source_hash() or ROLE_KERNEL[role] not in rec:
+    names = [k for k in rec if k.startswith(ROLE_KERNEL[role])]
+    if src != kernel_source_hash() or len(names) != 1:
         return None
-    rd, wr = rec[ROLE_KERNEL[role]]
+    rd, wr = rec[names[0]]
     return {"read_bytes": rd, "write_bytes": wr, "bytes": rd + wr}
 
 
