@@ -66,6 +66,16 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
 // Block scale from the amax bit pattern (sign already cleared):
 //   exponent field E; byte = max(E - 2, 0); E == 255 (NaN/Inf) -> 0xFF.
 // ---------------------------------------------------------------------------
+// One 16-byte vector store to a 16-byte-aligned global address.  Used where
+// the compiler's address strength reduction would otherwise split the store
+// into four dword stores.  The trailing s_nop covers the one wait state a
+// VALU write to the store's data registers needs after a 16-byte store.
+__device__ __forceinline__ void store_b128(void* p, uint4 v) {
+    typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+    const u32x4v d = {v.x, v.y, v.z, v.w};
+    asm volatile("global_store_dwordx4 %0, %1, off\n\ts_nop 1" :: "v"(p), "v"(d) : "memory");
+}
+
 __device__ __forceinline__ uint32_t scale_byte_from_amax_bits(uint32_t amax_bits) {
     const uint32_t E = amax_bits >> 23;
     if (E >= 255u) return 0xFFu;

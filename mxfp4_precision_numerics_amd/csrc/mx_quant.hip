@@ -389,6 +389,32 @@ __global__ __launch_bounds__(256) void q1d_col_kernel(const void* __restrict__ x
 // ===========================================================================
 constexpr int Q2_TR = 8;   // tile rows per super-strip
 
+// Transpose an 8 x 8 matrix of 4-bit codes held as 8 words, element (r, c) in
+// nibble c of a[r]: afterwards element (r, c) is nibble r of a[c].  Three
+// rounds swap the off-diagonal 4x4, 2x2 and 1x1 blocks.
+__device__ __forceinline__ void transpose_nibbles_8x8(uint32_t* a) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const uint32_t t = ((a[r] >> 16) ^ a[r + 4]) & 0x0000FFFFu;
+        a[r] ^= t << 16;
+        a[r + 4] ^= t;
+    }
+    constexpr int rows2[4] = {0, 1, 4, 5};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = rows2[i];
+        const uint32_t t = ((a[r] >> 8) ^ a[r + 2]) & 0x00FF00FFu;
+        a[r] ^= t << 8;
+        a[r + 2] ^= t;
+    }
+#pragma unroll
+    for (int r = 0; r < 8; r += 2) {
+        const uint32_t t = ((a[r] >> 4) ^ a[r + 1]) & 0x0F0F0F0Fu;
+        a[r] ^= t << 4;
+        a[r + 1] ^= t;
+    }
+}
+
 template <bool BF16>
 __global__ __launch_bounds__(256) void q2d_kernel(const void* __restrict__ w, int64_t rows, int64_t cols,
                                                   int64_t col_strips, int64_t row_strips, int64_t nsuper,
@@ -396,7 +422,10 @@ __global__ __launch_bounds__(256) void q2d_kernel(const void* __restrict__ w, in
                                                   uint8_t* __restrict__ codes_t, uint8_t* __restrict__ scales_t) {
     __shared__ uint32_t wave_amax[4][8];
     __shared__ uint8_t tile_scale[Q2_TR][8];
-    __shared__ uint4 tcodes[Q2_TR][8][32];   // [tile row][tile][row] 16 bytes of row codes
+    // [tile row][tile][row] 16 bytes of row codes; each tile row padded by one
+    // entry so the 8 tile rows of one tile fall in different LDS banks
+    constexpr int TC_TS = 8 * 32 + 1;
+    __shared__ uint4 tcodes[Q2_TR * TC_TS];
     const int t = threadIdx.x;
     const int r = t >> 3;          // 0..31
     const int j = t & 7;           // tile within the strip
@@ -457,33 +486,43 @@ __global__ __launch_bounds__(256) void q2d_kernel(const void* __restrict__ w, in
             __syncthreads();
             const uint32_t byte = tile_scale[ts][j];
             const float sc = scale_operand(byte);
+            // non-finite tile: codes are 0 (a mask, so the four converts stay
+            // branch-free and the row's 16 code bytes go out as one store)
+            const uint32_t keep = byte == 0xFFu ? 0u : 0xFFFFFFFFu;
             uint32_t cw[4];
 #pragma unroll
-            for (int k = 0; k < 4; ++k) cw[k] = byte == 0xFFu ? 0u : cvt8_rne(v + 8 * k, sc);
-            if (valid && codes) *(uint4*)(codes + grow * (cols >> 1) + tile * 16) = make_uint4(cw[0], cw[1], cw[2], cw[3]);
+            for (int k = 0; k < 4; ++k) cw[k] = cvt8_rne(v + 8 * k, sc) & keep;
+            if (valid && codes)
+                store_b128(codes + grow * (cols >> 1) + tile * 16, make_uint4(cw[0], cw[1], cw[2], cw[3]));
             if (valid && r == 0 && scales) scales[(bt * row_tiles + tr) * tiles_per_row + tile] = (uint8_t)byte;
-            tcodes[ts][j][r] = make_uint4(cw[0], cw[1], cw[2], cw[3]);
+            tcodes[ts * TC_TS + j * 32 + r] = make_uint4(cw[0], cw[1], cw[2], cw[3]);
         }
         __syncthreads();
         if (codes_t) {
-            // thread t: tile jj = t / 32, column cc = t % 32 of that tile; one
-            // 16-byte run per tile row, the runs of a column contiguous
-            const int jj = t >> 5;
-            const int cc = t & 31;
+            // thread t: tile row ts = t % 8, code word w = (t / 8) % 4 (columns
+            // 8w .. 8w+7) of tile jj = t / 32.  It reads that word of the
+            // tile's 32 rows, transposes four 8 x 8 nibble blocks, and writes
+            // the 8 columns' 16-byte runs; the 8 threads of one (tile, word)
+            // cover tile rows 0..7, i.e. 128 contiguous bytes per column.
+            const int ts = t & 7, w = (t >> 3) & 3, jj = t >> 5;
             const int64_t tile2 = cs * 8 + jj;
-            if (tile2 < tiles_per_row) {
-                const int word = cc >> 3;            // dword holding column cc in a row
-                const int sh = (cc & 7) * 4;
-                const int64_t col = tile2 * 32 + cc;
-                uint8_t* dst = codes_t + (bt * cols + col) * (rows >> 1) + tr0 * 16;
-                for (int ts = 0; ts < ntr; ++ts) {
-                    uint32_t o[4] = {0, 0, 0, 0};
+            if (tile2 < tiles_per_row && ts < ntr) {
+                const uint32_t* src = (const uint32_t*)&tcodes[ts * TC_TS + jj * 32] + w;
+                uint32_t out[8][4];             // [column 8w + c][rows 8 rb .. 8 rb + 7]
 #pragma unroll
-                    for (int rr = 0; rr < 32; ++rr) {
-                        const uint32_t wd = ((const uint32_t*)&tcodes[ts][jj][rr])[word];
-                        o[rr >> 3] |= ((wd >> sh) & 0xFu) << ((rr & 7) * 4);
-                    }
-                    *(uint4*)(dst + ts * 16) = make_uint4(o[0], o[1], o[2], o[3]);
+                for (int rb = 0; rb < 4; ++rb) {
+                    uint32_t a[8];
+#pragma unroll
+                    for (int r = 0; r < 8; ++r) a[r] = src[(rb * 8 + r) * 4];
+                    transpose_nibbles_8x8(a);
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) out[c][rb] = a[c];
+                }
+#pragma unroll
+                for (int c = 0; c < 8; ++c) {
+                    const int64_t col = tile2 * 32 + 8 * w + c;
+                    store_b128(codes_t + (bt * cols + col) * (rows >> 1) + (tr0 + ts) * 16,
+                               make_uint4(out[c][0], out[c][1], out[c][2], out[c][3]));
                 }
             }
             // transposed scales: lanes 8 jj .. 8 jj + 7 write one tile column's
