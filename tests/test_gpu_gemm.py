@@ -166,3 +166,59 @@ def test_config4_full_size_fprop_sampled_rows():
     cb = mx.grouped_gemm(dev(ac), dev(asc), dev(bct), dev(bst), dev(off), M, N, K,
                          a_row_index=dev(idx), b_scale_2d=True, out_dtype=torch.bfloat16)
     _check_bf16(host(cb[torch.as_tensor(rows[:, 1], device=cb.device)]), want)
+
+
+def _random_operand(rng, rows, k):
+    """Random code bytes and scale bytes near 2^0 (products stay well inside fp32)."""
+    codes = rng.integers(0, 256, (rows, k // 2), dtype=np.uint8)
+    scales = rng.integers(120, 135, (rows, k // 32), dtype=np.uint8)
+    return codes, scales
+
+
+def test_full_size_dgrad_sampled_rows():
+    """Data-gradient GEMM of the gate_up layer at full size: dX_e = dY1_e W1_e^T
+    with M = 65536 routed rows, N = 2880, K = 5760, B in the as-given W layout
+    with 2D scales (32 experts).  The oracle checks 4 rows per expert."""
+    import torch
+    rng = np.random.default_rng(51)
+    counts = synth.zipf_counts()
+    off = synth.offsets_from_counts(counts)
+    M, N, K = 65536, 2880, 5760
+    ac, asc = _random_operand(rng, M, K)
+    bc = rng.integers(0, 256, (32, N, K // 2), dtype=np.uint8)
+    bs = rng.integers(120, 135, (32, N // 32, K // 32), dtype=np.uint8)
+    c = mx.grouped_gemm(dev(ac), dev(asc), dev(bc), dev(bs), dev(off), M, N, K, b_scale_2d=True,
+                        out_dtype=torch.float32)
+    sample = []
+    for g in range(32):
+        a, b = int(off[g]), int(off[g + 1])
+        sample += [(g, a), (g, b - 1)] + [(g, int(m)) for m in rng.integers(a, b, 2)]
+    rows, want = oracle.grouped_gemm(ac, asc, bc, bs, off, M, N, K, b_scale_2d=True, rows=sample)
+    got = host(c[torch.as_tensor(rows[:, 1], device=c.device)])
+    for g in range(32):
+        sel = rows[:, 0] == g
+        assert rel_fro(got[sel], want[sel]) <= TOL, g
+
+
+def test_full_size_wgrad_sampled_rows():
+    """Weight-gradient GEMM of the gate_up layer at full size: dW1_e =
+    X_e^T dY1_e with groups splitting K: 32 Zipf-sized token segments, each
+    padded to 32 (K = padded capacity 66560), M = 2880, N = 5760, fp32 out.
+    The oracle checks 3 rows of every expert's dW."""
+    import torch
+    rng = np.random.default_rng(52)
+    counts = synth.zipf_counts()
+    pad = (counts + 31) // 32 * 32
+    poff = np.concatenate([[0], np.cumsum(pad)]).astype(np.int32)
+    M, N = 2880, 5760
+    Kt = mx.padded_capacity(65536, 32)
+    ac, asc = _random_operand(rng, M, Kt)
+    bc, bs = _random_operand(rng, N, Kt)
+    c = mx.grouped_gemm(dev(ac), dev(asc), dev(bc), dev(bs), dev(poff), M, N, Kt, group_dim_k=True,
+                        out_dtype=torch.float32)
+    sample = [(g, int(m)) for g in range(32) for m in (0, M - 1, rng.integers(0, M))]
+    rows, want = oracle.grouped_gemm(ac, asc, bc, bs, poff, M, N, Kt, group_dim_k=True, rows=sample)
+    for g in range(32):
+        sel = rows[:, 0] == g
+        got = host(c[g][torch.as_tensor(rows[sel, 1], device=c.device)]).astype(np.float64)
+        assert rel_fro(got, want[sel]) <= TOL, g
