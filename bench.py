@@ -35,7 +35,7 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic.txt")
 # kernel-name prefix (template arguments without spaces) of each GEMM role:
 # bf16 output with 2D weight scales, fp32 output with 1D scales
-ROLE_KERNEL = {"gemm": "gemm_kernel<true,true,", "gemm_wgrad": "gemm_kernel<false,false,"}
+ROLE_KERNEL = {"gemm": "gemm_kernel<true,true", "gemm_wgrad": "gemm_kernel<false,false"}
 PEAK_FP4_TFLOPS = 10100.0      # MI355X dense FP4 MFMA, TFLOP/s
 E, D, F2, T, TOPK = 32, 2880, 5760, 16384, 4
 ROWS = T * TOPK

@@ -17,9 +17,9 @@
 // Tiling: a workgroup of 8 waves (2 x 4) computes a 256 x 256 tile of one
 // group; each wave owns 128 x 64 (8 MFMA blocks, 128 accumulators), two waves
 // per SIMD so that one wave's LDS and DMA waits are covered by the other's
-// MFMAs.  (A 4-wave form, 2 x 2 waves of 128 x 128 with 256 accumulators in
-// AGPRs and one wave per SIMD, is the same template with NW = 4.)  K advances 256 per stage, so every operand row contributes one
-// 128-byte line per stage (half-line requests cost nearly as much as full
+// MFMAs (4 waves of 128 x 128, one per SIMD, measured 8-9% slower).  K
+// advances 256 per stage, so every operand row contributes one 128-byte
+// line per stage (half-line requests cost nearly as much as full
 // ones at the L2).  Every operand byte moves global -> LDS by the CDNA
 // LDS-DMA loads (global_load_lds_dwordx4 for 16-byte code chunks, 8 lanes per
 // row line; global_load_lds_ubyte for scale bytes, each landing as a dword),
@@ -72,9 +72,8 @@ struct GemmArgs {
 };
 
 constexpr int BM = 256, BN = 256;
-// waves per workgroup: 8 (two per SIMD) measured 8-9% faster than 4 on the
-// expert-step shapes; the kernel is written for both
-constexpr int GEMM_NW = 8;
+constexpr int NW = 8;               // waves per workgroup (two per SIMD)
+constexpr int NT = NW * 64;          // threads per workgroup
 constexpr int BK = 256;            // K elements per stage: 128 code bytes per row
 constexpr int NST = 2;             // LDS ring depth (2 x 80 KiB: all of a CU's LDS)
 constexpr int GROUP_M = 4;         // M-tiles per tile-order group
@@ -86,8 +85,8 @@ constexpr int OFF_A = 0, OFF_B = 32768, OFF_AS = 65536, OFF_BS = 73728;
 constexpr int STAGE_BYTES = 81920;
 // DMA ops per thread per stage: 16 code moves, 8 A-scale moves, and 8 B-scale
 // moves (1D B scales) or 1 (2D B scales: 8 row groups of 32 per tile).
-template <bool B2D, int NW>
-constexpr int dma_per_stage() { return NW == 4 ? (B2D ? 25 : 32) : (B2D ? 13 : 16); }
+template <bool B2D>
+constexpr int dma_per_stage() { return B2D ? 13 : 16; }
 
 // 16-byte chunk swizzle of a 128-byte row: the rows an MFMA operand read
 // touches at one chunk index land in distinct 16-byte bank groups whether
@@ -116,18 +115,16 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
 }
 
-template <bool OUT_BF16, bool B2D, int NW>
-__global__ __launch_bounds__(NW * 64, 1) void gemm_kernel(GemmArgs p) {
-    // NW = 4: 2 x 2 waves of 128 x 128; NW = 8: 2 x 4 waves of 128 x 64 (two
-    // waves per SIMD, so one wave's waits are covered by the other's MFMAs)
-    constexpr int NT = NW * 64;
-    constexpr int WM = 128, WN = NW == 4 ? 128 : 64, FM = 4, FN = WN / 32;
+template <bool OUT_BF16, bool B2D>
+__global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
+    // 2 x 4 waves of 128 x 64
+    constexpr int WM = 128, WN = 64, FM = 4, FN = WN / 32;
     __shared__ __attribute__((aligned(16))) uint8_t lds[NST * STAGE_BYTES];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = NW == 4 ? wave >> 1 : wave >> 2, wn = NW == 4 ? wave & 1 : wave & 3;
+    const int wm = wave >> 2, wn = wave & 3;
 
     // ---------------- tile id: XCD-aware remap of the workgroup id ----------
     const int64_t wg = blockIdx.x;
@@ -334,16 +331,10 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_kernel(GemmArgs p) {
 
     // "every DMA but the newest stage's has landed"
     auto wait_all_but_one_stage = [] {
-        if (NW == 4) {
-            if (B2D) asm volatile("s_waitcnt vmcnt(25)" ::: "memory");
-            else asm volatile("s_waitcnt vmcnt(32)" ::: "memory");
-        } else {
-            if (B2D) asm volatile("s_waitcnt vmcnt(13)" ::: "memory");
-            else asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-        }
+        if (B2D) asm volatile("s_waitcnt vmcnt(13)" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
     };
-    static_assert(dma_per_stage<true, 4>() == 25 && dma_per_stage<false, 4>() == 32 &&
-                  dma_per_stage<true, 8>() == 13 && dma_per_stage<false, 8>() == 16, "wait counts");
+    static_assert(dma_per_stage<true>() == 13 && dma_per_stage<false>() == 16, "wait counts");
     // one MFMA block, optionally followed by one piece of the next read
     auto mma1 = [&](const Frag& f, const Scl& s, int q, bool tail, int m) {
         const int i = m / FM, jj = m % FM;
@@ -499,10 +490,10 @@ extern "C" mx_status mx_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_sc
     hipStream_t s = (hipStream_t)stream;
     (void)hipGetLastError();
     if (ct == MX_BF16)
-        if (b_scale_2d) hipLaunchKernelGGL((gemm_kernel<true, true, GEMM_NW>), dim3((unsigned)tiles), dim3(GEMM_NW * 64), 0, s, p);
-        else hipLaunchKernelGGL((gemm_kernel<true, false, GEMM_NW>), dim3((unsigned)tiles), dim3(GEMM_NW * 64), 0, s, p);
+        if (b_scale_2d) hipLaunchKernelGGL((gemm_kernel<true, true>), dim3((unsigned)tiles), dim3(NT), 0, s, p);
+        else hipLaunchKernelGGL((gemm_kernel<true, false>), dim3((unsigned)tiles), dim3(NT), 0, s, p);
     else
-        if (b_scale_2d) hipLaunchKernelGGL((gemm_kernel<false, true, GEMM_NW>), dim3((unsigned)tiles), dim3(GEMM_NW * 64), 0, s, p);
-        else hipLaunchKernelGGL((gemm_kernel<false, false, GEMM_NW>), dim3((unsigned)tiles), dim3(GEMM_NW * 64), 0, s, p);
+        if (b_scale_2d) hipLaunchKernelGGL((gemm_kernel<false, true>), dim3((unsigned)tiles), dim3(NT), 0, s, p);
+        else hipLaunchKernelGGL((gemm_kernel<false, false>), dim3((unsigned)tiles), dim3(NT), 0, s, p);
     return hipGetLastError() == hipSuccess ? MX_OK : MX_ERR_LAUNCH;
 }
