@@ -60,10 +60,9 @@ def build_inputs(torch, dev):
     dY1 = (torch.randn(ROWS, F2, device=dev, generator=g5) * 1e-3).to(torch.bfloat16)
     dY2 = (torch.randn(ROWS, D, device=dev, generator=g5) * 1e-3).to(torch.bfloat16)
     idx_d = torch.from_numpy(idx).to(dev)
-    Xp = X.index_select(0, idx_d.long()).contiguous()      # tokens in expert order
     pad = (counts + 31) // 32 * 32
     poff = np.concatenate([[0], np.cumsum(pad)]).astype(np.int32)
-    return dict(X=X, Xp=Xp, W1=W1, W2=W2, h=h, dY1=dY1, dY2=dY2, counts=counts,
+    return dict(X=X, W1=W1, W2=W2, h=h, dY1=dY1, dY2=dY2, counts=counts,
                 off=torch.from_numpy(off).to(dev), idx=idx_d,
                 poff=torch.from_numpy(poff).to(dev), kp_used=int(poff[-1]))
 
@@ -126,7 +125,10 @@ class Step:
         self._t("q1d_col", lambda: mx.quantize_1d(i["dY2"], stream_id=5, codes=b["g2Tc"], scales=b["g2Ts"], **col))
         self._t("gemm_wgrad", lambda: mx.grouped_gemm(b["hTc"], b["hTs"], b["g2Tc"], b["g2Ts"], poff, D, D, self.kp,
                                                       group_dim_k=True, out=b["dW2"]))
-        self._t("q1d_col", lambda: mx.quantize_1d(i["Xp"], stream_id=2, codes=b["xTc"], scales=b["xTs"], **col))
+        # X^T: the routed rows are gathered from the 16384-token X inside the
+        # quantizer (no permuted copy)
+        self._t("q1d_col", lambda: mx.quantize_1d(i["X"], stream_id=2, codes=b["xTc"], scales=b["xTs"],
+                                                  row_index=idx, **col))
         self._t("q1d_col", lambda: mx.quantize_1d(i["dY1"], stream_id=3, codes=b["g1Tc"], scales=b["g1Ts"], **col))
         self._t("gemm_wgrad", lambda: mx.grouped_gemm(b["xTc"], b["xTs"], b["g1Tc"], b["g1Ts"], poff, D, F2, self.kp,
                                                       group_dim_k=True, out=b["dW1"]))

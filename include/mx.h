@@ -95,7 +95,8 @@ mx_status mx_rht(const void* x, mx_dtype xt, float* y, int64_t rows, int64_t col
  *
  * block_axis = 1 (row-wise): x [rows x cols], cols % 32 == 0.  Blocks of 32
  *   run along cols.  codes [rows x cols/2], scales [rows x cols/32].
- *   group_offsets must be NULL, num_groups 0, kp 0.
+ *   group_offsets and row_index must be NULL, num_groups 0, kp 0 (a
+ *   row_index here returns MX_ERR_UNSUPPORTED).
  * block_axis = 0 (column-wise, grouped): the rows of x (tokens) are split
  *   into num_groups groups by group_offsets (DEVICE int32[num_groups+1],
  *   non-decreasing, [0] = 0, [num_groups] = rows; produced on the device by
@@ -106,6 +107,11 @@ mx_status mx_rht(const void* x, mx_dtype xt, float* y, int64_t rows, int64_t col
  *   of 32) is the capacity of that axis; the caller guarantees
  *   kp >= sum_g ceil32(n_g) (rows + 31 * num_groups always suffices).
  *   Positions beyond the padded total are not written.
+ *   row_index (optional, DEVICE int32[rows]): the rows are gathered, so the
+ *   token at grouped position p is x[row_index[p]] (x itself may have any
+ *   number of rows; every index must be a valid row of it).  This fuses the
+ *   permutation of tokens into expert order with the quantization: no
+ *   permuted copy of x is written.  NULL: position p is x[p].
  * use_rht != 0 applies the RHT (sign_mask) to each block before quantizing.
  * rnd: MX_RNE or MX_SR (seed, stream_id, index_base as above; index_base %
  *   32 == 0).
@@ -114,7 +120,7 @@ mx_status mx_rht(const void* x, mx_dtype xt, float* y, int64_t rows, int64_t col
  * LLM in MXFP4"); E2M1 + UE8M0 ("What ALTO Actually Does"). */
 mx_status mx_quantize_1d(const void* x, mx_dtype xt, int64_t rows, int64_t cols,
                          int block_axis, const int32_t* group_offsets, int32_t num_groups,
-                         int64_t kp, int use_rht, uint32_t sign_mask, mx_round rnd,
+                         int64_t kp, const int32_t* row_index, int use_rht, uint32_t sign_mask, mx_round rnd,
                          uint64_t seed, uint32_t stream_id, uint64_t index_base,
                          uint8_t* codes, uint8_t* scales, mx_stream stream);
 

@@ -180,6 +180,7 @@ struct ColTile {
 template <bool BF16, bool RHT, bool SR>
 __global__ __launch_bounds__(256) void q1d_col_kernel(const void* __restrict__ x, int64_t cols,
                                                       const int32_t* __restrict__ off, int num_groups,
+                                                      const int32_t* __restrict__ ridx,
                                                       int64_t kp, int64_t col_tiles, int64_t tiles, int vec,
                                                       uint32_t mask, uint32_t k0, uint32_t k1,
                                                       uint32_t stream_id, uint64_t index_base,
@@ -259,8 +260,10 @@ __global__ __launch_bounds__(256) void q1d_col_kernel(const void* __restrict__ x
             const int64_t tb = bcast64(t0, b);
             const int32_t nb = __builtin_amdgcn_readlane(n, b);
             v[k] = make_uint4(0, 0, 0, 0);
-            if (j < nb && col < cols)
-                v[k] = *(const uint4*)((const uint8_t*)x + ((tb + j) * cols + col) * TL::EB);
+            if (j < nb && col < cols) {
+                const int64_t xr = ridx ? (int64_t)ridx[tb + j] : tb + j;   // gathered row
+                v[k] = *(const uint4*)((const uint8_t*)x + (xr * cols + col) * TL::EB);
+            }
         }
     };
 
@@ -292,7 +295,7 @@ __global__ __launch_bounds__(256) void q1d_col_kernel(const void* __restrict__ x
                 const int64_t col = c0 + cc;
                 uint8_t* dst = tile + b * TL::BSTRIDE + j * TL::ROWB + cc * TL::EB;
                 const bool ok = j < nb && col < cols;
-                const int64_t src = (tb + j) * cols + col;
+                const int64_t src = ok ? ((ridx ? (int64_t)ridx[tb + j] : tb + j) * cols + col) : 0;
                 if (BF16) *(uint16_t*)dst = ok ? ((const uint16_t*)x)[src] : (uint16_t)0;
                 else *(float*)dst = ok ? ((const float*)x)[src] : 0.0f;
             }
@@ -688,7 +691,8 @@ mx_status mx_rht(const void* x, mx_dtype xt, float* y, int64_t rows, int64_t col
 #define MX_DISPATCH3(KERNEL, B, R, S, GRID, STREAM, ...) MX_DISPATCH3_LDS(KERNEL, B, R, S, GRID, 0, STREAM, __VA_ARGS__)
 
 mx_status mx_quantize_1d(const void* x, mx_dtype xt, int64_t rows, int64_t cols, int block_axis,
-                         const int32_t* group_offsets, int32_t num_groups, int64_t kp, int use_rht,
+                         const int32_t* group_offsets, int32_t num_groups, int64_t kp,
+                         const int32_t* row_index, int use_rht,
                          uint32_t sign_mask, mx_round rnd, uint64_t seed, uint32_t stream_id,
                          uint64_t index_base, uint8_t* codes, uint8_t* scales, mx_stream stream) {
     if (xt != MX_F32 && xt != MX_BF16) return MX_ERR_DTYPE;
@@ -701,6 +705,7 @@ mx_status mx_quantize_1d(const void* x, mx_dtype xt, int64_t rows, int64_t cols,
     if (block_axis == 1) {
         if (cols % 32) return MX_ERR_SHAPE;
         if (group_offsets || num_groups || kp) return MX_ERR_SHAPE;
+        if (row_index) return MX_ERR_UNSUPPORTED;
         if (rows == 0) return MX_OK;
         if (!x || !codes || !scales) return MX_ERR_NULL;
         if (!aligned16(x) || !aligned16(codes)) return MX_ERR_ALIGN;
@@ -738,7 +743,7 @@ mx_status mx_quantize_1d(const void* x, mx_dtype xt, int64_t rows, int64_t cols,
         }
     }
     (void)hipGetLastError();
-    MX_DISPATCH3_LDS(q1d_col_kernel, bf, rh, sr, dim3(grid), lds, s, x, cols, group_offsets, (int)num_groups, kp,
+    MX_DISPATCH3_LDS(q1d_col_kernel, bf, rh, sr, dim3(grid), lds, s, x, cols, group_offsets, (int)num_groups, row_index, kp,
                      col_tiles, tiles, vec, sign_mask, k0, k1, stream_id, index_base, codes, scales);
     return launched();
 }

@@ -46,7 +46,7 @@ def lib():
         L.mx_rht_sign_mask.argtypes = [u64]
         L.mx_rht_sign_mask.restype = u32
         L.mx_rht.argtypes = [P, c_int, P, i64, i64, u32, c_int, P]
-        L.mx_quantize_1d.argtypes = [P, c_int, i64, i64, c_int, P, i32, i64, c_int, u32, c_int,
+        L.mx_quantize_1d.argtypes = [P, c_int, i64, i64, c_int, P, i32, i64, P, c_int, u32, c_int,
                                      u64, u32, u64, P, P, P]
         L.mx_quantize_2d.argtypes = [P, c_int, i64, i64, i64, P, P, P, P, P]
         L.mx_dequantize.argtypes = [P, P, i64, i64, i64, c_int, P, c_int, P]
@@ -126,11 +126,16 @@ def padded_capacity(rows: int, num_groups: int) -> int:
 
 def quantize_1d(x, block_axis: int = 1, group_offsets=None, kp: int = 0, use_rht: bool = False,
                 sign_mask: int = 0, rnd: int = RNE, seed: int = 0, stream_id: int = 0,
-                index_base: int = 0, codes=None, scales=None):
-    """Returns (codes, scales) uint8 device tensors; see mx_quantize_1d."""
+                index_base: int = 0, codes=None, scales=None, row_index=None):
+    """Returns (codes, scales) uint8 device tensors; see mx_quantize_1d.
+    row_index (column-wise only): gather x's rows through it; the grouped
+    positions then number row_index.numel()."""
     torch = _torch()
     _dev(x, "x")
     rows, cols = x.shape
+    if row_index is not None:
+        _dev(row_index, "row_index")
+        rows = row_index.numel()
     ng = 0
     if block_axis == 1:
         shape_c, shape_s = (rows, cols // 2), (rows, cols // 32)
@@ -146,7 +151,7 @@ def quantize_1d(x, block_axis: int = 1, group_offsets=None, kp: int = 0, use_rht
         scales = torch.empty(shape_s, dtype=torch.uint8, device=x.device)
     _check("mx_quantize_1d", lib().mx_quantize_1d(
         _ptr(x), _dtype_code(x), rows, cols, block_axis, _ptr(group_offsets), ng, kp,
-        int(use_rht), sign_mask, rnd, seed, stream_id, index_base, _ptr(codes), _ptr(scales),
+        _ptr(row_index), int(use_rht), sign_mask, rnd, seed, stream_id, index_base, _ptr(codes), _ptr(scales),
         _stream()))
     return codes, scales
 

@@ -38,25 +38,27 @@ FAKE = 0x1000  # a 16-byte aligned non-null address; never dereferenced (validat
 def test_quantize_1d_validation(L):
     q = L.mx_quantize_1d
     # cols not a multiple of 32
-    assert q(FAKE, mx.MX_BF16, 4, 33, 1, None, 0, 0, 0, 0, 0, 0, 0, 0, FAKE, FAKE, None) == 2
+    assert q(FAKE, mx.MX_BF16, 4, 33, 1, None, 0, 0, None, 0, 0, 0, 0, 0, 0, FAKE, FAKE, None) == 2
     # bad dtype, bad rounding mode
-    assert q(FAKE, 7, 4, 32, 1, None, 0, 0, 0, 0, 0, 0, 0, 0, FAKE, FAKE, None) == 4
-    assert q(FAKE, mx.MX_BF16, 4, 32, 1, None, 0, 0, 0, 0, 3, 0, 0, 0, FAKE, FAKE, None) == 5
+    assert q(FAKE, 7, 4, 32, 1, None, 0, 0, None, 0, 0, 0, 0, 0, 0, FAKE, FAKE, None) == 4
+    assert q(FAKE, mx.MX_BF16, 4, 32, 1, None, 0, 0, None, 0, 0, 3, 0, 0, 0, FAKE, FAKE, None) == 5
     # null pointers
-    assert q(None, mx.MX_BF16, 4, 32, 1, None, 0, 0, 0, 0, 0, 0, 0, 0, FAKE, FAKE, None) == 1
-    assert q(FAKE, mx.MX_BF16, 4, 32, 1, None, 0, 0, 0, 0, 0, 0, 0, 0, None, FAKE, None) == 1
+    assert q(None, mx.MX_BF16, 4, 32, 1, None, 0, 0, None, 0, 0, 0, 0, 0, 0, FAKE, FAKE, None) == 1
+    assert q(FAKE, mx.MX_BF16, 4, 32, 1, None, 0, 0, None, 0, 0, 0, 0, 0, 0, None, FAKE, None) == 1
     # misaligned input
-    assert q(FAKE + 2, mx.MX_BF16, 4, 32, 1, None, 0, 0, 0, 0, 0, 0, 0, 0, FAKE, FAKE, None) == 3
+    assert q(FAKE + 2, mx.MX_BF16, 4, 32, 1, None, 0, 0, None, 0, 0, 0, 0, 0, 0, FAKE, FAKE, None) == 3
     # index base not a multiple of 32
-    assert q(FAKE, mx.MX_BF16, 4, 32, 1, None, 0, 0, 0, 0, 1, 7, 0, 8, FAKE, FAKE, None) == 2
+    assert q(FAKE, mx.MX_BF16, 4, 32, 1, None, 0, 0, None, 0, 0, 1, 7, 0, 8, FAKE, FAKE, None) == 2
     # row-wise with groups given
-    assert q(FAKE, mx.MX_BF16, 4, 32, 1, FAKE, 2, 0, 0, 0, 0, 0, 0, 0, FAKE, FAKE, None) == 2
+    assert q(FAKE, mx.MX_BF16, 4, 32, 1, FAKE, 2, 0, None, 0, 0, 0, 0, 0, 0, FAKE, FAKE, None) == 2
     # column-wise: missing offsets, bad kp, bad group count
-    assert q(FAKE, mx.MX_BF16, 4, 32, 0, None, 2, 64, 0, 0, 0, 0, 0, 0, FAKE, FAKE, None) == 1
-    assert q(FAKE, mx.MX_BF16, 4, 32, 0, FAKE, 2, 40, 0, 0, 0, 0, 0, 0, FAKE, FAKE, None) == 2
-    assert q(FAKE, mx.MX_BF16, 4, 32, 0, FAKE, 0, 64, 0, 0, 0, 0, 0, 0, FAKE, FAKE, None) == 2
+    assert q(FAKE, mx.MX_BF16, 4, 32, 0, None, 2, 64, None, 0, 0, 0, 0, 0, 0, FAKE, FAKE, None) == 1
+    assert q(FAKE, mx.MX_BF16, 4, 32, 0, FAKE, 2, 40, None, 0, 0, 0, 0, 0, 0, FAKE, FAKE, None) == 2
+    assert q(FAKE, mx.MX_BF16, 4, 32, 0, FAKE, 0, 64, None, 0, 0, 0, 0, 0, 0, FAKE, FAKE, None) == 2
+    # a row gather is column-wise only
+    assert q(FAKE, mx.MX_BF16, 4, 32, 1, None, 0, 0, FAKE, 0, 0, 0, 0, 0, 0, FAKE, FAKE, None) == 5
     # empty input is a no-op that launches nothing
-    assert q(None, mx.MX_BF16, 0, 32, 1, None, 0, 0, 0, 0, 0, 0, 0, 0, None, None, None) == 0
+    assert q(None, mx.MX_BF16, 0, 32, 1, None, 0, 0, None, 0, 0, 0, 0, 0, 0, None, None, None) == 0
 
 
 def test_quantize_2d_validation(L):

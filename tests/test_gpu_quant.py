@@ -234,6 +234,55 @@ def test_colwise_full_size_sampled_columns():
         _assert_same(ch[col:col + 1, :total // 2], oc[:, :total // 2], "codes col %d" % col)
 
 
+@pytest.mark.parametrize("dt,cols", [("bf16", 96), ("f32", 100), ("bf16", 70)])
+def test_colwise_gathered_rows(dt, cols):
+    # the grouped positions read x through a row index (with repeats, like
+    # top-k routing); the oracle quantizes the host-gathered matrix
+    counts = [45, 0, 32, 7, 70, 300]
+    off = synth.offsets_from_counts(counts)
+    rows = int(off[-1])
+    rng = np.random.default_rng(cols + 1)
+    x_rows = 200
+    idx = rng.integers(0, x_rows, rows).astype(np.int32)
+    x = (rng.standard_normal((x_rows, cols)) * np.exp2(rng.integers(-6, 6, (1, cols)))).astype(np.float32)
+    if dt == "bf16":
+        x = synth.f32_to_bf16_bits(x)
+        xd = dev_bf16(x)
+    else:
+        xd = dev(x)
+    kp = mx.padded_capacity(rows, len(counts))
+    mask = mx.rht_sign_mask(3)
+    c, s = mx.quantize_1d(xd, block_axis=0, group_offsets=dev(off), kp=kp, use_rht=True, sign_mask=mask,
+                          rnd=1, seed=8, stream_id=2, row_index=dev(idx))
+    oc, os_ = oracle.quantize_1d(np.ascontiguousarray(x[idx]), block_axis=0, group_offsets=off, kp=kp,
+                                 use_rht=True, sign_mask=mask, rnd=1, seed=8, stream=2)
+    total = oracle.padded_total(off)
+    _assert_same(host(s)[:, :total // 32], os_[:, :total // 32], "scales")
+    _assert_same(host(c)[:, :total // 2], oc[:, :total // 2], "codes")
+
+
+def test_colwise_gathered_full_size_sampled_columns():
+    # the routed activations of the weight gradient at their real shape: the
+    # 16,384-token matrix read through the top-4 routing index (65,536
+    # positions, 32 Zipf segments), RHT + SR, without a permuted copy
+    counts = synth.zipf_counts()
+    off = synth.offsets_from_counts(counts)
+    idx = synth.routing_row_index(counts)
+    x = synth.channel_scaled_activations()
+    kp = mx.padded_capacity(int(off[-1]), len(counts))
+    mask = mx.rht_sign_mask(5)
+    c, s = mx.quantize_1d(dev_bf16(x), block_axis=0, group_offsets=dev(off), kp=kp, use_rht=True,
+                          sign_mask=mask, rnd=1, seed=5, stream_id=2, row_index=dev(idx))
+    ch, sh = host(c), host(s)
+    total = oracle.padded_total(off)
+    for col in (0, 5, 64, 2047, 2879):
+        xc = np.ascontiguousarray(x[idx, col:col + 1])
+        oc, os_ = oracle.quantize_1d(xc, block_axis=0, group_offsets=off, kp=kp, use_rht=True, sign_mask=mask,
+                                     rnd=1, seed=5, stream=2, index_base=col * kp)
+        _assert_same(sh[col:col + 1, :total // 32], os_[:, :total // 32], "scales col %d" % col)
+        _assert_same(ch[col:col + 1, :total // 2], oc[:, :total // 2], "codes col %d" % col)
+
+
 # ---------------------------------------------------------------------------
 # 2D 32x32
 # ---------------------------------------------------------------------------
