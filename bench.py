@@ -174,11 +174,16 @@ def measured_traffic(role):
         if len(f) >= 2 and f[0] == "source_sha256":
             src = f[1]
         elif len(f) >= 6 and f[0] == "kernel":
-            rec[f[1]] = (float(f[3]), float(f[5]))
+            calls = float(f[7]) if len(f) >= 8 and f[6] == "calls" else 1.0
+            rec[f[1]] = (float(f[3]), float(f[5]), calls)
+    # a role may launch several instantiations (e.g. with and without a row
+    # gather): average over all of its dispatches
     names = [k for k in rec if k.startswith(ROLE_KERNEL[role])]
-    if src != kernel_source_hash() or len(names) != 1:
+    if src != kernel_source_hash() or not names:
         return None
-    rd, wr = rec[names[0]]
+    n = sum(rec[k][2] for k in names)
+    rd = sum(rec[k][0] * rec[k][2] for k in names) / n
+    wr = sum(rec[k][1] * rec[k][2] for k in names) / n
     return {"read_bytes": rd, "write_bytes": wr, "bytes": rd + wr}
 
 

@@ -159,7 +159,13 @@ mx_status mx_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t bat
  *   multiples of 32, [num_groups] <= K); A [M x K], B [N x K], 1D scales;
  *   C [num_groups x M x N]; a group with an empty K range writes zeros.
  * K % 32 == 0, N % 32 == 0, M >= 0; ct = MX_BF16 (round to nearest even) or
- * MX_F32.  Code and C pointers 16-byte aligned. */
+ * MX_F32.  Code and C pointers 16-byte aligned.  The kernel addresses each
+ * operand with 32-bit byte offsets: N*K/2 (one B group) and, without a row
+ * index, M*K/2 must not exceed 4 GiB - 1 (else MX_ERR_SHAPE); with a row
+ * index the indexed rows must lie within the first 4 GiB of a_codes.
+ * Errors: MX_ERR_DTYPE (ct), MX_ERR_SHAPE (sizes, num_groups < 1,
+ * group_dim_k), MX_ERR_UNSUPPORTED (group_dim_k = 1 with 2D B scales or a row
+ * index), MX_ERR_NULL, MX_ERR_ALIGN, MX_ERR_LAUNCH.  M == 0 launches nothing. */
 mx_status mx_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
                           const int32_t* a_row_index,
                           const uint8_t* b_codes, const uint8_t* b_scales, int b_scale_2d,

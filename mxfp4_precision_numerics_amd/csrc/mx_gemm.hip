@@ -12,25 +12,38 @@
 // The MFMA's first operand is the weight tile (rows = output columns n) and
 // its second the activation tile (rows = output rows m), so D = C^T per
 // 32x32 block and each lane ends up holding 4 consecutive output columns of
-// one output row: the epilogue stores 8-byte (bf16) or 16-byte (fp32) runs.
+// one output row.
 //
-// Tiling: a workgroup of 8 waves (2 x 4) computes a 256 x 256 tile of one
-// group; each wave owns 128 x 64 (8 MFMA blocks, 128 accumulators), two waves
-// per SIMD so that one wave's LDS and DMA waits are covered by the other's
-// MFMAs (4 waves of 128 x 128, one per SIMD, measured 8-9% slower).  K
-// advances 256 per stage, so every operand row contributes one 128-byte
-// line per stage (half-line requests cost nearly as much as full
-// ones at the L2).  Every operand byte moves global -> LDS by the CDNA
-// LDS-DMA loads (global_load_lds_dwordx4 for 16-byte code chunks, 8 lanes per
-// row line; global_load_lds_ubyte for scale bytes, each landing as a dword),
-// so no staging registers are needed.  The ring has two 80 KiB buffers (all
-// of a CU's LDS): stage kt+2 is issued at stage kt's barrier into the buffer
-// stage kt has just finished reading, which leaves it a full stage to land.
-// The DMA is issued from register-only inline assembly and its completion is
+// Tiling: a workgroup of 8 waves (2 x 4) computes 256 x 256 tiles; each wave
+// owns 128 x 64 (8 MFMA blocks, 128 accumulators), two waves per SIMD so
+// that one wave's LDS and DMA waits are covered by the other's MFMAs (4
+// waves of 128 x 128, one per SIMD, measured 8-9% slower).  K advances 256
+// per stage, so every operand row contributes one 128-byte line per stage
+// (half-line requests cost nearly as much as full ones at the L2).  Every
+// operand byte moves global -> LDS by the CDNA LDS-DMA loads
+// (global_load_lds_dwordx4 for 16-byte code chunks, 8 lanes per row line;
+// global_load_lds_ubyte for scale bytes, each landing as a dword), so no
+// staging registers are needed.  The ring has two 80 KiB buffers (all of a
+// CU's LDS): stage kt+2 is issued at stage kt's barrier into the buffer stage
+// kt has just finished reading, which leaves it a full stage to land.  The
+// DMA is issued from register-only inline assembly and its completion is
 // awaited explicitly (s_waitcnt vmcnt + s_barrier).  A stage runs as four
-// K-quarters of 64; operand fragments are double-buffered in registers and
-// the next quarter's fragment reads are interleaved one per MFMA with the
-// current quarter's MFMAs.
+// K-quarters of 64; each of the quarter's 8 MFMAs is followed by the read of
+// the next quarter's fragment piece whose last use it was, into the same
+// registers.  A row's four K-quarter scale bytes are packed in one register
+// and the MFMA's scale byte-select picks the quarter.
+//
+// Persistence: one workgroup per CU walks its tiles in snake order (round r
+// takes position r P + w, or r P + P - 1 - w on odd rounds), so groups of
+// unequal cost (the weight gradient's K follows the routing counts) spread
+// evenly.  The ring runs on across tiles: the last two stages of a tile
+// issue the next tile's first two, and the last K-quarter already reads its
+// first fragments, so a tile starts its MFMAs without a prologue.  The
+// epilogue stores straight from the accumulators (two lane-group register
+// swaps give 16 rows x 64 contiguous bytes per store) through a buffer
+// resource whose range check drops rows and columns outside C, so every wave
+// issues a fixed number of stores and the next tile's first barrier leaves
+// them in flight.
 //
 // LDS code tiles use an XOR swizzle of the eight 16-byte chunks of a row;
 // each row's 8 scale dwords are stored in the order (s0, s2, s4, s6, s1, s3,
@@ -46,6 +59,8 @@
 // one XCD share A rows and B columns in its L2.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "../../include/mx.h"
 #include "mx_device.h"
@@ -69,6 +84,7 @@ struct GemmArgs {
     int32_t tiles_n;
     int32_t tiles_m;     // group_dim_k = 1: tiles along M per group
     float alpha;
+    int64_t tiles;       // size of the tile-id space (a multiple of XCDS * XCD_BLOCK)
 };
 
 constexpr int BM = 256, BN = 256;
@@ -110,177 +126,209 @@ __device__ __forceinline__ void dma1(const void* base, uint32_t voff, uint32_t l
                  :: "v"(voff), "s"(base), "s"(lds) : "memory");
 }
 
+// a value every lane holds alike, moved to scalar registers
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)((uint64_t)v >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     const __bf16 x = (__bf16)a, y = (__bf16)b;   // v_cvt_pk_bf16_f32: round to nearest even
     return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
 }
 
-template <bool OUT_BF16, bool B2D>
+template <bool OUT_BF16, bool B2D, bool GK, bool GATHER>
 __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
+    static_assert(!(GK && (B2D || GATHER)), "groups along K take 1D B scales and no row index");
     // 2 x 4 waves of 128 x 64
     constexpr int WM = 128, WN = 64, FM = 4, FN = WN / 32;
+    constexpr int NJ = 2048 / NT;               // code (and scale) moves per operand per thread
     __shared__ __attribute__((aligned(16))) uint8_t lds[NST * STAGE_BYTES];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 2, wn = wave & 3;
-
-    // ---------------- tile id: XCD-aware remap of the workgroup id ----------
-    const int64_t wg = blockIdx.x;
-    const int64_t xcd = wg % XCDS, j = wg / XCDS;
-    int64_t id = (j / XCD_BLOCK) * (XCDS * XCD_BLOCK) + xcd * XCD_BLOCK + (j % XCD_BLOCK);
-
-    // ---------------- tile decode ----------------
-    // Groups split M: wave 0 reads all group offsets at once, scans the tile
-    // counts ceil(n_g / BM) * tiles_n across its lanes and publishes the
-    // group holding tile `id` (one round trip to memory instead of one per
-    // group).
-    // the tile decode's result lives in the first ring bytes until every
-    // thread has read it (the ring fills all 160 KiB of LDS)
-    int32_t* tile_group = (int32_t*)lds;
-    int g = 0;
-    int64_t m_begin = 0, m_end = 0, k_begin = 0, k_end = p.K, mtiles = 0;
-    if (p.group_dim_k == 0) {
-        if (wave == 0) {
-            if (lane == 0) tile_group[0] = -1;
-            int64_t running = 0;
-            for (int base = 0; base < p.G; base += 64) {
-                const int gg = base + lane;
-                int64_t t = 0, gb = 0, ge = 0;
-                if (gg < p.G) {
-                    gb = p.off[gg];
-                    ge = p.off[gg + 1];
-                    t = (ge - gb + BM - 1) / BM * p.tiles_n;
-                }
-                int64_t incl = t;
-#pragma unroll
-                for (int d = 1; d < 64; d <<= 1) {
-                    const int64_t v = __shfl_up(incl, d);
-                    if (lane >= d) incl += v;
-                }
-                const int64_t start = running + incl - t;
-                if (gg < p.G && id >= start && id < start + t) {
-                    tile_group[0] = gg;
-                    tile_group[1] = (int32_t)(id - start);
-                }
-                running += __shfl(incl, 63);
-            }
-        }
-        __syncthreads();
-        g = __builtin_amdgcn_readfirstlane(tile_group[0]);   // uniform: the DMA takes scalar bases
-        if (g < 0) return;                      // past the last tile (uniform)
-        id = __builtin_amdgcn_readfirstlane(tile_group[1]);
-        __syncthreads();                        // read by all before the ring's first DMA
-        m_begin = p.off[g];
-        m_end = p.off[g + 1];
-        mtiles = (m_end - m_begin + BM - 1) / BM;
-    } else {
-        const int64_t per = (int64_t)p.tiles_m * p.tiles_n;
-        g = (int)(id / per);
-        if (g >= p.G) return;
-        id -= (int64_t)g * per;
-        mtiles = p.tiles_m;
-        m_begin = 0;
-        m_end = p.M;
-        k_begin = p.off[g];
-        k_end = p.off[g + 1];
-    }
-    // grouped order inside the group: GROUP_M M-tiles x all N-tiles, m fastest
-    const int64_t span = (int64_t)GROUP_M * p.tiles_n;
-    const int64_t sgrp = id / span;
-    const int64_t rem = id - sgrp * span;
-    const int64_t gm = min((int64_t)GROUP_M, mtiles - sgrp * GROUP_M);
-    const int64_t nt = rem / gm;
-    const int64_t mt = sgrp * GROUP_M + (rem - nt * gm);
-    const int64_t grp_end = m_end;
-    m_begin = m_begin + mt * BM;
-    m_end = min(grp_end, m_begin + BM);
-    const int64_t n_begin = nt * BN;
-
     const int64_t KB = p.K / 2;      // code bytes per operand row
     const int64_t KS = p.K / 32;     // scale bytes per operand row
 
-    const uint8_t* bcodes = p.b_codes;
-    const uint8_t* bscales = p.b_scales;
-    if (p.group_dim_k == 0) {
-        bcodes += (int64_t)g * p.N * KB;
-        bscales += (int64_t)g * (B2D ? (p.N / 32) * KS : p.N * KS);
-    }
-
-    // ---------------- per-thread DMA assignments ----------------
-    // Code DMA j of thread t fills 16-byte slot t + 256 j of an operand tile:
-    // row r = t/8 + 32 j, slot position pc = t % 8 of the row's 128 bytes, so
-    // 8 lanes move one full 128-byte line.  Scale DMA j fills dword slot
-    // t + 256 j: the same row, scale position pc.
-    const int pc = tid & 7;
-    const int a_chunk = pc ^ swz(tid >> 3);    // swz(t/8 + 32 j) is the same for every j
-    const int s_chunk = sperm(pc);
-    constexpr int NJ = 2048 / NT;               // code (and scale) moves per operand per thread
-    uint32_t a_off[NJ], b_off[NJ], as_off[NJ], bs_off[NJ];
+    // ---------------- group table ----------------
+    // With fewer than 64 groups every wave keeps the offsets in its lanes
+    // (lane g: off[g]) and, when groups split M, the first tile id of each
+    // group (a prefix sum of ceil(n_g / BM) * tiles_n), so finding a tile's
+    // group is a ballot and two lane reads, with no memory round trip.
+    const bool table = p.G < 64;
+    int32_t off_l = 0, first_l = 0;
+    if (table) {
+        if (lane <= p.G) off_l = p.off[lane];
+        if (!GK) {
+            const int32_t next = __shfl_down(off_l, 1);
+            const int32_t t = lane < p.G ? (next - off_l + BM - 1) / BM * p.tiles_n : 0;
+            int32_t incl = t;
 #pragma unroll
-    for (int jj = 0; jj < NJ; ++jj) {
-        const int r = (tid >> 3) + (NT / 8) * jj;
-        int64_t m = m_begin + r;
-        if (m >= m_end) m = m_end - 1;        // rows past the tile end are never stored
-        const int64_t arow = p.a_row_index ? (int64_t)p.a_row_index[m] : m;
-        a_off[jj] = (uint32_t)(arow * KB);
-        as_off[jj] = (uint32_t)(arow * KS);
-        int64_t n = n_begin + r;
-        if (n >= p.N) n = p.N - 1;
-        b_off[jj] = (uint32_t)(n * KB);
-        bs_off[jj] = (uint32_t)(n * KS);
-    }
-    // 2D B scales: lane l of every wave fetches row group l / 8 of the tile at
-    // scale position l % 8, into its wave's own 256-byte copy
-    uint32_t bs2_off = 0;
-    if (B2D) {
-        int64_t grp = n_begin / 32 + (lane >> 3);
-        if (grp > p.N / 32 - 1) grp = p.N / 32 - 1;    // groups past N are never stored
-        bs2_off = (uint32_t)(grp * KS);
-    }
-    const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
-
-    const int64_t klen = k_end - k_begin;
-    const int nkt = (int)((klen + BK - 1) / BK);
-    const int64_t kc0 = k_begin / 32;        // first K-chunk of the range
-    const int64_t kc_end = k_end / 32;
-    // K chunks relative to kc0 (32-bit: the host bounds an operand row to 4 GiB)
-    const int kc_last = (int)(kc_end - kc0) - 1;
-#pragma unroll
-    for (int jj = 0; jj < NJ; ++jj) {
-        a_off[jj] += (uint32_t)(kc0 * 16);
-        b_off[jj] += (uint32_t)(kc0 * 16);
-        as_off[jj] += (uint32_t)kc0;
-        bs_off[jj] += (uint32_t)kc0;
-    }
-    bs2_off += (uint32_t)kc0;
-
-    // stage kt -> LDS buffer `buf`; chunks past the end are clamped in range
-    auto issue = [&](int kt, int buf) {
-        const uint32_t sb = lds_base + (uint32_t)buf * STAGE_BYTES;
-        const int kc = min(kt * 8 + a_chunk, kc_last);
-        const int ks = min(kt * 8 + s_chunk, kc_last);
-#pragma unroll
-        for (int jj = 0; jj < NJ; ++jj) {
-            dma16(p.a_codes, a_off[jj] + (uint32_t)(kc * 16), sb + OFF_A + jj * NT * 16 + wave * 1024);
-            dma16(bcodes, b_off[jj] + (uint32_t)(kc * 16), sb + OFF_B + jj * NT * 16 + wave * 1024);
+            for (int d = 1; d < 64; d <<= 1) {
+                const int32_t v = __shfl_up(incl, d);
+                if (lane >= d) incl += v;
+            }
+            first_l = incl - t;                  // lane G: the total tile count
         }
+    }
+
+    struct Tile {
+        int32_t m0, m1, n0;      // output rows [m0, m1) and first output column
+        int32_t g;               // group
+        int32_t kc0, kc_last;    // first K chunk (of 32); last valid chunk relative to it
+        int32_t nkt;             // K stages
+    };
+    // (the host bounds M, N, K and the tile count to int32)
+    const int32_t M32 = (int32_t)p.M, N32 = (int32_t)p.N, K32 = (int32_t)p.K;
+
+    // tile id -> tile; false if the id is past the last tile
+    auto decode = [&](int32_t L, Tile& t) -> bool {
+        // XCD-aware remap of the position: 32 consecutive ids per XCD turn
+        const int32_t xcd = L % XCDS, j = L / XCDS;
+        int32_t id = (j / XCD_BLOCK) * (XCDS * XCD_BLOCK) + xcd * XCD_BLOCK + (j % XCD_BLOCK);
+        int32_t g = -1, mb = 0, me = M32, kb = 0, ke = K32, mtiles;
+        if (!GK) {
+            if (table) {
+                if (id >= __builtin_amdgcn_readlane(first_l, p.G)) return false;
+                // the last group whose first tile is at or before id holds it
+                const uint64_t below = __ballot(lane < p.G && first_l <= id);
+                g = 63 - __builtin_clzll(below);
+                id -= __builtin_amdgcn_readlane(first_l, g);
+                mb = __builtin_amdgcn_readlane(off_l, g);
+                me = __builtin_amdgcn_readlane(off_l, g + 1);
+            } else {
+                // many groups: scan the offsets 64 at a time
+                int32_t running = 0;
+                for (int base = 0; base < p.G; base += 64) {
+                    const int gg = base + lane;
+                    int32_t t = 0, gb = 0, ge = 0;
+                    if (gg < p.G) {
+                        gb = p.off[gg];
+                        ge = p.off[gg + 1];
+                        t = (ge - gb + BM - 1) / BM * p.tiles_n;
+                    }
+                    int32_t incl = t;
 #pragma unroll
-        for (int jj = 0; jj < NJ; ++jj) {
-            dma1(p.a_scales, as_off[jj] + (uint32_t)ks, sb + OFF_AS + jj * NT * 4 + wave * 256);
-            if (!B2D) dma1(bscales, bs_off[jj] + (uint32_t)ks, sb + OFF_BS + jj * NT * 4 + wave * 256);
+                    for (int d = 1; d < 64; d <<= 1) {
+                        const int32_t v = __shfl_up(incl, d);
+                        if (lane >= d) incl += v;
+                    }
+                    const int32_t start = running + incl - t;
+                    const uint64_t hit = __ballot(gg < p.G && id >= start && id < start + t);
+                    if (hit) {
+                        const int h = __builtin_ctzll(hit);
+                        g = base + h;
+                        id -= __builtin_amdgcn_readlane(start, h);
+                        mb = __builtin_amdgcn_readlane(gb, h);
+                        me = __builtin_amdgcn_readlane(ge, h);
+                        break;
+                    }
+                    running += __builtin_amdgcn_readlane(incl, 63);
+                }
+                if (g < 0) return false;
+            }
+            mtiles = (me - mb + BM - 1) / BM;
+        } else {
+            const int32_t per = p.tiles_m * p.tiles_n;
+            if (id / per >= p.G) return false;
+            g = id / per;
+            id -= g * per;
+            mtiles = p.tiles_m;
+            kb = table ? __builtin_amdgcn_readlane(off_l, g) : p.off[g];
+            ke = table ? __builtin_amdgcn_readlane(off_l, g + 1) : p.off[g + 1];
         }
-        if (B2D) dma1(bscales, bs2_off + (uint32_t)ks, sb + OFF_BS + wave * 256);
+        // grouped order inside the group: GROUP_M M-tiles x all N-tiles, m fastest
+        const int32_t span = GROUP_M * p.tiles_n;
+        const int32_t sgrp = id / span;
+        const int32_t rem = id - sgrp * span;
+        const int32_t gm = min(GROUP_M, mtiles - sgrp * GROUP_M);
+        const int32_t nt = rem / gm;
+        const int32_t mt = sgrp * GROUP_M + (rem - nt * gm);
+        t.m0 = mb + mt * BM;
+        t.m1 = min(me, t.m0 + BM);
+        t.n0 = nt * BN;
+        t.g = g;
+        t.kc0 = kb / 32;
+        t.kc_last = ke / 32 - kb / 32 - 1;
+        t.nkt = (ke - kb + BK - 1) / BK;
+        return true;
     };
 
-    v16f acc[FN][FM];
+    // Persistent tile loop: in round r this workgroup takes position
+    // r * P + w (w = its id) on even rounds and r * P + P - 1 - w on odd ones.
+    // Tile ids within a group have equal cost, so the snake keeps the total
+    // per workgroup even when groups differ in cost (weight gradient: K per
+    // group follows the routing counts).
+    const int32_t P = gridDim.x;
+    const int32_t w = blockIdx.x;
+    const int32_t tiles = (int32_t)p.tiles;
+    auto find_tile = [&](int32_t& r, Tile& t) -> bool {
+        for (;; ++r) {
+            const int32_t L = r * P + ((r & 1) ? P - 1 - w : w);
+            if (L >= tiles) return false;
+            if (decode(L, t)) return true;
+        }
+    };
+    // the A rows of this thread's DMA moves: r = t/8 + (NT/8) j
+    auto load_rows = [&](const Tile& t, int32_t (&arow)[NJ]) {
 #pragma unroll
-    for (int i = 0; i < FN; ++i)
+        for (int jj = 0; jj < NJ; ++jj) {
+            int32_t m = t.m0 + (tid >> 3) + (NT / 8) * jj;
+            if (m >= t.m1) m = t.m1 - 1;          // rows past the tile end are never stored
+            arow[jj] = GATHER ? p.a_row_index[m] : m;
+        }
+    };
+
+    // ---------------- per-thread DMA assignments ----------------
+    // Code DMA j of thread t fills 16-byte slot t + NT j of an operand tile:
+    // row t/8 + (NT/8) j, slot position pc = t % 8 of the row's 128 bytes, so
+    // 8 lanes move one full 128-byte line.  Scale DMA j fills dword slot
+    // t + NT j: the same row, scale position pc.  Byte offsets are 32-bit
+    // (the host bounds every operand to 4 GiB).
+    const int pc = tid & 7;
+    const int a_chunk = pc ^ swz(tid >> 3);    // swz(t/8 + (NT/8) j) is the same for every j
+    const int s_chunk = sperm(pc);
+    const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
+
+    // stage kt of tile t -> LDS buffer `buf`; chunks past the end are clamped in range
+    auto issue = [&](const Tile& t, const int32_t (&arow)[NJ], int kt, int buf) {
+        const uint32_t sb = lds_base + (uint32_t)buf * STAGE_BYTES;
+        const uint32_t kc = (uint32_t)(t.kc0 + min(kt * 8 + a_chunk, t.kc_last));
+        const uint32_t ks = (uint32_t)(t.kc0 + min(kt * 8 + s_chunk, t.kc_last));
+        const uint8_t* bcodes = p.b_codes;
+        const uint8_t* bscales = p.b_scales;
+        if (!GK) {
+            bcodes += (int64_t)t.g * p.N * KB;
+            bscales += (int64_t)t.g * (B2D ? (p.N / 32) * KS : p.N * KS);
+        }
+        uint32_t nrow[NJ], mrow[NJ];
 #pragma unroll
-        for (int jj = 0; jj < FM; ++jj)
+        for (int jj = 0; jj < NJ; ++jj) {
+            const int32_t n = t.n0 + (tid >> 3) + (NT / 8) * jj;
+            nrow[jj] = (uint32_t)(n < N32 ? n : N32 - 1);   // rows past N are never stored
+            mrow[jj] = (uint32_t)arow[jj];
+        }
 #pragma unroll
-            for (int e = 0; e < 16; ++e) acc[i][jj][e] = 0.0f;
+        for (int jj = 0; jj < NJ; ++jj) {
+            dma16(p.a_codes, mrow[jj] * (uint32_t)KB + kc * 16, sb + OFF_A + jj * NT * 16 + wave * 1024);
+            dma16(bcodes, nrow[jj] * (uint32_t)KB + kc * 16, sb + OFF_B + jj * NT * 16 + wave * 1024);
+        }
+#pragma unroll
+        for (int jj = 0; jj < NJ; ++jj) {
+            dma1(p.a_scales, mrow[jj] * (uint32_t)KS + ks, sb + OFF_AS + jj * NT * 4 + wave * 256);
+            if (!B2D) dma1(bscales, nrow[jj] * (uint32_t)KS + ks, sb + OFF_BS + jj * NT * 4 + wave * 256);
+        }
+        if (B2D) {
+            // lane l of every wave fetches row group l / 8 of the tile at
+            // scale position l % 8, into its wave's own 256-byte copy
+            int32_t grp = t.n0 / 32 + (lane >> 3);
+            if (grp > N32 / 32 - 1) grp = N32 / 32 - 1;    // groups past N are never stored
+            dma1(bscales, (uint32_t)grp * (uint32_t)KS + ks, sb + OFF_BS + wave * 256);
+        }
+    };
 
     const int lr = lane & 31;      // operand row within a 32-row MFMA block
     const int lh = lane >> 5;      // which 32-element half of a K-quarter (64)
@@ -290,8 +338,11 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
     const uint32_t fb_b = OFF_B + (uint32_t)(wn * WN + lr) * 128;
     const uint32_t fb_a = OFF_A + (uint32_t)(wm * WM + lr) * 128;
 
+    v16f acc[FN][FM];
     struct Frag { v8i b[FN]; v8i a[FM]; };
-    struct Scl { uint4 b[FN]; uint4 a[FM]; };   // component q: K-quarter q
+    // a row's four K-quarter scale bytes packed in one register (byte q:
+    // K-quarter q); the MFMA's scale operand selects the byte
+    struct Scl { uint32_t b[FN]; uint32_t a[FM]; };
     auto read_frag = [&](Frag& f, int buf, int q) {
         const uint8_t* sb = lds + buf * STAGE_BYTES + (((2 * q + lh) ^ sw) * 16);
 #pragma unroll
@@ -305,7 +356,10 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
             f.a[i] = (v8i){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
         }
     };
-    auto read_scl = [&](Scl& s, int buf) {
+    // the next stage's scales are read during the current stage's last
+    // K-quarter and packed only after its MFMAs, when the reads have landed
+    struct SclRaw { uint4 b[FN]; uint4 a[FM]; };
+    auto read_scl = [&](SclRaw& s, int buf) {
         const uint8_t* sb = lds + buf * STAGE_BYTES;
 #pragma unroll
         for (int i = 0; i < FN; ++i)
@@ -315,18 +369,12 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
         for (int i = 0; i < FM; ++i)
             s.a[i] = *(const uint4*)(sb + OFF_AS + (wm * WM + i * 32 + lr) * 32 + lh * 16);
     };
-    auto qsel = [](const uint4& v, int q) { return q == 0 ? v.x : q == 1 ? v.y : q == 2 ? v.z : v.w; };
-    auto mma = [&](const Frag& f, const Scl& s, int q, bool tail) {
+    auto pack = [](Scl& s, const SclRaw& r) {
+        auto pack4 = [](const uint4& v) { return v.x | (v.y << 8) | (v.z << 16) | (v.w << 24); };
 #pragma unroll
-        for (int i = 0; i < FN; ++i) {
-            const int sb = tail ? 0 : (int)qsel(s.b[i], q);
+        for (int i = 0; i < FN; ++i) s.b[i] = pack4(r.b[i]);
 #pragma unroll
-            for (int jj = 0; jj < FM; ++jj) {
-                const int sa = tail ? 0 : (int)qsel(s.a[jj], q);
-                acc[i][jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                    f.b[i], f.a[jj], acc[i][jj], 4, 4, 0, sb, 0, sa);
-            }
-        }
+        for (int i = 0; i < FM; ++i) s.a[i] = pack4(r.a[i]);
     };
 
     // "every DMA but the newest stage's has landed"
@@ -338,9 +386,16 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
     // one MFMA block, optionally followed by one piece of the next read
     auto mma1 = [&](const Frag& f, const Scl& s, int q, bool tail, int m) {
         const int i = m / FM, jj = m % FM;
-        const int sb = tail ? 0 : (int)qsel(s.b[i], q);
-        const int sa = tail ? 0 : (int)qsel(s.a[jj], q);
-        acc[i][jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[i], f.a[jj], acc[i][jj], 4, 4, 0, sb, 0, sa);
+        const int sb = tail ? 0 : (int)s.b[i];
+        const int sa = tail ? 0 : (int)s.a[jj];
+        v16f& d = acc[i][jj];
+        // the byte select is an immediate: q is a constant once inlined
+        switch (q) {
+        case 0: d = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[i], f.a[jj], d, 4, 4, 0, sb, 0, sa); break;
+        case 1: d = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[i], f.a[jj], d, 4, 4, 1, sb, 1, sa); break;
+        case 2: d = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[i], f.a[jj], d, 4, 4, 2, sb, 2, sa); break;
+        default: d = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[i], f.a[jj], d, 4, 4, 3, sb, 3, sa); break;
+        }
     };
     auto read_piece = [&](Frag& f, int buf, int q, int k) {
         const uint8_t* sb = lds + buf * STAGE_BYTES + (((2 * q + lh) ^ sw) * 16);
@@ -348,93 +403,227 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
         v8i& d = k < FN ? f.b[k] : f.a[k - FN];
         d = (v8i){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
     };
-    auto mma_rd = [&](const Frag& f, const Scl& s, int q, bool tail, Frag& nf, int nbuf, int nq) {
+    // One K-quarter: 8 MFMA blocks (m = i * FM + jj), each followed by the
+    // read of the next quarter's fragment piece whose last use it was, into
+    // the same registers (B piece i is last used by block i FM + FM - 1, A
+    // piece jj by block FM + jj), so a single fragment set suffices and every
+    // read still has at least three MFMAs to land.
+    auto mma_rd = [&](Frag& f, const Scl& s, int q, bool tail, int nbuf, int nq) {
 #pragma unroll
         for (int m = 0; m < FN * FM; ++m) {
             mma1(f, s, q, tail, m);
-            if (m < FN + FM) read_piece(nf, nbuf, nq, m);
+            if (m == FM - 1) read_piece(f, nbuf, nq, 0);                 // B 0
+            if (m >= FM) read_piece(f, nbuf, nq, FN + (m - FM));         // A m - FM
+            if (m == FN * FM - 1) read_piece(f, nbuf, nq, 1);            // B 1
             __builtin_amdgcn_sched_barrier(0);
         }
     };
-    if (nkt > 0) {
-        Frag f0, f1;
-        Scl sc, nsc;
-        // Stage kt+1's DMA is issued at stage kt-1's barrier, into the buffer
-        // stage kt-1 has finished reading; at stage kt's barrier it is the
-        // only DMA outstanding, so vmcnt(0) means it has landed.
-        issue(0, 0);
-        issue(1, 1);
-        wait_all_but_one_stage();
-        __builtin_amdgcn_s_barrier();
-        read_frag(f0, 0, 0);
-        read_scl(sc, 0);
-        for (int kt = 0; kt < nkt; ++kt) {
-            const int buf = kt & 1;
-            const int kcl = kt * 8 + lh;              // this lane's chunk in K-quarter 0
-            mma_rd(f0, sc, 0, kcl > kc_last, f1, buf, 1);
-            mma_rd(f1, sc, 1, kcl + 2 > kc_last, f0, buf, 2);
-            mma_rd(f0, sc, 2, kcl + 4 > kc_last, f1, buf, 3);
-            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-            __builtin_amdgcn_s_barrier();
-            issue(kt + 2, buf);
-            read_scl(nsc, buf ^ 1);
-            mma_rd(f1, sc, 3, kcl + 6 > kc_last, f0, buf ^ 1, 0);
-            sc = nsc;
-        }
-        // drain the DMA of the two past-the-end stages before the LDS is reused
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    }
 
-    // ---------------- epilogue ----------------
-    // Each wave stages its 128 x 128 result through LDS one 32-row slab at a
-    // time (row pitch padded by 16 bytes against bank conflicts) and stores
-    // whole 16-byte runs, so a store instruction covers 4 full row segments
-    // of 256 (bf16) or 2 of 512 (fp32) bytes instead of 32 scattered pieces.
-    constexpr int EB = OUT_BF16 ? 2 : 4;              // output element bytes
-    constexpr int PITCH = WN * EB + 16;                // LDS bytes per staged row
-    constexpr int SEGS = WN * EB / 16;                 // 16-byte runs per row
-    static_assert(NW * 32 * PITCH <= NST * STAGE_BYTES, "epilogue staging fits the ring");
-    __syncthreads();                                   // every wave is done with the ring
-    uint8_t* stage_c = lds + wave * 32 * PITCH;
-    const int64_t rows_here = m_end - m_begin;
-    uint8_t* cbase = (uint8_t*)p.c;
-    if (p.group_dim_k == 1) cbase += (int64_t)g * p.M * p.N * EB;
-    const float alpha = p.alpha;
-    const int64_t col0 = n_begin + wn * WN;            // first output column of this wave
+    // ---------------- epilogue: straight from the accumulators ----------------
+    // Lane (lr, lh) of a 32 x 32 block holds output row lr, columns
+    // 8 q + 4 lh + (0..3).  Two register swaps across lane groups
+    // (v_permlane32_swap, v_permlane16_swap) regroup a block so that one
+    // 16-byte store per lane writes 16 rows x 64 contiguous bytes, instead of
+    // 32 rows x 16 bytes, which quarters the write requests.  The LDS is left
+    // alone, so the next tile's first stages land meanwhile.
+    auto swap32 = [](uint32_t& x, uint32_t& y) {   // x[32..63] <-> y[0..31]
+        const auto r = __builtin_amdgcn_permlane32_swap(x, y, false, false);
+        x = r[0];
+        y = r[1];
+    };
+    auto swap16 = [](uint32_t& x, uint32_t& y) {   // x[16..31], x[48..63] <-> y[0..15], y[32..47]
+        const auto r = __builtin_amdgcn_permlane16_swap(x, y, false, false);
+        x = r[0];
+        y = r[1];
+    };
+    // Stores go through a buffer resource spanning the tile's rows of C, so
+    // a row or column outside C is dropped by the hardware range check
+    // instead of a branch: every wave issues exactly EPI_STORES stores, which
+    // lets the next tile's first barrier wait for its own loads only.
+    constexpr int EPI_STORES = OUT_BF16 ? FN * FM * 2 : FN * FM * 4;
+    auto epilogue = [&](const Tile& t) {
+        constexpr int EB = OUT_BF16 ? 2 : 4;
+        // (base and size are uniform: kept in scalar registers, the resource
+        // needs no per-lane loop)
+        uint8_t* cb = (uint8_t*)p.c + uniform64(((GK ? (int64_t)t.g * p.M : 0) + t.m0) * p.N * EB);
+        const int32_t nrec = __builtin_amdgcn_readfirstlane((t.m1 - t.m0) * N32 * EB);
+        const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(cb, (short)0, nrec, 0x00020000);
+        const float alpha = p.alpha;
+        const int32_t col0 = t.n0 + wn * WN;            // first output column of this wave
+        // the lane's coordinates pass through an empty asm so that the store
+        // offsets are formed here: hoisted out of the tile loop they would
+        // hold 16 registers through the K loop
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        const int elr = ln & 31, elh = ln >> 5;
+        const int rr = elr & 15, rh = elr >> 4;
+        const int32_t nrows = t.m1 - t.m0;
+        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+        auto put = [&](int32_t row, int32_t col, uint32_t v0, uint32_t v1, uint32_t v2, uint32_t v3) {
+            // row relative to the tile; out-of-range offsets (2 GiB) are dropped
+            const uint32_t off = row < nrows && col < N32 ? (uint32_t)(row * N32 + col) * EB : 0x80000000u;
+            __builtin_amdgcn_raw_buffer_store_b128((u32x4){v0, v1, v2, v3}, rsrc, off, 0, 0);
+        };
 #pragma unroll
-    for (int jj = 0; jj < FM; ++jj) {
-        // lane (lr, lh) holds row lr of the slab, columns i*32 + 8q + 4lh + (0..3)
+        for (int jj = 0; jj < FM; ++jj) {
+            const int32_t r0 = wm * WM + jj * 32 + rr;     // rows r0 and r0 + 16 of the tile
 #pragma unroll
-        for (int i = 0; i < FN; ++i) {
+            for (int i = 0; i < FN; ++i) {
+                const v16f& c = acc[i][jj];
+                if (OUT_BF16) {
+                    // P[q][d]: columns 8 q + 4 lh + 2 d, +1
+                    uint32_t P[4][2];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int cl = i * 32 + 8 * q + 4 * lh;
-                const float v0 = acc[i][jj][4 * q + 0] * alpha;
-                const float v1 = acc[i][jj][4 * q + 1] * alpha;
-                const float v2 = acc[i][jj][4 * q + 2] * alpha;
-                const float v3 = acc[i][jj][4 * q + 3] * alpha;
-                uint8_t* dst = stage_c + lr * PITCH + cl * EB;
-                if (OUT_BF16)
-                    *(uint2*)dst = make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
-                else
-                    *(uint4*)dst = make_uint4(__float_as_uint(v0), __float_as_uint(v1),
-                                              __float_as_uint(v2), __float_as_uint(v3));
+                    for (int q = 0; q < 4; ++q)
+#pragma unroll
+                        for (int d = 0; d < 2; ++d)
+                            P[q][d] = pack_bf16x2(c[4 * q + 2 * d] * alpha, c[4 * q + 2 * d + 1] * alpha);
+                    // -> lane (lr, lh): P[0..1] columns 8 lh + (0..7), P[2..3] 16 + 8 lh + (0..7)
+#pragma unroll
+                    for (int d = 0; d < 2; ++d) {
+                        swap32(P[0][d], P[1][d]);
+                        swap32(P[2][d], P[3][d]);
+                    }
+                    // -> first group: row rr, columns 16 rh + 8 lh + (0..7); second: row 16 + rr
+#pragma unroll
+                    for (int d = 0; d < 2; ++d) {
+                        swap16(P[0][d], P[2][d]);
+                        swap16(P[1][d], P[3][d]);
+                    }
+                    const int32_t col = col0 + i * 32 + 16 * rh + 8 * elh;
+                    put(r0, col, P[0][0], P[0][1], P[1][0], P[1][1]);
+                    put(r0 + 16, col, P[2][0], P[2][1], P[3][0], P[3][1]);
+                } else {
+                    // Y[q]: columns 8 q + 4 lh + (0..3)
+                    uint32_t Y[4][4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) Y[q][e] = __float_as_uint(c[4 * q + e] * alpha);
+                    // -> Y[2h]: row rr, columns 16 h + 8 rh + 4 lh + (0..3); Y[2h+1]: row 16 + rr
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        swap16(Y[0][e], Y[1][e]);
+                        swap16(Y[2][e], Y[3][e]);
+                    }
+                    const int32_t col = col0 + i * 32 + 8 * rh + 4 * elh;
+                    put(r0, col, Y[0][0], Y[0][1], Y[0][2], Y[0][3]);
+                    put(r0 + 16, col, Y[1][0], Y[1][1], Y[1][2], Y[1][3]);
+                    put(r0, col + 16, Y[2][0], Y[2][1], Y[2][2], Y[2][3]);
+                    put(r0 + 16, col + 16, Y[3][0], Y[3][1], Y[3][2], Y[3][3]);
+                }
             }
         }
-        __builtin_amdgcn_s_waitcnt(0xC07F);            // lgkmcnt(0): the slab is in LDS
-        __builtin_amdgcn_wave_barrier();
-        const int64_t row_base = m_begin + wm * WM + jj * 32;
+    };
+
+    // ---------------- tile loop ----------------
+    // The LDS ring runs on across tiles: at the barriers of the last two
+    // stages of a tile (K stage count >= 2) the first two stages of the next
+    // tile are issued, exactly as a tile's own stage kt+2 is issued at stage
+    // kt's barrier, and the last K-quarter's reads already fetch the next
+    // tile's first fragments.  The epilogue then overlaps those loads, and the
+    // next tile starts its MFMAs without a prologue.
+    Tile cur, nxt;
+    int32_t arow[NJ], narow[NJ];
+    int32_t round = 0;
+    if (!find_tile(round, cur)) return;
+    load_rows(cur, arow);
+    Frag f0;
+    Scl sc;
+    SclRaw nsc;
+    int par = 0;            // LDS buffer of the current tile's stage 0
+    bool primed = false;    // its first two stages are issued and f0 / sc hold its first K-quarter
+    for (;;) {
+        // (every wave decodes the same tiles: the flags are uniform)
+        int32_t nround = round + 1;
+        const bool has_next = __builtin_amdgcn_readfirstlane((int)find_tile(nround, nxt)) != 0;
+        if (has_next) load_rows(nxt, narow);
+        const bool chain = __builtin_amdgcn_readfirstlane((int)(has_next && cur.nkt >= 2 && nxt.nkt >= 1)) != 0;
 #pragma unroll
-        for (int k = 0; k < 32 * SEGS / 64; ++k) {
-            const int sidx = lane + 64 * k;
-            const int r = sidx / SEGS, sg = sidx % SEGS;
-            const uint4 v = *(const uint4*)(stage_c + r * PITCH + sg * 16);
-            const int64_t col = col0 + sg * (16 / EB);
-            if (wm * WM + jj * 32 + r < rows_here && col < p.N)
-                *(uint4*)(cbase + ((row_base + r) * p.N + col) * EB) = v;
+        for (int i = 0; i < FN; ++i)
+#pragma unroll
+            for (int jj = 0; jj < FM; ++jj)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) acc[i][jj][e] = 0.0f;
+        if (cur.nkt > 0) {
+            if (!primed) {
+                // the previous tile's clamped past-the-end stage may still be
+                // landing in the ring
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                issue(cur, arow, 0, par);
+                issue(cur, arow, 1, par ^ 1);
+                wait_all_but_one_stage();
+                __builtin_amdgcn_s_barrier();
+                read_frag(f0, par, 0);
+                read_scl(nsc, par);
+                pack(sc, nsc);
+            }
+            // Stage kt+1's DMA was issued at stage kt-1's barrier, into the
+            // buffer stage kt-1 had finished reading; at stage kt's barrier it
+            // is the only DMA outstanding, so vmcnt(0) means it has landed.
+            // At a chained tile's first barrier the previous tile's
+            // EPI_STORES stores are the newest memory operations (without a
+            // row gather nothing is loaded after them) and may stay in flight.
+            auto stage = [&](int kt, auto first_c) {
+                constexpr bool FIRST = decltype(first_c)::value;
+                const int buf = (kt & 1) ^ par;
+                const int kcl = kt * 8 + lh;              // this lane's chunk in K-quarter 0
+                mma_rd(f0, sc, 0, kcl > cur.kc_last, buf, 1);
+                mma_rd(f0, sc, 1, kcl + 2 > cur.kc_last, buf, 2);
+                mma_rd(f0, sc, 2, kcl + 4 > cur.kc_last, buf, 3);
+                if (FIRST) {
+                    if (OUT_BF16) asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)" ::: "memory");
+                    else asm volatile("s_waitcnt vmcnt(32) lgkmcnt(0)" ::: "memory");
+                } else {
+                    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+                }
+                __builtin_amdgcn_s_barrier();
+                // Stage kt+2 of this tile, or at the last two stages the next
+                // tile's stage 0 / 1 (chained), or else a clamped repeat of the
+                // last stage that nothing reads.  Selected, not branched: a
+                // branch here splits the loop body and the registers spill.
+                const bool to_next = chain && kt + 2 >= cur.nkt;
+                Tile t2;
+                t2.n0 = to_next ? nxt.n0 : cur.n0;
+                t2.g = to_next ? nxt.g : cur.g;
+                t2.kc0 = to_next ? nxt.kc0 : cur.kc0;
+                t2.kc_last = to_next ? nxt.kc_last : cur.kc_last;
+                // The row select is pinned here, after the barrier's wait:
+                // gathered row indices are ordinary loads, and the
+                // compiler's wait for them lands before their first use.
+                const uint64_t sel = __builtin_amdgcn_readfirstlane((int)to_next) ? ~0ull : 0ull;
+                int32_t r2[NJ];
+#pragma unroll
+                for (int jj = 0; jj < NJ; ++jj)
+                    asm volatile("v_cndmask_b32_e64 %0, %1, %2, %3"
+                                 : "=v"(r2[jj]) : "v"(arow[jj]), "v"(narow[jj]), "s"(sel));
+                issue(t2, r2, to_next ? kt + 2 - cur.nkt : kt + 2, buf);
+                read_scl(nsc, buf ^ 1);
+                mma_rd(f0, sc, 3, kcl + 6 > cur.kc_last, buf ^ 1, 0);
+                pack(sc, nsc);
+            };
+            // At a chained tile's first barrier the previous tile's
+            // EPI_STORES stores are the newest memory operations (without a
+            // row gather nothing is loaded after them) and may stay in flight.
+            int kt0 = 0;
+            if (!GATHER && primed) {
+                stage(0, std::true_type{});
+                kt0 = 1;
+            }
+            for (int kt = kt0; kt < cur.nkt; ++kt) stage(kt, std::false_type{});
         }
-        __builtin_amdgcn_s_waitcnt(0xC07F);            // reads done before the slab is reused
-        __builtin_amdgcn_wave_barrier();
+        static_assert(EPI_STORES == (OUT_BF16 ? 16 : 32), "first-barrier wait counts");
+        epilogue(cur);
+        if (!has_next) break;
+        // unchained: the reads after the last barrier only fetched values
+        // that are never used, so the next tile's prologue may refill both
+        // buffers once the clamped stage still in flight has landed
+        primed = chain;
+        par = chain ? par ^ (cur.nkt & 1) : 0;
+        cur = nxt;
+#pragma unroll
+        for (int jj = 0; jj < NJ; ++jj) arow[jj] = narow[jj];
+        round = nround;
     }
 }
 
@@ -455,11 +644,14 @@ extern "C" mx_status mx_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_sc
     if (M == 0) return MX_OK;
     if (!a_codes || !a_scales || !b_codes || !b_scales || !c) return MX_ERR_NULL;
     if (!aligned16(a_codes) || !aligned16(b_codes) || !aligned16(c)) return MX_ERR_ALIGN;
-    // operand rows are addressed by 32-bit byte offsets: each B group and the
-    // A rows (wherever a row index can point) must lie within 4 GiB
-    if (group_dim_k == 0 && N * (K / 2) > 0xFFFFFFFFLL) return MX_ERR_SHAPE;
-    if (group_dim_k == 1 && (M > 0 && (M - 1) * (K / 2) > 0xFFFFFFFFLL || (N - 1) * (K / 2) > 0xFFFFFFFFLL))
-        return MX_ERR_SHAPE;
+    // operand bytes are addressed by 32-bit offsets from the operand's (or
+    // the B group's) base: each must span at most 4 GiB.  With a row index
+    // the caller keeps the indexed rows within that range.
+    const int64_t lim = 0xFFFFFFFFLL;
+    if (N * (K / 2) > lim) return MX_ERR_SHAPE;
+    if (!a_row_index && M * (K / 2) > lim) return MX_ERR_SHAPE;
+    // tile coordinates are 32-bit
+    if (M > 0x7FFFFF00LL || N > 0x7FFFFF00LL || K > 0x7FFFFF00LL) return MX_ERR_SHAPE;
 
     GemmArgs p;
     p.a_codes = a_codes;
@@ -486,14 +678,36 @@ extern "C" mx_status mx_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_sc
     // the XCD remap is a bijection on multiples of XCDS * XCD_BLOCK
     const int64_t quantum = XCDS * XCD_BLOCK;
     tiles = (tiles + quantum - 1) / quantum * quantum;
-    if (tiles > 0x7FFFFFFF) return MX_ERR_SHAPE;
+    if (tiles > 0x7FFF0000) return MX_ERR_SHAPE;
+    p.tiles = tiles;
+    // persistent: one workgroup per CU (the ring takes all of its LDS)
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
+    }
+    const unsigned grid = (unsigned)min(tiles, (int64_t)cus);
     hipStream_t s = (hipStream_t)stream;
     (void)hipGetLastError();
-    if (ct == MX_BF16)
-        if (b_scale_2d) hipLaunchKernelGGL((gemm_kernel<true, true>), dim3((unsigned)tiles), dim3(NT), 0, s, p);
-        else hipLaunchKernelGGL((gemm_kernel<true, false>), dim3((unsigned)tiles), dim3(NT), 0, s, p);
-    else
-        if (b_scale_2d) hipLaunchKernelGGL((gemm_kernel<false, true>), dim3((unsigned)tiles), dim3(NT), 0, s, p);
-        else hipLaunchKernelGGL((gemm_kernel<false, false>), dim3((unsigned)tiles), dim3(NT), 0, s, p);
+    const dim3 gd(grid), bd(NT);
+    const bool gather = a_row_index != nullptr;
+    if (group_dim_k == 1) {
+        if (ct == MX_BF16) hipLaunchKernelGGL((gemm_kernel<true, false, true, false>), gd, bd, 0, s, p);
+        else hipLaunchKernelGGL((gemm_kernel<false, false, true, false>), gd, bd, 0, s, p);
+    } else if (gather) {
+        if (ct == MX_BF16) {
+            if (b_scale_2d) hipLaunchKernelGGL((gemm_kernel<true, true, false, true>), gd, bd, 0, s, p);
+            else hipLaunchKernelGGL((gemm_kernel<true, false, false, true>), gd, bd, 0, s, p);
+        } else {
+            if (b_scale_2d) hipLaunchKernelGGL((gemm_kernel<false, true, false, true>), gd, bd, 0, s, p);
+            else hipLaunchKernelGGL((gemm_kernel<false, false, false, true>), gd, bd, 0, s, p);
+        }
+    } else if (ct == MX_BF16) {
+        if (b_scale_2d) hipLaunchKernelGGL((gemm_kernel<true, true, false, false>), gd, bd, 0, s, p);
+        else hipLaunchKernelGGL((gemm_kernel<true, false, false, false>), gd, bd, 0, s, p);
+    } else {
+        if (b_scale_2d) hipLaunchKernelGGL((gemm_kernel<false, true, false, false>), gd, bd, 0, s, p);
+        else hipLaunchKernelGGL((gemm_kernel<false, false, false, false>), gd, bd, 0, s, p);
+    }
     return hipGetLastError() == hipSuccess ? MX_OK : MX_ERR_LAUNCH;
 }
