@@ -96,13 +96,14 @@ constexpr int GROUP_M = 4;         // M-tiles per tile-order group
 constexpr int XCDS = 8;
 constexpr int XCD_BLOCK = 32;      // consecutive tile ids per XCD turn
 // one stage in LDS: A codes, B codes (256 rows x 128 bytes each), A and B
-// scales (256 rows x 8 dwords each)
+// scales (256 rows x 8 dwords each; A scales moved in pairs take 4 dwords)
 constexpr int OFF_A = 0, OFF_B = 32768, OFF_AS = 65536, OFF_BS = 73728;
 constexpr int STAGE_BYTES = 81920;
-// DMA ops per thread per stage: 16 code moves, 8 A-scale moves, and 8 B-scale
+// DMA ops per thread per stage: 8 code moves (4 rows of each operand), 4
+// A-scale moves (one byte each) or 2 (SA2: two bytes each), and 4 B-scale
 // moves (1D B scales) or 1 (2D B scales: 8 row groups of 32 per tile).
-template <bool B2D>
-constexpr int dma_per_stage() { return B2D ? 13 : 16; }
+template <bool B2D, bool SA2>
+constexpr int dma_per_stage() { return 8 + (SA2 ? 2 : 4) + (B2D ? 1 : 4); }
 
 // 16-byte chunk swizzle of a 128-byte row: the rows an MFMA operand read
 // touches at one chunk index land in distinct 16-byte bank groups whether
@@ -119,6 +120,10 @@ __device__ __forceinline__ int sperm(int p) { return p < 4 ? 2 * p : 2 * (p - 4)
 // awaited with an explicit s_waitcnt vmcnt.
 __device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :: "v"(voff), "s"(base), "s"(lds) : "memory");
+}
+__device__ __forceinline__ void dma2(const void* base, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_ushort %0, %1"
                  :: "v"(voff), "s"(base), "s"(lds) : "memory");
 }
 __device__ __forceinline__ void dma1(const void* base, uint32_t voff, uint32_t lds) {
@@ -138,9 +143,13 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
 }
 
-template <bool OUT_BF16, bool B2D, bool GK, bool GATHER>
+// SA2: the A scales of a stage move two bytes per lane (global_load_lds_ushort),
+// half the DMA instructions of one byte per lane.  It needs every pair of
+// scale bytes 2-byte aligned: an even K / 32, an even scale pointer, and a K
+// range starting at 0 (groups split M).
+template <bool OUT_BF16, bool B2D, bool GK, bool GATHER, bool SA2>
 __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
-    static_assert(!(GK && (B2D || GATHER)), "groups along K take 1D B scales and no row index");
+    static_assert(!(GK && (B2D || GATHER || SA2)), "groups along K take 1D scales and no row index");
     // 2 x 4 waves of 128 x 64
     constexpr int WM = 128, WN = 64, FM = 4, FN = WN / 32;
     constexpr int NJ = 2048 / NT;               // code (and scale) moves per operand per thread
@@ -316,9 +325,20 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
             dma16(p.a_codes, mrow[jj] * (uint32_t)KB + kc * 16, sb + OFF_A + jj * NT * 16 + wave * 1024);
             dma16(bcodes, nrow[jj] * (uint32_t)KB + kc * 16, sb + OFF_B + jj * NT * 16 + wave * 1024);
         }
+        if (SA2) {
+            // move j: lanes with pc < 4 take scale pair pc of row slot 2 j,
+            // lanes with pc >= 4 pair pc - 4 of slot 2 j + 1 (the rows of
+            // this thread's code moves); the last pair is K / 32 - 2
+            const int half = pc >> 2;
+            const uint32_t kp = (uint32_t)(t.kc0 + min(kt * 8 + 2 * (pc & 3), t.kc_last - 1));
+#pragma unroll
+            for (int j = 0; j < NJ / 2; ++j)
+                dma2(p.a_scales, (half ? mrow[2 * j + 1] : mrow[2 * j]) * (uint32_t)KS + kp,
+                     sb + OFF_AS + (j * NW + wave) * 256);
+        }
 #pragma unroll
         for (int jj = 0; jj < NJ; ++jj) {
-            dma1(p.a_scales, mrow[jj] * (uint32_t)KS + ks, sb + OFF_AS + jj * NT * 4 + wave * 256);
+            if (!SA2) dma1(p.a_scales, mrow[jj] * (uint32_t)KS + ks, sb + OFF_AS + jj * NT * 4 + wave * 256);
             if (!B2D) dma1(bscales, nrow[jj] * (uint32_t)KS + ks, sb + OFF_BS + jj * NT * 4 + wave * 256);
         }
         if (B2D) {
@@ -367,22 +387,37 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
                          : *(const uint4*)(sb + OFF_BS + (wn * WN + i * 32 + lr) * 32 + lh * 16);
 #pragma unroll
         for (int i = 0; i < FM; ++i)
-            s.a[i] = *(const uint4*)(sb + OFF_AS + (wm * WM + i * 32 + lr) * 32 + lh * 16);
+            // SA2: row r = wm WM + 32 i + lr was moved by wave (r % 64) / 8,
+            // lane 8 (r % 8) + 4 ((r / 64) % 2) of move (r / 64) / 2 = wm:
+            // its four pair dwords are consecutive
+            s.a[i] = SA2 ? *(const uint4*)(sb + OFF_AS + (wm * NW + (i & 1) * 4 + (lr >> 3)) * 256 + (lr & 7) * 32 +
+                                           (i >> 1) * 16)
+                         : *(const uint4*)(sb + OFF_AS + (wm * WM + i * 32 + lr) * 32 + lh * 16);
     };
-    auto pack = [](Scl& s, const SclRaw& r) {
+    // SA2: dword q holds chunks 2 q (byte 0) and 2 q + 1 (byte 1); lane half
+    // lh takes byte lh of each (v_perm: selectors 0-3 pick the second
+    // operand's bytes, 4-7 the first's, 12 gives zero)
+    const uint32_t sa2_sel = (uint32_t)lh | ((4u + lh) << 8) | 0x0C0C0000u;
+    auto pack = [&](Scl& s, const SclRaw& r) {
         auto pack4 = [](const uint4& v) { return v.x | (v.y << 8) | (v.z << 16) | (v.w << 24); };
 #pragma unroll
         for (int i = 0; i < FN; ++i) s.b[i] = pack4(r.b[i]);
 #pragma unroll
-        for (int i = 0; i < FM; ++i) s.a[i] = pack4(r.a[i]);
+        for (int i = 0; i < FM; ++i)
+            s.a[i] = SA2 ? __builtin_amdgcn_perm(r.a[i].y, r.a[i].x, sa2_sel) |
+                               (__builtin_amdgcn_perm(r.a[i].w, r.a[i].z, sa2_sel) << 16)
+                         : pack4(r.a[i]);
     };
 
     // "every DMA but the newest stage's has landed"
     auto wait_all_but_one_stage = [] {
-        if (B2D) asm volatile("s_waitcnt vmcnt(13)" ::: "memory");
+        if (B2D && SA2) asm volatile("s_waitcnt vmcnt(11)" ::: "memory");
+        else if (B2D) asm volatile("s_waitcnt vmcnt(13)" ::: "memory");
+        else if (SA2) asm volatile("s_waitcnt vmcnt(14)" ::: "memory");
         else asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
     };
-    static_assert(dma_per_stage<true>() == 13 && dma_per_stage<false>() == 16, "wait counts");
+    static_assert(dma_per_stage<true, true>() == 11 && dma_per_stage<true, false>() == 13 &&
+                  dma_per_stage<false, true>() == 14 && dma_per_stage<false, false>() == 16, "wait counts");
     // one MFMA block, optionally followed by one piece of the next read
     auto mma1 = [&](const Frag& f, const Scl& s, int q, bool tail, int m) {
         const int i = m / FM, jj = m % FM;
@@ -691,23 +726,24 @@ extern "C" mx_status mx_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_sc
     (void)hipGetLastError();
     const dim3 gd(grid), bd(NT);
     const bool gather = a_row_index != nullptr;
+    const bool sa2 = group_dim_k == 0 && (K / 32) % 2 == 0 && ((uintptr_t)a_scales & 1) == 0;
+#define MX_GEMM_LAUNCH(BF, B2, GA, S2) hipLaunchKernelGGL((gemm_kernel<BF, B2, false, GA, S2>), gd, bd, 0, s, p)
+#define MX_GEMM_M(BF, B2, GA) \
+    do { if (sa2) MX_GEMM_LAUNCH(BF, B2, GA, true); else MX_GEMM_LAUNCH(BF, B2, GA, false); } while (0)
+#define MX_GEMM_G(BF, B2) \
+    do { if (gather) MX_GEMM_M(BF, B2, true); else MX_GEMM_M(BF, B2, false); } while (0)
     if (group_dim_k == 1) {
-        if (ct == MX_BF16) hipLaunchKernelGGL((gemm_kernel<true, false, true, false>), gd, bd, 0, s, p);
-        else hipLaunchKernelGGL((gemm_kernel<false, false, true, false>), gd, bd, 0, s, p);
-    } else if (gather) {
-        if (ct == MX_BF16) {
-            if (b_scale_2d) hipLaunchKernelGGL((gemm_kernel<true, true, false, true>), gd, bd, 0, s, p);
-            else hipLaunchKernelGGL((gemm_kernel<true, false, false, true>), gd, bd, 0, s, p);
-        } else {
-            if (b_scale_2d) hipLaunchKernelGGL((gemm_kernel<false, true, false, true>), gd, bd, 0, s, p);
-            else hipLaunchKernelGGL((gemm_kernel<false, false, false, true>), gd, bd, 0, s, p);
-        }
+        if (ct == MX_BF16) hipLaunchKernelGGL((gemm_kernel<true, false, true, false, false>), gd, bd, 0, s, p);
+        else hipLaunchKernelGGL((gemm_kernel<false, false, true, false, false>), gd, bd, 0, s, p);
     } else if (ct == MX_BF16) {
-        if (b_scale_2d) hipLaunchKernelGGL((gemm_kernel<true, true, false, false>), gd, bd, 0, s, p);
-        else hipLaunchKernelGGL((gemm_kernel<true, false, false, false>), gd, bd, 0, s, p);
+        if (b_scale_2d) MX_GEMM_G(true, true);
+        else MX_GEMM_G(true, false);
     } else {
-        if (b_scale_2d) hipLaunchKernelGGL((gemm_kernel<false, true, false, false>), gd, bd, 0, s, p);
-        else hipLaunchKernelGGL((gemm_kernel<false, false, false, false>), gd, bd, 0, s, p);
+        if (b_scale_2d) MX_GEMM_G(false, true);
+        else MX_GEMM_G(false, false);
     }
+#undef MX_GEMM_G
+#undef MX_GEMM_M
+#undef MX_GEMM_LAUNCH
     return hipGetLastError() == hipSuccess ? MX_OK : MX_ERR_LAUNCH;
 }
