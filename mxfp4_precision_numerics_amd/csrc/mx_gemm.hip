@@ -342,9 +342,11 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
             if (!B2D) dma1(bscales, nrow[jj] * (uint32_t)KS + ks, sb + OFF_BS + jj * NT * 4 + wave * 256);
         }
         if (B2D) {
-            // lane l of every wave fetches row group l / 8 of the tile at
-            // scale position l % 8, into its wave's own 256-byte copy
-            int32_t grp = t.n0 / 32 + (lane >> 3);
+            // wave w fetches row group w of the tile (8 groups of 32 rows):
+            // lane l takes scale position l % 8, so the 8 copies of the same
+            // 8 bytes coalesce into one line request (one group per wave
+            // instead of all 8 in every wave: 8x fewer requests)
+            int32_t grp = t.n0 / 32 + wave;
             if (grp > N32 / 32 - 1) grp = N32 / 32 - 1;    // groups past N are never stored
             dma1(bscales, (uint32_t)grp * (uint32_t)KS + ks, sb + OFF_BS + wave * 256);
         }
@@ -383,7 +385,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
         const uint8_t* sb = lds + buf * STAGE_BYTES;
 #pragma unroll
         for (int i = 0; i < FN; ++i)
-            s.b[i] = B2D ? *(const uint4*)(sb + OFF_BS + wave * 256 + (wn * FN + i) * 32 + lh * 16)
+            s.b[i] = B2D ? *(const uint4*)(sb + OFF_BS + (wn * FN + i) * 256 + lh * 16)
                          : *(const uint4*)(sb + OFF_BS + (wn * WN + i * 32 + lr) * 32 + lh * 16);
 #pragma unroll
         for (int i = 0; i < FM; ++i)
