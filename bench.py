@@ -187,6 +187,37 @@ def measured_traffic(role):
     return {"read_bytes": rd, "write_bytes": wr, "bytes": rd + wr}
 
 
+def fused_epilogue(torch, step, reps=5):
+    """The quantizing epilogue on the second expert linear's forward GEMM
+    (65536 x 2880 x 2880): its bf16 output quantized row-wise (1x32, RTNE) as
+    the next MXFP4 GEMM's operand.  Times the GEMM followed by the 1D
+    quantizer against the fused call, with and without the bf16 output.
+    Measured after the timed steps, on the step's own buffers."""
+    mx, b, i = step.mx, step.b, step.inp
+    args = (b["hc"], b["hs"], b["w2tc"], b["w2ts"], i["off"], ROWS, D, D)
+    runs = {
+        "gemm_then_quantize_ms": lambda: (mx.grouped_gemm(*args, b_scale_2d=True, out=b["Y2"]),
+                                          mx.quantize_1d(b["Y2"], codes=b["g2c"], scales=b["g2s"])),
+        "fused_ms": lambda: mx.grouped_gemm_q(*args, b_scale_2d=True, out=b["Y2"], codes=b["g2c"],
+                                              scales=b["g2s"]),
+        "fused_mxfp4_only_ms": lambda: mx.grouped_gemm_q(*args, b_scale_2d=True, with_bf16=False,
+                                                         codes=b["g2c"], scales=b["g2s"]),
+    }
+    res = {"shape": "%dx%dx%d" % (ROWS, D, D)}
+    for name, fn in runs.items():
+        for _ in range(2):
+            fn()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        s.record()
+        for _ in range(reps):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        res[name] = s.elapsed_time(e) / reps
+    return res
+
+
 def cpu_baseline(gemm_seconds=8.0):
     """The oracle, untuned, on a bounded sample of the same step; its rate per
     role is extrapolated to the full step.  The quantizers run on fixed
@@ -350,6 +381,7 @@ def main():
         "gemm_frac_fp4": total_flops / (gemm_ms / 1e3) / 1e12 / PEAK_FP4_TFLOPS,
         "kernels": kernels,
         "roofline": roof,
+        "fused_epilogue": fused_epilogue(torch, step),
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()

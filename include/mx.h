@@ -173,6 +173,27 @@ mx_status mx_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
                           int64_t M, int64_t N, int64_t K, float alpha,
                           void* c, mx_dtype ct, mx_stream stream);
 
+/* mx_grouped_gemm with groups splitting M (group_dim_k = 0) and the output
+ * also emitted as the next layer's MXFP4 operand: with y = RNE_bf16(alpha *
+ * A . B^T) per row, c_codes [M x N/2] and c_scales [M x N/32] are the
+ * row-wise 1x32 quantization of y along N, round to nearest even, bit for
+ * bit what mx_quantize_1d(y, MX_BF16, M, N, block_axis = 1, use_rht = 0,
+ * MX_RNE) writes.  The quantizer is fused into the GEMM's epilogue, so y
+ * need not make a round trip through memory: the expert layers dominate
+ * memory traffic as well as compute ("What ALTO Actually Does", news digest
+ * "AMD's ALTO Gets 4-Bit MoE Training to Within 0.007 of BF16").
+ * c: bf16 [M x N] as in mx_grouped_gemm, or NULL to write only the MXFP4
+ * output.  c (when given) and c_codes 16-byte aligned; c_scales any.
+ * Arguments and errors otherwise as mx_grouped_gemm; additionally
+ * MX_ERR_NULL (c_codes or c_scales NULL) and MX_ERR_SHAPE (M * N / 2 above
+ * 4 GiB - 1). */
+mx_status mx_grouped_gemm_q(const uint8_t* a_codes, const uint8_t* a_scales,
+                            const int32_t* a_row_index,
+                            const uint8_t* b_codes, const uint8_t* b_scales, int b_scale_2d,
+                            const int32_t* group_offsets, int32_t num_groups,
+                            int64_t M, int64_t N, int64_t K, float alpha,
+                            void* c, uint8_t* c_codes, uint8_t* c_scales, mx_stream stream);
+
 #ifdef __cplusplus
 }
 #endif

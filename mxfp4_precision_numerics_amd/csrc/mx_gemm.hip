@@ -85,6 +85,8 @@ struct GemmArgs {
     int32_t tiles_m;     // group_dim_k = 1: tiles along M per group
     float alpha;
     int64_t tiles;       // size of the tile-id space (a multiple of XCDS * XCD_BLOCK)
+    uint8_t* qcodes;     // QOUT: row-wise MXFP4 of the bf16 output, codes [M x N/2]
+    uint8_t* qscales;    //       and scales [M x N/32]
 };
 
 constexpr int BM = 256, BN = 256;
@@ -147,9 +149,12 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 // half the DMA instructions of one byte per lane.  It needs every pair of
 // scale bytes 2-byte aligned: an even K / 32, an even scale pointer, and a K
 // range starting at 0 (groups split M).
-template <bool OUT_BF16, bool B2D, bool GK, bool GATHER, bool SA2>
+// QOUT: the epilogue also quantizes the bf16 output row-wise (1x32 blocks
+// along N, round to nearest even), as the 1D quantizer would.
+template <bool OUT_BF16, bool B2D, bool GK, bool GATHER, bool SA2, bool QOUT>
 __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
     static_assert(!(GK && (B2D || GATHER || SA2)), "groups along K take 1D scales and no row index");
+    static_assert(!QOUT || (OUT_BF16 && !GK), "the quantized output is the bf16 output of groups along M");
     // 2 x 4 waves of 128 x 64
     constexpr int WM = 128, WN = 64, FM = 4, FN = WN / 32;
     constexpr int NJ = 2048 / NT;               // code (and scale) moves per operand per thread
@@ -477,14 +482,26 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
     // a row or column outside C is dropped by the hardware range check
     // instead of a branch: every wave issues exactly EPI_STORES stores, which
     // lets the next tile's first barrier wait for its own loads only.
-    constexpr int EPI_STORES = OUT_BF16 ? FN * FM * 2 : FN * FM * 4;
+    // (QOUT adds one 8-byte code store and one scale-byte store per block)
+    constexpr int EPI_STORES = OUT_BF16 ? FN * FM * (QOUT ? 4 : 2) : FN * FM * 4;
     auto epilogue = [&](const Tile& t) {
         constexpr int EB = OUT_BF16 ? 2 : 4;
         // (base and size are uniform: kept in scalar registers, the resource
         // needs no per-lane loop)
         uint8_t* cb = (uint8_t*)p.c + uniform64(((GK ? (int64_t)t.g * p.M : 0) + t.m0) * p.N * EB);
-        const int32_t nrec = __builtin_amdgcn_readfirstlane((t.m1 - t.m0) * N32 * EB);
+        // (QOUT may leave C out: a resource of size 0 drops every store)
+        const int32_t nrec = __builtin_amdgcn_readfirstlane(QOUT && !p.c ? 0 : (t.m1 - t.m0) * N32 * EB);
         const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(cb, (short)0, nrec, 0x00020000);
+        // QOUT: the tile's rows of the code and scale outputs
+        __amdgpu_buffer_rsrc_t qc_rsrc = rsrc, qs_rsrc = rsrc;
+        if (QOUT) {
+            uint8_t* qc = p.qcodes + uniform64((int64_t)t.m0 * (p.N / 2));
+            uint8_t* qs = p.qscales + uniform64((int64_t)t.m0 * (p.N / 32));
+            qc_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+                qc, (short)0, __builtin_amdgcn_readfirstlane((t.m1 - t.m0) * (N32 / 2)), 0x00020000);
+            qs_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+                qs, (short)0, __builtin_amdgcn_readfirstlane((t.m1 - t.m0) * (N32 / 32)), 0x00020000);
+        }
         const float alpha = p.alpha;
         const int32_t col0 = t.n0 + wn * WN;            // first output column of this wave
         // the lane's coordinates pass through an empty asm so that the store
@@ -515,6 +532,44 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
 #pragma unroll
                         for (int d = 0; d < 2; ++d)
                             P[q][d] = pack_bf16x2(c[4 * q + 2 * d] * alpha, c[4 * q + 2 * d + 1] * alpha);
+                    if (QOUT) {
+                        // The block of 32 columns of row lr is split over lanes
+                        // lr and lr + 32 (16 values each: columns 8 q + 4 lh + e).
+                        float w[16];
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            w[4 * q + 0] = bf16lo(P[q][0]);
+                            w[4 * q + 1] = bf16hi(P[q][0]);
+                            w[4 * q + 2] = bf16lo(P[q][1]);
+                            w[4 * q + 3] = bf16hi(P[q][1]);
+                        }
+                        uint32_t m = 0;
+#pragma unroll
+                        for (int e = 0; e < 16; ++e) m = max(m, __float_as_uint(w[e]) & 0x7FFFFFFFu);
+                        const auto pm = __builtin_amdgcn_permlane32_swap(m, m, false, false);
+                        m = max(pm[0], pm[1]);                      // own and partner half
+                        const uint32_t byte = scale_byte_from_amax_bits(m);
+                        const float scl = scale_operand(byte);
+                        // d0: columns 4 lh + (0..3), 8 + 4 lh + (0..3); d1: the same + 16
+                        uint32_t d0 = cvt8_rne(w, scl), d1 = cvt8_rne(w + 8, scl);
+                        if (byte == 0xFFu) d0 = d1 = 0;             // non-finite block: codes 0
+                        // lane lh = 0 holds block bytes (0 1 4 5 | 8 9 12 13), lh = 1
+                        // (2 3 6 7 | 10 11 14 15): after the swap lh = 0 has bytes
+                        // 0-7 and lh = 1 bytes 8-15 in (own, partner) pieces
+                        swap32(d0, d1);
+                        const uint32_t o0 = __builtin_amdgcn_perm(d1, d0, 0x05040100u);
+                        const uint32_t o1 = __builtin_amdgcn_perm(d1, d0, 0x07060302u);
+                        const int32_t qrow = wm * WM + jj * 32 + elr;
+                        const int32_t qcol = col0 + i * 32;
+                        const bool ok = qrow < nrows && qcol < N32;
+                        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+                        __builtin_amdgcn_raw_buffer_store_b64(
+                            (u32x2){o0, o1}, qc_rsrc,
+                            ok ? (uint32_t)(qrow * (N32 / 2) + qcol / 2 + 8 * elh) : 0x80000000u, 0, 0);
+                        __builtin_amdgcn_raw_buffer_store_b8(
+                            (uint8_t)byte, qs_rsrc,
+                            ok && elh == 0 ? (uint32_t)(qrow * (N32 / 32) + qcol / 32) : 0x80000000u, 0, 0);
+                    }
                     // -> lane (lr, lh): P[0..1] columns 8 lh + (0..7), P[2..3] 16 + 8 lh + (0..7)
 #pragma unroll
                     for (int d = 0; d < 2; ++d) {
@@ -609,7 +664,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
                 mma_rd(f0, sc, 1, kcl + 2 > cur.kc_last, buf, 2);
                 mma_rd(f0, sc, 2, kcl + 4 > cur.kc_last, buf, 3);
                 if (FIRST) {
-                    if (OUT_BF16) asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)" ::: "memory");
+                    if (EPI_STORES == 16) asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)" ::: "memory");
                     else asm volatile("s_waitcnt vmcnt(32) lgkmcnt(0)" ::: "memory");
                 } else {
                     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
@@ -649,7 +704,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
             }
             for (int kt = kt0; kt < cur.nkt; ++kt) stage(kt, std::false_type{});
         }
-        static_assert(EPI_STORES == (OUT_BF16 ? 16 : 32), "first-barrier wait counts");
+        static_assert(EPI_STORES == 16 || EPI_STORES == 32, "first-barrier wait counts");
         epilogue(cur);
         if (!has_next) break;
         // unchained: the reads after the last barrier only fetched values
@@ -666,21 +721,19 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
 
 inline bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 
-}  // namespace
-
-extern "C" mx_status mx_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const int32_t* a_row_index,
-                                     const uint8_t* b_codes, const uint8_t* b_scales, int b_scale_2d,
-                                     const int32_t* group_offsets, int32_t num_groups, int group_dim_k, int64_t M,
-                                     int64_t N, int64_t K, float alpha, void* c, mx_dtype ct, mx_stream stream) {
-    if (ct != MX_F32 && ct != MX_BF16) return MX_ERR_DTYPE;
+// Validation shared by both entry points; fills everything but the outputs.
+mx_status gemm_setup(const uint8_t* a_codes, const uint8_t* a_scales, const int32_t* a_row_index,
+                            const uint8_t* b_codes, const uint8_t* b_scales, int b_scale_2d,
+                            const int32_t* group_offsets, int32_t num_groups, int group_dim_k, int64_t M,
+                            int64_t N, int64_t K, float alpha, GemmArgs& p, unsigned& grid) {
     if (M < 0 || N <= 0 || K <= 0 || N % 32 || K % 32) return MX_ERR_SHAPE;
     if (num_groups < 1) return MX_ERR_SHAPE;
     if (group_dim_k != 0 && group_dim_k != 1) return MX_ERR_SHAPE;
     if (group_dim_k == 1 && (b_scale_2d || a_row_index)) return MX_ERR_UNSUPPORTED;
     if (!group_offsets) return MX_ERR_NULL;
     if (M == 0) return MX_OK;
-    if (!a_codes || !a_scales || !b_codes || !b_scales || !c) return MX_ERR_NULL;
-    if (!aligned16(a_codes) || !aligned16(b_codes) || !aligned16(c)) return MX_ERR_ALIGN;
+    if (!a_codes || !a_scales || !b_codes || !b_scales) return MX_ERR_NULL;
+    if (!aligned16(a_codes) || !aligned16(b_codes)) return MX_ERR_ALIGN;
     // operand bytes are addressed by 32-bit offsets from the operand's (or
     // the B group's) base: each must span at most 4 GiB.  With a row index
     // the caller keeps the indexed rows within that range.
@@ -690,14 +743,13 @@ extern "C" mx_status mx_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_sc
     // tile coordinates are 32-bit
     if (M > 0x7FFFFF00LL || N > 0x7FFFFF00LL || K > 0x7FFFFF00LL) return MX_ERR_SHAPE;
 
-    GemmArgs p;
+    p = GemmArgs{};
     p.a_codes = a_codes;
     p.a_scales = a_scales;
     p.a_row_index = a_row_index;
     p.b_codes = b_codes;
     p.b_scales = b_scales;
     p.off = group_offsets;
-    p.c = c;
     p.M = M;
     p.N = N;
     p.K = K;
@@ -723,29 +775,77 @@ extern "C" mx_status mx_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_sc
         int v = 0;
         if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
     }
-    const unsigned grid = (unsigned)min(tiles, (int64_t)cus);
+    grid = (unsigned)min(tiles, (int64_t)cus);
+    return MX_OK;
+}
+
+// groups split M: pick the instantiation for the B scale kind, the row gather
+// and the A-scale move width
+template <bool BF, bool QOUT>
+void launch_m(const GemmArgs& p, unsigned grid, hipStream_t s) {
+    const dim3 gd(grid), bd(NT);
+    const bool gather = p.a_row_index != nullptr;
+    const bool sa2 = (p.K / 32) % 2 == 0 && ((uintptr_t)p.a_scales & 1) == 0;
+#define MX_GEMM_LAUNCH(B2, GA, S2) hipLaunchKernelGGL((gemm_kernel<BF, B2, false, GA, S2, QOUT>), gd, bd, 0, s, p)
+#define MX_GEMM_S(B2, GA) \
+    do { if (sa2) MX_GEMM_LAUNCH(B2, GA, true); else MX_GEMM_LAUNCH(B2, GA, false); } while (0)
+#define MX_GEMM_G(B2) \
+    do { if (gather) MX_GEMM_S(B2, true); else MX_GEMM_S(B2, false); } while (0)
+    if (p.b_scale_2d) MX_GEMM_G(true);
+    else MX_GEMM_G(false);
+#undef MX_GEMM_G
+#undef MX_GEMM_S
+#undef MX_GEMM_LAUNCH
+}
+
+}  // namespace
+
+extern "C" mx_status mx_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const int32_t* a_row_index,
+                                     const uint8_t* b_codes, const uint8_t* b_scales, int b_scale_2d,
+                                     const int32_t* group_offsets, int32_t num_groups, int group_dim_k, int64_t M,
+                                     int64_t N, int64_t K, float alpha, void* c, mx_dtype ct, mx_stream stream) {
+    if (ct != MX_F32 && ct != MX_BF16) return MX_ERR_DTYPE;
+    GemmArgs p;
+    unsigned grid = 0;
+    const mx_status st = gemm_setup(a_codes, a_scales, a_row_index, b_codes, b_scales, b_scale_2d, group_offsets,
+                                    num_groups, group_dim_k, M, N, K, alpha, p, grid);
+    if (st != MX_OK || M == 0) return st;
+    if (!c) return MX_ERR_NULL;
+    if (!aligned16(c)) return MX_ERR_ALIGN;
+    p.c = c;
     hipStream_t s = (hipStream_t)stream;
     (void)hipGetLastError();
-    const dim3 gd(grid), bd(NT);
-    const bool gather = a_row_index != nullptr;
-    const bool sa2 = group_dim_k == 0 && (K / 32) % 2 == 0 && ((uintptr_t)a_scales & 1) == 0;
-#define MX_GEMM_LAUNCH(BF, B2, GA, S2) hipLaunchKernelGGL((gemm_kernel<BF, B2, false, GA, S2>), gd, bd, 0, s, p)
-#define MX_GEMM_M(BF, B2, GA) \
-    do { if (sa2) MX_GEMM_LAUNCH(BF, B2, GA, true); else MX_GEMM_LAUNCH(BF, B2, GA, false); } while (0)
-#define MX_GEMM_G(BF, B2) \
-    do { if (gather) MX_GEMM_M(BF, B2, true); else MX_GEMM_M(BF, B2, false); } while (0)
     if (group_dim_k == 1) {
-        if (ct == MX_BF16) hipLaunchKernelGGL((gemm_kernel<true, false, true, false, false>), gd, bd, 0, s, p);
-        else hipLaunchKernelGGL((gemm_kernel<false, false, true, false, false>), gd, bd, 0, s, p);
+        const dim3 gd(grid), bd(NT);
+        if (ct == MX_BF16) hipLaunchKernelGGL((gemm_kernel<true, false, true, false, false, false>), gd, bd, 0, s, p);
+        else hipLaunchKernelGGL((gemm_kernel<false, false, true, false, false, false>), gd, bd, 0, s, p);
     } else if (ct == MX_BF16) {
-        if (b_scale_2d) MX_GEMM_G(true, true);
-        else MX_GEMM_G(true, false);
+        launch_m<true, false>(p, grid, s);
     } else {
-        if (b_scale_2d) MX_GEMM_G(false, true);
-        else MX_GEMM_G(false, false);
+        launch_m<false, false>(p, grid, s);
     }
-#undef MX_GEMM_G
-#undef MX_GEMM_M
-#undef MX_GEMM_LAUNCH
+    return hipGetLastError() == hipSuccess ? MX_OK : MX_ERR_LAUNCH;
+}
+
+extern "C" mx_status mx_grouped_gemm_q(const uint8_t* a_codes, const uint8_t* a_scales, const int32_t* a_row_index,
+                                       const uint8_t* b_codes, const uint8_t* b_scales, int b_scale_2d,
+                                       const int32_t* group_offsets, int32_t num_groups, int64_t M, int64_t N,
+                                       int64_t K, float alpha, void* c, uint8_t* c_codes, uint8_t* c_scales,
+                                       mx_stream stream) {
+    GemmArgs p;
+    unsigned grid = 0;
+    const mx_status st = gemm_setup(a_codes, a_scales, a_row_index, b_codes, b_scales, b_scale_2d, group_offsets,
+                                    num_groups, 0, M, N, K, alpha, p, grid);
+    if (st != MX_OK || M == 0) return st;
+    if (!c_codes || !c_scales) return MX_ERR_NULL;
+    if ((c && !aligned16(c)) || !aligned16(c_codes)) return MX_ERR_ALIGN;
+    // the code and scale outputs are addressed by 32-bit offsets per tile
+    if (M * (N / 2) > 0xFFFFFFFFLL) return MX_ERR_SHAPE;
+    p.c = c;
+    p.qcodes = c_codes;
+    p.qscales = c_scales;
+    hipStream_t s = (hipStream_t)stream;
+    (void)hipGetLastError();
+    launch_m<true, true>(p, grid, s);
     return hipGetLastError() == hipSuccess ? MX_OK : MX_ERR_LAUNCH;
 }

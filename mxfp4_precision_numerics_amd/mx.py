@@ -52,8 +52,10 @@ def lib():
         L.mx_dequantize.argtypes = [P, P, i64, i64, i64, c_int, P, c_int, P]
         L.mx_grouped_gemm.argtypes = [P, P, P, P, P, c_int, P, i32, c_int, i64, i64, i64,
                                       ctypes.c_float, P, c_int, P]
+        L.mx_grouped_gemm_q.argtypes = [P, P, P, P, P, c_int, P, i32, i64, i64, i64,
+                                        ctypes.c_float, P, P, P, P]
         for name in ("mx_rht", "mx_quantize_1d", "mx_quantize_2d", "mx_dequantize",
-                     "mx_grouped_gemm"):
+                     "mx_grouped_gemm", "mx_grouped_gemm_q"):
             getattr(L, name).restype = c_int
         _lib = L
     return _lib
@@ -220,3 +222,30 @@ def grouped_gemm(a_codes, a_scales, b_codes, b_scales, group_offsets, M, N, K,
         int(bool(b_scale_2d)), _ptr(group_offsets), G, int(bool(group_dim_k)), M, N, K,
         float(alpha), _ptr(out), _dtype_code(out), _stream()))
     return out
+
+
+def grouped_gemm_q(a_codes, a_scales, b_codes, b_scales, group_offsets, M, N, K,
+                   a_row_index=None, b_scale_2d=False, alpha=1.0, with_bf16=True,
+                   out=None, codes=None, scales=None):
+    """Grouped GEMM (groups split M) whose bf16 output is also written as
+    row-wise MXFP4 (1x32 along N, RTNE) by the GEMM's epilogue.  Returns
+    (c or None, codes [M x N/2], scales [M x N/32]); out / codes / scales
+    are optional preallocated outputs."""
+    torch = _torch()
+    for t, nm in ((a_codes, "a_codes"), (a_scales, "a_scales"), (b_codes, "b_codes"),
+                  (b_scales, "b_scales"), (group_offsets, "group_offsets")):
+        _dev(t, nm)
+    if a_row_index is not None:
+        _dev(a_row_index, "a_row_index")
+    G = group_offsets.numel() - 1
+    dev = a_codes.device
+    c = None
+    if with_bf16:
+        c = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    codes = codes if codes is not None else torch.empty((M, N // 2), dtype=torch.uint8, device=dev)
+    scales = scales if scales is not None else torch.empty((M, N // 32), dtype=torch.uint8, device=dev)
+    _check("mx_grouped_gemm_q", lib().mx_grouped_gemm_q(
+        _ptr(a_codes), _ptr(a_scales), _ptr(a_row_index), _ptr(b_codes), _ptr(b_scales),
+        int(bool(b_scale_2d)), _ptr(group_offsets), G, M, N, K, float(alpha),
+        _ptr(c), _ptr(codes), _ptr(scales), _stream()))
+    return c, codes, scales

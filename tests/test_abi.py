@@ -16,7 +16,8 @@ def L():
 def test_every_declared_symbol_is_exported(L):
     names = mx.declared_functions()
     assert set(names) >= {"mx_rht", "mx_quantize_1d", "mx_quantize_2d", "mx_dequantize",
-                          "mx_grouped_gemm", "mx_rht_sign_mask", "mx_status_str", "mx_version"}
+                          "mx_grouped_gemm", "mx_grouped_gemm_q", "mx_rht_sign_mask", "mx_status_str",
+                          "mx_version"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -111,4 +112,29 @@ def test_gemm_validation(L):
     assert call(a_codes=FAKE + 1) == 3
     assert call(gk=1, b_scale_2d=1) == 5
     assert call(gk=1, a_row_index=FAKE) == 5
+    assert call(M=0) == 0
+
+
+def test_gemm_q_validation(L):
+    g = L.mx_grouped_gemm_q
+
+    def call(**kw):
+        a = dict(a_codes=FAKE, a_scales=FAKE, a_row_index=None, b_codes=FAKE, b_scales=FAKE,
+                 b_scale_2d=0, off=FAKE, G=1, M=64, N=64, K=64, alpha=1.0, c=FAKE, qc=FAKE, qs=FAKE)
+        a.update(kw)
+        return g(a["a_codes"], a["a_scales"], a["a_row_index"], a["b_codes"], a["b_scales"],
+                 a["b_scale_2d"], a["off"], a["G"], a["M"], a["N"], a["K"], ctypes.c_float(a["alpha"]),
+                 a["c"], a["qc"], a["qs"], None)
+
+    assert call(K=48) == 2
+    assert call(N=48) == 2
+    assert call(G=0) == 2
+    assert call(off=None) == 1
+    assert call(qc=None) == 1
+    assert call(qs=None) == 1
+    assert call(a_codes=FAKE + 1) == 3
+    assert call(qc=FAKE + 8) == 3
+    assert call(c=FAKE + 2) == 3
+    # codes of M x N / 2 bytes beyond 4 GiB - 1
+    assert call(M=2**20, N=2**13, K=64) == 2
     assert call(M=0) == 0

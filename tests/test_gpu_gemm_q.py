@@ -1,0 +1,110 @@
+"""GPU parity of the grouped GEMM with the quantizing epilogue (mx_grouped_gemm_q).
+
+The fused output is the row-wise MXFP4 quantization (1x32 blocks along N,
+round to nearest even) of the GEMM's bf16 output, y = RNE_bf16(alpha A.B^T).
+
+- Against the oracle, bit for bit, on operands for which the fp32
+  accumulation is exact.  All scale bytes are 127 and K <= 256, so every
+  partial sum is a multiple of 1/4 below 9216 (exact in fp32).  The kernel's
+  bf16 output is then RNE_bf16 of the FP64 oracle, and its codes and scales
+  are the oracle quantizer's.
+- With general data (K = 2880, random scales), against the oracle block by
+  block: a block may differ only where the kernel's bf16 output differs from
+  RNE_bf16 of the FP64 oracle (fp32 accumulation order), and such blocks are
+  rare.
+- With general data, bit for bit against the unfused path (the GEMM, then the
+  1D quantizer), each half of which is pinned to the oracle by its own tests.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from mxfp4_precision_numerics_amd import mx, synth
+from tests.gpu_util import dev, first_mismatch, host
+
+pytestmark = pytest.mark.gpu
+
+
+def _operands(rng, counts, K, N, a_rows, b_2d, unit_scales):
+    off = synth.offsets_from_counts(counts)
+    G = len(counts)
+    ac = rng.integers(0, 256, (a_rows, K // 2), dtype=np.uint8)
+    bc = rng.integers(0, 256, (G, N, K // 2), dtype=np.uint8)
+    bshape = (G, N // 32, K // 32) if b_2d else (G, N, K // 32)
+    if unit_scales:
+        asc = np.full((a_rows, K // 32), 127, dtype=np.uint8)
+        bs = np.full(bshape, 127, dtype=np.uint8)
+    else:
+        asc = rng.integers(120, 135, (a_rows, K // 32), dtype=np.uint8)
+        bs = rng.integers(120, 135, bshape, dtype=np.uint8)
+    return off, ac, asc, bc, bs
+
+
+def _case(seed, counts, K, N, gather, b_2d, unit_scales):
+    rng = np.random.default_rng(seed)
+    M = int(sum(counts))
+    a_rows = 150 if gather else M
+    off, ac, asc, bc, bs = _operands(rng, counts, K, N, a_rows, b_2d, unit_scales)
+    idx = rng.integers(0, a_rows, M).astype(np.int32) if gather else None
+    return off, M, ac, asc, bc, bs, idx
+
+
+def _oracle_y_bits(ac, asc, bc, bs, off, M, N, K, idx, b_2d, alpha):
+    """RNE_bf16 of the FP64 oracle GEMM, rows in m order."""
+    rows, want = oracle.grouped_gemm(ac, asc, bc, bs, off, M, N, K, a_row_index=idx,
+                                     b_scale_2d=b_2d, alpha=alpha)
+    want = want[np.argsort(rows[:, 1], kind="stable")]
+    return oracle.round_bf16_bits(want)
+
+
+@pytest.mark.parametrize("counts,K,N,gather,b_2d,alpha", [
+    ([70, 0, 200, 33], 256, 320, True, True, 1.0),
+    ([300], 64, 96, False, False, 0.125),
+    ([5, 1, 260, 0, 31], 128, 64, True, False, 1.0),
+    ([1], 32, 32, False, True, 4.0),
+])
+def test_fused_quant_exact_vs_oracle(counts, K, N, gather, b_2d, alpha):
+    off, M, ac, asc, bc, bs, idx = _case(K * 7 + N, counts, K, N, gather, b_2d, unit_scales=True)
+    c, codes, scales = mx.grouped_gemm_q(dev(ac), dev(asc), dev(bc), dev(bs), dev(off), M, N, K,
+                                         a_row_index=None if idx is None else dev(idx),
+                                         b_scale_2d=b_2d, alpha=alpha)
+    yb = _oracle_y_bits(ac, asc, bc, bs, off, M, N, K, idx, b_2d, alpha)
+    assert first_mismatch(host(c), yb) is None
+    wc, ws = oracle.quantize_1d(yb)
+    assert first_mismatch(host(codes), wc) is None
+    assert first_mismatch(host(scales), ws) is None
+
+
+def test_fused_quant_general_data_vs_oracle():
+    counts, K, N = [300, 0, 50], 2880, 320
+    off, M, ac, asc, bc, bs, idx = _case(11, counts, K, N, True, True, unit_scales=False)
+    c, codes, scales = mx.grouped_gemm_q(dev(ac), dev(asc), dev(bc), dev(bs), dev(off), M, N, K,
+                                         a_row_index=dev(idx), b_scale_2d=True)
+    yb = _oracle_y_bits(ac, asc, bc, bs, off, M, N, K, idx, True, 1.0)
+    wc, ws = oracle.quantize_1d(yb)
+    got_c, got_codes, got_scales = host(c), host(codes), host(scales)
+    # a block (row, 32 columns) may differ only if its bf16 inputs differ
+    y_diff = (got_c != yb).reshape(M, N // 32, 32).any(axis=2)
+    q_diff = (got_codes != wc).reshape(M, N // 32, 16).any(axis=2) | (got_scales != ws)
+    assert not np.any(q_diff & ~y_diff), int(np.sum(q_diff & ~y_diff))
+    assert q_diff.mean() <= 0.01, float(q_diff.mean())
+
+
+@pytest.mark.parametrize("gather", [True, False])
+def test_fused_quant_matches_unfused_path(gather):
+    import torch
+    counts, K, N = [1000, 0, 37, 2100], 2880, 576
+    off, M, ac, asc, bc, bs, idx = _case(5 + int(gather), counts, K, N, gather, True, unit_scales=False)
+    args = (dev(ac), dev(asc), dev(bc), dev(bs), dev(off), M, N, K)
+    kw = dict(a_row_index=None if idx is None else dev(idx), b_scale_2d=True, alpha=0.5)
+    c, codes, scales = mx.grouped_gemm_q(*args, **kw)
+    c2 = mx.grouped_gemm(*args, out_dtype=torch.bfloat16, **kw)
+    codes2, scales2 = mx.quantize_1d(c2)
+    assert first_mismatch(host(c), host(c2)) is None
+    assert first_mismatch(host(codes), host(codes2)) is None
+    assert first_mismatch(host(scales), host(scales2)) is None
+    # without the bf16 output the quantized output is the same
+    c3, codes3, scales3 = mx.grouped_gemm_q(*args, with_bf16=False, **kw)
+    assert c3 is None
+    assert first_mismatch(host(codes3), host(codes2)) is None
+    assert first_mismatch(host(scales3), host(scales2)) is None
