@@ -108,6 +108,44 @@ def test_fprop_a_scale_paths_without_gather(K, odd_ptr):
             assert rel_fro(c[rows[sel, 1]], want[sel]) <= TOL, g
 
 
+@pytest.mark.parametrize("K,b_2d", [(512, True), (2880, False)])
+def test_fprop_many_groups_and_two_stage_tiles(K, b_2d):
+    """More than 64 groups: the tile decode scans the offsets 64 at a time
+    instead of keeping them in the lanes.  K = 512 gives tiles of two K
+    stages, the shortest that chain into the next tile."""
+    rng = np.random.default_rng(77 + K)
+    counts = [int(v) for v in rng.integers(0, 40, 100)]
+    counts[3], counts[50], counts[99] = 0, 300, 257
+    off, rows, got, want = _run_fprop(counts, K, 96, a_rows=200, b_2d=b_2d, seed=K + 1)
+    for g in range(len(counts)):
+        sel = rows[:, 0] == g
+        if np.any(sel):
+            assert rel_fro(got[rows[sel, 1]], want[sel]) <= TOL, g
+
+
+def test_wgrad_many_groups():
+    """70 groups split K (the decode scans offsets 64 at a time), with empty
+    groups and groups of one to four 32-token blocks."""
+    import torch
+    rng = np.random.default_rng(70)
+    counts = [int(v) * 32 for v in rng.integers(0, 5, 70)]
+    counts[10] = 640
+    M, N = 64, 96
+    off = synth.offsets_from_counts(counts)
+    Kt = int(off[-1])
+    ac, asc = _q1d(rng, M, Kt)
+    bc, bs = _q1d(rng, N, Kt)
+    c = host(mx.grouped_gemm(dev(ac), dev(asc), dev(bc), dev(bs), dev(off), M, N, Kt,
+                             group_dim_k=True, out_dtype=torch.float32))
+    rows, want = oracle.grouped_gemm(ac, asc, bc, bs, off, M, N, Kt, group_dim_k=True)
+    for g in range(len(counts)):
+        sel = rows[:, 0] == g
+        if counts[g] == 0:
+            assert np.all(c[g] == 0), g
+        else:
+            assert rel_fro(c[g][rows[sel, 1]], want[sel]) <= TOL, g
+
+
 def test_fprop_bf16_output():
     off, rows, got, want = _run_fprop([40, 90], 2880, 192, a_rows=64, b_2d=True, seed=4,
                                       out_dtype="bf16")

@@ -62,6 +62,7 @@ def _oracle_y_bits(ac, asc, bc, bs, off, M, N, K, idx, b_2d, alpha):
     ([300], 64, 96, False, False, 0.125),
     ([5, 1, 260, 0, 31], 128, 64, True, False, 1.0),
     ([1], 32, 32, False, True, 4.0),
+    ([int(v) for v in np.random.default_rng(80).integers(0, 24, 80)], 256, 64, True, True, 1.0),
 ])
 def test_fused_quant_exact_vs_oracle(counts, K, N, gather, b_2d, alpha):
     off, M, ac, asc, bc, bs, idx = _case(K * 7 + N, counts, K, N, gather, b_2d, unit_scales=True)
