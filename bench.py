@@ -35,7 +35,9 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic.txt")
 # kernel-name prefix (template arguments without spaces) of each GEMM role:
 # bf16 output with 2D weight scales, fp32 output with 1D scales
-ROLE_KERNEL = {"gemm": "gemm_kernel<true,true", "gemm_wgrad": "gemm_kernel<false,false"}
+# kernel-name prefixes of each role's launches (the last template argument,
+# the quantizing epilogue, is off in the step)
+ROLE_KERNEL = {"gemm": "gemm_kernel<true,true,", "gemm_wgrad": "gemm_kernel<false,false,true,"}
 PEAK_FP4_TFLOPS = 10100.0      # MI355X dense FP4 MFMA, TFLOP/s
 E, D, F2, T, TOPK = 32, 2880, 5760, 16384, 4
 ROWS = T * TOPK
@@ -178,7 +180,7 @@ def measured_traffic(role):
             rec[f[1]] = (float(f[3]), float(f[5]), calls)
     # a role may launch several instantiations (e.g. with and without a row
     # gather): average over all of its dispatches
-    names = [k for k in rec if k.startswith(ROLE_KERNEL[role])]
+    names = [k for k in rec if k.startswith(ROLE_KERNEL[role]) and k.endswith(",false>")]
     if src != kernel_source_hash() or not names:
         return None
     n = sum(rec[k][2] for k in names)
@@ -286,6 +288,8 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-fused-epilogue", action="store_true",
+                    help="skip the fused-epilogue comparison run after the timed steps (profiling runs)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device copy of this many bytes (3 launches), to "
                          "calibrate the HBM byte counters against a kernel of known traffic")
@@ -381,8 +385,9 @@ def main():
         "gemm_frac_fp4": total_flops / (gemm_ms / 1e3) / 1e12 / PEAK_FP4_TFLOPS,
         "kernels": kernels,
         "roofline": roof,
-        "fused_epilogue": fused_epilogue(torch, step),
     }
+    if not args.no_fused_epilogue:
+        out["fused_epilogue"] = fused_epilogue(torch, step)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out))
