@@ -656,13 +656,17 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
             // At a chained tile's first barrier the previous tile's
             // EPI_STORES stores are the newest memory operations (without a
             // row gather nothing is loaded after them) and may stay in flight.
-            auto stage = [&](int kt, auto first_c) {
+            // Only a tile's last stage can hold chunks past the end of K, so
+            // only its copy of the stage computes the tail flags (they cost a
+            // select per MFMA operand per K-quarter).
+            auto stage = [&](int kt, auto first_c, auto last_c) {
                 constexpr bool FIRST = decltype(first_c)::value;
+                constexpr bool LAST = decltype(last_c)::value;
                 const int buf = (kt & 1) ^ par;
                 const int kcl = kt * 8 + lh;              // this lane's chunk in K-quarter 0
-                mma_rd(f0, sc, 0, kcl > cur.kc_last, buf, 1);
-                mma_rd(f0, sc, 1, kcl + 2 > cur.kc_last, buf, 2);
-                mma_rd(f0, sc, 2, kcl + 4 > cur.kc_last, buf, 3);
+                mma_rd(f0, sc, 0, LAST && kcl > cur.kc_last, buf, 1);
+                mma_rd(f0, sc, 1, LAST && kcl + 2 > cur.kc_last, buf, 2);
+                mma_rd(f0, sc, 2, LAST && kcl + 4 > cur.kc_last, buf, 3);
                 if (FIRST) {
                     if (EPI_STORES == 16) asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)" ::: "memory");
                     else asm volatile("s_waitcnt vmcnt(32) lgkmcnt(0)" ::: "memory");
@@ -691,18 +695,22 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
                                  : "=v"(r2[jj]) : "v"(arow[jj]), "v"(narow[jj]), "s"(sel));
                 issue(t2, r2, to_next ? kt + 2 - cur.nkt : kt + 2, buf);
                 read_scl(nsc, buf ^ 1);
-                mma_rd(f0, sc, 3, kcl + 6 > cur.kc_last, buf ^ 1, 0);
+                mma_rd(f0, sc, 3, LAST && kcl + 6 > cur.kc_last, buf ^ 1, 0);
                 pack(sc, nsc);
             };
             // At a chained tile's first barrier the previous tile's
             // EPI_STORES stores are the newest memory operations (without a
             // row gather nothing is loaded after them) and may stay in flight.
-            int kt0 = 0;
-            if (!GATHER && primed) {
-                stage(0, std::true_type{});
-                kt0 = 1;
+            // (a one-stage tile takes the general first wait, vmcnt(0): it
+            // also waits for the stores, which is correct, only slower)
+            const int last = cur.nkt - 1;
+            int kt = 0;
+            if (!GATHER && primed && last > 0) {
+                stage(0, std::true_type{}, std::false_type{});
+                kt = 1;
             }
-            for (int kt = kt0; kt < cur.nkt; ++kt) stage(kt, std::false_type{});
+            for (; kt < last; ++kt) stage(kt, std::false_type{}, std::false_type{});
+            stage(last, std::false_type{}, std::true_type{});
         }
         static_assert(EPI_STORES == 16 || EPI_STORES == 32, "first-barrier wait counts");
         epilogue(cur);
