@@ -112,9 +112,6 @@ constexpr int dma_per_stage() { return 8 + (SA2 ? 2 : 4) + (B2D ? 1 : 4); }
 // the LDS serves 8 lanes (32 banks: rows r..r+7) or 16 lanes (64 banks: the
 // even and the odd rows of r..r+15) of a ds_read_b128 per cycle.
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
-// scale dword slot p of a row holds chunk (0, 2, 4, 6, 1, 3, 5, 7)[p], so
-// lane half h reads the chunks of its four K-quarters (2 q + h) in one go
-__device__ __forceinline__ int sperm(int p) { return p < 4 ? 2 * p : 2 * (p - 4) + 1; }
 
 // LDS-DMA: every lane moves 16 bytes (or 1 byte, zero-extended to a dword)
 // from base + voff to LDS byte address lds + 16 lane (or + 4 lane).  M0
@@ -145,10 +142,10 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
 }
 
-// SA2: the A scales of a stage move two bytes per lane (global_load_lds_ushort),
-// half the DMA instructions of one byte per lane.  It needs every pair of
-// scale bytes 2-byte aligned: an even K / 32, an even scale pointer, and a K
-// range starting at 0 (groups split M).
+// SA2: the A scales of a stage (and 2D B scales) move two bytes per lane
+// (global_load_lds_ushort), half the DMA instructions of one byte per lane.
+// It needs every pair of scale bytes 2-byte aligned: an even K / 32, even
+// scale pointers, and a K range starting at 0 (groups split M).
 // QOUT: the epilogue also quantizes the bf16 output row-wise (1x32 blocks
 // along N, round to nearest even), as the 1D quantizer would.
 template <bool OUT_BF16, bool B2D, bool GK, bool GATHER, bool SA2, bool QOUT>
@@ -304,14 +301,13 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
     // (the host bounds every operand to 4 GiB).
     const int pc = tid & 7;
     const int a_chunk = pc ^ swz(tid >> 3);    // swz(t/8 + (NT/8) j) is the same for every j
-    const int s_chunk = sperm(pc);
     const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
 
     // stage kt of tile t -> LDS buffer `buf`; chunks past the end are clamped in range
     auto issue = [&](const Tile& t, const int32_t (&arow)[NJ], int kt, int buf) {
         const uint32_t sb = lds_base + (uint32_t)buf * STAGE_BYTES;
         const uint32_t kc = (uint32_t)(t.kc0 + min(kt * 8 + a_chunk, t.kc_last));
-        const uint32_t ks = (uint32_t)(t.kc0 + min(kt * 8 + s_chunk, t.kc_last));
+        const uint32_t ks = (uint32_t)(t.kc0 + min(kt * 8 + pc, t.kc_last));
         const uint8_t* bcodes = p.b_codes;
         const uint8_t* bscales = p.b_scales;
         if (!GK) {
@@ -348,17 +344,25 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
         }
         if (B2D) {
             // wave w fetches row group w of the tile (8 groups of 32 rows):
-            // lane l takes scale position l % 8, so the 8 copies of the same
-            // 8 bytes coalesce into one line request (one group per wave
-            // instead of all 8 in every wave: 8x fewer requests)
+            // lane l takes scale position l % 8 (SA2: pair l % 4), so the
+            // copies of the same 8 bytes coalesce into one line request (one
+            // group per wave instead of all 8 in every wave: 8x fewer requests)
             int32_t grp = t.n0 / 32 + wave;
             if (grp > N32 / 32 - 1) grp = N32 / 32 - 1;    // groups past N are never stored
-            dma1(bscales, (uint32_t)grp * (uint32_t)KS + ks, sb + OFF_BS + wave * 256);
+            if (SA2) {
+                const uint32_t kp = (uint32_t)(t.kc0 + min(kt * 8 + 2 * (pc & 3), t.kc_last - 1));
+                dma2(bscales, (uint32_t)grp * (uint32_t)KS + kp, sb + OFF_BS + wave * 256);
+            } else {
+                dma1(bscales, (uint32_t)grp * (uint32_t)KS + ks, sb + OFF_BS + wave * 256);
+            }
         }
     };
 
     const int lr = lane & 31;      // operand row within a 32-row MFMA block
-    const int lh = lane >> 5;      // which 32-element half of a K-quarter (64)
+    // K-quarter q of a stage (64 elements, one MFMA) takes chunk 4 h + q
+    // in lane half h: any split of K works if both operands and their
+    // scales agree, and this one keeps a lane's four scale bytes adjacent
+    const int lh = lane >> 5;
     // operand rows w*128 + i*32 + lr share swz(lr) for every i, so a fragment
     // read is one per-lane base plus an immediate i * 4096
     const int sw = swz(lr);
@@ -371,7 +375,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
     // K-quarter q); the MFMA's scale operand selects the byte
     struct Scl { uint32_t b[FN]; uint32_t a[FM]; };
     auto read_frag = [&](Frag& f, int buf, int q) {
-        const uint8_t* sb = lds + buf * STAGE_BYTES + (((2 * q + lh) ^ sw) * 16);
+        const uint8_t* sb = lds + buf * STAGE_BYTES + (((4 * lh + q) ^ sw) * 16);
 #pragma unroll
         for (int i = 0; i < FN; ++i) {
             const uint4 v = *(const uint4*)(sb + fb_b + i * 4096);
@@ -385,35 +389,43 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
     };
     // the next stage's scales are read during the current stage's last
     // K-quarter and packed only after its MFMAs, when the reads have landed
-    struct SclRaw { uint4 b[FN]; uint4 a[FM]; };
+    // Scale dword p of a row holds chunk p (one byte moves) or chunks 2 p
+    // and 2 p + 1 (pair moves, SA2): lane half h takes dwords 4 h .. 4 h + 3
+    // or 2 h, 2 h + 1.  2D B scales move in pairs along with the A scales.
+    constexpr bool SB2 = B2D && SA2;
+    using ARaw = typename std::conditional<SA2, uint2, uint4>::type;
+    using BRaw = typename std::conditional<SB2, uint2, uint4>::type;
+    struct SclRaw { BRaw b[FN]; ARaw a[FM]; };
     auto read_scl = [&](SclRaw& s, int buf) {
         const uint8_t* sb = lds + buf * STAGE_BYTES;
 #pragma unroll
         for (int i = 0; i < FN; ++i)
-            s.b[i] = B2D ? *(const uint4*)(sb + OFF_BS + (wn * FN + i) * 256 + lh * 16)
-                         : *(const uint4*)(sb + OFF_BS + (wn * WN + i * 32 + lr) * 32 + lh * 16);
+            s.b[i] = B2D ? *(const BRaw*)(sb + OFF_BS + (wn * FN + i) * 256 + lh * (int)sizeof(BRaw))
+                         : *(const BRaw*)(sb + OFF_BS + (wn * WN + i * 32 + lr) * 32 + lh * 16);
 #pragma unroll
         for (int i = 0; i < FM; ++i)
             // SA2: row r = wm WM + 32 i + lr was moved by wave (r % 64) / 8,
             // lane 8 (r % 8) + 4 ((r / 64) % 2) of move (r / 64) / 2 = wm:
             // its four pair dwords are consecutive
-            s.a[i] = SA2 ? *(const uint4*)(sb + OFF_AS + (wm * NW + (i & 1) * 4 + (lr >> 3)) * 256 + (lr & 7) * 32 +
-                                           (i >> 1) * 16)
-                         : *(const uint4*)(sb + OFF_AS + (wm * WM + i * 32 + lr) * 32 + lh * 16);
+            s.a[i] = SA2 ? *(const ARaw*)(sb + OFF_AS + (wm * NW + (i & 1) * 4 + (lr >> 3)) * 256 + (lr & 7) * 32 +
+                                          (i >> 1) * 16 + lh * 8)
+                         : *(const ARaw*)(sb + OFF_AS + (wm * WM + i * 32 + lr) * 32 + lh * 16);
     };
-    // SA2: dword q holds chunks 2 q (byte 0) and 2 q + 1 (byte 1); lane half
-    // lh takes byte lh of each (v_perm: selectors 0-3 pick the second
-    // operand's bytes, 4-7 the first's, 12 gives zero)
-    const uint32_t sa2_sel = (uint32_t)lh | ((4u + lh) << 8) | 0x0C0C0000u;
+    // byte q of the packed register: K-quarter q (a pair move leaves the
+    // upper half of its dword zero)
+    auto pack4 = [](const uint4& v) { return v.x | (v.y << 8) | (v.z << 16) | (v.w << 24); };
+    auto pack2 = [](const uint2& v) { return v.x | (v.y << 16); };
     auto pack = [&](Scl& s, const SclRaw& r) {
-        auto pack4 = [](const uint4& v) { return v.x | (v.y << 8) | (v.z << 16) | (v.w << 24); };
 #pragma unroll
-        for (int i = 0; i < FN; ++i) s.b[i] = pack4(r.b[i]);
+        for (int i = 0; i < FN; ++i) {
+            if constexpr (SB2) s.b[i] = pack2(r.b[i]);
+            else s.b[i] = pack4(r.b[i]);
+        }
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
-            s.a[i] = SA2 ? __builtin_amdgcn_perm(r.a[i].y, r.a[i].x, sa2_sel) |
-                               (__builtin_amdgcn_perm(r.a[i].w, r.a[i].z, sa2_sel) << 16)
-                         : pack4(r.a[i]);
+        for (int i = 0; i < FM; ++i) {
+            if constexpr (SA2) s.a[i] = pack2(r.a[i]);
+            else s.a[i] = pack4(r.a[i]);
+        }
     };
 
     // "every DMA but the newest stage's has landed"
@@ -440,7 +452,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
         }
     };
     auto read_piece = [&](Frag& f, int buf, int q, int k) {
-        const uint8_t* sb = lds + buf * STAGE_BYTES + (((2 * q + lh) ^ sw) * 16);
+        const uint8_t* sb = lds + buf * STAGE_BYTES + (((4 * lh + q) ^ sw) * 16);
         const uint4 v = k < FN ? *(const uint4*)(sb + fb_b + k * 4096) : *(const uint4*)(sb + fb_a + (k - FN) * 4096);
         v8i& d = k < FN ? f.b[k] : f.a[k - FN];
         d = (v8i){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
@@ -663,10 +675,10 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
                 constexpr bool FIRST = decltype(first_c)::value;
                 constexpr bool LAST = decltype(last_c)::value;
                 const int buf = (kt & 1) ^ par;
-                const int kcl = kt * 8 + lh;              // this lane's chunk in K-quarter 0
+                const int kcl = kt * 8 + 4 * lh;          // this lane's chunk in K-quarter 0
                 mma_rd(f0, sc, 0, LAST && kcl > cur.kc_last, buf, 1);
-                mma_rd(f0, sc, 1, LAST && kcl + 2 > cur.kc_last, buf, 2);
-                mma_rd(f0, sc, 2, LAST && kcl + 4 > cur.kc_last, buf, 3);
+                mma_rd(f0, sc, 1, LAST && kcl + 1 > cur.kc_last, buf, 2);
+                mma_rd(f0, sc, 2, LAST && kcl + 2 > cur.kc_last, buf, 3);
                 if (FIRST) {
                     if (EPI_STORES == 16) asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)" ::: "memory");
                     else asm volatile("s_waitcnt vmcnt(32) lgkmcnt(0)" ::: "memory");
@@ -695,7 +707,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
                                  : "=v"(r2[jj]) : "v"(arow[jj]), "v"(narow[jj]), "s"(sel));
                 issue(t2, r2, to_next ? kt + 2 - cur.nkt : kt + 2, buf);
                 read_scl(nsc, buf ^ 1);
-                mma_rd(f0, sc, 3, LAST && kcl + 6 > cur.kc_last, buf ^ 1, 0);
+                mma_rd(f0, sc, 3, LAST && kcl + 3 > cur.kc_last, buf ^ 1, 0);
                 pack(sc, nsc);
             };
             // At a chained tile's first barrier the previous tile's
@@ -793,7 +805,8 @@ template <bool BF, bool QOUT>
 void launch_m(const GemmArgs& p, unsigned grid, hipStream_t s) {
     const dim3 gd(grid), bd(NT);
     const bool gather = p.a_row_index != nullptr;
-    const bool sa2 = (p.K / 32) % 2 == 0 && ((uintptr_t)p.a_scales & 1) == 0;
+    const bool sa2 = (p.K / 32) % 2 == 0 && ((uintptr_t)p.a_scales & 1) == 0 &&
+                     (!p.b_scale_2d || ((uintptr_t)p.b_scales & 1) == 0);
 #define MX_GEMM_LAUNCH(B2, GA, S2) hipLaunchKernelGGL((gemm_kernel<BF, B2, false, GA, S2, QOUT>), gd, bd, 0, s, p)
 #define MX_GEMM_S(B2, GA) \
     do { if (sa2) MX_GEMM_LAUNCH(B2, GA, true); else MX_GEMM_LAUNCH(B2, GA, false); } while (0)

@@ -79,27 +79,35 @@ def test_fprop_grouped_fp32(counts, K, N, b_2d):
         assert rel_fro(got[ms], want[sel]) <= TOL, g
 
 
-@pytest.mark.parametrize("K,odd_ptr", [(160, False), (2880, True), (2880, False)])
-def test_fprop_a_scale_paths_without_gather(K, odd_ptr):
-    """A scales move two bytes per DMA lane when every pair is 2-byte aligned
-    (K / 32 even, even scale pointer) and one byte otherwise.  Both paths,
-    without a row gather: K = 160 (K / 32 odd), K = 2880 with the scales at an
-    odd address, and K = 2880 aligned."""
+def _at_odd_address(t):
     import torch
-    rng = np.random.default_rng(K + int(odd_ptr))
+    buf = torch.zeros(t.numel() + 1, dtype=torch.uint8, device=t.device)
+    buf[1:] = t.reshape(-1)
+    out = buf[1:].view(t.shape)
+    assert out.data_ptr() % 2 == 1
+    return out
+
+
+@pytest.mark.parametrize("K,odd_ptr", [(160, ""), (2880, "a"), (2880, "b"), (2880, "")])
+def test_fprop_scale_paths_without_gather(K, odd_ptr):
+    """Scales (A, and 2D B) move two bytes per DMA lane when every pair is
+    2-byte aligned (K / 32 even, even scale pointers) and one byte otherwise.
+    Both paths, without a row gather: K = 160 (K / 32 odd), K = 2880 with the
+    A or the B scales at an odd address, and K = 2880 aligned."""
+    import torch
+    rng = np.random.default_rng(K + len(odd_ptr) + (odd_ptr == "b"))
     counts = [70, 0, 200, 33]
     off = synth.offsets_from_counts(counts)
     M, N, G = int(off[-1]), 96, len(counts)
     ac, asc = _q1d(rng, M, K)
     w = (rng.standard_normal((G, N, K)) * 0.02).astype(np.float32)
     bc, bs, _, _ = oracle.quantize_2d(w)
-    a_scales = dev(asc)
-    if odd_ptr:
-        buf = torch.zeros(asc.size + 1, dtype=torch.uint8, device=a_scales.device)
-        buf[1:] = a_scales.reshape(-1)
-        a_scales = buf[1:].view(asc.shape)
-        assert a_scales.data_ptr() % 2 == 1
-    c = host(mx.grouped_gemm(dev(ac), a_scales, dev(bc), dev(bs), dev(off), M, N, K,
+    a_scales, b_scales = dev(asc), dev(bs)
+    if odd_ptr == "a":
+        a_scales = _at_odd_address(a_scales)
+    if odd_ptr == "b":
+        b_scales = _at_odd_address(b_scales)
+    c = host(mx.grouped_gemm(dev(ac), a_scales, dev(bc), b_scales, dev(off), M, N, K,
                              b_scale_2d=True, out_dtype=torch.float32))
     rows, want = oracle.grouped_gemm(ac, asc, bc, bs, off, M, N, K, b_scale_2d=True)
     for g in range(G):
