@@ -112,6 +112,7 @@ mx_status mx_rht(const void* x, mx_dtype xt, float* y, int64_t rows, int64_t col
  *   number of rows; every index must be a valid row of it).  This fuses the
  *   permutation of tokens into expert order with the quantization: no
  *   permuted copy of x is written.  NULL: position p is x[p].
+ *   One row of x must span at most 4 GiB - 1 bytes (else MX_ERR_SHAPE).
  * use_rht != 0 applies the RHT (sign_mask) to each block before quantizing.
  * rnd: MX_RNE or MX_SR (seed, stream_id, index_base as above; index_base %
  *   32 == 0).

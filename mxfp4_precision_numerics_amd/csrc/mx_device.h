@@ -118,32 +118,37 @@ __device__ __forceinline__ uint32_t cvt_sr_fp4_byte(uint32_t old, v2f src, uint3
 }
 
 // SR: r = the 4 Philox words for these 8 elements (element e uses word e>>1,
-// low half for even e, high half for odd e).  Each element is converted on
-// its own (first slot of the pair, second slot 0.0) with the random word
-// (~r16) << 16; even elements build one dword, odd ones another, merged with
-// a 4-bit shift.
+// low half for even e, high half for odd e).  Each element is converted in
+// the first slot of a pair with the random word (~r16) << 16.  The second
+// slot is rounded from the same word shifted by one bit, so its nibble is
+// not used: even elements go in with their odd neighbour as the (ignored)
+// second slot, odd ones with an unspecified one; the low nibbles of the even
+// and odd dwords are merged.
 __device__ __forceinline__ uint32_t cvt8_sr(const float* v, float sc, const u32x4& r) {
     const uint32_t w0 = ~r.x, w1 = ~r.y, w2 = ~r.z, w3 = ~r.w;
-    uint32_t ue = 0, uo = 0;
-    ue = cvt_sr_fp4_byte<0>(ue, (v2f){v[0], 0.0f}, w0 << 16, sc);
-    uo = cvt_sr_fp4_byte<0>(uo, (v2f){v[1], 0.0f}, w0 & 0xFFFF0000u, sc);
-    ue = cvt_sr_fp4_byte<1>(ue, (v2f){v[2], 0.0f}, w1 << 16, sc);
-    uo = cvt_sr_fp4_byte<1>(uo, (v2f){v[3], 0.0f}, w1 & 0xFFFF0000u, sc);
-    ue = cvt_sr_fp4_byte<2>(ue, (v2f){v[4], 0.0f}, w2 << 16, sc);
-    uo = cvt_sr_fp4_byte<2>(uo, (v2f){v[5], 0.0f}, w2 & 0xFFFF0000u, sc);
-    ue = cvt_sr_fp4_byte<3>(ue, (v2f){v[6], 0.0f}, w3 << 16, sc);
-    uo = cvt_sr_fp4_byte<3>(uo, (v2f){v[7], 0.0f}, w3 & 0xFFFF0000u, sc);
-    return ue | (uo << 4);
+    auto odd = [](float a) { return (v2f){a, __builtin_nondeterministic_value(a)}; };
+    // byte 0 starts each dword: the builtin form (its destination not tied to
+    // "old") leaves the other bytes unspecified, and they are written next
+    uint32_t ue = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, (v2f){v[0], v[1]}, w0 << 16, sc, 0);
+    uint32_t uo = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, odd(v[1]), w0 & 0xFFFF0000u, sc, 0);
+    ue = cvt_sr_fp4_byte<1>(ue, (v2f){v[2], v[3]}, w1 << 16, sc);
+    uo = cvt_sr_fp4_byte<1>(uo, odd(v[3]), w1 & 0xFFFF0000u, sc);
+    ue = cvt_sr_fp4_byte<2>(ue, (v2f){v[4], v[5]}, w2 << 16, sc);
+    uo = cvt_sr_fp4_byte<2>(uo, odd(v[5]), w2 & 0xFFFF0000u, sc);
+    ue = cvt_sr_fp4_byte<3>(ue, (v2f){v[6], v[7]}, w3 << 16, sc);
+    uo = cvt_sr_fp4_byte<3>(uo, odd(v[7]), w3 & 0xFFFF0000u, sc);
+    return (ue & 0x0F0F0F0Fu) | ((uo << 4) & 0xF0F0F0F0u);
 }
 
 // ---------------------------------------------------------------------------
 // In-lane fp32 Walsh-Hadamard butterflies over n = 2^k values, stages
-// h = 1, 2, ..., n/2 (pairs (i, i+h) -> (a+b, a-b)).
+// h = 1, 2, ..., n/2 (pairs (i, i+h) -> (a+b, a-b)); HEND < n stops before
+// stage HEND.
 // ---------------------------------------------------------------------------
-template <int N>
+template <int N, int HEND = N>
 __device__ __forceinline__ void fwht_inlane(float* t) {
 #pragma unroll
-    for (int h = 1; h < N; h <<= 1) {
+    for (int h = 1; h < HEND; h <<= 1) {
 #pragma unroll
         for (int i = 0; i < N; ++i) {
             if (i & h) continue;

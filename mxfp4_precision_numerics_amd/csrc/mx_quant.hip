@@ -178,10 +178,10 @@ struct ColTile {
 };
 
 template <bool BF16, bool RHT, bool SR>
-__global__ __launch_bounds__(256) void q1d_col_kernel(const void* __restrict__ x, int64_t cols,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BF16 ? 3 : 2))) void q1d_col_kernel(const void* __restrict__ x, int64_t cols,
                                                       const int32_t* __restrict__ off, int num_groups,
                                                       const int32_t* __restrict__ ridx,
-                                                      int64_t kp, int64_t col_tiles, int64_t tiles, int vec,
+                                                      int64_t kp, int64_t col_tiles, int vec,
                                                       uint32_t mask, uint32_t k0, uint32_t k1,
                                                       uint32_t stream_id, uint64_t index_base,
                                                       uint8_t* __restrict__ codes,
@@ -248,42 +248,80 @@ __global__ __launch_bounds__(256) void q1d_col_kernel(const void* __restrict__ x
     auto chunk_b = [&](int k) { return BF16 ? k : (k >> 1); };
     auto chunk_j = [&](int k) { return BF16 ? (tid >> 3) : ((tid >> 4) + 16 * (k & 1)); };
     const int chunk_c = tid & (CH - 1);
-    // vector path: the tile's rows into registers (zeros outside the data)
-    auto load_regs = [&](uint4* v, int64_t pb0, int64_t c0) {
+    // The RHT's random signs are applied as the tile enters LDS: a chunk is
+    // one token row j of its block, so one sign bit (mask bit j) covers it.
+    auto sign_word = [&](int j) -> uint32_t {
+        if (!RHT) return 0u;
+        const uint32_t sb = (mask >> j) & 1u;
+        return BF16 ? sb * 0x80008000u : sb << 31;
+    };
+
+    // Vector path.  Per block row, each thread resolves the row of x behind
+    // each of its chunks once (a valid row where the chunk holds no token)
+    // and keeps one bit per chunk, set where it holds a token; the column
+    // tiles of that block row then cost one address per chunk.
+    int32_t xr[NLD];
+    uint32_t keep = 0;
+    auto rows_for = [&](int64_t pb0) {
         int64_t t0;
         int32_t n;
         block_info(pb0, t0, n);
-        const int64_t col = c0 + chunk_c * (16 / TL::EB);
+        keep = 0;
 #pragma unroll
         for (int k = 0; k < NLD; ++k) {
             const int b = chunk_b(k), j = chunk_j(k);
             const int64_t tb = bcast64(t0, b);
             const int32_t nb = __builtin_amdgcn_readlane(n, b);
-            v[k] = make_uint4(0, 0, 0, 0);
-            if (j < nb && col < cols) {
-                const int64_t xr = ridx ? (int64_t)ridx[tb + j] : tb + j;   // gathered row
-                v[k] = *(const uint4*)((const uint8_t*)x + (xr * cols + col) * TL::EB);
-            }
+            const bool ok = j < nb;
+            const int64_t r = ok ? tb + j : (nb > 0 ? tb : 0);   // a block past the end: position 0
+            xr[k] = ridx ? ridx[r] : (int32_t)r;
+            keep |= (ok ? 1u : 0u) << k;
+        }
+    };
+    // one row of x spans at most 4 GiB - 1 bytes (checked by the host)
+    const uint32_t rowbytes = (uint32_t)cols * (uint32_t)TL::EB;
+    auto load_regs = [&](uint4* v, uint32_t& kb, int64_t c0) {
+        int64_t col = c0 + chunk_c * (16 / TL::EB);
+        const bool cok = col < cols;
+        kb = cok ? keep : 0u;
+        if (!cok) col = 0;                                  // loaded, then zeroed
+        const uint8_t* base = (const uint8_t*)x + col * TL::EB;
+#pragma unroll
+        for (int k = 0; k < NLD; ++k) v[k] = *(const uint4*)(base + (uint64_t)(uint32_t)xr[k] * rowbytes);
+    };
+    // into LDS: chunks without a token become zeros, then the sign applies
+    // (a zero with its sign flipped is -0, as in the scalar path)
+    auto store_regs = [&](const uint4* v, uint32_t kb) {
+#pragma unroll
+        for (int k = 0; k < NLD; ++k) {
+            const uint32_t m = (uint32_t)__builtin_amdgcn_sbfe((int)kb, k, 1);   // all ones or zero
+            const uint32_t sg = sign_word(chunk_j(k));
+            const uint4 w = make_uint4((v[k].x & m) ^ sg, (v[k].y & m) ^ sg, (v[k].z & m) ^ sg, (v[k].w & m) ^ sg);
+            *(uint4*)(tile + chunk_b(k) * TL::BSTRIDE + chunk_j(k) * TL::ROWB + chunk_c * 16) = w;
         }
     };
 
-    const int64_t stride = gridDim.x;
-    int64_t tl = blockIdx.x;
+    // Tiles run block-row-major; workgroup w takes the contiguous range
+    // [w T / G, (w + 1) T / G) of the T tiles that hold data, so its tiles
+    // share block rows (and their source rows) and every workgroup gets the
+    // same count within one.
+    const int64_t brows = (nblk_total + CT_BLOCKS - 1) / CT_BLOCKS;
+    const int64_t ntiles = brows * col_tiles;
+    const int64_t tbeg = ntiles * blockIdx.x / gridDim.x, tend = ntiles * (blockIdx.x + 1) / gridDim.x;
+    int64_t br = tbeg / col_tiles, ct = tbeg % col_tiles;
     uint4 pre[NLD];
-    if (vec && tl < tiles) load_regs(pre, (tl / col_tiles) * CT_BLOCKS, (tl % col_tiles) * CT_COLS);
-    for (; tl < tiles; tl += stride) {
-        const int64_t ct = tl % col_tiles;
-        const int64_t pb0 = (tl / col_tiles) * CT_BLOCKS;
-        // tiles run block-row-major, so once a tile is past the padded total
-        // every later tile of this workgroup is too (uniform exit)
-        if (pb0 >= nblk_total) break;
+    uint32_t pkb = 0;
+    if (vec && tbeg < tend) {
+        rows_for(br * CT_BLOCKS);
+        load_regs(pre, pkb, ct * CT_COLS);
+    }
+    for (int64_t tl = tbeg; tl < tend; ++tl) {
+        const int64_t pb0 = br * CT_BLOCKS;
         const int64_t c0 = ct * CT_COLS;
 
         // ---- the tile into LDS (rows past a group's end, columns past cols: 0)
         if (vec) {
-#pragma unroll
-            for (int k = 0; k < NLD; ++k)
-                *(uint4*)(tile + chunk_b(k) * TL::BSTRIDE + chunk_j(k) * TL::ROWB + chunk_c * 16) = pre[k];
+            store_regs(pre, pkb);
         } else {
             int64_t t0;
             int32_t n;
@@ -296,16 +334,19 @@ __global__ __launch_bounds__(256) void q1d_col_kernel(const void* __restrict__ x
                 uint8_t* dst = tile + b * TL::BSTRIDE + j * TL::ROWB + cc * TL::EB;
                 const bool ok = j < nb && col < cols;
                 const int64_t src = ok ? ((ridx ? (int64_t)ridx[tb + j] : tb + j) * cols + col) : 0;
-                if (BF16) *(uint16_t*)dst = ok ? ((const uint16_t*)x)[src] : (uint16_t)0;
-                else *(float*)dst = ok ? ((const float*)x)[src] : 0.0f;
+                const uint32_t sg = sign_word(j);
+                if (BF16) *(uint16_t*)dst = (uint16_t)((ok ? ((const uint16_t*)x)[src] : 0u) ^ (sg & 0xFFFFu));
+                else *(uint32_t*)dst = (ok ? ((const uint32_t*)x)[src] : 0u) ^ sg;
             }
         }
         __syncthreads();
-        // ---- prefetch the next tile while this one is quantized
-        if (vec) {
-            const int64_t nx = tl + stride;
-            if (nx < tiles && (nx / col_tiles) * CT_BLOCKS < nblk_total)
-                load_regs(pre, (nx / col_tiles) * CT_BLOCKS, (nx % col_tiles) * CT_COLS);
+        // ---- the next tile (of this or the next block row) into registers
+        // while this one is quantized
+        const bool wrap = ct + 1 == col_tiles;
+        const int64_t nbr = wrap ? br + 1 : br, nct = wrap ? 0 : ct + 1;
+        if (vec && tl + 1 < tend) {
+            if (wrap) rows_for(nbr * CT_BLOCKS);
+            load_regs(pre, pkb, nct * CT_COLS);
         }
 
         // ---- quantize: thread = (block b, column pair cp), one column at a time
@@ -322,17 +363,29 @@ __global__ __launch_bounds__(256) void q1d_col_kernel(const void* __restrict__ x
                 else t[j] = *(const float*)src;
             }
             const int64_t c = c0 + 2 * cp + side;
+            uint32_t am = 0;
             if (RHT) {
+                // the signs are already in t (applied on the way into LDS).
+                // The block amax comes from the last butterfly stage's
+                // inputs: the larger of |a + b| and |a - b| is fl(|a| + |b|)
+                // (rounding is monotonic and symmetric), a NaN input gives a
+                // NaN sum, and the scaling by c32 preserves the maximum.
+                fwht_inlane<32, 16>(t);
 #pragma unroll
-                for (int j = 0; j < 32; ++j) t[j] = __uint_as_float(__float_as_uint(t[j]) ^ (((mask >> j) & 1u) << 31));
-                fwht_inlane<32>(t);
+                for (int j = 0; j < 16; ++j) {
+                    const float a = t[j], bb = t[j + 16];
+                    am = max(am, __float_as_uint(fabsf(a) + fabsf(bb)));
+                    t[j] = a + bb;
+                    t[j + 16] = a - bb;
+                }
                 const float cc = __uint_as_float(0x3E3504F3u);
+                am = __float_as_uint(__uint_as_float(am) * cc) & 0x7FFFFFFFu;
 #pragma unroll
                 for (int j = 0; j < 32; ++j) t[j] = t[j] * cc;
-            }
-            uint32_t am = 0;
+            } else {
 #pragma unroll
-            for (int j = 0; j < 32; ++j) am = max(am, __float_as_uint(t[j]) & 0x7FFFFFFFu);
+                for (int j = 0; j < 32; ++j) am = max(am, __float_as_uint(t[j]) & 0x7FFFFFFFu);
+            }
             const uint32_t byte = scale_byte_from_amax_bits(am);
             const float sc = scale_operand(byte);
             uint32_t w[4];
@@ -375,6 +428,8 @@ __global__ __launch_bounds__(256) void q1d_col_kernel(const void* __restrict__ x
             }
         }
         __syncthreads();                                     // LDS is reused by the next tile
+        br = nbr;
+        ct = nct;
     }
 }
 
@@ -723,6 +778,7 @@ mx_status mx_quantize_1d(const void* x, mx_dtype xt, int64_t rows, int64_t cols,
     if (kp == 0 || rows == 0) return MX_OK;
     if (!x || !codes || !scales) return MX_ERR_NULL;
     if (!aligned16(x) || !aligned16(codes)) return MX_ERR_ALIGN;
+    if (cols > (int64_t)(0xFFFFFFFFu / (bf ? 2u : 4u))) return MX_ERR_SHAPE;   // one row of x within 4 GiB
     const int64_t col_tiles = (cols + CT_COLS - 1) / CT_COLS;
     const int64_t tiles = col_tiles * ((kp / 32 + CT_BLOCKS - 1) / CT_BLOCKS);
     // persistent grid, sized to residency: the bf16 RHT+SR variant needs
@@ -744,7 +800,7 @@ mx_status mx_quantize_1d(const void* x, mx_dtype xt, int64_t rows, int64_t cols,
     }
     (void)hipGetLastError();
     MX_DISPATCH3_LDS(q1d_col_kernel, bf, rh, sr, dim3(grid), lds, s, x, cols, group_offsets, (int)num_groups, row_index, kp,
-                     col_tiles, tiles, vec, sign_mask, k0, k1, stream_id, index_base, codes, scales);
+                     col_tiles, vec, sign_mask, k0, k1, stream_id, index_base, codes, scales);
     return launched();
 }
 

@@ -56,6 +56,8 @@ def test_quantize_1d_validation(L):
     assert q(FAKE, mx.MX_BF16, 4, 32, 0, None, 2, 64, None, 0, 0, 0, 0, 0, 0, FAKE, FAKE, None) == 1
     assert q(FAKE, mx.MX_BF16, 4, 32, 0, FAKE, 2, 40, None, 0, 0, 0, 0, 0, 0, FAKE, FAKE, None) == 2
     assert q(FAKE, mx.MX_BF16, 4, 32, 0, FAKE, 0, 64, None, 0, 0, 0, 0, 0, 0, FAKE, FAKE, None) == 2
+    # column-wise: one row of x over 4 GiB (2^31 bf16 columns)
+    assert q(FAKE, mx.MX_BF16, 4, 2 ** 31, 0, FAKE, 2, 64, None, 0, 0, 0, 0, 0, 0, FAKE, FAKE, None) == 2
     # a row gather is column-wise only
     assert q(FAKE, mx.MX_BF16, 4, 32, 1, None, 0, 0, FAKE, 0, 0, 0, 0, 0, 0, FAKE, FAKE, None) == 5
     # empty input is a no-op that launches nothing

@@ -83,6 +83,39 @@ def test_nonfinite_blocks_get_nan_scale():
     assert s[0, 0] == 0xFF and s[1, 1] == 0xFF and s[0, 1] == 125 and s[1, 0] == 125
 
 
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("use_rht", [False, True])
+def test_colwise_nonfinite_and_overflowing_blocks(dt, use_rht):
+    # column-wise blocks holding Inf, -Inf, NaN, and finite values whose RHT
+    # butterfly sums overflow fp32: scale 0xFF and zero codes wherever the
+    # (transformed) block is not finite, as the oracle decides
+    rng = np.random.default_rng(12)
+    counts = [64, 40, 96]
+    off = synth.offsets_from_counts(counts)
+    rows, cols = int(off[-1]), 96
+    x = rng.standard_normal((rows, cols)).astype(np.float32)
+    x[3, 0] = np.inf
+    x[40, 5] = -np.inf
+    x[70, 33] = np.nan
+    x[100:104, 64] = 3.0e38          # overflows when summed
+    x[130, 65] = -3.0e38             # alone in its block: finite
+    if dt == "bf16":
+        x = synth.f32_to_bf16_bits(x)
+        xd = dev_bf16(x)
+    else:
+        xd = dev(x)
+    kp = mx.padded_capacity(rows, len(counts))
+    mask = mx.rht_sign_mask(4)
+    c, s = mx.quantize_1d(xd, block_axis=0, group_offsets=dev(off), kp=kp, use_rht=use_rht, sign_mask=mask,
+                          rnd=1, seed=3, stream_id=1)
+    oc, os_ = oracle.quantize_1d(x, block_axis=0, group_offsets=off, kp=kp, use_rht=use_rht, sign_mask=mask,
+                                 rnd=1, seed=3, stream=1)
+    total = oracle.padded_total(off)
+    assert np.count_nonzero(os_[:, :total // 32] == 0xFF) >= 3 + use_rht
+    _assert_same(host(s)[:, :total // 32], os_[:, :total // 32], "scales")
+    _assert_same(host(c)[:, :total // 2], oc[:, :total // 2], "codes")
+
+
 def test_sharded_rows_with_index_base_match_whole_tensor():
     x = synth.channel_scaled_activations(rows=96, cols=2880, seed=1)
     mask = mx.rht_sign_mask(1)
@@ -254,6 +287,35 @@ def test_colwise_gathered_rows(dt, cols):
     mask = mx.rht_sign_mask(3)
     c, s = mx.quantize_1d(xd, block_axis=0, group_offsets=dev(off), kp=kp, use_rht=True, sign_mask=mask,
                           rnd=1, seed=8, stream_id=2, row_index=dev(idx))
+    oc, os_ = oracle.quantize_1d(np.ascontiguousarray(x[idx]), block_axis=0, group_offsets=off, kp=kp,
+                                 use_rht=True, sign_mask=mask, rnd=1, seed=8, stream=2)
+    total = oracle.padded_total(off)
+    _assert_same(host(s)[:, :total // 32], os_[:, :total // 32], "scales")
+    _assert_same(host(c)[:, :total // 2], oc[:, :total // 2], "codes")
+
+
+@pytest.mark.parametrize("dt,gather", [("bf16", True), ("bf16", False), ("f32", True)])
+def test_colwise_several_tiles_per_workgroup(dt, gather):
+    # about 14,000 tokens x 2880 columns: more tiles than resident
+    # workgroups, so a workgroup walks several consecutive tiles and crosses
+    # from one block row of tokens to the next (its source rows are resolved
+    # again there); compared in full against the oracle
+    rng = np.random.default_rng(31 + gather)
+    counts = [2100, 0, 33, 5700, 5, 3000, 991, 0, 2222]
+    off = synth.offsets_from_counts(counts)
+    rows, cols = int(off[-1]), 2880
+    x_rows = 4000 if gather else rows
+    idx = rng.integers(0, x_rows, rows).astype(np.int32) if gather else np.arange(rows, dtype=np.int32)
+    x = rng.standard_normal((x_rows, cols)).astype(np.float32)
+    if dt == "bf16":
+        x = synth.f32_to_bf16_bits(x)
+        xd = dev_bf16(x)
+    else:
+        xd = dev(x)
+    kp = mx.padded_capacity(rows, len(counts))
+    mask = mx.rht_sign_mask(7)
+    c, s = mx.quantize_1d(xd, block_axis=0, group_offsets=dev(off), kp=kp, use_rht=True, sign_mask=mask,
+                          rnd=1, seed=8, stream_id=2, row_index=dev(idx) if gather else None)
     oc, os_ = oracle.quantize_1d(np.ascontiguousarray(x[idx]), block_axis=0, group_offsets=off, kp=kp,
                                  use_rht=True, sign_mask=mask, rnd=1, seed=8, stream=2)
     total = oracle.padded_total(off)
