@@ -500,34 +500,35 @@ __global__ __launch_bounds__(256) void q2d_kernel(const void* __restrict__ w, in
         const int ntr = (int)min((int64_t)Q2_TR, row_tiles - tr0);
         const int64_t tile = cs * 8 + j;
         const bool valid = tile < tiles_per_row;
+        // this thread's 32 elements of tile row ts, as raw words; the next
+        // tile row's are loaded before this one's block-wide amax reduction
+        constexpr int NQ = BF16 ? 4 : 8;
+        uint4 raw[NQ];
+        auto load_raw = [&](int ts) {
+            const int64_t grow = bt * rows + (tr0 + ts) * 32 + r;
+            const uint4* p = (const uint4*)((const uint8_t*)w + (grow * cols + tile * 32) * (BF16 ? 2 : 4));
+#pragma unroll
+            for (int k = 0; k < NQ; ++k) raw[k] = valid ? p[k] : make_uint4(0, 0, 0, 0);
+        };
+        load_raw(0);
         for (int ts = 0; ts < ntr; ++ts) {
             const int64_t tr = tr0 + ts;
             const int64_t grow = bt * rows + tr * 32 + r;      // global row in the batch stack
             float v[32];
-            if (valid) {
+#pragma unroll
+            for (int k = 0; k < NQ; ++k) {
+                const uint4 q = raw[k];
                 if (BF16) {
-                    const uint4* p = (const uint4*)((const uint16_t*)w + grow * cols + tile * 32);
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        const uint4 q = p[k];
-                        v[8 * k + 0] = bf16lo(q.x); v[8 * k + 1] = bf16hi(q.x);
-                        v[8 * k + 2] = bf16lo(q.y); v[8 * k + 3] = bf16hi(q.y);
-                        v[8 * k + 4] = bf16lo(q.z); v[8 * k + 5] = bf16hi(q.z);
-                        v[8 * k + 6] = bf16lo(q.w); v[8 * k + 7] = bf16hi(q.w);
-                    }
+                    v[8 * k + 0] = bf16lo(q.x); v[8 * k + 1] = bf16hi(q.x);
+                    v[8 * k + 2] = bf16lo(q.y); v[8 * k + 3] = bf16hi(q.y);
+                    v[8 * k + 4] = bf16lo(q.z); v[8 * k + 5] = bf16hi(q.z);
+                    v[8 * k + 6] = bf16lo(q.w); v[8 * k + 7] = bf16hi(q.w);
                 } else {
-                    const uint4* p = (const uint4*)((const float*)w + grow * cols + tile * 32);
-#pragma unroll
-                    for (int k = 0; k < 8; ++k) {
-                        const uint4 q = p[k];
-                        v[4 * k + 0] = __uint_as_float(q.x); v[4 * k + 1] = __uint_as_float(q.y);
-                        v[4 * k + 2] = __uint_as_float(q.z); v[4 * k + 3] = __uint_as_float(q.w);
-                    }
+                    v[4 * k + 0] = __uint_as_float(q.x); v[4 * k + 1] = __uint_as_float(q.y);
+                    v[4 * k + 2] = __uint_as_float(q.z); v[4 * k + 3] = __uint_as_float(q.w);
                 }
-            } else {
-#pragma unroll
-                for (int k = 0; k < 32; ++k) v[k] = 0.0f;
             }
+            if (ts + 1 < ntr) load_raw(ts + 1);
             uint32_t am = 0;
 #pragma unroll
             for (int k = 0; k < 32; ++k) am = max(am, __float_as_uint(v[k]) & 0x7FFFFFFFu);
