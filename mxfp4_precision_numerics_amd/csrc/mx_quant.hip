@@ -7,9 +7,10 @@
 //     lane, one 16-byte bf16 load), a wave covers 16 consecutive blocks; the
 //     RHT's stages 8 and 16 cross lanes through DPP quad permutes; the lane's
 //     8 elements take exactly one Philox call when rounding stochastically.
-//   column-wise 1D: a persistent workgroup streams tiles of 256 padded
-//     tokens x 64 columns through LDS (128-byte row reads, the next tile
-//     prefetched into registers while the current one is quantized); a
+//   column-wise 1D: a persistent workgroup streams a contiguous run of
+//     tiles of 256 padded tokens x 64 columns through LDS (128-byte row
+//     reads, the next tile prefetched into registers while the current one
+//     is quantized; the source rows of a block row are resolved once); a
 //     thread takes 32 tokens of one column from LDS so the RHT and the block
 //     amax stay in-lane, and codes are regrouped in LDS so each column's
 //     tile leaves as one 128-byte run of the token-contiguous layout.
