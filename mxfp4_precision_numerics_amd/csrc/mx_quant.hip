@@ -790,14 +790,16 @@ mx_status mx_quantize_1d(const void* x, mx_dtype xt, int64_t rows, int64_t cols,
     const int vec = (cols % (bf ? 8 : 4)) == 0;
     const size_t lds = (size_t)(bf ? ColTile<true>::TILE : ColTile<false>::TILE) + 4 * (size_t)(num_groups + 1);
     if (!bf) {
-        static bool attr_set = false;
-        if (!attr_set) {
-            const int mx_lds = ColTile<false>::TILE + 4 * (COL_MAX_GROUPS + 1);
-            (void)hipFuncSetAttribute((const void*)q1d_col_kernel<false, false, false>, hipFuncAttributeMaxDynamicSharedMemorySize, mx_lds);
-            (void)hipFuncSetAttribute((const void*)q1d_col_kernel<false, false, true>, hipFuncAttributeMaxDynamicSharedMemorySize, mx_lds);
-            (void)hipFuncSetAttribute((const void*)q1d_col_kernel<false, true, false>, hipFuncAttributeMaxDynamicSharedMemorySize, mx_lds);
-            (void)hipFuncSetAttribute((const void*)q1d_col_kernel<false, true, true>, hipFuncAttributeMaxDynamicSharedMemorySize, mx_lds);
-            attr_set = true;
+        // fp32 tiles take more than 64 KiB of dynamic LDS: raise the limit of
+        // the instantiation about to run, on the current device, every call
+        // (the library keeps no state)
+        const void* fn = rh ? (sr ? (const void*)q1d_col_kernel<false, true, true>
+                                  : (const void*)q1d_col_kernel<false, true, false>)
+                            : (sr ? (const void*)q1d_col_kernel<false, false, true>
+                                  : (const void*)q1d_col_kernel<false, false, false>);
+        if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess) {
+            (void)hipGetLastError();
+            return MX_ERR_LAUNCH;
         }
     }
     (void)hipGetLastError();
