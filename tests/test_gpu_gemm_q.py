@@ -109,3 +109,33 @@ def test_fused_quant_matches_unfused_path(gather):
     assert c3 is None
     assert first_mismatch(host(codes3), host(codes2)) is None
     assert first_mismatch(host(scales3), host(scales2)) is None
+
+
+@pytest.mark.parametrize("gather", [False, True])
+def test_fused_quant_matches_unfused_path_full_size(gather):
+    """The expert-step shapes: 65,536 routed rows (32 Zipf-sized experts) x 2880
+    x 2880 without a row index (the second linear), and x 5760 x 2880 read
+    through the top-4 routing index from the 16,384-token matrix (the first).
+    Random codes and scale bytes 124..129 on the device; the fused outputs
+    must equal the GEMM's bf16 output and the 1D quantizer's codes and scales
+    of it, everywhere (compared on the device)."""
+    import torch
+    d = torch.device("cuda:0")
+    counts = synth.zipf_counts()
+    off = dev(synth.offsets_from_counts(counts))
+    M, K, G = 65536, 2880, len(counts)
+    N = 5760 if gather else 2880
+    g = torch.Generator(device=d).manual_seed(11 + int(gather))
+    a_rows = 16384 if gather else M
+    ac = torch.randint(0, 256, (a_rows, K // 2), dtype=torch.uint8, device=d, generator=g)
+    asc = torch.randint(124, 130, (a_rows, K // 32), dtype=torch.uint8, device=d, generator=g)
+    bc = torch.randint(0, 256, (G, N, K // 2), dtype=torch.uint8, device=d, generator=g)
+    bs = torch.randint(124, 130, (G, N // 32, K // 32), dtype=torch.uint8, device=d, generator=g)
+    idx = dev(synth.routing_row_index(counts)) if gather else None
+    kw = dict(a_row_index=idx, b_scale_2d=True)
+    c, codes, scales = mx.grouped_gemm_q(ac, asc, bc, bs, off, M, N, K, **kw)
+    c2 = mx.grouped_gemm(ac, asc, bc, bs, off, M, N, K, out_dtype=torch.bfloat16, **kw)
+    codes2, scales2 = mx.quantize_1d(c2)
+    assert torch.equal(c.view(torch.int16), c2.view(torch.int16))
+    assert torch.equal(codes, codes2)
+    assert torch.equal(scales, scales2)
