@@ -244,11 +244,11 @@ def test_colwise_many_groups():
     _assert_same(host(c)[:, :total // 2], oc[:, :total // 2], "codes")
 
 
-def test_colwise_full_size_sampled_columns():
+def test_colwise_full_size():
     # the weight-gradient operand at its real shape: 65,536 routed token rows
     # x 2880, 32 Zipf-sized expert segments, RHT + SR.  The GPU quantizes the
-    # whole matrix; the oracle checks sampled columns, each run on its own
-    # with the column's element-index offset (c * kp) as index_base.
+    # whole matrix; the oracle checks all of it, and sampled columns run on
+    # their own with the column's element-index offset (c * kp) as index_base.
     counts = synth.zipf_counts()
     off = synth.offsets_from_counts(counts)
     rows, cols = int(off[-1]), 2880
@@ -259,6 +259,13 @@ def test_colwise_full_size_sampled_columns():
                           sign_mask=mask, rnd=1, seed=5, stream_id=5)
     ch, sh = host(c), host(s)
     total = oracle.padded_total(off)
+    # the whole matrix (a few seconds of oracle time)
+    oc, os_ = oracle.quantize_1d(x, block_axis=0, group_offsets=off, kp=kp, use_rht=True, sign_mask=mask,
+                                 rnd=1, seed=5, stream=5)
+    _assert_same(sh[:, :total // 32], os_[:, :total // 32], "scales")
+    _assert_same(ch[:, :total // 2], oc[:, :total // 2], "codes")
+    # single columns quantized on their own with index_base = c * kp (a
+    # column shard) reproduce the same bits
     for col in (0, 1, 63, 64, 1407, 2879):
         oc, os_ = oracle.quantize_1d(np.ascontiguousarray(x[:, col:col + 1]), block_axis=0, group_offsets=off,
                                      kp=kp, use_rht=True, sign_mask=mask, rnd=1, seed=5, stream=5,
@@ -323,7 +330,7 @@ def test_colwise_several_tiles_per_workgroup(dt, gather):
     _assert_same(host(c)[:, :total // 2], oc[:, :total // 2], "codes")
 
 
-def test_colwise_gathered_full_size_sampled_columns():
+def test_colwise_gathered_full_size():
     # the routed activations of the weight gradient at their real shape: the
     # 16,384-token matrix read through the top-4 routing index (65,536
     # positions, 32 Zipf segments), RHT + SR, without a permuted copy
@@ -337,6 +344,10 @@ def test_colwise_gathered_full_size_sampled_columns():
                           sign_mask=mask, rnd=1, seed=5, stream_id=2, row_index=dev(idx))
     ch, sh = host(c), host(s)
     total = oracle.padded_total(off)
+    oc, os_ = oracle.quantize_1d(np.ascontiguousarray(x[idx]), block_axis=0, group_offsets=off, kp=kp,
+                                 use_rht=True, sign_mask=mask, rnd=1, seed=5, stream=2)
+    _assert_same(sh[:, :total // 32], os_[:, :total // 32], "scales")
+    _assert_same(ch[:, :total // 2], oc[:, :total // 2], "codes")
     for col in (0, 5, 64, 2047, 2879):
         xc = np.ascontiguousarray(x[idx, col:col + 1])
         oc, os_ = oracle.quantize_1d(xc, block_axis=0, group_offsets=off, kp=kp, use_rht=True, sign_mask=mask,
