@@ -303,59 +303,79 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
     const int a_chunk = pc ^ swz(tid >> 3);    // swz(t/8 + (NT/8) j) is the same for every j
     const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
 
-    // stage kt of tile t -> LDS buffer `buf`; chunks past the end are clamped in range
-    auto issue = [&](const Tile& t, const int32_t (&arow)[NJ], int kt, int buf) {
+    // stage kt of tile t -> LDS buffer `buf`; chunks past the end are clamped
+    // in range.  A stage's DMAs are numbered: A code rows (NJ), B code rows
+    // (NJ), A scales (NJ / 2 pair moves or NJ byte moves), B scales (one 2D
+    // group move or NJ byte moves).  issue_slot(m) issues those with number
+    // p % 8 == m, so the main loop can spread a stage's DMAs over the eight
+    // MFMA blocks of a K-quarter instead of issuing them in one burst.
+    constexpr int NA_S = SA2 ? NJ / 2 : NJ, NB_S = B2D ? 1 : NJ;
+    constexpr int NPARTS = 2 * NJ + NA_S + NB_S;
+    static_assert(NPARTS == dma_per_stage<B2D, SA2>(), "DMA count");
+    auto issue_slot = [&](const Tile& t, const int32_t (&arow)[NJ], int kt, int buf, int slot) {
         const uint32_t sb = lds_base + (uint32_t)buf * STAGE_BYTES;
-        const uint32_t kc = (uint32_t)(t.kc0 + min(kt * 8 + a_chunk, t.kc_last));
-        const uint32_t ks = (uint32_t)(t.kc0 + min(kt * 8 + pc, t.kc_last));
         const uint8_t* bcodes = p.b_codes;
         const uint8_t* bscales = p.b_scales;
         if (!GK) {
             bcodes += (int64_t)t.g * p.N * KB;
             bscales += (int64_t)t.g * (B2D ? (p.N / 32) * KS : p.N * KS);
         }
-        uint32_t nrow[NJ], mrow[NJ];
-#pragma unroll
-        for (int jj = 0; jj < NJ; ++jj) {
+        auto nrow = [&](int jj) {
             const int32_t n = t.n0 + (tid >> 3) + (NT / 8) * jj;
-            nrow[jj] = (uint32_t)(n < N32 ? n : N32 - 1);   // rows past N are never stored
-            mrow[jj] = (uint32_t)arow[jj];
-        }
+            return (uint32_t)(n < N32 ? n : N32 - 1);       // rows past N are never stored
+        };
 #pragma unroll
-        for (int jj = 0; jj < NJ; ++jj) {
-            dma16(p.a_codes, mrow[jj] * (uint32_t)KB + kc * 16, sb + OFF_A + jj * NT * 16 + wave * 1024);
-            dma16(bcodes, nrow[jj] * (uint32_t)KB + kc * 16, sb + OFF_B + jj * NT * 16 + wave * 1024);
-        }
-        if (SA2) {
-            // move j: lanes with pc < 4 take scale pair pc of row slot 2 j,
-            // lanes with pc >= 4 pair pc - 4 of slot 2 j + 1 (the rows of
-            // this thread's code moves); the last pair is K / 32 - 2
-            const int half = pc >> 2;
-            const uint32_t kp = (uint32_t)(t.kc0 + min(kt * 8 + 2 * (pc & 3), t.kc_last - 1));
-#pragma unroll
-            for (int j = 0; j < NJ / 2; ++j)
-                dma2(p.a_scales, (half ? mrow[2 * j + 1] : mrow[2 * j]) * (uint32_t)KS + kp,
-                     sb + OFF_AS + (j * NW + wave) * 256);
-        }
-#pragma unroll
-        for (int jj = 0; jj < NJ; ++jj) {
-            if (!SA2) dma1(p.a_scales, mrow[jj] * (uint32_t)KS + ks, sb + OFF_AS + jj * NT * 4 + wave * 256);
-            if (!B2D) dma1(bscales, nrow[jj] * (uint32_t)KS + ks, sb + OFF_BS + jj * NT * 4 + wave * 256);
-        }
-        if (B2D) {
-            // wave w fetches row group w of the tile (8 groups of 32 rows):
-            // lane l takes scale position l % 8 (SA2: pair l % 4), so the
-            // copies of the same 8 bytes coalesce into one line request (one
-            // group per wave instead of all 8 in every wave: 8x fewer requests)
-            int32_t grp = t.n0 / 32 + wave;
-            if (grp > N32 / 32 - 1) grp = N32 / 32 - 1;    // groups past N are never stored
-            if (SA2) {
-                const uint32_t kp = (uint32_t)(t.kc0 + min(kt * 8 + 2 * (pc & 3), t.kc_last - 1));
-                dma2(bscales, (uint32_t)grp * (uint32_t)KS + kp, sb + OFF_BS + wave * 256);
+        for (int part = slot; part < NPARTS; part += 8) {
+            if (part < NJ) {
+                const int jj = part;
+                const uint32_t kc = (uint32_t)(t.kc0 + min(kt * 8 + a_chunk, t.kc_last));
+                dma16(p.a_codes, (uint32_t)arow[jj] * (uint32_t)KB + kc * 16, sb + OFF_A + jj * NT * 16 + wave * 1024);
+            } else if (part < 2 * NJ) {
+                const int jj = part - NJ;
+                const uint32_t kc = (uint32_t)(t.kc0 + min(kt * 8 + a_chunk, t.kc_last));
+                dma16(bcodes, nrow(jj) * (uint32_t)KB + kc * 16, sb + OFF_B + jj * NT * 16 + wave * 1024);
+            } else if (part < 2 * NJ + NA_S) {
+                const int j = part - 2 * NJ;
+                if (SA2) {
+                    // move j: lanes with pc < 4 take scale pair pc of row slot
+                    // 2 j, lanes with pc >= 4 pair pc - 4 of slot 2 j + 1 (the
+                    // rows of this thread's code moves); the last pair is
+                    // K / 32 - 2
+                    const int half = pc >> 2;
+                    const uint32_t kp = (uint32_t)(t.kc0 + min(kt * 8 + 2 * (pc & 3), t.kc_last - 1));
+                    dma2(p.a_scales, (uint32_t)(half ? arow[2 * j + 1] : arow[2 * j]) * (uint32_t)KS + kp,
+                         sb + OFF_AS + (j * NW + wave) * 256);
+                } else {
+                    const uint32_t ks = (uint32_t)(t.kc0 + min(kt * 8 + pc, t.kc_last));
+                    dma1(p.a_scales, (uint32_t)arow[j] * (uint32_t)KS + ks, sb + OFF_AS + j * NT * 4 + wave * 256);
+                }
             } else {
-                dma1(bscales, (uint32_t)grp * (uint32_t)KS + ks, sb + OFF_BS + wave * 256);
+                const int j = part - 2 * NJ - NA_S;
+                if (B2D) {
+                    // wave w fetches row group w of the tile (8 groups of 32
+                    // rows): lane l takes scale position l % 8 (SA2: pair
+                    // l % 4), so the copies of the same 8 bytes coalesce into
+                    // one line request (one group per wave instead of all 8 in
+                    // every wave: 8x fewer requests)
+                    int32_t grp = t.n0 / 32 + wave;
+                    if (grp > N32 / 32 - 1) grp = N32 / 32 - 1;    // groups past N are never stored
+                    if (SA2) {
+                        const uint32_t kp = (uint32_t)(t.kc0 + min(kt * 8 + 2 * (pc & 3), t.kc_last - 1));
+                        dma2(bscales, (uint32_t)grp * (uint32_t)KS + kp, sb + OFF_BS + wave * 256);
+                    } else {
+                        const uint32_t ks = (uint32_t)(t.kc0 + min(kt * 8 + pc, t.kc_last));
+                        dma1(bscales, (uint32_t)grp * (uint32_t)KS + ks, sb + OFF_BS + wave * 256);
+                    }
+                } else {
+                    const uint32_t ks = (uint32_t)(t.kc0 + min(kt * 8 + pc, t.kc_last));
+                    dma1(bscales, nrow(j) * (uint32_t)KS + ks, sb + OFF_BS + j * NT * 4 + wave * 256);
+                }
             }
         }
+    };
+    auto issue = [&](const Tile& t, const int32_t (&arow)[NJ], int kt, int buf) {
+#pragma unroll
+        for (int slot = 0; slot < 8; ++slot) issue_slot(t, arow, kt, buf, slot);
     };
 
     const int lr = lane & 31;      // operand row within a 32-row MFMA block
@@ -462,10 +482,12 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
     // the same registers (B piece i is last used by block i FM + FM - 1, A
     // piece jj by block FM + jj), so a single fragment set suffices and every
     // read still has at least three MFMAs to land.
-    auto mma_rd = [&](Frag& f, const Scl& s, int q, bool tail, int nbuf, int nq) {
+    auto no_extra = [](int) {};
+    auto mma_rd = [&](Frag& f, const Scl& s, int q, bool tail, int nbuf, int nq, auto&& extra) {
 #pragma unroll
         for (int m = 0; m < FN * FM; ++m) {
             mma1(f, s, q, tail, m);
+            extra(m);
             if (m == FM - 1) read_piece(f, nbuf, nq, 0);                 // B 0
             if (m >= FM) read_piece(f, nbuf, nq, FN + (m - FM));         // A m - FM
             if (m == FN * FM - 1) read_piece(f, nbuf, nq, 1);            // B 1
@@ -676,9 +698,9 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
                 constexpr bool LAST = decltype(last_c)::value;
                 const int buf = (kt & 1) ^ par;
                 const int kcl = kt * 8 + 4 * lh;          // this lane's chunk in K-quarter 0
-                mma_rd(f0, sc, 0, LAST && kcl > cur.kc_last, buf, 1);
-                mma_rd(f0, sc, 1, LAST && kcl + 1 > cur.kc_last, buf, 2);
-                mma_rd(f0, sc, 2, LAST && kcl + 2 > cur.kc_last, buf, 3);
+                mma_rd(f0, sc, 0, LAST && kcl > cur.kc_last, buf, 1, no_extra);
+                mma_rd(f0, sc, 1, LAST && kcl + 1 > cur.kc_last, buf, 2, no_extra);
+                mma_rd(f0, sc, 2, LAST && kcl + 2 > cur.kc_last, buf, 3, no_extra);
                 if (FIRST) {
                     if (EPI_STORES == 16) asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)" ::: "memory");
                     else asm volatile("s_waitcnt vmcnt(32) lgkmcnt(0)" ::: "memory");
@@ -705,9 +727,13 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
                 for (int jj = 0; jj < NJ; ++jj)
                     asm volatile("v_cndmask_b32_e64 %0, %1, %2, %3"
                                  : "=v"(r2[jj]) : "v"(arow[jj]), "v"(narow[jj]), "s"(sel));
-                issue(t2, r2, to_next ? kt + 2 - cur.nkt : kt + 2, buf);
+                // the DMAs of stage kt + 2 go out between the last K-quarter's
+                // MFMA blocks (one or two after each), so a wave blocked on a
+                // full memory pipeline stalls one block, not the whole burst
+                const int kt2 = to_next ? kt + 2 - cur.nkt : kt + 2;
                 read_scl(nsc, buf ^ 1);
-                mma_rd(f0, sc, 3, LAST && kcl + 3 > cur.kc_last, buf ^ 1, 0);
+                mma_rd(f0, sc, 3, LAST && kcl + 3 > cur.kc_last, buf ^ 1, 0,
+                       [&](int m) { issue_slot(t2, r2, kt2, buf, m); });
                 pack(sc, nsc);
             };
             // At a chained tile's first barrier the previous tile's
