@@ -98,14 +98,15 @@ constexpr int GROUP_M = 4;         // M-tiles per tile-order group
 constexpr int XCDS = 8;
 constexpr int XCD_BLOCK = 32;      // consecutive tile ids per XCD turn
 // one stage in LDS: A codes, B codes (256 rows x 128 bytes each), A and B
-// scales (256 rows x 8 dwords each; A scales moved in pairs take 4 dwords)
+// scales (256 rows x 8 dwords each; scales moved in pairs take 4 dwords)
 constexpr int OFF_A = 0, OFF_B = 32768, OFF_AS = 65536, OFF_BS = 73728;
 constexpr int STAGE_BYTES = 81920;
 // DMA ops per thread per stage: 8 code moves (4 rows of each operand), 4
-// A-scale moves (one byte each) or 2 (SA2: two bytes each), and 4 B-scale
-// moves (1D B scales) or 1 (2D B scales: 8 row groups of 32 per tile).
+// A-scale moves (one byte each) or 2 (SA2: two bytes each), and 4 or 2
+// (SA2) B-scale moves for 1D B scales, or 1 for 2D B scales (8 row groups
+// of 32 per tile).
 template <bool B2D, bool SA2>
-constexpr int dma_per_stage() { return 8 + (SA2 ? 2 : 4) + (B2D ? 1 : 4); }
+constexpr int dma_per_stage() { return 8 + (SA2 ? 2 : 4) + (B2D ? 1 : (SA2 ? 2 : 4)); }
 
 // 16-byte chunk swizzle of a 128-byte row: the rows an MFMA operand read
 // touches at one chunk index land in distinct 16-byte bank groups whether
@@ -142,15 +143,15 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
 }
 
-// SA2: the A scales of a stage (and 2D B scales) move two bytes per lane
-// (global_load_lds_ushort), half the DMA instructions of one byte per lane.
-// It needs every pair of scale bytes 2-byte aligned: an even K / 32, even
-// scale pointers, and a K range starting at 0 (groups split M).
+// SA2: the scales of a stage move two bytes per lane (global_load_lds_ushort),
+// half the DMA instructions of one byte per lane.  It needs every pair of
+// scale bytes 2-byte aligned: an even K / 32 and even scale pointers; with
+// groups along K each tile's K window starts at an even chunk (Tile::head).
 // QOUT: the epilogue also quantizes the bf16 output row-wise (1x32 blocks
 // along N, round to nearest even), as the 1D quantizer would.
 template <bool OUT_BF16, bool B2D, bool GK, bool GATHER, bool SA2, bool QOUT>
 __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
-    static_assert(!(GK && (B2D || GATHER || SA2)), "groups along K take 1D scales and no row index");
+    static_assert(!(GK && (B2D || GATHER)), "groups along K take 1D scales and no row index");
     static_assert(!QOUT || (OUT_BF16 && !GK), "the quantized output is the bf16 output of groups along M");
     // 2 x 4 waves of 128 x 64
     constexpr int WM = 128, WN = 64, FM = 4, FN = WN / 32;
@@ -191,6 +192,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
         int32_t g;               // group
         int32_t kc0, kc_last;    // first K chunk (of 32); last valid chunk relative to it
         int32_t nkt;             // K stages
+        int32_t head;            // 1: chunk kc0 lies before the group (groups along K, SA2)
     };
     // (the host bounds M, N, K and the tile count to int32)
     const int32_t M32 = (int32_t)p.M, N32 = (int32_t)p.N, K32 = (int32_t)p.K;
@@ -262,9 +264,13 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
         t.m1 = min(me, t.m0 + BM);
         t.n0 = nt * BN;
         t.g = g;
-        t.kc0 = kb / 32;
-        t.kc_last = ke / 32 - kb / 32 - 1;
-        t.nkt = (ke - kb + BK - 1) / BK;
+        // groups along K with pair moves: the K window starts at the even
+        // chunk at or below the group's first, so every scale pair is 2-byte
+        // aligned; a chunk before the group (head) is masked like the tail
+        t.head = GK && SA2 ? (kb / 32) & 1 : 0;
+        t.kc0 = kb / 32 - t.head;
+        t.kc_last = ke / 32 - t.kc0 - 1;
+        t.nkt = ke > kb ? (ke / 32 - t.kc0 + BK / 32 - 1) / (BK / 32) : 0;
         return true;
     };
 
@@ -309,7 +315,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
     // group move or NJ byte moves).  issue_slot(m) issues those with number
     // p % 8 == m, so the main loop can spread a stage's DMAs over the eight
     // MFMA blocks of a K-quarter instead of issuing them in one burst.
-    constexpr int NA_S = SA2 ? NJ / 2 : NJ, NB_S = B2D ? 1 : NJ;
+    constexpr int NA_S = SA2 ? NJ / 2 : NJ, NB_S = B2D ? 1 : (SA2 ? NJ / 2 : NJ);
     constexpr int NPARTS = 2 * NJ + NA_S + NB_S;
     static_assert(NPARTS == dma_per_stage<B2D, SA2>(), "DMA count");
     auto issue_slot = [&](const Tile& t, const int32_t (&arow)[NJ], int kt, int buf, int slot) {
@@ -339,10 +345,10 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
                 if (SA2) {
                     // move j: lanes with pc < 4 take scale pair pc of row slot
                     // 2 j, lanes with pc >= 4 pair pc - 4 of slot 2 j + 1 (the
-                    // rows of this thread's code moves); the last pair is
-                    // K / 32 - 2
+                    // rows of this thread's code moves); pairs past the end
+                    // repeat the pair that holds the last chunk
                     const int half = pc >> 2;
-                    const uint32_t kp = (uint32_t)(t.kc0 + min(kt * 8 + 2 * (pc & 3), t.kc_last - 1));
+                    const uint32_t kp = (uint32_t)(t.kc0 + min(kt * 8 + 2 * (pc & 3), t.kc_last & ~1));
                     dma2(p.a_scales, (uint32_t)(half ? arow[2 * j + 1] : arow[2 * j]) * (uint32_t)KS + kp,
                          sb + OFF_AS + (j * NW + wave) * 256);
                 } else {
@@ -360,12 +366,18 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
                     int32_t grp = t.n0 / 32 + wave;
                     if (grp > N32 / 32 - 1) grp = N32 / 32 - 1;    // groups past N are never stored
                     if (SA2) {
-                        const uint32_t kp = (uint32_t)(t.kc0 + min(kt * 8 + 2 * (pc & 3), t.kc_last - 1));
+                        const uint32_t kp = (uint32_t)(t.kc0 + min(kt * 8 + 2 * (pc & 3), t.kc_last & ~1));
                         dma2(bscales, (uint32_t)grp * (uint32_t)KS + kp, sb + OFF_BS + wave * 256);
                     } else {
                         const uint32_t ks = (uint32_t)(t.kc0 + min(kt * 8 + pc, t.kc_last));
                         dma1(bscales, (uint32_t)grp * (uint32_t)KS + ks, sb + OFF_BS + wave * 256);
                     }
+                } else if (SA2) {
+                    // as the A scales, for this thread's B rows
+                    const int half = pc >> 2;
+                    const uint32_t kp = (uint32_t)(t.kc0 + min(kt * 8 + 2 * (pc & 3), t.kc_last & ~1));
+                    dma2(bscales, (half ? nrow(2 * j + 1) : nrow(2 * j)) * (uint32_t)KS + kp,
+                         sb + OFF_BS + (j * NW + wave) * 256);
                 } else {
                     const uint32_t ks = (uint32_t)(t.kc0 + min(kt * 8 + pc, t.kc_last));
                     dma1(bscales, nrow(j) * (uint32_t)KS + ks, sb + OFF_BS + j * NT * 4 + wave * 256);
@@ -411,8 +423,8 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
     // K-quarter and packed only after its MFMAs, when the reads have landed
     // Scale dword p of a row holds chunk p (one byte moves) or chunks 2 p
     // and 2 p + 1 (pair moves, SA2): lane half h takes dwords 4 h .. 4 h + 3
-    // or 2 h, 2 h + 1.  2D B scales move in pairs along with the A scales.
-    constexpr bool SB2 = B2D && SA2;
+    // or 2 h, 2 h + 1.  B scales (1D or 2D) move in pairs along with A's.
+    constexpr bool SB2 = SA2;
     using ARaw = typename std::conditional<SA2, uint2, uint4>::type;
     using BRaw = typename std::conditional<SB2, uint2, uint4>::type;
     struct SclRaw { BRaw b[FN]; ARaw a[FM]; };
@@ -420,7 +432,11 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
         const uint8_t* sb = lds + buf * STAGE_BYTES;
 #pragma unroll
         for (int i = 0; i < FN; ++i)
+            // SB2, 1D: row r = wn WN + 32 i + lr was moved by wave (r % 64) / 8,
+            // lane 8 (r % 8) + 4 ((r / 64) % 2) of move r / 128 (as for A)
             s.b[i] = B2D ? *(const BRaw*)(sb + OFF_BS + (wn * FN + i) * 256 + lh * (int)sizeof(BRaw))
+                   : SB2 ? *(const BRaw*)(sb + OFF_BS + ((wn >> 1) * NW + 4 * i + (lr >> 3)) * 256 + (lr & 7) * 32 +
+                                          (wn & 1) * 16 + lh * 8)
                          : *(const BRaw*)(sb + OFF_BS + (wn * WN + i * 32 + lr) * 32 + lh * 16);
 #pragma unroll
         for (int i = 0; i < FM; ++i)
@@ -435,6 +451,16 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
     // upper half of its dword zero)
     auto pack4 = [](const uint4& v) { return v.x | (v.y << 8) | (v.z << 16) | (v.w << 24); };
     auto pack2 = [](const uint2& v) { return v.x | (v.y << 16); };
+    // groups along K with pair moves: a tile whose window starts one chunk
+    // before its group clears that chunk's scale byte (K-quarter 0, lane half
+    // 0) on both operands, so its products vanish as in the K tail
+    auto head_mask = [&](Scl& s, int32_t head) {
+        const uint32_t m = (head != 0 && lh == 0) ? 0xFFFFFF00u : 0xFFFFFFFFu;
+#pragma unroll
+        for (int i = 0; i < FN; ++i) s.b[i] &= m;
+#pragma unroll
+        for (int i = 0; i < FM; ++i) s.a[i] &= m;
+    };
     auto pack = [&](Scl& s, const SclRaw& r) {
 #pragma unroll
         for (int i = 0; i < FN; ++i) {
@@ -452,11 +478,11 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
     auto wait_all_but_one_stage = [] {
         if (B2D && SA2) asm volatile("s_waitcnt vmcnt(11)" ::: "memory");
         else if (B2D) asm volatile("s_waitcnt vmcnt(13)" ::: "memory");
-        else if (SA2) asm volatile("s_waitcnt vmcnt(14)" ::: "memory");
+        else if (SA2) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
         else asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
     };
     static_assert(dma_per_stage<true, true>() == 11 && dma_per_stage<true, false>() == 13 &&
-                  dma_per_stage<false, true>() == 14 && dma_per_stage<false, false>() == 16, "wait counts");
+                  dma_per_stage<false, true>() == 12 && dma_per_stage<false, false>() == 16, "wait counts");
     // one MFMA block, optionally followed by one piece of the next read
     auto mma1 = [&](const Frag& f, const Scl& s, int q, bool tail, int m) {
         const int i = m / FM, jj = m % FM;
@@ -683,6 +709,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
                 read_frag(f0, par, 0);
                 read_scl(nsc, par);
                 pack(sc, nsc);
+                if (GK && SA2) head_mask(sc, cur.head);
             }
             // Stage kt+1's DMA was issued at stage kt-1's barrier, into the
             // buffer stage kt-1 had finished reading; at stage kt's barrier it
@@ -735,6 +762,8 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
                 mma_rd(f0, sc, 3, LAST && kcl + 3 > cur.kc_last, buf ^ 1, 0,
                        [&](int m) { issue_slot(t2, r2, kt2, buf, m); });
                 pack(sc, nsc);
+                // the last stage packed the next tile's first scales (chained)
+                if (GK && SA2 && LAST) head_mask(sc, chain ? nxt.head : 0);
             };
             // At a chained tile's first barrier the previous tile's
             // EPI_STORES stores are the newest memory operations (without a
@@ -831,8 +860,7 @@ template <bool BF, bool QOUT>
 void launch_m(const GemmArgs& p, unsigned grid, hipStream_t s) {
     const dim3 gd(grid), bd(NT);
     const bool gather = p.a_row_index != nullptr;
-    const bool sa2 = (p.K / 32) % 2 == 0 && ((uintptr_t)p.a_scales & 1) == 0 &&
-                     (!p.b_scale_2d || ((uintptr_t)p.b_scales & 1) == 0);
+    const bool sa2 = (p.K / 32) % 2 == 0 && ((uintptr_t)p.a_scales & 1) == 0 && ((uintptr_t)p.b_scales & 1) == 0;
 #define MX_GEMM_LAUNCH(B2, GA, S2) hipLaunchKernelGGL((gemm_kernel<BF, B2, false, GA, S2, QOUT>), gd, bd, 0, s, p)
 #define MX_GEMM_S(B2, GA) \
     do { if (sa2) MX_GEMM_LAUNCH(B2, GA, true); else MX_GEMM_LAUNCH(B2, GA, false); } while (0)
@@ -864,8 +892,14 @@ extern "C" mx_status mx_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_sc
     (void)hipGetLastError();
     if (group_dim_k == 1) {
         const dim3 gd(grid), bd(NT);
-        if (ct == MX_BF16) hipLaunchKernelGGL((gemm_kernel<true, false, true, false, false, false>), gd, bd, 0, s, p);
-        else hipLaunchKernelGGL((gemm_kernel<false, false, true, false, false, false>), gd, bd, 0, s, p);
+        const bool sa2 = (p.K / 32) % 2 == 0 && ((uintptr_t)p.a_scales & 1) == 0 && ((uintptr_t)p.b_scales & 1) == 0;
+        if (ct == MX_BF16) {
+            if (sa2) hipLaunchKernelGGL((gemm_kernel<true, false, true, false, true, false>), gd, bd, 0, s, p);
+            else hipLaunchKernelGGL((gemm_kernel<true, false, true, false, false, false>), gd, bd, 0, s, p);
+        } else {
+            if (sa2) hipLaunchKernelGGL((gemm_kernel<false, false, true, false, true, false>), gd, bd, 0, s, p);
+            else hipLaunchKernelGGL((gemm_kernel<false, false, true, false, false, false>), gd, bd, 0, s, p);
+        }
     } else if (ct == MX_BF16) {
         launch_m<true, false>(p, grid, s);
     } else {

@@ -122,8 +122,11 @@ def rht(x, sign_mask: int, inverse: bool = False, out=None):
 
 def padded_capacity(rows: int, num_groups: int) -> int:
     """A token capacity that holds any grouping of `rows` tokens into
-    `num_groups` groups each padded to a multiple of 32."""
-    return (rows + 31 * num_groups + 31) // 32 * 32
+    `num_groups` groups each padded to a multiple of 32, rounded up to a
+    multiple of 256 tokens: every row of the column-wise codes is then a
+    whole number of 128-byte lines, and the number of 32-token blocks is even
+    (the grouped GEMM moves scale bytes in pairs)."""
+    return (rows + 31 * num_groups + 255) // 256 * 256
 
 
 def quantize_1d(x, block_axis: int = 1, group_offsets=None, kp: int = 0, use_rht: bool = False,

@@ -131,13 +131,19 @@ def test_fprop_many_groups_and_two_stage_tiles(K, b_2d):
             assert rel_fro(got[rows[sel, 1]], want[sel]) <= TOL, g
 
 
-def test_wgrad_many_groups():
+@pytest.mark.parametrize("even_total", [True, False])
+def test_wgrad_many_groups(even_total):
     """70 groups split K (the decode scans offsets 64 at a time), with empty
-    groups and groups of one to four 32-token blocks."""
+    groups and groups of one to four 32-token blocks, so many groups start at
+    an odd 32-token block.  With an even number of blocks in K the scales
+    move in pairs and a tile's K window may start one block before its group;
+    with an odd number they move one byte at a time."""
     import torch
     rng = np.random.default_rng(70)
     counts = [int(v) * 32 for v in rng.integers(0, 5, 70)]
     counts[10] = 640
+    if (sum(counts) // 32) % 2 != (0 if even_total else 1):
+        counts[-1] += 32
     M, N = 64, 96
     off = synth.offsets_from_counts(counts)
     Kt = int(off[-1])
