@@ -77,13 +77,20 @@ class Step:
         self.mx, self.torch, self.inp = mx, torch, inp
         u8, bf, f32 = torch.uint8, torch.bfloat16, torch.float32
         z = lambda *s, dt=u8: torch.empty(*s, dtype=dt, device=dev)  # noqa: E731
+
+        def zc(*s):
+            # code rows padded to whole 128-byte lines (the GEMM reads each
+            # operand row as whole lines); a view of the row's bytes
+            return z(*s[:-1], (s[-1] + 127) // 128 * 128)[..., :s[-1]]
+
         self.kp = mx.padded_capacity(ROWS, E)
         self.mask = mx.rht_sign_mask(5)
         self.b = dict(
-            w1c=z(E, D, F2 // 2), w1s=z(E, D // 32, F2 // 32), w1tc=z(E, F2, D // 2), w1ts=z(E, F2 // 32, D // 32),
-            w2c=z(E, D, D // 2), w2s=z(E, D // 32, D // 32), w2tc=z(E, D, D // 2), w2ts=z(E, D // 32, D // 32),
-            xc=z(T, D // 2), xs=z(T, D // 32), hc=z(ROWS, D // 2), hs=z(ROWS, D // 32),
-            g2c=z(ROWS, D // 2), g2s=z(ROWS, D // 32), g1c=z(ROWS, F2 // 2), g1s=z(ROWS, F2 // 32),
+            w1c=zc(E, D, F2 // 2), w1s=z(E, D // 32, F2 // 32), w1tc=zc(E, F2, D // 2),
+            w1ts=z(E, F2 // 32, D // 32),
+            w2c=zc(E, D, D // 2), w2s=z(E, D // 32, D // 32), w2tc=zc(E, D, D // 2), w2ts=z(E, D // 32, D // 32),
+            xc=zc(T, D // 2), xs=z(T, D // 32), hc=zc(ROWS, D // 2), hs=z(ROWS, D // 32),
+            g2c=zc(ROWS, D // 2), g2s=z(ROWS, D // 32), g1c=zc(ROWS, F2 // 2), g1s=z(ROWS, F2 // 32),
             hTc=z(D, self.kp // 2), hTs=z(D, self.kp // 32), g2Tc=z(D, self.kp // 2), g2Ts=z(D, self.kp // 32),
             xTc=z(D, self.kp // 2), xTs=z(D, self.kp // 32), g1Tc=z(F2, self.kp // 2), g1Ts=z(F2, self.kp // 32),
             Y1=z(ROWS, F2, dt=bf), Y2=z(ROWS, D, dt=bf), dh=z(ROWS, D, dt=bf), dX=z(ROWS, D, dt=bf),

@@ -94,7 +94,9 @@ mx_status mx_rht(const void* x, mx_dtype xt, float* y, int64_t rows, int64_t col
  * activations and gradients).
  *
  * block_axis = 1 (row-wise): x [rows x cols], cols % 32 == 0.  Blocks of 32
- *   run along cols.  codes [rows x cols/2], scales [rows x cols/32].
+ *   run along cols.  codes [rows x cols/2] with rows codes_ld bytes apart
+ *   (0 = cols/2; else at least cols/2 and a multiple of 16, so the rows can
+ *   be padded to whole 128-byte lines for the GEMM), scales [rows x cols/32].
  *   group_offsets and row_index must be NULL, num_groups 0, kp 0 (a
  *   row_index here returns MX_ERR_UNSUPPORTED).
  * block_axis = 0 (column-wise, grouped): the rows of x (tokens) are split
@@ -106,7 +108,7 @@ mx_status mx_rht(const void* x, mx_dtype xt, float* y, int64_t rows, int64_t col
  *   of group g.  codes [cols x kp/2], scales [cols x kp/32].  kp (a multiple
  *   of 32) is the capacity of that axis; the caller guarantees
  *   kp >= sum_g ceil32(n_g) (rows + 31 * num_groups always suffices).
- *   Positions beyond the padded total are not written.
+ *   Positions beyond the padded total are not written.  codes_ld: 0 or kp/2.
  *   row_index (optional, DEVICE int32[rows]): the rows are gathered, so the
  *   token at grouped position p is x[row_index[p]] (x itself may have any
  *   number of rows; every index must be a valid row of it).  This fuses the
@@ -123,7 +125,7 @@ mx_status mx_quantize_1d(const void* x, mx_dtype xt, int64_t rows, int64_t cols,
                          int block_axis, const int32_t* group_offsets, int32_t num_groups,
                          int64_t kp, const int32_t* row_index, int use_rht, uint32_t sign_mask, mx_round rnd,
                          uint64_t seed, uint32_t stream_id, uint64_t index_base,
-                         uint8_t* codes, uint8_t* scales, mx_stream stream);
+                         uint8_t* codes, int64_t codes_ld, uint8_t* scales, mx_stream stream);
 
 /* 32x32 MXFP4 quantization, round to nearest even (the "2D" half of the
  * hybrid scheme, used for weights).  w: batch x [rows x cols], rows % 32 ==
@@ -132,44 +134,53 @@ mx_status mx_quantize_1d(const void* x, mx_dtype xt, int64_t rows, int64_t cols,
  * transposed layout (codes_t [batch x cols x rows/2], scales_t
  * [batch x cols/32 x rows/32]); a 32x32 block has the same scale and codes in
  * both, so the transposed pair is exactly the quantization of w^T.  Either
- * pair may be NULL (not both).  Pages: "What ALTO Actually Does" (UE8M0 per
- * block), Abstract (hybrid 1D/2D). */
+ * pair may be NULL (not both).  codes_ld / codes_t_ld: bytes from one code
+ * row to the next in each layout (0 = cols/2 and rows/2; else at least that
+ * and a multiple of 16); a batch entry spans rows (cols) such rows.
+ * Pages: "What ALTO Actually Does" (UE8M0 per block), Abstract (hybrid
+ * 1D/2D). */
 mx_status mx_quantize_2d(const void* w, mx_dtype wt, int64_t batch, int64_t rows, int64_t cols,
-                         uint8_t* codes, uint8_t* scales, uint8_t* codes_t, uint8_t* scales_t,
-                         mx_stream stream);
+                         uint8_t* codes, int64_t codes_ld, uint8_t* scales, uint8_t* codes_t,
+                         int64_t codes_t_ld, uint8_t* scales_t, mx_stream stream);
 
 /* Exact decode: y = (-1)^s * E2M1[m] * 2^(byte - 127).
- * codes batch x [rows x cols/2]; block_rows = 1 (scales [rows x cols/32]) or
+ * codes batch x [rows x cols/2], rows codes_ld bytes apart (0 = cols/2;
+ * else at least that and a multiple of 16); block_rows = 1 (scales [rows x cols/32]) or
  * 32 (scales [rows/32 x cols/32], rows % 32 == 0); y batch x [rows x cols],
  * yt fp32 or bf16 (every decoded value is exact in both, except 6*2^(>=127)
  * which overflows to Inf).  cols % 32 == 0. */
-mx_status mx_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t batch, int64_t rows,
+mx_status mx_dequantize(const uint8_t* codes, int64_t codes_ld, const uint8_t* scales, int64_t batch, int64_t rows,
                         int64_t cols, int block_rows, void* y, mx_dtype yt, mx_stream stream);
 
 /* Grouped MXFP4 GEMM with FP32 accumulation: per group,
  *   C = alpha * deq(A) . deq(B)^T,
  * both operands K-contiguous (codes [. x K/2], scales [. x K/32]).
  * The GEMM only ever sees the quantized operands ("What ALTO Actually Does").
+ * a_ld, b_ld: bytes from one code row of A (of B) to the next; 0 means K/2
+ * (contiguous rows).  Otherwise at least K/2 and a multiple of 16.  Rows
+ * padded to a multiple of 128 bytes are read as whole cache lines, which is
+ * markedly faster when K/2 is not a multiple of 128.  Scales are always
+ * contiguous.
  *
  * group_dim_k = 0 (forward / data gradient): groups split the M rows of C by
  *   group_offsets (DEVICE int32[num_groups+1], [0] = 0, [num_groups] = M).
  *   Row m of group g reads A row a_row_index[m] (DEVICE int32[M]; NULL = m)
- *   and multiplies B_g = b_codes + g*N*K/2 ([N x K]); b_scale_2d selects 2D
+ *   and multiplies B_g = b_codes + g*N*b_ld ([N x K]); b_scale_2d selects 2D
  *   scales [N/32 x K/32] per group (else 1D [N x K/32]).  C [M x N].
  * group_dim_k = 1 (weight gradient): groups split K by group_offsets (DEVICE,
  *   multiples of 32, [num_groups] <= K); A [M x K], B [N x K], 1D scales;
  *   C [num_groups x M x N]; a group with an empty K range writes zeros.
  * K % 32 == 0, N % 32 == 0, M >= 0; ct = MX_BF16 (round to nearest even) or
  * MX_F32.  Code and C pointers 16-byte aligned.  The kernel addresses each
- * operand with 32-bit byte offsets: N*K/2 (one B group) and, without a row
- * index, M*K/2 must not exceed 4 GiB - 1 (else MX_ERR_SHAPE); with a row
+ * operand with 32-bit byte offsets: N*b_ld (one B group) and, without a row
+ * index, M*a_ld must not exceed 4 GiB - 1 (else MX_ERR_SHAPE); with a row
  * index the indexed rows must lie within the first 4 GiB of a_codes.
- * Errors: MX_ERR_DTYPE (ct), MX_ERR_SHAPE (sizes, num_groups < 1,
- * group_dim_k), MX_ERR_UNSUPPORTED (group_dim_k = 1 with 2D B scales or a row
+ * Errors: MX_ERR_DTYPE (ct), MX_ERR_SHAPE (sizes, row pitches, num_groups
+ * < 1, group_dim_k), MX_ERR_UNSUPPORTED (group_dim_k = 1 with 2D B scales or a row
  * index), MX_ERR_NULL, MX_ERR_ALIGN, MX_ERR_LAUNCH.  M == 0 launches nothing. */
-mx_status mx_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
+mx_status mx_grouped_gemm(const uint8_t* a_codes, int64_t a_ld, const uint8_t* a_scales,
                           const int32_t* a_row_index,
-                          const uint8_t* b_codes, const uint8_t* b_scales, int b_scale_2d,
+                          const uint8_t* b_codes, int64_t b_ld, const uint8_t* b_scales, int b_scale_2d,
                           const int32_t* group_offsets, int32_t num_groups, int group_dim_k,
                           int64_t M, int64_t N, int64_t K, float alpha,
                           void* c, mx_dtype ct, mx_stream stream);
@@ -184,16 +195,20 @@ mx_status mx_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
  * memory traffic as well as compute ("What ALTO Actually Does", news digest
  * "AMD's ALTO Gets 4-Bit MoE Training to Within 0.007 of BF16").
  * c: bf16 [M x N] as in mx_grouped_gemm, or NULL to write only the MXFP4
- * output.  c (when given) and c_codes 16-byte aligned; c_scales any.
+ * output.  c_codes_ld: the code rows' pitch in bytes (0 = N/2, else >= N/2
+ * and a multiple of 16); the bytes between N/2 and the pitch are not
+ * written.  c (when given) and c_codes 16-byte aligned; c_scales any.
  * Arguments and errors otherwise as mx_grouped_gemm; additionally
- * MX_ERR_NULL (c_codes or c_scales NULL) and MX_ERR_SHAPE (M * N / 2 above
- * 4 GiB - 1). */
-mx_status mx_grouped_gemm_q(const uint8_t* a_codes, const uint8_t* a_scales,
+ * MX_ERR_NULL (c_codes or c_scales NULL), MX_ERR_SHAPE (c_codes_ld below
+ * N/2, or M * c_codes_ld above 4 GiB - 1) and MX_ERR_ALIGN (c_codes_ld not
+ * a multiple of 16). */
+mx_status mx_grouped_gemm_q(const uint8_t* a_codes, int64_t a_ld, const uint8_t* a_scales,
                             const int32_t* a_row_index,
-                            const uint8_t* b_codes, const uint8_t* b_scales, int b_scale_2d,
+                            const uint8_t* b_codes, int64_t b_ld, const uint8_t* b_scales, int b_scale_2d,
                             const int32_t* group_offsets, int32_t num_groups,
                             int64_t M, int64_t N, int64_t K, float alpha,
-                            void* c, uint8_t* c_codes, uint8_t* c_scales, mx_stream stream);
+                            void* c, uint8_t* c_codes, int64_t c_codes_ld, uint8_t* c_scales,
+                            mx_stream stream);
 
 #ifdef __cplusplus
 }

@@ -78,6 +78,7 @@ struct GemmArgs {
     const int32_t* off;
     void* c;
     int64_t M, N, K;
+    int64_t lda, ldb;    // bytes from one code row to the next (A, B)
     int32_t G;
     int32_t b_scale_2d;
     int32_t group_dim_k;
@@ -85,8 +86,9 @@ struct GemmArgs {
     int32_t tiles_m;     // group_dim_k = 1: tiles along M per group
     float alpha;
     int64_t tiles;       // size of the tile-id space (a multiple of XCDS * XCD_BLOCK)
-    uint8_t* qcodes;     // QOUT: row-wise MXFP4 of the bf16 output, codes [M x N/2]
+    uint8_t* qcodes;     // QOUT: row-wise MXFP4 of the bf16 output, codes [M rows of qld bytes]
     uint8_t* qscales;    //       and scales [M x N/32]
+    int64_t qld;         //       the code rows' pitch in bytes (>= N/2)
 };
 
 constexpr int BM = 256, BN = 256;
@@ -162,7 +164,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 2, wn = wave & 3;
-    const int64_t KB = p.K / 2;      // code bytes per operand row
+    const int64_t KBA = p.lda, KBB = p.ldb;   // code row pitch of A and B (>= K / 2 bytes)
     const int64_t KS = p.K / 32;     // scale bytes per operand row
 
     // ---------------- group table ----------------
@@ -323,7 +325,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
         const uint8_t* bcodes = p.b_codes;
         const uint8_t* bscales = p.b_scales;
         if (!GK) {
-            bcodes += (int64_t)t.g * p.N * KB;
+            bcodes += (int64_t)t.g * p.N * KBB;
             bscales += (int64_t)t.g * (B2D ? (p.N / 32) * KS : p.N * KS);
         }
         auto nrow = [&](int jj) {
@@ -335,11 +337,11 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
             if (part < NJ) {
                 const int jj = part;
                 const uint32_t kc = (uint32_t)(t.kc0 + min(kt * 8 + a_chunk, t.kc_last));
-                dma16(p.a_codes, (uint32_t)arow[jj] * (uint32_t)KB + kc * 16, sb + OFF_A + jj * NT * 16 + wave * 1024);
+                dma16(p.a_codes, (uint32_t)arow[jj] * (uint32_t)KBA + kc * 16, sb + OFF_A + jj * NT * 16 + wave * 1024);
             } else if (part < 2 * NJ) {
                 const int jj = part - NJ;
                 const uint32_t kc = (uint32_t)(t.kc0 + min(kt * 8 + a_chunk, t.kc_last));
-                dma16(bcodes, nrow(jj) * (uint32_t)KB + kc * 16, sb + OFF_B + jj * NT * 16 + wave * 1024);
+                dma16(bcodes, nrow(jj) * (uint32_t)KBB + kc * 16, sb + OFF_B + jj * NT * 16 + wave * 1024);
             } else if (part < 2 * NJ + NA_S) {
                 const int j = part - 2 * NJ;
                 if (SA2) {
@@ -555,10 +557,10 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
         // QOUT: the tile's rows of the code and scale outputs
         __amdgpu_buffer_rsrc_t qc_rsrc = rsrc, qs_rsrc = rsrc;
         if (QOUT) {
-            uint8_t* qc = p.qcodes + uniform64((int64_t)t.m0 * (p.N / 2));
+            uint8_t* qc = p.qcodes + uniform64((int64_t)t.m0 * p.qld);
             uint8_t* qs = p.qscales + uniform64((int64_t)t.m0 * (p.N / 32));
             qc_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-                qc, (short)0, __builtin_amdgcn_readfirstlane((t.m1 - t.m0) * (N32 / 2)), 0x00020000);
+                qc, (short)0, __builtin_amdgcn_readfirstlane((t.m1 - t.m0) * (int32_t)p.qld), 0x00020000);
             qs_rsrc = __builtin_amdgcn_make_buffer_rsrc(
                 qs, (short)0, __builtin_amdgcn_readfirstlane((t.m1 - t.m0) * (N32 / 32)), 0x00020000);
         }
@@ -625,7 +627,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
                         typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
                         __builtin_amdgcn_raw_buffer_store_b64(
                             (u32x2){o0, o1}, qc_rsrc,
-                            ok ? (uint32_t)(qrow * (N32 / 2) + qcol / 2 + 8 * elh) : 0x80000000u, 0, 0);
+                            ok ? (uint32_t)(qrow * (int32_t)p.qld + qcol / 2 + 8 * elh) : 0x80000000u, 0, 0);
                         __builtin_amdgcn_raw_buffer_store_b8(
                             (uint8_t)byte, qs_rsrc,
                             ok && elh == 0 ? (uint32_t)(qrow * (N32 / 32) + qcol / 32) : 0x80000000u, 0, 0);
@@ -797,11 +799,16 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
 inline bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 
 // Validation shared by both entry points; fills everything but the outputs.
-mx_status gemm_setup(const uint8_t* a_codes, const uint8_t* a_scales, const int32_t* a_row_index,
-                            const uint8_t* b_codes, const uint8_t* b_scales, int b_scale_2d,
+mx_status gemm_setup(const uint8_t* a_codes, int64_t a_ld, const uint8_t* a_scales, const int32_t* a_row_index,
+                            const uint8_t* b_codes, int64_t b_ld, const uint8_t* b_scales, int b_scale_2d,
                             const int32_t* group_offsets, int32_t num_groups, int group_dim_k, int64_t M,
                             int64_t N, int64_t K, float alpha, GemmArgs& p, unsigned& grid) {
     if (M < 0 || N <= 0 || K <= 0 || N % 32 || K % 32) return MX_ERR_SHAPE;
+    // code row pitch: 0 = K / 2 (contiguous rows); else at least K / 2 and
+    // a multiple of 16 (every row starts 16-byte aligned)
+    if (a_ld == 0) a_ld = K / 2;
+    if (b_ld == 0) b_ld = K / 2;
+    if (a_ld < K / 2 || b_ld < K / 2 || a_ld % 16 || b_ld % 16) return MX_ERR_SHAPE;
     if (num_groups < 1) return MX_ERR_SHAPE;
     if (group_dim_k != 0 && group_dim_k != 1) return MX_ERR_SHAPE;
     if (group_dim_k == 1 && (b_scale_2d || a_row_index)) return MX_ERR_UNSUPPORTED;
@@ -813,8 +820,8 @@ mx_status gemm_setup(const uint8_t* a_codes, const uint8_t* a_scales, const int3
     // the B group's) base: each must span at most 4 GiB.  With a row index
     // the caller keeps the indexed rows within that range.
     const int64_t lim = 0xFFFFFFFFLL;
-    if (N * (K / 2) > lim) return MX_ERR_SHAPE;
-    if (!a_row_index && M * (K / 2) > lim) return MX_ERR_SHAPE;
+    if (N * b_ld > lim) return MX_ERR_SHAPE;
+    if (!a_row_index && M * a_ld > lim) return MX_ERR_SHAPE;
     // tile coordinates are 32-bit
     if (M > 0x7FFFFF00LL || N > 0x7FFFFF00LL || K > 0x7FFFFF00LL) return MX_ERR_SHAPE;
 
@@ -828,6 +835,8 @@ mx_status gemm_setup(const uint8_t* a_codes, const uint8_t* a_scales, const int3
     p.M = M;
     p.N = N;
     p.K = K;
+    p.lda = a_ld;
+    p.ldb = b_ld;
     p.G = num_groups;
     p.b_scale_2d = b_scale_2d ? 1 : 0;
     p.group_dim_k = group_dim_k;
@@ -875,15 +884,16 @@ void launch_m(const GemmArgs& p, unsigned grid, hipStream_t s) {
 
 }  // namespace
 
-extern "C" mx_status mx_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const int32_t* a_row_index,
-                                     const uint8_t* b_codes, const uint8_t* b_scales, int b_scale_2d,
+extern "C" mx_status mx_grouped_gemm(const uint8_t* a_codes, int64_t a_ld, const uint8_t* a_scales,
+                                     const int32_t* a_row_index, const uint8_t* b_codes, int64_t b_ld,
+                                     const uint8_t* b_scales, int b_scale_2d,
                                      const int32_t* group_offsets, int32_t num_groups, int group_dim_k, int64_t M,
                                      int64_t N, int64_t K, float alpha, void* c, mx_dtype ct, mx_stream stream) {
     if (ct != MX_F32 && ct != MX_BF16) return MX_ERR_DTYPE;
     GemmArgs p;
     unsigned grid = 0;
-    const mx_status st = gemm_setup(a_codes, a_scales, a_row_index, b_codes, b_scales, b_scale_2d, group_offsets,
-                                    num_groups, group_dim_k, M, N, K, alpha, p, grid);
+    const mx_status st = gemm_setup(a_codes, a_ld, a_scales, a_row_index, b_codes, b_ld, b_scales, b_scale_2d,
+                                    group_offsets, num_groups, group_dim_k, M, N, K, alpha, p, grid);
     if (st != MX_OK || M == 0) return st;
     if (!c) return MX_ERR_NULL;
     if (!aligned16(c)) return MX_ERR_ALIGN;
@@ -908,22 +918,26 @@ extern "C" mx_status mx_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_sc
     return hipGetLastError() == hipSuccess ? MX_OK : MX_ERR_LAUNCH;
 }
 
-extern "C" mx_status mx_grouped_gemm_q(const uint8_t* a_codes, const uint8_t* a_scales, const int32_t* a_row_index,
-                                       const uint8_t* b_codes, const uint8_t* b_scales, int b_scale_2d,
+extern "C" mx_status mx_grouped_gemm_q(const uint8_t* a_codes, int64_t a_ld, const uint8_t* a_scales,
+                                       const int32_t* a_row_index, const uint8_t* b_codes, int64_t b_ld,
+                                       const uint8_t* b_scales, int b_scale_2d,
                                        const int32_t* group_offsets, int32_t num_groups, int64_t M, int64_t N,
-                                       int64_t K, float alpha, void* c, uint8_t* c_codes, uint8_t* c_scales,
-                                       mx_stream stream) {
+                                       int64_t K, float alpha, void* c, uint8_t* c_codes, int64_t c_codes_ld,
+                                       uint8_t* c_scales, mx_stream stream) {
     GemmArgs p;
     unsigned grid = 0;
-    const mx_status st = gemm_setup(a_codes, a_scales, a_row_index, b_codes, b_scales, b_scale_2d, group_offsets,
-                                    num_groups, 0, M, N, K, alpha, p, grid);
+    const mx_status st = gemm_setup(a_codes, a_ld, a_scales, a_row_index, b_codes, b_ld, b_scales, b_scale_2d,
+                                    group_offsets, num_groups, 0, M, N, K, alpha, p, grid);
     if (st != MX_OK || M == 0) return st;
     if (!c_codes || !c_scales) return MX_ERR_NULL;
-    if ((c && !aligned16(c)) || !aligned16(c_codes)) return MX_ERR_ALIGN;
+    if (c_codes_ld == 0) c_codes_ld = N / 2;
+    if (c_codes_ld < N / 2) return MX_ERR_SHAPE;
+    if ((c && !aligned16(c)) || !aligned16(c_codes) || c_codes_ld % 16) return MX_ERR_ALIGN;
     // the code and scale outputs are addressed by 32-bit offsets per tile
-    if (M * (N / 2) > 0xFFFFFFFFLL) return MX_ERR_SHAPE;
+    if (M * c_codes_ld > 0xFFFFFFFFLL) return MX_ERR_SHAPE;
     p.c = c;
     p.qcodes = c_codes;
+    p.qld = c_codes_ld;
     p.qscales = c_scales;
     hipStream_t s = (hipStream_t)stream;
     (void)hipGetLastError();

@@ -32,12 +32,20 @@ using namespace mx;
 // ===========================================================================
 constexpr int ROW_UNROLL = 4;   // blocks per quad per loop trip (loads in flight)
 
-template <bool BF16, bool RHT, bool SR>
-__global__ __launch_bounds__(256) void q1d_row_kernel(const void* __restrict__ x, int64_t nblocks,
-                                                      uint32_t mask, uint32_t k0, uint32_t k1,
-                                                      uint32_t stream_id, uint64_t index_base,
-                                                      uint8_t* __restrict__ codes,
-                                                      uint8_t* __restrict__ scales) {
+// Code rows may be padded (PITCH): block blk is block b of row r with
+// blk = r * bpr + b, and its 16 code bytes go to codes + r * ld + 16 b
+// = codes + 16 blk + r * pad, pad = ld - 16 bpr.
+struct RowPitch {
+    int64_t bpr;        // blocks per row (cols / 32)
+    double inv_bpr;     // 1 / bpr
+    int64_t pad;        // bytes between the end of a code row and the next row
+};
+
+template <bool BF16, bool RHT, bool SR, bool PITCH>
+__device__ __forceinline__ void q1d_row_body(const void* __restrict__ x, int64_t nblocks, uint32_t mask,
+                                             uint32_t k0, uint32_t k1, uint32_t stream_id,
+                                             uint64_t index_base, uint8_t* __restrict__ codes,
+                                             uint8_t* __restrict__ scales, RowPitch rp) {
     const int lane = threadIdx.x & 63;
     const int q = lane & 3;
     const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
@@ -73,9 +81,35 @@ __global__ __launch_bounds__(256) void q1d_row_kernel(const void* __restrict__ x
                 for (int e = 0; e < 8; ++e) v[u][e] = 0.0f;
             }
         }
+        // PITCH: the quad's first block split into (row, b) once per trip,
+        // r = floor(blk / bpr) from the double quotient, which is within one
+        // of it for any index below 2^53, and one correction step; the later
+        // blocks step b by 16 and carry into the row
+        int64_t pb = 0, pofs = 0;
+        if (PITCH) {
+            const int64_t blk = base + (lane >> 2);
+            int64_t row = (int64_t)((double)blk * rp.inv_bpr);
+            pb = blk - row * rp.bpr;
+            if (pb < 0) {
+                --row;
+                pb += rp.bpr;
+            } else if (pb >= rp.bpr) {
+                ++row;
+                pb -= rp.bpr;
+            }
+            pofs = blk * 16 + row * rp.pad;
+        }
 #pragma unroll
         for (int u = 0; u < ROW_UNROLL; ++u) {
             const int64_t blk = base + u * 16 + (lane >> 2);
+            if (PITCH && u > 0) {
+                pb += 16;
+                pofs += 256;
+                while (pb >= rp.bpr) {
+                    pb -= rp.bpr;
+                    pofs += rp.pad;
+                }
+            }
             float* t = v[u];
             if (RHT) {
 #pragma unroll
@@ -98,11 +132,31 @@ __global__ __launch_bounds__(256) void q1d_row_kernel(const void* __restrict__ x
             }
             if (byte == 0xFFu) packed = 0;   // non-finite block: codes are 0
             if (blk < nblocks) {
-                *((uint32_t*)(codes + blk * 16) + q) = packed;
+                const int64_t cofs = PITCH ? pofs : blk * 16;
+                *((uint32_t*)(codes + cofs) + q) = packed;
                 if (q == 0) scales[blk] = (uint8_t)byte;
             }
         }
     }
+}
+
+template <bool BF16, bool RHT, bool SR>
+__global__ __launch_bounds__(256) void q1d_row_kernel(const void* __restrict__ x, int64_t nblocks,
+                                                      uint32_t mask, uint32_t k0, uint32_t k1,
+                                                      uint32_t stream_id, uint64_t index_base,
+                                                      uint8_t* __restrict__ codes,
+                                                      uint8_t* __restrict__ scales, RowPitch rp) {
+    q1d_row_body<BF16, RHT, SR, false>(x, nblocks, mask, k0, k1, stream_id, index_base, codes, scales, rp);
+}
+
+// the same with padded code rows
+template <bool BF16, bool RHT, bool SR>
+__global__ __launch_bounds__(256) void q1d_row_kernel_p(const void* __restrict__ x, int64_t nblocks,
+                                                        uint32_t mask, uint32_t k0, uint32_t k1,
+                                                        uint32_t stream_id, uint64_t index_base,
+                                                        uint8_t* __restrict__ codes,
+                                                        uint8_t* __restrict__ scales, RowPitch rp) {
+    q1d_row_body<BF16, RHT, SR, true>(x, nblocks, mask, k0, k1, stream_id, index_base, codes, scales, rp);
 }
 
 // ===========================================================================
@@ -477,8 +531,10 @@ __device__ __forceinline__ void transpose_nibbles_8x8(uint32_t* a) {
 template <bool BF16>
 __global__ __launch_bounds__(256) void q2d_kernel(const void* __restrict__ w, int64_t rows, int64_t cols,
                                                   int64_t col_strips, int64_t row_strips, int64_t nsuper,
-                                                  uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
-                                                  uint8_t* __restrict__ codes_t, uint8_t* __restrict__ scales_t) {
+                                                  uint8_t* __restrict__ codes, int64_t ld,
+                                                  uint8_t* __restrict__ scales,
+                                                  uint8_t* __restrict__ codes_t, int64_t ld_t,
+                                                  uint8_t* __restrict__ scales_t) {
     __shared__ uint32_t wave_amax[4][8];
     __shared__ uint8_t tile_scale[Q2_TR][8];
     // [tile row][tile][row] 16 bytes of row codes; each tile row padded by one
@@ -553,7 +609,7 @@ __global__ __launch_bounds__(256) void q2d_kernel(const void* __restrict__ w, in
 #pragma unroll
             for (int k = 0; k < 4; ++k) cw[k] = cvt8_rne(v + 8 * k, sc) & keep;
             if (valid && codes)
-                store_b128(codes + grow * (cols >> 1) + tile * 16, make_uint4(cw[0], cw[1], cw[2], cw[3]));
+                store_b128(codes + grow * ld + tile * 16, make_uint4(cw[0], cw[1], cw[2], cw[3]));
             if (valid && r == 0 && scales) scales[(bt * row_tiles + tr) * tiles_per_row + tile] = (uint8_t)byte;
             tcodes[ts * TC_TS + j * 32 + r] = make_uint4(cw[0], cw[1], cw[2], cw[3]);
         }
@@ -581,7 +637,7 @@ __global__ __launch_bounds__(256) void q2d_kernel(const void* __restrict__ w, in
 #pragma unroll
                 for (int c = 0; c < 8; ++c) {
                     const int64_t col = tile2 * 32 + 8 * w + c;
-                    store_b128(codes_t + (bt * cols + col) * (rows >> 1) + (tr0 + ts) * 16,
+                    store_b128(codes_t + (bt * cols + col) * ld_t + (tr0 + ts) * 16,
                                make_uint4(out[c][0], out[c][1], out[c][2], out[c][3]));
                 }
             }
@@ -602,7 +658,8 @@ __global__ __launch_bounds__(256) void q2d_kernel(const void* __restrict__ w, in
 // Dequantize: a lane decodes 8 elements (one dword of codes).
 // ===========================================================================
 template <bool OUT_BF16, int BLOCK_ROWS>
-__global__ __launch_bounds__(256) void deq_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
+__global__ __launch_bounds__(256) void deq_kernel(const uint8_t* __restrict__ codes, int64_t ld,
+                                                  const uint8_t* __restrict__ scales,
                                                   int64_t rows, int64_t cols, int64_t nunits,
                                                   void* __restrict__ y) {
     const int64_t units_per_row = cols >> 3;
@@ -613,7 +670,7 @@ __global__ __launch_bounds__(256) void deq_kernel(const uint8_t* __restrict__ co
         const int64_t cu = u - grow * units_per_row;
         const int64_t bt = grow / rows;
         const int64_t r = grow - bt * rows;
-        const uint32_t cw = *((const uint32_t*)codes + u);
+        const uint32_t cw = *(const uint32_t*)(codes + grow * ld + cu * 4);
         const uint8_t sb = scales[(bt * srows + r / BLOCK_ROWS) * (cols >> 5) + (cu >> 2)];
         const float sc = scale_operand(sb);
         float f[8];
@@ -751,7 +808,8 @@ mx_status mx_quantize_1d(const void* x, mx_dtype xt, int64_t rows, int64_t cols,
                          const int32_t* group_offsets, int32_t num_groups, int64_t kp,
                          const int32_t* row_index, int use_rht,
                          uint32_t sign_mask, mx_round rnd, uint64_t seed, uint32_t stream_id,
-                         uint64_t index_base, uint8_t* codes, uint8_t* scales, mx_stream stream) {
+                         uint64_t index_base, uint8_t* codes, int64_t codes_ld, uint8_t* scales,
+                         mx_stream stream) {
     if (xt != MX_F32 && xt != MX_BF16) return MX_ERR_DTYPE;
     if (rnd != MX_RNE && rnd != MX_SR) return MX_ERR_UNSUPPORTED;
     if (rows < 0 || cols <= 0) return MX_ERR_SHAPE;
@@ -766,16 +824,26 @@ mx_status mx_quantize_1d(const void* x, mx_dtype xt, int64_t rows, int64_t cols,
         if (rows == 0) return MX_OK;
         if (!x || !codes || !scales) return MX_ERR_NULL;
         if (!aligned16(x) || !aligned16(codes)) return MX_ERR_ALIGN;
+        // code row pitch: 0 = cols / 2; else at least that and a multiple of 16
+        const int64_t ld = codes_ld ? codes_ld : cols / 2;
+        if (ld < cols / 2 || ld % 16) return MX_ERR_SHAPE;
         const int64_t nblocks = rows * (cols / 32);
         const int grid = grid_for(nblocks, 4 * 16 * ROW_UNROLL);
+        const RowPitch rp{cols / 32, 1.0 / (double)(cols / 32), ld - cols / 2};
         (void)hipGetLastError();
-        MX_DISPATCH3(q1d_row_kernel, bf, rh, sr, dim3(grid), s, x, nblocks, sign_mask, k0, k1, stream_id,
-                     index_base, codes, scales);
+        if (ld == cols / 2) {
+            MX_DISPATCH3(q1d_row_kernel, bf, rh, sr, dim3(grid), s, x, nblocks, sign_mask, k0, k1, stream_id,
+                         index_base, codes, scales, rp);
+        } else {
+            MX_DISPATCH3(q1d_row_kernel_p, bf, rh, sr, dim3(grid), s, x, nblocks, sign_mask, k0, k1, stream_id,
+                         index_base, codes, scales, rp);
+        }
         return launched();
     }
     if (block_axis != 0) return MX_ERR_SHAPE;
     if (num_groups < 1 || num_groups > COL_MAX_GROUPS) return MX_ERR_SHAPE;
     if (kp < 0 || kp % 32) return MX_ERR_SHAPE;
+    if (codes_ld != 0 && codes_ld != kp / 2) return MX_ERR_SHAPE;   // the layout's rows are kp / 2 bytes
     if (!group_offsets) return MX_ERR_NULL;
     if (kp == 0 || rows == 0) return MX_OK;
     if (!x || !codes || !scales) return MX_ERR_NULL;
@@ -809,7 +877,8 @@ mx_status mx_quantize_1d(const void* x, mx_dtype xt, int64_t rows, int64_t cols,
 }
 
 mx_status mx_quantize_2d(const void* w, mx_dtype wt, int64_t batch, int64_t rows, int64_t cols, uint8_t* codes,
-                         uint8_t* scales, uint8_t* codes_t, uint8_t* scales_t, mx_stream stream) {
+                         int64_t codes_ld, uint8_t* scales, uint8_t* codes_t, int64_t codes_t_ld,
+                         uint8_t* scales_t, mx_stream stream) {
     if (wt != MX_F32 && wt != MX_BF16) return MX_ERR_DTYPE;
     if (batch < 0 || rows < 0 || cols < 0 || rows % 32 || cols % 32) return MX_ERR_SHAPE;
     if ((codes == nullptr) != (scales == nullptr)) return MX_ERR_NULL;
@@ -818,6 +887,10 @@ mx_status mx_quantize_2d(const void* w, mx_dtype wt, int64_t batch, int64_t rows
     if (batch == 0 || rows == 0 || cols == 0) return MX_OK;
     if (!w) return MX_ERR_NULL;
     if (!aligned16(w) || (codes && !aligned16(codes)) || (codes_t && !aligned16(codes_t))) return MX_ERR_ALIGN;
+    // code row pitches: 0 = contiguous rows (cols / 2, rows / 2 bytes); else
+    // at least that and a multiple of 16
+    const int64_t ld = codes_ld ? codes_ld : cols / 2, ld_t = codes_t_ld ? codes_t_ld : rows / 2;
+    if (ld < cols / 2 || ld % 16 || ld_t < rows / 2 || ld_t % 16) return MX_ERR_SHAPE;
     const int64_t col_strips = (cols / 32 + 7) / 8;
     const int64_t row_strips = (rows / 32 + Q2_TR - 1) / Q2_TR;
     const int64_t nsuper = batch * row_strips * col_strips;
@@ -826,15 +899,15 @@ mx_status mx_quantize_2d(const void* w, mx_dtype wt, int64_t batch, int64_t rows
     (void)hipGetLastError();
     if (wt == MX_BF16)
         hipLaunchKernelGGL((q2d_kernel<true>), dim3(grid), dim3(256), 0, s, w, rows, cols, col_strips, row_strips,
-                           nsuper, codes, scales, codes_t, scales_t);
+                           nsuper, codes, ld, scales, codes_t, ld_t, scales_t);
     else
         hipLaunchKernelGGL((q2d_kernel<false>), dim3(grid), dim3(256), 0, s, w, rows, cols, col_strips, row_strips,
-                           nsuper, codes, scales, codes_t, scales_t);
+                           nsuper, codes, ld, scales, codes_t, ld_t, scales_t);
     return launched();
 }
 
-mx_status mx_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t batch, int64_t rows, int64_t cols,
-                        int block_rows, void* y, mx_dtype yt, mx_stream stream) {
+mx_status mx_dequantize(const uint8_t* codes, int64_t codes_ld, const uint8_t* scales, int64_t batch, int64_t rows,
+                        int64_t cols, int block_rows, void* y, mx_dtype yt, mx_stream stream) {
     if (yt != MX_F32 && yt != MX_BF16) return MX_ERR_DTYPE;
     if (batch < 0 || rows < 0 || cols < 0 || cols % 32) return MX_ERR_SHAPE;
     if (block_rows != 1 && block_rows != 32) return MX_ERR_SHAPE;
@@ -842,16 +915,18 @@ mx_status mx_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t bat
     if (batch == 0 || rows == 0 || cols == 0) return MX_OK;
     if (!codes || !scales || !y) return MX_ERR_NULL;
     if (!aligned16(codes) || !aligned16(y)) return MX_ERR_ALIGN;
+    const int64_t ld = codes_ld ? codes_ld : cols / 2;       // code row pitch
+    if (ld < cols / 2 || ld % 16) return MX_ERR_SHAPE;
     const int64_t nunits = batch * rows * (cols / 8);
     const int grid = grid_for(nunits, 256);
     hipStream_t s = (hipStream_t)stream;
     (void)hipGetLastError();
     if (yt == MX_BF16) {
-        if (block_rows == 1) hipLaunchKernelGGL((deq_kernel<true, 1>), dim3(grid), dim3(256), 0, s, codes, scales, rows, cols, nunits, y);
-        else hipLaunchKernelGGL((deq_kernel<true, 32>), dim3(grid), dim3(256), 0, s, codes, scales, rows, cols, nunits, y);
+        if (block_rows == 1) hipLaunchKernelGGL((deq_kernel<true, 1>), dim3(grid), dim3(256), 0, s, codes, ld, scales, rows, cols, nunits, y);
+        else hipLaunchKernelGGL((deq_kernel<true, 32>), dim3(grid), dim3(256), 0, s, codes, ld, scales, rows, cols, nunits, y);
     } else {
-        if (block_rows == 1) hipLaunchKernelGGL((deq_kernel<false, 1>), dim3(grid), dim3(256), 0, s, codes, scales, rows, cols, nunits, y);
-        else hipLaunchKernelGGL((deq_kernel<false, 32>), dim3(grid), dim3(256), 0, s, codes, scales, rows, cols, nunits, y);
+        if (block_rows == 1) hipLaunchKernelGGL((deq_kernel<false, 1>), dim3(grid), dim3(256), 0, s, codes, ld, scales, rows, cols, nunits, y);
+        else hipLaunchKernelGGL((deq_kernel<false, 32>), dim3(grid), dim3(256), 0, s, codes, ld, scales, rows, cols, nunits, y);
     }
     return launched();
 }

@@ -47,13 +47,13 @@ def lib():
         L.mx_rht_sign_mask.restype = u32
         L.mx_rht.argtypes = [P, c_int, P, i64, i64, u32, c_int, P]
         L.mx_quantize_1d.argtypes = [P, c_int, i64, i64, c_int, P, i32, i64, P, c_int, u32, c_int,
-                                     u64, u32, u64, P, P, P]
-        L.mx_quantize_2d.argtypes = [P, c_int, i64, i64, i64, P, P, P, P, P]
-        L.mx_dequantize.argtypes = [P, P, i64, i64, i64, c_int, P, c_int, P]
-        L.mx_grouped_gemm.argtypes = [P, P, P, P, P, c_int, P, i32, c_int, i64, i64, i64,
+                                     u64, u32, u64, P, i64, P, P]
+        L.mx_quantize_2d.argtypes = [P, c_int, i64, i64, i64, P, i64, P, P, i64, P, P]
+        L.mx_dequantize.argtypes = [P, i64, P, i64, i64, i64, c_int, P, c_int, P]
+        L.mx_grouped_gemm.argtypes = [P, i64, P, P, P, i64, P, c_int, P, i32, c_int, i64, i64, i64,
                                       ctypes.c_float, P, c_int, P]
-        L.mx_grouped_gemm_q.argtypes = [P, P, P, P, P, c_int, P, i32, i64, i64, i64,
-                                        ctypes.c_float, P, P, P, P]
+        L.mx_grouped_gemm_q.argtypes = [P, i64, P, P, P, i64, P, c_int, P, i32, i64, i64, i64,
+                                        ctypes.c_float, P, P, i64, P, P]
         for name in ("mx_rht", "mx_quantize_1d", "mx_quantize_2d", "mx_dequantize",
                      "mx_grouped_gemm", "mx_grouped_gemm_q"):
             getattr(L, name).restype = c_int
@@ -105,6 +105,25 @@ def _dev(t, name):
     return t
 
 
+def _codes(t, name):
+    """A code tensor [..., rows, row_bytes] whose rows may be padded: its
+    rows are contiguous and any row pitch (stride between rows, in bytes) is
+    allowed, and leading dimensions are contiguous over pitched rows (a
+    row-slice view t = buf[..., :row_bytes] of a wider buffer).  Returns the
+    row pitch to pass to the library, 0 when the rows are contiguous."""
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if t.dtype.itemsize != 1 or t.dim() < 2 or t.stride(-1) != 1:
+        raise ValueError("%s must be uint8 [..., rows, bytes] with contiguous rows" % name)
+    ld = t.stride(-2)
+    expect = ld * t.shape[-2]
+    for d in range(t.dim() - 3, -1, -1):
+        if t.shape[d] > 1 and t.stride(d) != expect:
+            raise ValueError("%s: leading dimensions must be contiguous over its rows" % name)
+        expect *= t.shape[d]
+    return 0 if ld == t.shape[-1] else ld
+
+
 def rht_sign_mask(seed: int) -> int:
     return int(lib().mx_rht_sign_mask(seed))
 
@@ -154,10 +173,12 @@ def quantize_1d(x, block_axis: int = 1, group_offsets=None, kp: int = 0, use_rht
         codes = torch.empty(shape_c, dtype=torch.uint8, device=x.device)
     if scales is None:
         scales = torch.empty(shape_s, dtype=torch.uint8, device=x.device)
+    # codes may be a row-slice view of a wider buffer (padded rows)
+    codes_ld = _codes(codes, "codes")
     _check("mx_quantize_1d", lib().mx_quantize_1d(
         _ptr(x), _dtype_code(x), rows, cols, block_axis, _ptr(group_offsets), ng, kp,
-        _ptr(row_index), int(use_rht), sign_mask, rnd, seed, stream_id, index_base, _ptr(codes), _ptr(scales),
-        _stream()))
+        _ptr(row_index), int(use_rht), sign_mask, rnd, seed, stream_id, index_base, _ptr(codes), codes_ld,
+        _ptr(scales), _stream()))
     return codes, scales
 
 
@@ -181,8 +202,10 @@ def quantize_2d_into(w, codes, scales, codes_t, scales_t):
     squeeze = w.dim() == 2
     w3 = w.unsqueeze(0) if squeeze else w
     b, r, c = w3.shape
+    ld = 0 if codes is None else _codes(codes, "codes")
+    ld_t = 0 if codes_t is None else _codes(codes_t, "codes_t")
     _check("mx_quantize_2d", lib().mx_quantize_2d(
-        _ptr(w3), _dtype_code(w3), b, r, c, _ptr(codes), _ptr(scales), _ptr(codes_t),
+        _ptr(w3), _dtype_code(w3), b, r, c, _ptr(codes), ld, _ptr(scales), _ptr(codes_t), ld_t,
         _ptr(scales_t), _stream()))
     out = [codes, scales, codes_t, scales_t]
     if squeeze:
@@ -192,7 +215,7 @@ def quantize_2d_into(w, codes, scales, codes_t, scales_t):
 
 def dequantize(codes, scales, block_rows: int = 1, out_dtype=None, out=None):
     torch = _torch()
-    _dev(codes, "codes")
+    ld = _codes(codes, "codes")
     _dev(scales, "scales")
     out_dtype = out_dtype or torch.float32
     squeeze = codes.dim() == 2
@@ -201,7 +224,7 @@ def dequantize(codes, scales, block_rows: int = 1, out_dtype=None, out=None):
     if out is None:
         out = torch.empty((b, r, half * 2), dtype=out_dtype, device=codes.device)
     _check("mx_dequantize", lib().mx_dequantize(
-        _ptr(c3), _ptr(scales), b, r, half * 2, block_rows, _ptr(out), _dtype_code(out),
+        _ptr(c3), ld, _ptr(scales), b, r, half * 2, block_rows, _ptr(out), _dtype_code(out),
         _stream()))
     return out[0] if squeeze else out
 
@@ -210,9 +233,9 @@ def grouped_gemm(a_codes, a_scales, b_codes, b_scales, group_offsets, M, N, K,
                  a_row_index=None, b_scale_2d=False, group_dim_k=False, alpha=1.0,
                  out_dtype=None, out=None):
     torch = _torch()
-    for t, nm in ((a_codes, "a_codes"), (a_scales, "a_scales"), (b_codes, "b_codes"),
-                  (b_scales, "b_scales"), (group_offsets, "group_offsets")):
+    for t, nm in ((a_scales, "a_scales"), (b_scales, "b_scales"), (group_offsets, "group_offsets")):
         _dev(t, nm)
+    a_ld, b_ld = _codes(a_codes, "a_codes"), _codes(b_codes, "b_codes")
     if a_row_index is not None:
         _dev(a_row_index, "a_row_index")
     G = group_offsets.numel() - 1
@@ -221,7 +244,7 @@ def grouped_gemm(a_codes, a_scales, b_codes, b_scales, group_offsets, M, N, K,
         shape = (G, M, N) if group_dim_k else (M, N)
         out = torch.empty(shape, dtype=out_dtype, device=a_codes.device)
     _check("mx_grouped_gemm", lib().mx_grouped_gemm(
-        _ptr(a_codes), _ptr(a_scales), _ptr(a_row_index), _ptr(b_codes), _ptr(b_scales),
+        _ptr(a_codes), a_ld, _ptr(a_scales), _ptr(a_row_index), _ptr(b_codes), b_ld, _ptr(b_scales),
         int(bool(b_scale_2d)), _ptr(group_offsets), G, int(bool(group_dim_k)), M, N, K,
         float(alpha), _ptr(out), _dtype_code(out), _stream()))
     return out
@@ -235,9 +258,9 @@ def grouped_gemm_q(a_codes, a_scales, b_codes, b_scales, group_offsets, M, N, K,
     (c or None, codes [M x N/2], scales [M x N/32]); out / codes / scales
     are optional preallocated outputs."""
     torch = _torch()
-    for t, nm in ((a_codes, "a_codes"), (a_scales, "a_scales"), (b_codes, "b_codes"),
-                  (b_scales, "b_scales"), (group_offsets, "group_offsets")):
+    for t, nm in ((a_scales, "a_scales"), (b_scales, "b_scales"), (group_offsets, "group_offsets")):
         _dev(t, nm)
+    a_ld, b_ld = _codes(a_codes, "a_codes"), _codes(b_codes, "b_codes")
     if a_row_index is not None:
         _dev(a_row_index, "a_row_index")
     G = group_offsets.numel() - 1
@@ -246,9 +269,10 @@ def grouped_gemm_q(a_codes, a_scales, b_codes, b_scales, group_offsets, M, N, K,
     if with_bf16:
         c = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     codes = codes if codes is not None else torch.empty((M, N // 2), dtype=torch.uint8, device=dev)
+    c_ld = _codes(codes, "codes")
     scales = scales if scales is not None else torch.empty((M, N // 32), dtype=torch.uint8, device=dev)
     _check("mx_grouped_gemm_q", lib().mx_grouped_gemm_q(
-        _ptr(a_codes), _ptr(a_scales), _ptr(a_row_index), _ptr(b_codes), _ptr(b_scales),
+        _ptr(a_codes), a_ld, _ptr(a_scales), _ptr(a_row_index), _ptr(b_codes), b_ld, _ptr(b_scales),
         int(bool(b_scale_2d)), _ptr(group_offsets), G, M, N, K, float(alpha),
-        _ptr(c), _ptr(codes), _ptr(scales), _stream()))
+        _ptr(c), _ptr(codes), c_ld, _ptr(scales), _stream()))
     return c, codes, scales

@@ -39,48 +39,57 @@ FAKE = 0x1000  # a 16-byte aligned non-null address; never dereferenced (validat
 def test_quantize_1d_validation(L):
     q = L.mx_quantize_1d
     # cols not a multiple of 32
-    assert q(FAKE, mx.MX_BF16, 4, 33, 1, None, 0, 0, None, 0, 0, 0, 0, 0, 0, FAKE, FAKE, None) == 2
+    assert q(FAKE, mx.MX_BF16, 4, 33, 1, None, 0, 0, None, 0, 0, 0, 0, 0, 0, FAKE, 0, FAKE, None) == 2
     # bad dtype, bad rounding mode
-    assert q(FAKE, 7, 4, 32, 1, None, 0, 0, None, 0, 0, 0, 0, 0, 0, FAKE, FAKE, None) == 4
-    assert q(FAKE, mx.MX_BF16, 4, 32, 1, None, 0, 0, None, 0, 0, 3, 0, 0, 0, FAKE, FAKE, None) == 5
+    assert q(FAKE, 7, 4, 32, 1, None, 0, 0, None, 0, 0, 0, 0, 0, 0, FAKE, 0, FAKE, None) == 4
+    assert q(FAKE, mx.MX_BF16, 4, 32, 1, None, 0, 0, None, 0, 0, 3, 0, 0, 0, FAKE, 0, FAKE, None) == 5
     # null pointers
-    assert q(None, mx.MX_BF16, 4, 32, 1, None, 0, 0, None, 0, 0, 0, 0, 0, 0, FAKE, FAKE, None) == 1
-    assert q(FAKE, mx.MX_BF16, 4, 32, 1, None, 0, 0, None, 0, 0, 0, 0, 0, 0, None, FAKE, None) == 1
+    assert q(None, mx.MX_BF16, 4, 32, 1, None, 0, 0, None, 0, 0, 0, 0, 0, 0, FAKE, 0, FAKE, None) == 1
+    assert q(FAKE, mx.MX_BF16, 4, 32, 1, None, 0, 0, None, 0, 0, 0, 0, 0, 0, None, 0, FAKE, None) == 1
     # misaligned input
-    assert q(FAKE + 2, mx.MX_BF16, 4, 32, 1, None, 0, 0, None, 0, 0, 0, 0, 0, 0, FAKE, FAKE, None) == 3
+    assert q(FAKE + 2, mx.MX_BF16, 4, 32, 1, None, 0, 0, None, 0, 0, 0, 0, 0, 0, FAKE, 0, FAKE, None) == 3
     # index base not a multiple of 32
-    assert q(FAKE, mx.MX_BF16, 4, 32, 1, None, 0, 0, None, 0, 0, 1, 7, 0, 8, FAKE, FAKE, None) == 2
+    assert q(FAKE, mx.MX_BF16, 4, 32, 1, None, 0, 0, None, 0, 0, 1, 7, 0, 8, FAKE, 0, FAKE, None) == 2
     # row-wise with groups given
-    assert q(FAKE, mx.MX_BF16, 4, 32, 1, FAKE, 2, 0, None, 0, 0, 0, 0, 0, 0, FAKE, FAKE, None) == 2
+    assert q(FAKE, mx.MX_BF16, 4, 32, 1, FAKE, 2, 0, None, 0, 0, 0, 0, 0, 0, FAKE, 0, FAKE, None) == 2
     # column-wise: missing offsets, bad kp, bad group count
-    assert q(FAKE, mx.MX_BF16, 4, 32, 0, None, 2, 64, None, 0, 0, 0, 0, 0, 0, FAKE, FAKE, None) == 1
-    assert q(FAKE, mx.MX_BF16, 4, 32, 0, FAKE, 2, 40, None, 0, 0, 0, 0, 0, 0, FAKE, FAKE, None) == 2
-    assert q(FAKE, mx.MX_BF16, 4, 32, 0, FAKE, 0, 64, None, 0, 0, 0, 0, 0, 0, FAKE, FAKE, None) == 2
+    assert q(FAKE, mx.MX_BF16, 4, 32, 0, None, 2, 64, None, 0, 0, 0, 0, 0, 0, FAKE, 0, FAKE, None) == 1
+    assert q(FAKE, mx.MX_BF16, 4, 32, 0, FAKE, 2, 40, None, 0, 0, 0, 0, 0, 0, FAKE, 0, FAKE, None) == 2
+    assert q(FAKE, mx.MX_BF16, 4, 32, 0, FAKE, 0, 64, None, 0, 0, 0, 0, 0, 0, FAKE, 0, FAKE, None) == 2
     # column-wise: one row of x over 4 GiB (2^31 bf16 columns)
-    assert q(FAKE, mx.MX_BF16, 4, 2 ** 31, 0, FAKE, 2, 64, None, 0, 0, 0, 0, 0, 0, FAKE, FAKE, None) == 2
+    assert q(FAKE, mx.MX_BF16, 4, 2 ** 31, 0, FAKE, 2, 64, None, 0, 0, 0, 0, 0, 0, FAKE, 0, FAKE, None) == 2
     # a row gather is column-wise only
-    assert q(FAKE, mx.MX_BF16, 4, 32, 1, None, 0, 0, FAKE, 0, 0, 0, 0, 0, 0, FAKE, FAKE, None) == 5
+    assert q(FAKE, mx.MX_BF16, 4, 32, 1, None, 0, 0, FAKE, 0, 0, 0, 0, 0, 0, FAKE, 0, FAKE, None) == 5
+    # code row pitch: below cols / 2, not a multiple of 16; column-wise other than kp / 2
+    assert q(FAKE, mx.MX_BF16, 4, 64, 1, None, 0, 0, None, 0, 0, 0, 0, 0, 0, FAKE, 16, FAKE, None) == 2
+    assert q(FAKE, mx.MX_BF16, 4, 64, 1, None, 0, 0, None, 0, 0, 0, 0, 0, 0, FAKE, 40, FAKE, None) == 2
+    assert q(FAKE, mx.MX_BF16, 4, 32, 0, FAKE, 2, 64, None, 0, 0, 0, 0, 0, 0, FAKE, 48, FAKE, None) == 2
     # empty input is a no-op that launches nothing
-    assert q(None, mx.MX_BF16, 0, 32, 1, None, 0, 0, None, 0, 0, 0, 0, 0, 0, None, None, None) == 0
+    assert q(None, mx.MX_BF16, 0, 32, 1, None, 0, 0, None, 0, 0, 0, 0, 0, 0, None, 0, None, None) == 0
 
 
 def test_quantize_2d_validation(L):
     q = L.mx_quantize_2d
-    assert q(FAKE, mx.MX_BF16, 1, 48, 32, FAKE, FAKE, None, None, None) == 2
-    assert q(FAKE, mx.MX_BF16, 1, 32, 32, None, None, None, None, None) == 1
-    assert q(FAKE, mx.MX_BF16, 1, 32, 32, FAKE, None, None, None, None) == 1
-    assert q(FAKE, 9, 1, 32, 32, FAKE, FAKE, None, None, None) == 4
-    assert q(FAKE + 8, mx.MX_BF16, 1, 32, 32, FAKE, FAKE, None, None, None) == 3
-    assert q(FAKE, mx.MX_BF16, 0, 32, 32, FAKE, FAKE, None, None, None) == 0
+    assert q(FAKE, mx.MX_BF16, 1, 48, 32, FAKE, 0, FAKE, None, 0, None, None) == 2
+    assert q(FAKE, mx.MX_BF16, 1, 32, 32, None, 0, None, None, 0, None, None) == 1
+    assert q(FAKE, mx.MX_BF16, 1, 32, 32, FAKE, 0, None, None, 0, None, None) == 1
+    assert q(FAKE, 9, 1, 32, 32, FAKE, 0, FAKE, None, 0, None, None) == 4
+    assert q(FAKE + 8, mx.MX_BF16, 1, 32, 32, FAKE, 0, FAKE, None, 0, None, None) == 3
+    # code row pitches: W rows below cols / 2, W^T rows not a multiple of 16
+    assert q(FAKE, mx.MX_BF16, 1, 64, 64, FAKE, 16, FAKE, None, 0, None, None) == 2
+    assert q(FAKE, mx.MX_BF16, 1, 64, 64, None, 0, None, FAKE, 40, FAKE, None) == 2
+    assert q(FAKE, mx.MX_BF16, 0, 32, 32, FAKE, 0, FAKE, None, 0, None, None) == 0
 
 
 def test_dequantize_validation(L):
     d = L.mx_dequantize
-    assert d(FAKE, FAKE, 1, 4, 48, 1, FAKE, mx.MX_F32, None) == 2
-    assert d(FAKE, FAKE, 1, 4, 32, 16, FAKE, mx.MX_F32, None) == 2
-    assert d(FAKE, FAKE, 1, 40, 32, 32, FAKE, mx.MX_F32, None) == 2
-    assert d(FAKE, None, 1, 4, 32, 1, FAKE, mx.MX_F32, None) == 1
-    assert d(FAKE, FAKE, 1, 4, 32, 1, FAKE, 5, None) == 4
+    assert d(FAKE, 0, FAKE, 1, 4, 48, 1, FAKE, mx.MX_F32, None) == 2
+    assert d(FAKE, 0, FAKE, 1, 4, 32, 16, FAKE, mx.MX_F32, None) == 2
+    assert d(FAKE, 0, FAKE, 1, 40, 32, 32, FAKE, mx.MX_F32, None) == 2
+    assert d(FAKE, 0, None, 1, 4, 32, 1, FAKE, mx.MX_F32, None) == 1
+    assert d(FAKE, 0, FAKE, 1, 4, 32, 1, FAKE, 5, None) == 4
+    # code row pitch below cols / 2
+    assert d(FAKE, 16, FAKE, 1, 4, 64, 1, FAKE, mx.MX_F32, None) == 2
 
 
 def test_rht_validation(L):
@@ -96,12 +105,12 @@ def test_gemm_validation(L):
     args = dict(M=64, N=64, K=64)
 
     def call(**kw):
-        a = dict(a_codes=FAKE, a_scales=FAKE, a_row_index=None, b_codes=FAKE, b_scales=FAKE,
+        a = dict(a_codes=FAKE, a_ld=0, a_scales=FAKE, a_row_index=None, b_codes=FAKE, b_ld=0, b_scales=FAKE,
                  b_scale_2d=0, off=FAKE, G=1, gk=0, M=64, N=64, K=64, alpha=1.0, c=FAKE,
                  ct=mx.MX_BF16)
         a.update(kw)
-        return g(a["a_codes"], a["a_scales"], a["a_row_index"], a["b_codes"], a["b_scales"],
-                 a["b_scale_2d"], a["off"], a["G"], a["gk"], a["M"], a["N"], a["K"],
+        return g(a["a_codes"], a["a_ld"], a["a_scales"], a["a_row_index"], a["b_codes"], a["b_ld"],
+                 a["b_scales"], a["b_scale_2d"], a["off"], a["G"], a["gk"], a["M"], a["N"], a["K"],
                  ctypes.c_float(a["alpha"]), a["c"], a["ct"], None)
 
     assert call(K=48) == 2
@@ -114,6 +123,11 @@ def test_gemm_validation(L):
     assert call(a_codes=FAKE + 1) == 3
     assert call(gk=1, b_scale_2d=1) == 5
     assert call(gk=1, a_row_index=FAKE) == 5
+    # code row pitches: below K / 2, not a multiple of 16
+    assert call(a_ld=16) == 2
+    assert call(b_ld=40) == 2
+    # B group of N rows at the pitch beyond 4 GiB - 1
+    assert call(N=2**20, K=64, b_ld=2**13) == 2
     assert call(M=0) == 0
 
 
@@ -121,12 +135,12 @@ def test_gemm_q_validation(L):
     g = L.mx_grouped_gemm_q
 
     def call(**kw):
-        a = dict(a_codes=FAKE, a_scales=FAKE, a_row_index=None, b_codes=FAKE, b_scales=FAKE,
-                 b_scale_2d=0, off=FAKE, G=1, M=64, N=64, K=64, alpha=1.0, c=FAKE, qc=FAKE, qs=FAKE)
+        a = dict(a_codes=FAKE, a_ld=0, a_scales=FAKE, a_row_index=None, b_codes=FAKE, b_ld=0, b_scales=FAKE,
+                 b_scale_2d=0, off=FAKE, G=1, M=64, N=64, K=64, alpha=1.0, c=FAKE, qc=FAKE, qc_ld=0, qs=FAKE)
         a.update(kw)
-        return g(a["a_codes"], a["a_scales"], a["a_row_index"], a["b_codes"], a["b_scales"],
-                 a["b_scale_2d"], a["off"], a["G"], a["M"], a["N"], a["K"], ctypes.c_float(a["alpha"]),
-                 a["c"], a["qc"], a["qs"], None)
+        return g(a["a_codes"], a["a_ld"], a["a_scales"], a["a_row_index"], a["b_codes"], a["b_ld"],
+                 a["b_scales"], a["b_scale_2d"], a["off"], a["G"], a["M"], a["N"], a["K"],
+                 ctypes.c_float(a["alpha"]), a["c"], a["qc"], a["qc_ld"], a["qs"], None)
 
     assert call(K=48) == 2
     assert call(N=48) == 2
@@ -139,4 +153,8 @@ def test_gemm_q_validation(L):
     assert call(c=FAKE + 2) == 3
     # codes of M x N / 2 bytes beyond 4 GiB - 1
     assert call(M=2**20, N=2**13, K=64) == 2
+    # output code pitch: below N / 2, not a multiple of 16, M rows of it beyond 4 GiB - 1
+    assert call(qc_ld=16) == 2
+    assert call(qc_ld=40) == 3
+    assert call(M=2**20, N=64, qc_ld=2**12) == 2
     assert call(M=0) == 0
