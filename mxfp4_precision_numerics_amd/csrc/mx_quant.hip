@@ -57,6 +57,27 @@ __device__ __forceinline__ void q1d_row_body(const void* __restrict__ x, int64_t
     for (int e = 0; e < 8; ++e) sgn[e] = ((m8 >> e) & 1u) << 31;
 
     for (int64_t base = wave * 16 * ROW_UNROLL; base < nblocks; base += nwaves * 16 * ROW_UNROLL) {
+        const int32_t bpr32 = (int32_t)rp.bpr;   // (the host bounds bpr to int32)
+        // PITCH: the quad's first block split into (row, b) once per trip,
+        // r = floor(blk / bpr) from the double quotient, which is within one
+        // of it for any index below 2^53, and one correction step; the later
+        // blocks step b by 16 and carry into the row
+        int32_t pb = 0;
+        int64_t pofs = 0;
+        if (PITCH) {
+            const int64_t blk = base + (lane >> 2);
+            int64_t row = (int64_t)((double)blk * rp.inv_bpr);
+            int64_t b = blk - row * rp.bpr;
+            if (b < 0) {
+                --row;
+                b += rp.bpr;
+            } else if (b >= rp.bpr) {
+                ++row;
+                b -= rp.bpr;
+            }
+            pb = (int32_t)b;
+            pofs = blk * 16 + row * rp.pad;
+        }
         float v[ROW_UNROLL][8];
 #pragma unroll
         for (int u = 0; u < ROW_UNROLL; ++u) {
@@ -81,32 +102,14 @@ __device__ __forceinline__ void q1d_row_body(const void* __restrict__ x, int64_t
                 for (int e = 0; e < 8; ++e) v[u][e] = 0.0f;
             }
         }
-        // PITCH: the quad's first block split into (row, b) once per trip,
-        // r = floor(blk / bpr) from the double quotient, which is within one
-        // of it for any index below 2^53, and one correction step; the later
-        // blocks step b by 16 and carry into the row
-        int64_t pb = 0, pofs = 0;
-        if (PITCH) {
-            const int64_t blk = base + (lane >> 2);
-            int64_t row = (int64_t)((double)blk * rp.inv_bpr);
-            pb = blk - row * rp.bpr;
-            if (pb < 0) {
-                --row;
-                pb += rp.bpr;
-            } else if (pb >= rp.bpr) {
-                ++row;
-                pb -= rp.bpr;
-            }
-            pofs = blk * 16 + row * rp.pad;
-        }
 #pragma unroll
         for (int u = 0; u < ROW_UNROLL; ++u) {
             const int64_t blk = base + u * 16 + (lane >> 2);
             if (PITCH && u > 0) {
                 pb += 16;
                 pofs += 256;
-                while (pb >= rp.bpr) {
-                    pb -= rp.bpr;
+                while (pb >= bpr32) {
+                    pb -= bpr32;
                     pofs += rp.pad;
                 }
             }
@@ -827,6 +830,7 @@ mx_status mx_quantize_1d(const void* x, mx_dtype xt, int64_t rows, int64_t cols,
         // code row pitch: 0 = cols / 2; else at least that and a multiple of 16
         const int64_t ld = codes_ld ? codes_ld : cols / 2;
         if (ld < cols / 2 || ld % 16) return MX_ERR_SHAPE;
+        if (cols / 32 > INT32_MAX) return MX_ERR_SHAPE;
         const int64_t nblocks = rows * (cols / 32);
         const int grid = grid_for(nblocks, 4 * 16 * ROW_UNROLL);
         const RowPitch rp{cols / 32, 1.0 / (double)(cols / 32), ld - cols / 2};
