@@ -206,3 +206,20 @@ def test_fused_epilogue_pitched_codes(with_bf16):
     assert np.all(b[:, N // 2:] == FILL), "padding written"
     if with_bf16:
         assert torch.equal(c1.view(torch.int16), c0.view(torch.int16))
+
+
+@pytest.mark.parametrize("rnd", [0, 1])
+def test_rowwise_full_size_pitched(rnd):
+    """The expert step's largest row-wise operand, 65,536 x 5760 bf16 (the
+    gate-up gradient), quantized with its code rows padded from 2880 to 2944
+    bytes: codes and scales equal the unpadded call's everywhere and the
+    padding is untouched (compared on the device)."""
+    import torch
+    g = torch.Generator(device="cuda").manual_seed(11 + rnd)
+    x = (torch.randn(65536, 5760, device="cuda", generator=g) * 1e-3).to(torch.bfloat16)
+    c0, s0 = mx.quantize_1d(x, rnd=rnd, seed=5, stream_id=0)
+    buf, view = _pitched((65536, 2880), 2944)
+    c1, s1 = mx.quantize_1d(x, rnd=rnd, seed=5, stream_id=0, codes=view)
+    assert torch.equal(view, c0)
+    assert torch.equal(s1, s0)
+    assert bool((buf[:, 2880:] == FILL).all())
