@@ -32,29 +32,52 @@ using namespace mx;
 // ===========================================================================
 constexpr int ROW_UNROLL = 4;   // blocks per quad per loop trip (loads in flight)
 
-// Code rows may be padded (PITCH): block blk is block b of row r with
+// Code rows may be padded (PITCH > 0): block blk is block b of row r with
 // blk = r * bpr + b, and its 16 code bytes go to codes + r * ld + 16 b
 // = codes + 16 blk + r * pad, pad = ld - 16 bpr.
 struct RowPitch {
     int64_t bpr;        // blocks per row (cols / 32)
     double inv_bpr;     // 1 / bpr
     int64_t pad;        // bytes between the end of a code row and the next row
+    int64_t ld;         // bytes from one code row to the next
+    int64_t step_rows;  // PITCH 2: the grid stride in blocks, as whole rows
+    int64_t step_rem;   //          and the blocks left over
 };
 
-template <bool BF16, bool RHT, bool SR, bool PITCH>
+// row = floor(blk / bpr) from the double quotient, which is within one of it
+// for any index below 2^53, and one correction step
+__device__ __forceinline__ void split_block(int64_t blk, const RowPitch& rp, int64_t& row, int64_t& b) {
+    row = (int64_t)((double)blk * rp.inv_bpr);
+    b = blk - row * rp.bpr;
+    if (b < 0) {
+        --row;
+        b += rp.bpr;
+    } else if (b >= rp.bpr) {
+        ++row;
+        b -= rp.bpr;
+    }
+}
+
+// PITCH: 0 unpadded rows; 1 padded rows of any width; 2 padded rows of at
+// least 64 blocks, so a trip's 64 blocks cross at most one row end
+template <bool BF16, bool RHT, bool SR, int PITCH>
 __device__ __forceinline__ void q1d_row_body(const void* __restrict__ x, int64_t nblocks, uint32_t mask,
                                              uint32_t k0, uint32_t k1, uint32_t stream_id,
                                              uint64_t index_base, uint8_t* __restrict__ codes,
                                              uint8_t* __restrict__ scales, RowPitch rp) {
     const int lane = threadIdx.x & 63;
     const int q = lane & 3;
-    const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x >> 6);
     // per-lane sign words for the RHT: lane q holds block elements 8q..8q+7
     const uint32_t m8 = (mask >> (8 * q)) & 0xFFu;
     uint32_t sgn[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) sgn[e] = ((m8 >> e) & 1u) << 31;
+    // PITCH 2: the wave's first block of the trip as (row0, b0), wave-uniform,
+    // advanced by the grid stride with integer steps
+    int64_t row0 = 0, b0 = 0;
+    if (PITCH == 2) split_block(wave * 16 * ROW_UNROLL, rp, row0, b0);
 
     for (int64_t base = wave * 16 * ROW_UNROLL; base < nblocks; base += nwaves * 16 * ROW_UNROLL) {
         const int32_t bpr32 = (int32_t)rp.bpr;   // (the host bounds bpr to int32)
@@ -64,20 +87,17 @@ __device__ __forceinline__ void q1d_row_body(const void* __restrict__ x, int64_t
         // blocks step b by 16 and carry into the row
         int32_t pb = 0;
         int64_t pofs = 0;
-        if (PITCH) {
+        if (PITCH == 1) {
+            int64_t row, b;
             const int64_t blk = base + (lane >> 2);
-            int64_t row = (int64_t)((double)blk * rp.inv_bpr);
-            int64_t b = blk - row * rp.bpr;
-            if (b < 0) {
-                --row;
-                b += rp.bpr;
-            } else if (b >= rp.bpr) {
-                ++row;
-                b -= rp.bpr;
-            }
+            split_block(blk, rp, row, b);
             pb = (int32_t)b;
             pofs = blk * 16 + row * rp.pad;
         }
+        // PITCH 2: block base + o lies in row row0 while o < bpr - b0, else in
+        // the next row; its codes are o * 16 (+ pad) bytes past row0's block b0
+        uint8_t* const cbase = codes + (PITCH == 2 ? row0 * rp.ld + b0 * 16 : 0);
+        const int32_t thr = (int32_t)(rp.bpr - b0);
         float v[ROW_UNROLL][8];
 #pragma unroll
         for (int u = 0; u < ROW_UNROLL; ++u) {
@@ -105,7 +125,7 @@ __device__ __forceinline__ void q1d_row_body(const void* __restrict__ x, int64_t
 #pragma unroll
         for (int u = 0; u < ROW_UNROLL; ++u) {
             const int64_t blk = base + u * 16 + (lane >> 2);
-            if (PITCH && u > 0) {
+            if (PITCH == 1 && u > 0) {
                 pb += 16;
                 pofs += 256;
                 while (pb >= bpr32) {
@@ -135,9 +155,23 @@ __device__ __forceinline__ void q1d_row_body(const void* __restrict__ x, int64_t
             }
             if (byte == 0xFFu) packed = 0;   // non-finite block: codes are 0
             if (blk < nblocks) {
-                const int64_t cofs = PITCH ? pofs : blk * 16;
-                *((uint32_t*)(codes + cofs) + q) = packed;
+                if (PITCH == 2) {
+                    const int32_t o = u * 16 + (lane >> 2);
+                    const uint32_t rel = (uint32_t)o * 16u + (o >= thr ? (uint32_t)rp.pad : 0u);
+                    *((uint32_t*)(cbase + rel) + q) = packed;
+                } else {
+                    const int64_t cofs = PITCH ? pofs : blk * 16;
+                    *((uint32_t*)(codes + cofs) + q) = packed;
+                }
                 if (q == 0) scales[blk] = (uint8_t)byte;
+            }
+        }
+        if (PITCH == 2) {
+            b0 += rp.step_rem;
+            row0 += rp.step_rows;
+            if (b0 >= rp.bpr) {
+                b0 -= rp.bpr;
+                ++row0;
             }
         }
     }
@@ -149,7 +183,7 @@ __global__ __launch_bounds__(256) void q1d_row_kernel(const void* __restrict__ x
                                                       uint32_t stream_id, uint64_t index_base,
                                                       uint8_t* __restrict__ codes,
                                                       uint8_t* __restrict__ scales, RowPitch rp) {
-    q1d_row_body<BF16, RHT, SR, false>(x, nblocks, mask, k0, k1, stream_id, index_base, codes, scales, rp);
+    q1d_row_body<BF16, RHT, SR, 0>(x, nblocks, mask, k0, k1, stream_id, index_base, codes, scales, rp);
 }
 
 // the same with padded code rows
@@ -159,7 +193,17 @@ __global__ __launch_bounds__(256) void q1d_row_kernel_p(const void* __restrict__
                                                         uint32_t stream_id, uint64_t index_base,
                                                         uint8_t* __restrict__ codes,
                                                         uint8_t* __restrict__ scales, RowPitch rp) {
-    q1d_row_body<BF16, RHT, SR, true>(x, nblocks, mask, k0, k1, stream_id, index_base, codes, scales, rp);
+    q1d_row_body<BF16, RHT, SR, 1>(x, nblocks, mask, k0, k1, stream_id, index_base, codes, scales, rp);
+}
+
+// the same with padded code rows of at least 64 blocks
+template <bool BF16, bool RHT, bool SR>
+__global__ __launch_bounds__(256) void q1d_row_kernel_w(const void* __restrict__ x, int64_t nblocks,
+                                                        uint32_t mask, uint32_t k0, uint32_t k1,
+                                                        uint32_t stream_id, uint64_t index_base,
+                                                        uint8_t* __restrict__ codes,
+                                                        uint8_t* __restrict__ scales, RowPitch rp) {
+    q1d_row_body<BF16, RHT, SR, 2>(x, nblocks, mask, k0, k1, stream_id, index_base, codes, scales, rp);
 }
 
 // ===========================================================================
@@ -833,10 +877,17 @@ mx_status mx_quantize_1d(const void* x, mx_dtype xt, int64_t rows, int64_t cols,
         if (cols / 32 > INT32_MAX) return MX_ERR_SHAPE;
         const int64_t nblocks = rows * (cols / 32);
         const int grid = grid_for(nblocks, 4 * 16 * ROW_UNROLL);
-        const RowPitch rp{cols / 32, 1.0 / (double)(cols / 32), ld - cols / 2};
+        // the grid stride in blocks: grid workgroups of 4 waves, 16 blocks per
+        // wave per unrolled step
+        const int64_t stride = (int64_t)grid * 4 * 16 * ROW_UNROLL;
+        const int64_t bpr = cols / 32;
+        const RowPitch rp{bpr, 1.0 / (double)bpr, ld - cols / 2, ld, stride / bpr, stride % bpr};
         (void)hipGetLastError();
         if (ld == cols / 2) {
             MX_DISPATCH3(q1d_row_kernel, bf, rh, sr, dim3(grid), s, x, nblocks, sign_mask, k0, k1, stream_id,
+                         index_base, codes, scales, rp);
+        } else if (bpr >= 16 * ROW_UNROLL && ld - cols / 2 < (1LL << 31)) {
+            MX_DISPATCH3(q1d_row_kernel_w, bf, rh, sr, dim3(grid), s, x, nblocks, sign_mask, k0, k1, stream_id,
                          index_base, codes, scales, rp);
         } else {
             MX_DISPATCH3(q1d_row_kernel_p, bf, rh, sr, dim3(grid), s, x, nblocks, sign_mask, k0, k1, stream_id,

@@ -32,11 +32,13 @@ def _pitched(shape, ld):
     return buf, buf[..., :shape[-1]]
 
 
-@pytest.mark.parametrize("rows,cols,ld", [(37, 2880, 1536), (1, 32, 16), (300, 96, 64), (130, 5760, 2944)])
+@pytest.mark.parametrize("rows,cols,ld", [(37, 2880, 1536), (1, 32, 16), (300, 96, 64), (130, 5760, 2944),
+                                           (50, 2048, 1040), (50, 2016, 1024), (3, 4096, 2048 + 4096)])
 @pytest.mark.parametrize("rnd", [0, 1])
 def test_rowwise_pitched_equals_contiguous(rows, cols, ld, rnd):
-    # row counts that do not fill a loop trip, one-block rows, and the
-    # expert-step widths at their 128-byte pitches
+    # row counts that do not fill a loop trip, one-block rows, the
+    # expert-step widths at their 128-byte pitches, and rows of exactly 64
+    # and of 63 blocks (the two padded-row kernels' boundary)
     rng = np.random.default_rng(rows + cols + rnd)
     x = synth.f32_to_bf16_bits((rng.standard_normal((rows, cols)) * 3).astype(np.float32))
     xd = dev_bf16(x)
