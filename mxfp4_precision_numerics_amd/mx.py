@@ -124,6 +124,23 @@ def _codes(t, name):
     return 0 if ld == t.shape[-1] else ld
 
 
+def _out(t, shape, dtype, name, pitched=False):
+    """Check a caller-provided output against what the library writes: this
+    shape (a leading batch of 1 may be left out) and dtype, on the device,
+    contiguous, or for a code array with rows that may be padded.  Returns
+    the code rows' pitch (0 when unpadded or not a code array)."""
+    shape = tuple(int(v) for v in shape)
+    got = tuple(t.shape)
+    if got != shape and not (len(shape) == 3 and shape[0] == 1 and got == shape[1:]):
+        raise ValueError("%s: expected shape %s, got %s" % (name, shape, got))
+    if t.dtype != dtype:
+        raise TypeError("%s: expected %s, got %s" % (name, dtype, t.dtype))
+    if pitched:
+        return _codes(t, name)
+    _dev(t, name)
+    return 0
+
+
 def rht_sign_mask(seed: int) -> int:
     return int(lib().mx_rht_sign_mask(seed))
 
@@ -153,7 +170,10 @@ def quantize_1d(x, block_axis: int = 1, group_offsets=None, kp: int = 0, use_rht
                 index_base: int = 0, codes=None, scales=None, row_index=None):
     """Returns (codes, scales) uint8 device tensors; see mx_quantize_1d.
     row_index (column-wise only): gather x's rows through it; the grouped
-    positions then number row_index.numel()."""
+    positions then number row_index.numel().  A row-wise codes output may
+    have padded rows, e.g. buf[:, :cols // 2] of a wider buffer (its row
+    stride, a multiple of 16, is passed as the pitch; the padding is not
+    written)."""
     torch = _torch()
     _dev(x, "x")
     rows, cols = x.shape
@@ -174,7 +194,8 @@ def quantize_1d(x, block_axis: int = 1, group_offsets=None, kp: int = 0, use_rht
     if scales is None:
         scales = torch.empty(shape_s, dtype=torch.uint8, device=x.device)
     # codes may be a row-slice view of a wider buffer (padded rows)
-    codes_ld = _codes(codes, "codes")
+    codes_ld = _out(codes, shape_c, torch.uint8, "codes", pitched=True)
+    _out(scales, shape_s, torch.uint8, "scales")
     _check("mx_quantize_1d", lib().mx_quantize_1d(
         _ptr(x), _dtype_code(x), rows, cols, block_axis, _ptr(group_offsets), ng, kp,
         _ptr(row_index), int(use_rht), sign_mask, rnd, seed, stream_id, index_base, _ptr(codes), codes_ld,
@@ -197,23 +218,31 @@ def quantize_2d(w, layout=True, transposed=True):
 
 
 def quantize_2d_into(w, codes, scales, codes_t, scales_t):
-    """As quantize_2d, into caller-provided buffers (either pair may be None)."""
+    """As quantize_2d, into caller-provided buffers (either pair may be None).
+    codes and codes_t may have padded rows (row-slice views of wider buffers)."""
+    torch = _torch()
     _dev(w, "w")
     squeeze = w.dim() == 2
     w3 = w.unsqueeze(0) if squeeze else w
     b, r, c = w3.shape
-    ld = 0 if codes is None else _codes(codes, "codes")
-    ld_t = 0 if codes_t is None else _codes(codes_t, "codes_t")
+    u8 = torch.uint8
+    ld = 0 if codes is None else _out(codes, (b, r, c // 2), u8, "codes", pitched=True)
+    ld_t = 0 if codes_t is None else _out(codes_t, (b, c, r // 2), u8, "codes_t", pitched=True)
+    if scales is not None:
+        _out(scales, (b, r // 32, c // 32), u8, "scales")
+    if scales_t is not None:
+        _out(scales_t, (b, c // 32, r // 32), u8, "scales_t")
     _check("mx_quantize_2d", lib().mx_quantize_2d(
         _ptr(w3), _dtype_code(w3), b, r, c, _ptr(codes), ld, _ptr(scales), _ptr(codes_t), ld_t,
         _ptr(scales_t), _stream()))
     out = [codes, scales, codes_t, scales_t]
     if squeeze:
-        out = [None if t is None else t[0] for t in out]
+        out = [t[0] if t is not None and t.dim() == 3 else t for t in out]
     return tuple(out)
 
 
 def dequantize(codes, scales, block_rows: int = 1, out_dtype=None, out=None):
+    """Per mx_dequantize; codes may have padded rows."""
     torch = _torch()
     ld = _codes(codes, "codes")
     _dev(scales, "scales")
@@ -223,15 +252,20 @@ def dequantize(codes, scales, block_rows: int = 1, out_dtype=None, out=None):
     b, r, half = c3.shape
     if out is None:
         out = torch.empty((b, r, half * 2), dtype=out_dtype, device=codes.device)
+    else:
+        _out(out, (b, r, half * 2), out.dtype, "out")
     _check("mx_dequantize", lib().mx_dequantize(
         _ptr(c3), ld, _ptr(scales), b, r, half * 2, block_rows, _ptr(out), _dtype_code(out),
         _stream()))
-    return out[0] if squeeze else out
+    return out[0] if squeeze and out.dim() == 3 else out
 
 
 def grouped_gemm(a_codes, a_scales, b_codes, b_scales, group_offsets, M, N, K,
                  a_row_index=None, b_scale_2d=False, group_dim_k=False, alpha=1.0,
                  out_dtype=None, out=None):
+    """C (bf16 by default, or out_dtype float32) per mx_grouped_gemm.  a_codes
+    and b_codes may have padded rows (row-slice views of wider buffers); rows
+    padded to whole 128-byte lines are read fastest."""
     torch = _torch()
     for t, nm in ((a_scales, "a_scales"), (b_scales, "b_scales"), (group_offsets, "group_offsets")):
         _dev(t, nm)
@@ -239,10 +273,11 @@ def grouped_gemm(a_codes, a_scales, b_codes, b_scales, group_offsets, M, N, K,
     if a_row_index is not None:
         _dev(a_row_index, "a_row_index")
     G = group_offsets.numel() - 1
-    out_dtype = out_dtype or torch.bfloat16
+    shape = (G, M, N) if group_dim_k else (M, N)
     if out is None:
-        shape = (G, M, N) if group_dim_k else (M, N)
-        out = torch.empty(shape, dtype=out_dtype, device=a_codes.device)
+        out = torch.empty(shape, dtype=out_dtype or torch.bfloat16, device=a_codes.device)
+    else:
+        _out(out, shape, out_dtype or out.dtype, "out")
     _check("mx_grouped_gemm", lib().mx_grouped_gemm(
         _ptr(a_codes), a_ld, _ptr(a_scales), _ptr(a_row_index), _ptr(b_codes), b_ld, _ptr(b_scales),
         int(bool(b_scale_2d)), _ptr(group_offsets), G, int(bool(group_dim_k)), M, N, K,
@@ -268,9 +303,11 @@ def grouped_gemm_q(a_codes, a_scales, b_codes, b_scales, group_offsets, M, N, K,
     c = None
     if with_bf16:
         c = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        _out(c, (M, N), torch.bfloat16, "out")
     codes = codes if codes is not None else torch.empty((M, N // 2), dtype=torch.uint8, device=dev)
-    c_ld = _codes(codes, "codes")
+    c_ld = _out(codes, (M, N // 2), torch.uint8, "codes", pitched=True)
     scales = scales if scales is not None else torch.empty((M, N // 32), dtype=torch.uint8, device=dev)
+    _out(scales, (M, N // 32), torch.uint8, "scales")
     _check("mx_grouped_gemm_q", lib().mx_grouped_gemm_q(
         _ptr(a_codes), a_ld, _ptr(a_scales), _ptr(a_row_index), _ptr(b_codes), b_ld, _ptr(b_scales),
         int(bool(b_scale_2d)), _ptr(group_offsets), G, M, N, K, float(alpha),

@@ -158,3 +158,21 @@ def test_gemm_q_validation(L):
     assert call(qc_ld=40) == 3
     assert call(M=2**20, N=64, qc_ld=2**12) == 2
     assert call(M=0) == 0
+
+
+def test_output_buffer_checks():
+    """Caller-provided outputs are checked against the shape and dtype the
+    library writes before any call (the shape and dtype checks come before
+    the device check, so they run on the CPU)."""
+    import torch
+    u8 = torch.uint8
+    with pytest.raises(ValueError, match="expected shape"):
+        mx._out(torch.empty(3, 4, dtype=u8), (3, 5), u8, "codes", pitched=True)
+    with pytest.raises(ValueError, match="expected shape"):
+        mx._out(torch.empty(2, 3, 4, dtype=u8), (1, 3, 4), u8, "codes")
+    with pytest.raises(TypeError, match="expected"):
+        mx._out(torch.empty(3, 4, dtype=torch.float32), (3, 4), torch.bfloat16, "out")
+    # right shape (a leading batch of 1 may be left out) and dtype: only the
+    # device check remains
+    with pytest.raises(ValueError, match="device"):
+        mx._out(torch.empty(3, 4, dtype=u8), (1, 3, 4), u8, "codes", pitched=True)

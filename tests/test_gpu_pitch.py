@@ -225,3 +225,32 @@ def test_rowwise_full_size_pitched(rnd):
     assert torch.equal(view, c0)
     assert torch.equal(s1, s0)
     assert bool((buf[:, 2880:] == FILL).all())
+
+
+def test_output_buffers_are_checked():
+    """Outputs of the wrong logical shape or dtype, padded or not, are
+    refused by the binding before any launch."""
+    import torch
+    x = dev_bf16(synth.f32_to_bf16_bits(np.ones((64, 256), np.float32)))
+    buf, view = _pitched((64, 128), 256)
+    with pytest.raises(ValueError, match="expected shape"):
+        mx.quantize_1d(x, codes=view[:63])
+    with pytest.raises(ValueError, match="expected shape"):
+        mx.quantize_1d(x, scales=torch.empty(64, 4, dtype=torch.uint8, device="cuda"))
+    ac, asc = mx.quantize_1d(x)
+    off = dev(np.array([0, 64], np.int32))
+    with pytest.raises(ValueError, match="expected shape"):
+        mx.grouped_gemm(ac, asc, ac.unsqueeze(0), asc.unsqueeze(0), off, 64, 64, 256,
+                        out=torch.empty(64, 32, dtype=torch.bfloat16, device="cuda"))
+    with pytest.raises(TypeError):
+        mx.grouped_gemm(ac, asc, ac.unsqueeze(0), asc.unsqueeze(0), off, 64, 64, 256,
+                        out=torch.empty(64, 64, dtype=torch.float16, device="cuda"))
+    with pytest.raises(ValueError, match="expected shape"):
+        mx.dequantize(ac, asc, out=torch.empty(64, 128, device="cuda"))
+    w = dev_bf16(synth.normal_bf16((64, 64), 0.02, seed=1))
+    c, s_, ct, st = mx.quantize_2d(w)
+    assert c.shape == (64, 32) and st.shape == (2, 2)
+    # 2D weights into 2D buffers come back whole
+    c2, s2, ct2, st2 = mx.quantize_2d_into(w, torch.empty_like(c), torch.empty_like(s_),
+                                          torch.empty_like(ct), torch.empty_like(st))
+    assert c2.shape == (64, 32) and torch.equal(c2, c) and torch.equal(st2, st)
