@@ -124,8 +124,8 @@ def _codes(t, name):
     return 0 if ld == t.shape[-1] else ld
 
 
-def _out(t, shape, dtype, name, pitched=False):
-    """Check a caller-provided output against what the library writes: this
+def _shaped(t, shape, dtype, name, pitched=False):
+    """Check a tensor against the extent the library reads or writes: this
     shape (a leading batch of 1 may be left out) and dtype, on the device,
     contiguous, or for a code array with rows that may be padded.  Returns
     the code rows' pitch (0 when unpadded or not a code array)."""
@@ -194,8 +194,8 @@ def quantize_1d(x, block_axis: int = 1, group_offsets=None, kp: int = 0, use_rht
     if scales is None:
         scales = torch.empty(shape_s, dtype=torch.uint8, device=x.device)
     # codes may be a row-slice view of a wider buffer (padded rows)
-    codes_ld = _out(codes, shape_c, torch.uint8, "codes", pitched=True)
-    _out(scales, shape_s, torch.uint8, "scales")
+    codes_ld = _shaped(codes, shape_c, torch.uint8, "codes", pitched=True)
+    _shaped(scales, shape_s, torch.uint8, "scales")
     _check("mx_quantize_1d", lib().mx_quantize_1d(
         _ptr(x), _dtype_code(x), rows, cols, block_axis, _ptr(group_offsets), ng, kp,
         _ptr(row_index), int(use_rht), sign_mask, rnd, seed, stream_id, index_base, _ptr(codes), codes_ld,
@@ -226,12 +226,12 @@ def quantize_2d_into(w, codes, scales, codes_t, scales_t):
     w3 = w.unsqueeze(0) if squeeze else w
     b, r, c = w3.shape
     u8 = torch.uint8
-    ld = 0 if codes is None else _out(codes, (b, r, c // 2), u8, "codes", pitched=True)
-    ld_t = 0 if codes_t is None else _out(codes_t, (b, c, r // 2), u8, "codes_t", pitched=True)
+    ld = 0 if codes is None else _shaped(codes, (b, r, c // 2), u8, "codes", pitched=True)
+    ld_t = 0 if codes_t is None else _shaped(codes_t, (b, c, r // 2), u8, "codes_t", pitched=True)
     if scales is not None:
-        _out(scales, (b, r // 32, c // 32), u8, "scales")
+        _shaped(scales, (b, r // 32, c // 32), u8, "scales")
     if scales_t is not None:
-        _out(scales_t, (b, c // 32, r // 32), u8, "scales_t")
+        _shaped(scales_t, (b, c // 32, r // 32), u8, "scales_t")
     _check("mx_quantize_2d", lib().mx_quantize_2d(
         _ptr(w3), _dtype_code(w3), b, r, c, _ptr(codes), ld, _ptr(scales), _ptr(codes_t), ld_t,
         _ptr(scales_t), _stream()))
@@ -245,19 +245,46 @@ def dequantize(codes, scales, block_rows: int = 1, out_dtype=None, out=None):
     """Per mx_dequantize; codes may have padded rows."""
     torch = _torch()
     ld = _codes(codes, "codes")
-    _dev(scales, "scales")
     out_dtype = out_dtype or torch.float32
     squeeze = codes.dim() == 2
     c3 = codes.unsqueeze(0) if squeeze else codes
     b, r, half = c3.shape
+    _shaped(scales, (b, r // block_rows, half * 2 // 32), torch.uint8, "scales")
     if out is None:
         out = torch.empty((b, r, half * 2), dtype=out_dtype, device=codes.device)
     else:
-        _out(out, (b, r, half * 2), out.dtype, "out")
+        _shaped(out, (b, r, half * 2), out.dtype, "out")
     _check("mx_dequantize", lib().mx_dequantize(
         _ptr(c3), ld, _ptr(scales), b, r, half * 2, block_rows, _ptr(out), _dtype_code(out),
         _stream()))
     return out[0] if squeeze and out.dim() == 3 else out
+
+
+def _gemm_operands(a_codes, a_scales, a_row_index, b_codes, b_scales, group_offsets, M, N, K,
+                   b_scale_2d, group_dim_k):
+    """Check A, B and their scales against M, N, K and the group count (the
+    extents the kernel reads); returns (a_ld, b_ld, G)."""
+    torch = _torch()
+    u8 = torch.uint8
+    _dev(group_offsets, "group_offsets")
+    if group_offsets.dtype != torch.int32 or group_offsets.dim() != 1 or group_offsets.numel() < 2:
+        raise ValueError("group_offsets must be int32 [num_groups + 1]")
+    G = group_offsets.numel() - 1
+    a_rows = M
+    if a_row_index is not None:
+        _dev(a_row_index, "a_row_index")
+        if a_row_index.dtype != torch.int32 or a_row_index.numel() != M:
+            raise ValueError("a_row_index must be int32 [M]")
+        a_rows = a_codes.shape[0]
+    a_ld = _shaped(a_codes, (a_rows, K // 2), u8, "a_codes", pitched=True)
+    _shaped(a_scales, (a_rows, K // 32), u8, "a_scales")
+    if group_dim_k:
+        b_ld = _shaped(b_codes, (N, K // 2), u8, "b_codes", pitched=True)
+        _shaped(b_scales, (N, K // 32), u8, "b_scales")
+    else:
+        b_ld = _shaped(b_codes, (G, N, K // 2), u8, "b_codes", pitched=True)
+        _shaped(b_scales, (G, N // 32, K // 32) if b_scale_2d else (G, N, K // 32), u8, "b_scales")
+    return a_ld, b_ld, G
 
 
 def grouped_gemm(a_codes, a_scales, b_codes, b_scales, group_offsets, M, N, K,
@@ -267,17 +294,13 @@ def grouped_gemm(a_codes, a_scales, b_codes, b_scales, group_offsets, M, N, K,
     and b_codes may have padded rows (row-slice views of wider buffers); rows
     padded to whole 128-byte lines are read fastest."""
     torch = _torch()
-    for t, nm in ((a_scales, "a_scales"), (b_scales, "b_scales"), (group_offsets, "group_offsets")):
-        _dev(t, nm)
-    a_ld, b_ld = _codes(a_codes, "a_codes"), _codes(b_codes, "b_codes")
-    if a_row_index is not None:
-        _dev(a_row_index, "a_row_index")
-    G = group_offsets.numel() - 1
+    a_ld, b_ld, G = _gemm_operands(a_codes, a_scales, a_row_index, b_codes, b_scales, group_offsets,
+                                   M, N, K, b_scale_2d, group_dim_k)
     shape = (G, M, N) if group_dim_k else (M, N)
     if out is None:
         out = torch.empty(shape, dtype=out_dtype or torch.bfloat16, device=a_codes.device)
     else:
-        _out(out, shape, out_dtype or out.dtype, "out")
+        _shaped(out, shape, out_dtype or out.dtype, "out")
     _check("mx_grouped_gemm", lib().mx_grouped_gemm(
         _ptr(a_codes), a_ld, _ptr(a_scales), _ptr(a_row_index), _ptr(b_codes), b_ld, _ptr(b_scales),
         int(bool(b_scale_2d)), _ptr(group_offsets), G, int(bool(group_dim_k)), M, N, K,
@@ -293,21 +316,17 @@ def grouped_gemm_q(a_codes, a_scales, b_codes, b_scales, group_offsets, M, N, K,
     (c or None, codes [M x N/2], scales [M x N/32]); out / codes / scales
     are optional preallocated outputs."""
     torch = _torch()
-    for t, nm in ((a_scales, "a_scales"), (b_scales, "b_scales"), (group_offsets, "group_offsets")):
-        _dev(t, nm)
-    a_ld, b_ld = _codes(a_codes, "a_codes"), _codes(b_codes, "b_codes")
-    if a_row_index is not None:
-        _dev(a_row_index, "a_row_index")
-    G = group_offsets.numel() - 1
+    a_ld, b_ld, G = _gemm_operands(a_codes, a_scales, a_row_index, b_codes, b_scales, group_offsets,
+                                   M, N, K, b_scale_2d, False)
     dev = a_codes.device
     c = None
     if with_bf16:
         c = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-        _out(c, (M, N), torch.bfloat16, "out")
+        _shaped(c, (M, N), torch.bfloat16, "out")
     codes = codes if codes is not None else torch.empty((M, N // 2), dtype=torch.uint8, device=dev)
-    c_ld = _out(codes, (M, N // 2), torch.uint8, "codes", pitched=True)
+    c_ld = _shaped(codes, (M, N // 2), torch.uint8, "codes", pitched=True)
     scales = scales if scales is not None else torch.empty((M, N // 32), dtype=torch.uint8, device=dev)
-    _out(scales, (M, N // 32), torch.uint8, "scales")
+    _shaped(scales, (M, N // 32), torch.uint8, "scales")
     _check("mx_grouped_gemm_q", lib().mx_grouped_gemm_q(
         _ptr(a_codes), a_ld, _ptr(a_scales), _ptr(a_row_index), _ptr(b_codes), b_ld, _ptr(b_scales),
         int(bool(b_scale_2d)), _ptr(group_offsets), G, M, N, K, float(alpha),

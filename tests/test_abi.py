@@ -167,12 +167,12 @@ def test_output_buffer_checks():
     import torch
     u8 = torch.uint8
     with pytest.raises(ValueError, match="expected shape"):
-        mx._out(torch.empty(3, 4, dtype=u8), (3, 5), u8, "codes", pitched=True)
+        mx._shaped(torch.empty(3, 4, dtype=u8), (3, 5), u8, "codes", pitched=True)
     with pytest.raises(ValueError, match="expected shape"):
-        mx._out(torch.empty(2, 3, 4, dtype=u8), (1, 3, 4), u8, "codes")
+        mx._shaped(torch.empty(2, 3, 4, dtype=u8), (1, 3, 4), u8, "codes")
     with pytest.raises(TypeError, match="expected"):
-        mx._out(torch.empty(3, 4, dtype=torch.float32), (3, 4), torch.bfloat16, "out")
+        mx._shaped(torch.empty(3, 4, dtype=torch.float32), (3, 4), torch.bfloat16, "out")
     # right shape (a leading batch of 1 may be left out) and dtype: only the
     # device check remains
     with pytest.raises(ValueError, match="device"):
-        mx._out(torch.empty(3, 4, dtype=u8), (1, 3, 4), u8, "codes", pitched=True)
+        mx._shaped(torch.empty(3, 4, dtype=u8), (1, 3, 4), u8, "codes", pitched=True)
