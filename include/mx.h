@@ -136,7 +136,9 @@ mx_status mx_quantize_1d(const void* x, mx_dtype xt, int64_t rows, int64_t cols,
  * both, so the transposed pair is exactly the quantization of w^T.  Either
  * pair may be NULL (not both).  codes_ld / codes_t_ld: bytes from one code
  * row to the next in each layout (0 = cols/2 and rows/2; else at least that
- * and a multiple of 16); a batch entry spans rows (cols) such rows.
+ * and a multiple of 16); a batch entry spans rows (cols) such rows.  An
+ * empty input (batch, rows or cols 0) returns MX_OK before any pointer is
+ * checked.
  * Pages: "What ALTO Actually Does" (UE8M0 per block), Abstract (hybrid
  * 1D/2D). */
 mx_status mx_quantize_2d(const void* w, mx_dtype wt, int64_t batch, int64_t rows, int64_t cols,

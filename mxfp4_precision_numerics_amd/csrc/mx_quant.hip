@@ -936,10 +936,10 @@ mx_status mx_quantize_2d(const void* w, mx_dtype wt, int64_t batch, int64_t rows
                          uint8_t* scales_t, mx_stream stream) {
     if (wt != MX_F32 && wt != MX_BF16) return MX_ERR_DTYPE;
     if (batch < 0 || rows < 0 || cols < 0 || rows % 32 || cols % 32) return MX_ERR_SHAPE;
+    if (batch == 0 || rows == 0 || cols == 0) return MX_OK;     // (empty tensors may have null pointers)
     if ((codes == nullptr) != (scales == nullptr)) return MX_ERR_NULL;
     if ((codes_t == nullptr) != (scales_t == nullptr)) return MX_ERR_NULL;
     if (!codes && !codes_t) return MX_ERR_NULL;
-    if (batch == 0 || rows == 0 || cols == 0) return MX_OK;
     if (!w) return MX_ERR_NULL;
     if (!aligned16(w) || (codes && !aligned16(codes)) || (codes_t && !aligned16(codes_t))) return MX_ERR_ALIGN;
     // code row pitches: 0 = contiguous rows (cols / 2, rows / 2 bytes); else

@@ -79,6 +79,8 @@ def test_quantize_2d_validation(L):
     assert q(FAKE, mx.MX_BF16, 1, 64, 64, FAKE, 16, FAKE, None, 0, None, None) == 2
     assert q(FAKE, mx.MX_BF16, 1, 64, 64, None, 0, None, FAKE, 40, FAKE, None) == 2
     assert q(FAKE, mx.MX_BF16, 0, 32, 32, FAKE, 0, FAKE, None, 0, None, None) == 0
+    # empty: no pointer is looked at (zero-size tensors may have null pointers)
+    assert q(None, mx.MX_BF16, 0, 32, 32, None, 0, None, None, 0, None, None) == 0
 
 
 def test_dequantize_validation(L):

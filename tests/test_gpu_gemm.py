@@ -303,3 +303,21 @@ def test_full_size_wgrad_sampled_rows():
         sel = rows[:, 0] == g
         got = host(c[g][torch.as_tensor(rows[sel, 1], device=c.device)]).astype(np.float64)
         assert rel_fro(got, want[sel]) <= TOL, g
+
+
+def test_empty_m_through_binding():
+    """M = 0 (every group empty): the output has no rows and nothing is
+    launched; groups along K with empty ranges write zeros."""
+    import torch
+    a = torch.empty(0, 128, dtype=torch.uint8, device="cuda")
+    asc = torch.empty(0, 8, dtype=torch.uint8, device="cuda")
+    b = torch.zeros(2, 64, 128, dtype=torch.uint8, device="cuda")
+    bs = torch.full((2, 64, 8), 127, dtype=torch.uint8, device="cuda")
+    c = mx.grouped_gemm(a, asc, b, bs, dev(np.array([0, 0, 0], np.int32)), 0, 64, 256)
+    assert c.shape == (0, 64)
+    # groups along K, all of them empty: C is zero
+    ak = torch.zeros(64, 128, dtype=torch.uint8, device="cuda")
+    aks = torch.full((64, 8), 127, dtype=torch.uint8, device="cuda")
+    ck = mx.grouped_gemm(ak, aks, b[0], bs[0], dev(np.array([0, 0, 0], np.int32)), 64, 64, 256,
+                         group_dim_k=True, out=torch.full((2, 64, 64), 7.0, device="cuda"))
+    assert bool((ck == 0).all())

@@ -415,3 +415,19 @@ def test_dequantize_nan_scale():
     scales = np.array([[0xFF]], dtype=np.uint8)
     y = host(mx.dequantize(dev(codes), dev(scales)))
     assert np.all(np.isnan(y))
+
+
+def test_empty_inputs_through_binding():
+    """No rows, no batch: every call returns empty outputs of the right
+    shape and launches nothing."""
+    import torch
+    x = torch.empty(0, 64, dtype=torch.bfloat16, device="cuda")
+    c, s = mx.quantize_1d(x, rnd=mx.SR, seed=1)
+    assert c.shape == (0, 32) and s.shape == (0, 2)
+    w = torch.empty(0, 64, 96, dtype=torch.bfloat16, device="cuda")
+    c, s, ct, st = mx.quantize_2d(w)
+    assert c.shape == (0, 64, 48) and s.shape == (0, 2, 3) and ct.shape == (0, 96, 32) and st.shape == (0, 3, 2)
+    y = mx.dequantize(torch.empty(0, 32, dtype=torch.uint8, device="cuda"),
+                      torch.empty(0, 2, dtype=torch.uint8, device="cuda"))
+    assert y.shape == (0, 64)
+    torch.cuda.synchronize()
