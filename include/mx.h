@@ -8,8 +8,8 @@
  * power-of-two scale per block ("AMD's ALTO Gets 4-Bit MoE Training to
  * Within 0.007 of BF16", section "What ALTO Actually Does") -- an optional
  * randomized Hadamard transform (RHT) along the reduction dimension,
- * round-to-nearest-even or stochastic rounding, and the expert GEMM that only
- * ever sees the quantized operands, accumulated in FP32.
+ * round-to-nearest-even or stochastic rounding, and the expert GEMM over the
+ * quantized operands, accumulated in FP32.
  *
  * Conventions shared by every entry point
  *   - All tensor pointers are DEVICE pointers owned by the caller.  The library
@@ -78,7 +78,11 @@ int mx_version(void);
 const char* mx_status_str(mx_status s);
 
 /* The RHT sign mask for a seed: word 0 of Philox4x32-10 at counter 0 under
- * key (seed lo, seed hi).  Host function; no device work. */
+ * key (seed lo, seed hi).  Bit j set means element j of every 32-block has
+ * its sign flipped before the Walsh-Hadamard butterflies: the random-sign
+ * diagonal of the randomized Hadamard transform the recipe applies before
+ * quantizing (Abstract of "Training an MoE LLM in MXFP4: How We Closed the
+ * Gap to BF16").  Host function; no device work, cannot fail. */
 uint32_t mx_rht_sign_mask(uint64_t seed);
 
 /* Randomized Hadamard transform of every 32-block along the last axis.
@@ -145,19 +149,29 @@ mx_status mx_quantize_2d(const void* w, mx_dtype wt, int64_t batch, int64_t rows
                          uint8_t* codes, int64_t codes_ld, uint8_t* scales, uint8_t* codes_t,
                          int64_t codes_t_ld, uint8_t* scales_t, mx_stream stream);
 
-/* Exact decode: y = (-1)^s * E2M1[m] * 2^(byte - 127).
+/* Exact decode of MXFP4: each E2M1 element times the UE8M0 power-of-two
+ * scale its block shares (the format named in "What ALTO Actually Does",
+ * news digest "AMD's ALTO Gets 4-Bit MoE Training to Within 0.007 of
+ * BF16"), i.e.
+ * y = (-1)^s * E2M1[m] * 2^(byte - 127); a block with scale byte 0xFF
+ * decodes to NaN.
  * codes batch x [rows x cols/2], rows codes_ld bytes apart (0 = cols/2;
  * else at least that and a multiple of 16); block_rows = 1 (scales [rows x cols/32]) or
  * 32 (scales [rows/32 x cols/32], rows % 32 == 0); y batch x [rows x cols],
  * yt fp32 or bf16 (every decoded value is exact in both, except 6*2^(>=127)
- * which overflows to Inf).  cols % 32 == 0. */
+ * which overflows to Inf).  cols % 32 == 0.  Pointers are device pointers
+ * owned by the caller; codes and y 16-byte aligned, scales any.
+ * Errors: MX_ERR_DTYPE (yt), MX_ERR_SHAPE (sizes, block_rows, codes_ld),
+ * MX_ERR_NULL, MX_ERR_ALIGN, MX_ERR_LAUNCH.  An empty input returns MX_OK
+ * before any pointer is checked. */
 mx_status mx_dequantize(const uint8_t* codes, int64_t codes_ld, const uint8_t* scales, int64_t batch, int64_t rows,
                         int64_t cols, int block_rows, void* y, mx_dtype yt, mx_stream stream);
 
 /* Grouped MXFP4 GEMM with FP32 accumulation: per group,
  *   C = alpha * deq(A) . deq(B)^T,
  * both operands K-contiguous (codes [. x K/2], scales [. x K/32]).
- * The GEMM only ever sees the quantized operands ("What ALTO Actually Does").
+ * Both operands enter as MXFP4 codes and scales: the contraction consumes
+ * the quantized values, never the master values ("What ALTO Actually Does").
  * a_ld, b_ld: bytes from one code row of A (of B) to the next; 0 means K/2
  * (contiguous rows).  Otherwise at least K/2 and a multiple of 16.  Rows
  * padded to a multiple of 128 bytes are read as whole cache lines, which is

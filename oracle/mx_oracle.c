@@ -15,8 +15,9 @@
  *     high-precision GEMM, which is what oracle_grouped_gemm does in FP64.
  *   - "AMD's ALTO Gets 4-Bit MoE Training to Within 0.007 of BF16",
  *     section "What ALTO Actually Does": the format is E2M1 elements with one
- *     UE8M0 scale per block; the GEMM only ever sees the quantized value; one
- *     outlier sets the shared scale of its whole block.
+ *     UE8M0 scale per block; the expert GEMM consumes the quantized operands,
+ *     not the master values; one outlier sets the shared scale of its whole
+ *     block.
  *   - OCP Microscaling Formats (MX) Specification v1.0: E2M1 magnitudes
  *     {0, 0.5, 1, 1.5, 2, 3, 4, 6}, E8M0 scale with bias 127 (0xFF = NaN),
  *     block size 32, shared exponent floor(log2(amax)) - 2 for E2M1
@@ -396,17 +397,33 @@ int oracle_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t batch
     return 0;
 }
 
-/* Round a double to the nearest bf16 (ties to even), returned as its bits.
- * Used only to state what a bf16 output must be. */
+/* Round a double to the nearest bf16 (ties to the even significand), in one
+ * rounding from the double's exact value; returned as its bits.  bf16 has 8
+ * significant bits and fp32's exponent range: the spacing of bf16 values in
+ * [2^k, 2^(k+1)) is 2^(k-7), and 2^-133 below 2^-126 (subnormals).
+ * Magnitudes that round to 2^128 or above give Inf; NaN stays NaN.  Used
+ * only to state what a bf16 output must be. */
 uint16_t oracle_round_bf16(double v)
 {
-    float f = (float)v;  /* values handled here are exact in fp32 */
+    uint16_t sign = signbit(v) ? 0x8000u : 0u;
+    if (isnan(v)) return (uint16_t)(sign | 0x7FC0u);
+    double a = fabs(v);
+    if (isinf(a)) return (uint16_t)(sign | 0x7F80u);
+    if (a == 0.0) return sign;
+    int e;
+    (void)frexp(a, &e);                 /* a = f * 2^e, f in [0.5, 1) */
+    int k = e - 1;                      /* floor(log2 a) */
+    if (k < -126) k = -126;
+    double n = ldexp(a, 7 - k);         /* a / spacing: exact (power-of-two scaling) */
+    double fl = floor(n);
+    double frac = n - fl;               /* exact */
+    if (frac > 0.5 || (frac == 0.5 && fmod(fl, 2.0) != 0.0)) fl += 1.0;
+    double r = ldexp(fl, k - 7);        /* the rounded magnitude, exact */
+    if (r >= ldexp(1.0, 128)) return (uint16_t)(sign | 0x7F80u);
+    float f = (float)r;                 /* exact: r has at most 8 significant bits */
     uint32_t u;
     memcpy(&u, &f, 4);
-    if ((u & 0x7F800000u) == 0x7F800000u) return (uint16_t)((u >> 16) | ((u & 0xFFFF) ? 0x40 : 0));
-    uint32_t lsb = (u >> 16) & 1u;
-    u += 0x7FFFu + lsb;
-    return (uint16_t)(u >> 16);
+    return (uint16_t)(sign | (u >> 16));
 }
 
 /* ------------------------------------------------------------------ */

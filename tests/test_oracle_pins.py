@@ -559,3 +559,63 @@ def test_gemm_products_are_exact_in_fp64():
             _, C = oracle.grouped_gemm(a_codes, asc, b_codes[None], bsc[None],
                                        [0, 1], 1, 1, 32)
             assert C[0, 0] == oracle.decode(ca, 120) * oracle.decode(cb, 140)
+
+
+# --------------------------------------------------------------------------
+# Rounding a double to bf16 (what a bf16 GEMM output must be)
+# --------------------------------------------------------------------------
+def _bf16_value(bits):
+    return Fraction(float((np.uint32(bits) << np.uint32(16)).view(np.float32)))
+
+
+def _nearest_bf16_bits(v):
+    """Brute force: among a window of bf16 bit patterns around v, the one at
+    the smallest exact distance from v, ties to the even pattern; Inf when
+    v is at or beyond the point halfway between the largest finite bf16 and
+    2^128 (IEEE overflow rule)."""
+    sign = 0x8000 if math.copysign(1.0, v) < 0 else 0
+    a = abs(v)
+    if a >= float(Fraction(2) ** 128 - Fraction(2) ** (127 - 8)):
+        return sign | 0x7F80
+    mid = int(np.float32(a).view(np.uint32)) >> 16        # within one pattern of the answer
+    best = None
+    for b in range(max(0, mid - 3), min(0x7F7F, mid + 3) + 1):
+        d = abs(_bf16_value(b) - Fraction(a))
+        if best is None or d < best[0] or (d == best[0] and b % 2 == 0):
+            best = (d, b)
+    return sign | best[1]
+
+
+def test_round_bf16_is_one_rounding_from_double():
+    rng = np.random.default_rng(123)
+    vals = list(rng.standard_normal(400) * np.exp2(rng.integers(-140, 130, 400)))
+    # exact ties between neighbouring bf16 values (odd and even lower neighbour)
+    for b in (0x3F80, 0x3F81, 0x4110, 0x0001, 0x0080, 0x7F7E, 0x00FF):
+        m = (_bf16_value(b) + _bf16_value(b + 1)) / 2
+        vals += [float(m), -float(m)]
+    # just above a tie whose lower neighbour is even: the double is closer to
+    # the upper neighbour, but rounding it to fp32 first lands exactly on the
+    # tie, which then goes down to the even neighbour (a double rounding)
+    for b in (0x3F80, 0x4240, 0x3C00, 0x0100):
+        m = (_bf16_value(b) + _bf16_value(b + 1)) / 2
+        up = float(m + m * Fraction(1, 2 ** 40))
+        dn = float(m - m * Fraction(1, 2 ** 40))
+        assert float(np.float32(up)) == float(m)               # fp32 would round it to the tie
+        vals += [up, dn, -up]
+    # subnormal range, underflow to zero, overflow, signed zero
+    vals += [2.0 ** -133, 2.0 ** -134, 2.0 ** -134 * 1.0000001, 2.0 ** -135, 3 * 2.0 ** -135,
+             2.0 ** -126 * 0.75, 3.4e38, 3.3895e38, 3.39e38, 1e300, -1e300, 0.0, -0.0]
+    for v in vals:
+        want = _nearest_bf16_bits(v)
+        got = int(oracle.round_bf16_bits([v])[0])
+        assert got == want, (v, hex(got), hex(want))
+    # the double-rounding cases really differ from rounding through fp32
+    b = 0x3F80
+    m = (_bf16_value(b) + _bf16_value(b + 1)) / 2
+    assert int(oracle.round_bf16_bits([float(m + m * Fraction(1, 2 ** 40))])[0]) == b + 1
+
+
+def test_round_bf16_specials():
+    bits = oracle.round_bf16_bits([float("inf"), float("-inf"), float("nan")])
+    assert int(bits[0]) == 0x7F80 and int(bits[1]) == 0xFF80
+    assert (int(bits[2]) & 0x7F80) == 0x7F80 and (int(bits[2]) & 0x7F) != 0
