@@ -172,13 +172,19 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
     // (lane g: off[g]) and, when groups split M, the first tile id of each
     // group (a prefix sum of ceil(n_g / BM) * tiles_n), so finding a tile's
     // group is a ballot and two lane reads, with no memory round trip.
+    // The offsets come from the device and are trusted only this far: each
+    // is clamped to [0, M] (groups along M) or [0, K] (along K), and a group
+    // whose end lies below its start is empty, so malformed offsets can
+    // neither store outside C nor read past the operands.
+    const int32_t lim = GK ? (int32_t)p.K : (int32_t)p.M;
+    auto clamp_off = [lim](int32_t v) { return min(max(v, 0), lim); };
     const bool table = p.G < 64;
     int32_t off_l = 0, first_l = 0;
     if (table) {
-        if (lane <= p.G) off_l = p.off[lane];
+        if (lane <= p.G) off_l = clamp_off(p.off[lane]);
         if (!GK) {
             const int32_t next = __shfl_down(off_l, 1);
-            const int32_t t = lane < p.G ? (next - off_l + BM - 1) / BM * p.tiles_n : 0;
+            const int32_t t = lane < p.G && next > off_l ? (next - off_l + BM - 1) / BM * p.tiles_n : 0;
             int32_t incl = t;
 #pragma unroll
             for (int d = 1; d < 64; d <<= 1) {
@@ -213,7 +219,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
                 g = 63 - __builtin_clzll(below);
                 id -= __builtin_amdgcn_readlane(first_l, g);
                 mb = __builtin_amdgcn_readlane(off_l, g);
-                me = __builtin_amdgcn_readlane(off_l, g + 1);
+                me = max(mb, __builtin_amdgcn_readlane(off_l, g + 1));
             } else {
                 // many groups: scan the offsets 64 at a time
                 int32_t running = 0;
@@ -221,8 +227,8 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
                     const int gg = base + lane;
                     int32_t t = 0, gb = 0, ge = 0;
                     if (gg < p.G) {
-                        gb = p.off[gg];
-                        ge = p.off[gg + 1];
+                        gb = clamp_off(p.off[gg]);
+                        ge = max(gb, clamp_off(p.off[gg + 1]));
                         t = (ge - gb + BM - 1) / BM * p.tiles_n;
                     }
                     int32_t incl = t;
@@ -252,8 +258,8 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
             g = id / per;
             id -= g * per;
             mtiles = p.tiles_m;
-            kb = table ? __builtin_amdgcn_readlane(off_l, g) : p.off[g];
-            ke = table ? __builtin_amdgcn_readlane(off_l, g + 1) : p.off[g + 1];
+            kb = table ? __builtin_amdgcn_readlane(off_l, g) : clamp_off(p.off[g]);
+            ke = max(kb, table ? __builtin_amdgcn_readlane(off_l, g + 1) : clamp_off(p.off[g + 1]));
         }
         // grouped order inside the group: GROUP_M M-tiles x all N-tiles, m fastest
         const int32_t span = GROUP_M * p.tiles_n;

@@ -282,7 +282,7 @@ struct ColTile {
 template <bool BF16, bool RHT, bool SR>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BF16 ? 3 : 2))) void q1d_col_kernel(const void* __restrict__ x, int64_t cols,
                                                       const int32_t* __restrict__ off, int num_groups,
-                                                      const int32_t* __restrict__ ridx,
+                                                      const int32_t* __restrict__ ridx, int64_t npos,
                                                       int64_t kp, int64_t col_tiles, int vec,
                                                       uint32_t mask, uint32_t k0, uint32_t k1,
                                                       uint32_t stream_id, uint64_t index_base,
@@ -321,8 +321,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BF16 ? 3 : 
         if (tid == 255) pstart[num_groups] = run;
         __syncthreads();
     }
-    const int64_t nblk_total = pstart[num_groups];
+    // The offsets come from the device and are trusted only this far: the
+    // blocks written stop at the capacity kp, and a token position outside
+    // [0, npos) is read as padding, so malformed offsets can neither write
+    // past the outputs nor read past x (or the row index).
     const int64_t kp_blocks = kp >> 5;
+    const int64_t nblk_total = min((int64_t)pstart[num_groups], kp_blocks);
 
     // Token range of the tile's 8 blocks: lane b < 8 of every wave resolves
     // block b (its group by binary search over pstart); n = -1 marks a block
@@ -338,7 +342,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BF16 ? 3 : 
                 if (pstart[mid] <= pb) lo = mid; else hi = mid - 1;
             }
             t0 = (int64_t)off[lo] + (pb - pstart[lo]) * 32;
-            n = (int32_t)min((int64_t)32, (int64_t)off[lo + 1] - t0);
+            n = (int32_t)max((int64_t)0, min(min((int64_t)32, (int64_t)off[lo + 1] - t0), npos - t0));
+            if (t0 < 0) n = 0;
         }
     };
     auto bcast64 = [](int64_t v, int src) {
@@ -926,7 +931,7 @@ mx_status mx_quantize_1d(const void* x, mx_dtype xt, int64_t rows, int64_t cols,
         }
     }
     (void)hipGetLastError();
-    MX_DISPATCH3_LDS(q1d_col_kernel, bf, rh, sr, dim3(grid), lds, s, x, cols, group_offsets, (int)num_groups, row_index, kp,
+    MX_DISPATCH3_LDS(q1d_col_kernel, bf, rh, sr, dim3(grid), lds, s, x, cols, group_offsets, (int)num_groups, row_index, rows, kp,
                      col_tiles, vec, sign_mask, k0, k1, stream_id, index_base, codes, scales);
     return launched();
 }

@@ -145,12 +145,24 @@ def rht_sign_mask(seed: int) -> int:
     return int(lib().mx_rht_sign_mask(seed))
 
 
+def _index_vector(t, name, min_numel=0):
+    """A device int32 vector (offsets, row indices): a tensor of another type
+    would be read as int32 words and mis-group silently."""
+    torch = _torch()
+    if t.dtype != torch.int32 or t.dim() != 1 or t.numel() < min_numel:
+        raise ValueError("%s must be a 1-D int32 tensor%s" %
+                         (name, " of at least %d elements" % min_numel if min_numel else ""))
+    return _dev(t, name)
+
+
 def rht(x, sign_mask: int, inverse: bool = False, out=None):
     torch = _torch()
     _dev(x, "x")
     rows, cols = x.shape
     if out is None:
         out = torch.empty((rows, cols), dtype=torch.float32, device=x.device)
+    else:
+        _shaped(out, (rows, cols), torch.float32, "out")
     _check("mx_rht", lib().mx_rht(_ptr(x), _dtype_code(x), _ptr(out), rows, cols, sign_mask,
                                   int(inverse), _stream()))
     return out
@@ -178,13 +190,13 @@ def quantize_1d(x, block_axis: int = 1, group_offsets=None, kp: int = 0, use_rht
     _dev(x, "x")
     rows, cols = x.shape
     if row_index is not None:
-        _dev(row_index, "row_index")
+        _index_vector(row_index, "row_index")
         rows = row_index.numel()
     ng = 0
     if block_axis == 1:
         shape_c, shape_s = (rows, cols // 2), (rows, cols // 32)
     else:
-        _dev(group_offsets, "group_offsets")
+        _index_vector(group_offsets, "group_offsets", min_numel=2)
         ng = group_offsets.numel() - 1
         if not kp:
             kp = padded_capacity(rows, ng)
@@ -266,14 +278,12 @@ def _gemm_operands(a_codes, a_scales, a_row_index, b_codes, b_scales, group_offs
     extents the kernel reads); returns (a_ld, b_ld, G)."""
     torch = _torch()
     u8 = torch.uint8
-    _dev(group_offsets, "group_offsets")
-    if group_offsets.dtype != torch.int32 or group_offsets.dim() != 1 or group_offsets.numel() < 2:
-        raise ValueError("group_offsets must be int32 [num_groups + 1]")
+    _index_vector(group_offsets, "group_offsets", min_numel=2)
     G = group_offsets.numel() - 1
     a_rows = M
     if a_row_index is not None:
-        _dev(a_row_index, "a_row_index")
-        if a_row_index.dtype != torch.int32 or a_row_index.numel() != M:
+        _index_vector(a_row_index, "a_row_index")
+        if a_row_index.numel() != M:
             raise ValueError("a_row_index must be int32 [M]")
         a_rows = a_codes.shape[0]
     a_ld = _shaped(a_codes, (a_rows, K // 2), u8, "a_codes", pitched=True)

@@ -69,6 +69,8 @@ def lib():
         L.oracle_dequantize.argtypes = [P, P, i64, i64, i64, ctypes.c_int, P, i64, i64]
         L.oracle_round_bf16.argtypes = [ctypes.c_double]
         L.oracle_round_bf16.restype = ctypes.c_uint16
+        L.oracle_round_bf16_array.argtypes = [P, P, i64]
+        L.oracle_round_bf16_array.restype = None
         L.oracle_grouped_gemm.argtypes = [P, P, P, P, P, ctypes.c_int, P, i32, ctypes.c_int,
                                           i64, i64, i64, ctypes.c_double, P, P, i64, P]
         _lib = L
@@ -251,11 +253,19 @@ def decode(code: int, scale_byte: int) -> float:
     return float(lib().oracle_decode(code, scale_byte))
 
 
-def round_bf16_bits(values):
+def round_bf16_bits(values, threads: int | None = None):
+    """Nearest bf16 (ties to even) of each double, one rounding, as bit
+    patterns (uint16) of the same shape (see oracle_round_bf16)."""
     L = lib()
-    v = np.asarray(values, dtype=np.float64).ravel()
-    return np.array([L.oracle_round_bf16(float(t)) for t in v], dtype=np.uint16).reshape(
-        np.shape(values))
+    v = np.ascontiguousarray(np.asarray(values, dtype=np.float64).ravel())
+    out = np.empty(v.shape, dtype=np.uint16)
+    threads = threads or default_threads()
+
+    def job(a, b):
+        return lambda: L.oracle_round_bf16_array(v[a:].ctypes.data, out[a:].ctypes.data, b - a) or 0
+
+    _run([job(a, b) for a, b in _split(v.size, threads * 4)], threads)
+    return out.reshape(np.shape(values))
 
 
 def scale_byte(amax: float) -> int:

@@ -426,6 +426,12 @@ uint16_t oracle_round_bf16(double v)
     return (uint16_t)(sign | (u >> 16));
 }
 
+/* oracle_round_bf16 over an array: out[i] = round(v[i]) for i in [0, n). */
+void oracle_round_bf16_array(const double* v, uint16_t* out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_round_bf16(v[i]);
+}
+
 /* ------------------------------------------------------------------ */
 /* Grouped GEMM over dequantized operands, FP64, k ascending.            */
 /*                                                                      */

@@ -178,3 +178,21 @@ def test_output_buffer_checks():
     # device check remains
     with pytest.raises(ValueError, match="device"):
         mx._shaped(torch.empty(3, 4, dtype=u8), (1, 3, 4), u8, "codes", pitched=True)
+
+
+def test_index_vectors_are_checked():
+    """Group offsets and row indices must be 1-D int32 (an int64 tensor would
+    be read as pairs of int32 words); offsets need at least two entries.
+    These checks come before the device check, so they run on the CPU."""
+    import torch
+    with pytest.raises(ValueError, match="int32"):
+        mx._index_vector(torch.zeros(3, dtype=torch.int64), "group_offsets", min_numel=2)
+    with pytest.raises(ValueError, match="int32"):
+        mx._index_vector(torch.zeros(1, dtype=torch.int32), "group_offsets", min_numel=2)
+    with pytest.raises(ValueError, match="int32"):
+        mx._index_vector(torch.zeros(2, 2, dtype=torch.int32), "row_index")
+    with pytest.raises(ValueError, match="device"):
+        mx._index_vector(torch.zeros(2, dtype=torch.int32), "row_index")
+    # rht: a caller-provided output must be fp32 of x's shape
+    with pytest.raises(TypeError, match="float32"):
+        mx._shaped(torch.empty(4, 32, dtype=torch.bfloat16), (4, 32), torch.float32, "out")

@@ -2,8 +2,10 @@
 
 Operands are produced on the CPU (oracle quantizers or random bytes) and the
 same bytes are handed to both sides.  The bar: relative Frobenius error
-<= 1e-5 of the fp32 output against the FP64 oracle, per group; a bf16 output
-within half a bf16 ulp of the oracle value plus the fp32 accumulation error.
+<= 1e-5 of the fp32 output against the FP64 oracle, per group, and every fp32
+element within the worst-case fp32 accumulation error of its own products
+(check_elementwise); a bf16 output within half a bf16 ulp of the oracle value
+plus the fp32 accumulation error.
 """
 import numpy as np
 import pytest
@@ -38,7 +40,48 @@ def _check_bf16(got_bits, want):
     assert np.all(err <= bound), float(np.max(err / bound))
 
 
-def _run_fprop(counts, K, N, a_rows, b_2d, seed, out_dtype="f32", gather=True):
+def _abs_products(ac, asc, bc, bs, off, rows, N, idx=None, b_2d=False, group_dim_k=False):
+    """sum_k |deqA[m, k] deqB[n, k]| for each oracle row (group, m), from the
+    exactly dequantized operands in FP64: the scale of the fp32 accumulation
+    error of that output element."""
+    out = np.zeros((len(rows), N))
+    for g in np.unique(rows[:, 0]):
+        sel = rows[:, 0] == g
+        ms = rows[sel, 1]
+        if not group_dim_k:
+            ar = ms if idx is None else np.asarray(idx)[ms]
+            A = np.abs(oracle.dequantize(ac[ar], asc[ar]))
+            B = np.abs(oracle.dequantize(bc[g], bs[g], block_rows=32 if b_2d else 1))
+        else:
+            k0, k1 = int(off[g]), int(off[g + 1])
+            if k1 <= k0:
+                continue
+            A = np.abs(oracle.dequantize(np.ascontiguousarray(ac[ms, k0 // 2:k1 // 2]),
+                                         np.ascontiguousarray(asc[ms, k0 // 32:k1 // 32])))
+            B = np.abs(oracle.dequantize(np.ascontiguousarray(bc[:, k0 // 2:k1 // 2]),
+                                         np.ascontiguousarray(bs[:, k0 // 32:k1 // 32])))
+        out[sel] = A @ B.T
+    return out
+
+
+def check_elementwise(got, want, abs_prod, nterms):
+    """Every fp32 output element within the worst-case error of an fp32
+    accumulation of nterms exact products in any order,
+    |got - want| <= gamma_n * sum_k |a_k b_k|, gamma_n = n u / (1 - n u),
+    with u = 2^-23 (one unit in the last place per addition, so a
+    truncating accumulator is covered too).  A localized wrong element fails
+    here even when a norm over the whole output would hide it."""
+    nterms = np.asarray(nterms, dtype=np.float64)
+    u = 2.0 ** -23
+    gamma = nterms * u / (1 - nterms * u)
+    if gamma.ndim == 1:
+        gamma = gamma[:, None]
+    err = np.abs(np.asarray(got, np.float64) - want)
+    bound = gamma * abs_prod + 1e-37
+    assert np.all(err <= bound), (float(np.max(err / bound)), np.unravel_index(np.argmax(err / bound), err.shape))
+
+
+def _run_fprop(counts, K, N, a_rows, b_2d, seed, out_dtype="f32", gather=True, with_abs=False):
     import torch
     rng = np.random.default_rng(seed)
     off = synth.offsets_from_counts(counts)
@@ -59,6 +102,8 @@ def _run_fprop(counts, K, N, a_rows, b_2d, seed, out_dtype="f32", gather=True):
     rows, want = oracle.grouped_gemm(ac, asc, bc, bs, off, M, N, K, a_row_index=idx,
                                      b_scale_2d=b_2d)
     got = host(c)
+    if with_abs:
+        return off, rows, got, want, _abs_products(ac, asc, bc, bs, off, rows, N, idx=idx, b_2d=b_2d)
     return off, rows, got, want
 
 
@@ -70,13 +115,16 @@ def _run_fprop(counts, K, N, a_rows, b_2d, seed, out_dtype="f32", gather=True):
 ])
 @pytest.mark.parametrize("b_2d", [False, True])
 def test_fprop_grouped_fp32(counts, K, N, b_2d):
-    off, rows, got, want = _run_fprop(counts, K, N, a_rows=150, b_2d=b_2d, seed=sum(counts) + K)
+    off, rows, got, want, absp = _run_fprop(counts, K, N, a_rows=150, b_2d=b_2d, seed=sum(counts) + K,
+                                            with_abs=True)
     for g in range(len(counts)):
         sel = rows[:, 0] == g
         if not np.any(sel):
             continue
         ms = rows[sel, 1]
         assert rel_fro(got[ms], want[sel]) <= TOL, g
+    if len(rows):
+        check_elementwise(got[rows[:, 1]], want, absp, K)
 
 
 def _at_odd_address(t):
@@ -124,11 +172,12 @@ def test_fprop_many_groups_and_two_stage_tiles(K, b_2d):
     rng = np.random.default_rng(77 + K)
     counts = [int(v) for v in rng.integers(0, 40, 100)]
     counts[3], counts[50], counts[99] = 0, 300, 257
-    off, rows, got, want = _run_fprop(counts, K, 96, a_rows=200, b_2d=b_2d, seed=K + 1)
+    off, rows, got, want, absp = _run_fprop(counts, K, 96, a_rows=200, b_2d=b_2d, seed=K + 1, with_abs=True)
     for g in range(len(counts)):
         sel = rows[:, 0] == g
         if np.any(sel):
             assert rel_fro(got[rows[sel, 1]], want[sel]) <= TOL, g
+    check_elementwise(got[rows[:, 1]], want, absp, K)
 
 
 @pytest.mark.parametrize("even_total", [True, False])
@@ -152,12 +201,14 @@ def test_wgrad_many_groups(even_total):
     c = host(mx.grouped_gemm(dev(ac), dev(asc), dev(bc), dev(bs), dev(off), M, N, Kt,
                              group_dim_k=True, out_dtype=torch.float32))
     rows, want = oracle.grouped_gemm(ac, asc, bc, bs, off, M, N, Kt, group_dim_k=True)
+    absp = _abs_products(ac, asc, bc, bs, off, rows, N, group_dim_k=True)
     for g in range(len(counts)):
         sel = rows[:, 0] == g
         if counts[g] == 0:
             assert np.all(c[g] == 0), g
         else:
             assert rel_fro(c[g][rows[sel, 1]], want[sel]) <= TOL, g
+            check_elementwise(c[g][rows[sel, 1]], want[sel], absp[sel], counts[g])
 
 
 def test_fprop_bf16_output():
@@ -194,12 +245,14 @@ def test_wgrad_split_k_fp32(counts):
     c = host(mx.grouped_gemm(dev(ac), dev(asc), dev(bc), dev(bs), dev(off), M, N, Kt,
                              group_dim_k=True, out_dtype=torch.float32))
     rows, want = oracle.grouped_gemm(ac, asc, bc, bs, off, M, N, Kt, group_dim_k=True)
+    absp = _abs_products(ac, asc, bc, bs, off, rows, N, group_dim_k=True)
     for g in range(len(counts)):
         sel = rows[:, 0] == g
         if counts[g] == 0:
             assert np.all(c[g] == 0)
         else:
             assert rel_fro(c[g][rows[sel, 1]], want[sel]) <= TOL
+            check_elementwise(c[g][rows[sel, 1]], want[sel], absp[sel], counts[g])
 
 
 def test_alpha_scales_output():
@@ -244,6 +297,7 @@ def test_config4_full_size_fprop_sampled_rows():
     for g in range(32):
         sel = rows[:, 0] == g
         assert rel_fro(got[sel], want[sel]) <= TOL, g
+    check_elementwise(got, want, _abs_products(ac, asc, bct, bst, off, rows, N, idx=idx, b_2d=True), K)
     cb = mx.grouped_gemm(dev(ac), dev(asc), dev(bct), dev(bst), dev(off), M, N, K,
                          a_row_index=dev(idx), b_scale_2d=True, out_dtype=torch.bfloat16)
     _check_bf16(host(cb[torch.as_tensor(rows[:, 1], device=cb.device)]), want)
@@ -279,6 +333,7 @@ def test_full_size_dgrad_sampled_rows():
     for g in range(32):
         sel = rows[:, 0] == g
         assert rel_fro(got[sel], want[sel]) <= TOL, g
+    check_elementwise(got, want, _abs_products(ac, asc, bc, bs, off, rows, N, b_2d=True), K)
 
 
 def test_full_size_wgrad_sampled_rows():
@@ -299,10 +354,12 @@ def test_full_size_wgrad_sampled_rows():
                         out_dtype=torch.float32)
     sample = [(g, int(m)) for g in range(32) for m in (0, M - 1, rng.integers(0, M))]
     rows, want = oracle.grouped_gemm(ac, asc, bc, bs, poff, M, N, Kt, group_dim_k=True, rows=sample)
+    absp = _abs_products(ac, asc, bc, bs, poff, rows, N, group_dim_k=True)
     for g in range(32):
         sel = rows[:, 0] == g
         got = host(c[g][torch.as_tensor(rows[sel, 1], device=c.device)]).astype(np.float64)
         assert rel_fro(got, want[sel]) <= TOL, g
+        check_elementwise(got, want[sel], absp[sel], int(poff[g + 1] - poff[g]))
 
 
 def test_empty_m_through_binding():

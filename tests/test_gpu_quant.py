@@ -378,16 +378,33 @@ def test_2d_parity_both_layouts(batch, rows, cols, dt):
 
 def test_config3_full_size_2d():
     # 32 experts x bf16 [2880 x 5760] N(0, 0.02): the GPU quantizes all 32 in
-    # one launch, the oracle checks every expert in full (both layouts; about
-    # 0.13 s of oracle time per expert).
-    w = synth.normal_bf16((32, 2880, 5760), 0.02, seed=3)
-    c, s, ct, st = (host(t) for t in mx.quantize_2d(dev_bf16(w)))
-    for e in range(32):
+    # one launch, contiguous and with both code layouts' rows padded to whole
+    # 128-byte lines (2944 and 1536 bytes, as in the expert step); the oracle
+    # checks every expert in full, both layouts (about 0.13 s of oracle time
+    # per expert).  Then the bf16 dequantization of the W layout (read from
+    # the padded rows) against the oracle's exact decode, every element.
+    import torch
+    E, R, C = 32, 2880, 5760
+    w = synth.normal_bf16((E, R, C), 0.02, seed=3)
+    wd = dev_bf16(w)
+    c, s, ct, st = (host(t) for t in mx.quantize_2d(wd))
+    pbuf = torch.full((E, R, 2944), 0xA5, dtype=torch.uint8, device="cuda")
+    ptbuf = torch.full((E, C, 1536), 0xA5, dtype=torch.uint8, device="cuda")
+    ps = torch.empty((E, R // 32, C // 32), dtype=torch.uint8, device="cuda")
+    pst = torch.empty((E, C // 32, R // 32), dtype=torch.uint8, device="cuda")
+    mx.quantize_2d_into(wd, pbuf[..., :C // 2], ps, ptbuf[..., :R // 2], pst)
+    y = mx.dequantize(pbuf[..., :C // 2], ps, block_rows=32, out_dtype=torch.bfloat16)
+    pc, pct, hs, hst = host(pbuf[..., :C // 2].contiguous()), host(ptbuf[..., :R // 2].contiguous()), host(ps), host(pst)
+    assert bool((pbuf[..., C // 2:] == 0xA5).all()) and bool((ptbuf[..., R // 2:] == 0xA5).all())
+    for e in range(E):
         oc, os_, oct_, ost = oracle.quantize_2d(w[e])
-        _assert_same(s[e], os_, "scales e%d" % e)
-        _assert_same(c[e], oc, "codes e%d" % e)
-        _assert_same(st[e], ost, "scales_t e%d" % e)
-        _assert_same(ct[e], oct_, "codes_t e%d" % e)
+        for tag, (gc, gs, gct, gst) in (("", (c, s, ct, st)), ("pitched ", (pc, hs, pct, hst))):
+            _assert_same(gs[e], os_, tag + "scales e%d" % e)
+            _assert_same(gc[e], oc, tag + "codes e%d" % e)
+            _assert_same(gst[e], ost, tag + "scales_t e%d" % e)
+            _assert_same(gct[e], oct_, tag + "codes_t e%d" % e)
+        want = oracle.dequantize(oc, os_, block_rows=32)
+        _assert_same(host(y[e]), oracle.round_bf16_bits(want), "dequantized e%d" % e)
 
 
 # ---------------------------------------------------------------------------
