@@ -64,6 +64,8 @@ def lib():
                                          ctypes.c_int, u32, ctypes.c_int, u64, u32, u64,
                                          P, P, i64, i64]
         L.oracle_quantize_2d.argtypes = [P, ctypes.c_int, i64, i64, i64, P, P, P, P, i64, i64]
+        L.oracle_quantize_2d_deosc.argtypes = [P, ctypes.c_int, i64, i64, i64, P, P, ctypes.c_int,
+                                               P, P, P, P, P, i64, i64]
         L.oracle_decode.argtypes = [ctypes.c_uint8, ctypes.c_uint8]
         L.oracle_decode.restype = ctypes.c_double
         L.oracle_dequantize.argtypes = [P, P, i64, i64, i64, ctypes.c_int, P, i64, i64]
@@ -225,6 +227,37 @@ def quantize_2d(w, threads: int | None = None):
     if squeeze:
         return codes[0], scales[0], codes_t[0], scales_t[0]
     return codes, scales, codes_t, scales_t
+
+
+def quantize_2d_deosc(w, prev_codes, prev_scales, margin64: int, threads: int | None = None):
+    """32x32 RTNE quantization with the de-oscillation hysteresis against the
+    previous step's as-given codes and scales (see mx_oracle.c,
+    oracle_quantize_2d_deosc).  Returns (codes, scales, codes_t, scales_t,
+    flips)."""
+    w = np.ascontiguousarray(w)
+    squeeze = w.ndim == 2
+    if squeeze:
+        w = w[None]
+    batch, rows, cols = w.shape
+    pc = np.ascontiguousarray(prev_codes).reshape(batch, rows, cols // 2)
+    ps = np.ascontiguousarray(prev_scales).reshape(batch, rows // 32, cols // 32)
+    codes = np.zeros((batch, rows, cols // 2), dtype=np.uint8)
+    scales = np.zeros((batch, rows // 32, cols // 32), dtype=np.uint8)
+    codes_t = np.zeros((batch, cols, rows // 2), dtype=np.uint8)
+    scales_t = np.zeros((batch, cols // 32, rows // 32), dtype=np.uint8)
+    flips = np.zeros((batch, rows // 32, cols // 32), dtype=np.uint16)
+    L = lib()
+    dt = _dtype_code(w)
+    threads = threads or default_threads()
+
+    def job(a, b):
+        return lambda: L.oracle_quantize_2d_deosc(_ptr(w), dt, batch, rows, cols, _ptr(pc), _ptr(ps),
+                                                  int(margin64), _ptr(codes), _ptr(scales), _ptr(codes_t),
+                                                  _ptr(scales_t), _ptr(flips), a, b)
+
+    _run([job(a, b) for a, b in _split(rows // 32, threads * 4)], threads)
+    out = (codes, scales, codes_t, scales_t, flips)
+    return tuple(t[0] for t in out) if squeeze else out
 
 
 def dequantize(codes, scales, block_rows: int = 1, threads: int | None = None):

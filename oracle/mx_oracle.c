@@ -365,6 +365,111 @@ int oracle_quantize_2d(const void* w, int dtype, int64_t batch, int64_t rows, in
 }
 
 /* ------------------------------------------------------------------ */
+/* 2D quantize with weight de-oscillation (hysteresis against the        */
+/* previous step's quantized weights).                                   */
+/*                                                                      */
+/* "AMD's ALTO Gets 4-Bit MoE Training to Within 0.007 of BF16", section */
+/* "What ALTO Actually Does": the optimizer moves a full-precision      */
+/* master weight while the GEMM consumes its quantized value, so a     */
+/* weight sitting near a rounding boundary can alternate between two   */
+/* levels from updates far smaller than a level step.  The pages name a */
+/* simplified de-oscillation scheme (Abstract of "Training an MoE LLM  */
+/* in MXFP4") but give no formula; the reading implemented here is a   */
+/* hysteresis band:                                                    */
+/*   - the tile's scale byte comes from its amax as in                 */
+/*     oracle_quantize_2d;                                              */
+/*   - if it equals the previous step's byte for that tile (and neither */
+/*     is 0xFF), each element keeps its previous code c_p while its     */
+/*     scaled value v = w / 2^X lies strictly inside                    */
+/*       (q_p - f (q_p - q_dn),  q_p + f (q_up - q_p)),                */
+/*     q_p the value of c_p on the signed E2M1 grid                     */
+/*     {-6, -4, -3, -2, -1.5, -1, -0.5, 0, 0.5, ..., 6} (both zero     */
+/*     codes are the point 0), q_dn and q_up its neighbours on that     */
+/*     grid (none past +-6: the band is open on that side), and         */
+/*     f = 1/2 + margin64/64, margin64 in [0, 31].  f = 1/2 is exactly  */
+/*     the rounding interval of q_p, so margin64 = 0 changes no value;  */
+/*     a larger margin widens the band by margin64/64 of a grid step on */
+/*     each side;                                                        */
+/*   - otherwise the element takes its round-to-nearest-even code;      */
+/*   - a tile whose scale changed is quantized as without hysteresis.  */
+/* flips (optional): per tile, the number of elements whose value       */
+/* (code and scale, decoded) differs from the previous one; a NaN      */
+/* scale on either side counts every element.                          */
+/* prev_codes [batch x rows x cols/2], prev_scales [batch x rows/32 x   */
+/* cols/32] (the as-given layout of the previous call); outputs as in   */
+/* oracle_quantize_2d plus flips [batch x rows/32 x cols/32].           */
+/* ------------------------------------------------------------------ */
+double oracle_decode(uint8_t code, uint8_t scale_byte);
+
+static const double SIGNED_GRID[15] = {-6.0, -4.0, -3.0, -2.0, -1.5, -1.0, -0.5, 0.0,
+                                       0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+
+/* position of a code on the signed grid */
+static int signed_grid_index(uint8_t code)
+{
+    int m = code & 7;
+    if (m == 0) return 7;
+    return (code & 8) ? 7 - m : 7 + m;
+}
+
+int oracle_quantize_2d_deosc(const void* w, int dtype, int64_t batch, int64_t rows, int64_t cols,
+                             const uint8_t* prev_codes, const uint8_t* prev_scales, int margin64,
+                             uint8_t* codes, uint8_t* scales, uint8_t* codes_t, uint8_t* scales_t,
+                             uint16_t* flips, int64_t tr_begin, int64_t tr_end)
+{
+    if (rows % 32 || cols % 32) return 2;
+    if (margin64 < 0 || margin64 > 31) return 2;
+    const double f = 0.5 + margin64 / 64.0;
+    float v[1024];
+    uint8_t code[1024];
+    for (int64_t bt = 0; bt < batch; ++bt) {
+        for (int64_t tr = tr_begin; tr < tr_end; ++tr) {
+            for (int64_t tc = 0; tc < cols / 32; ++tc) {
+                for (int i = 0; i < 32; ++i)
+                    for (int j = 0; j < 32; ++j)
+                        v[i * 32 + j] = load_elem(w, dtype,
+                                                  bt * rows * cols + (tr * 32 + i) * cols + tc * 32 + j);
+                uint8_t byte = quantize_block(v, 1024, 0, NULL, code);
+                int64_t sidx = bt * (rows / 32) * (cols / 32) + tr * (cols / 32) + tc;
+                uint8_t pbyte = prev_scales[sidx];
+                const uint8_t* pc = prev_codes + bt * rows * (cols / 2);
+                int hyst = (byte == pbyte && byte != 0xFF);
+                int nflip = 0;
+                for (int i = 0; i < 32; ++i)
+                    for (int j = 0; j < 32; ++j) {
+                        int64_t e = (tr * 32 + i) * cols + tc * 32 + j;
+                        uint8_t pb = pc[e / 2];
+                        uint8_t cp = (e % 2 == 0) ? (pb & 0xF) : (pb >> 4);
+                        uint8_t* c = &code[i * 32 + j];
+                        if (hyst && *c != cp) {
+                            int k = signed_grid_index(cp);
+                            double q = SIGNED_GRID[k];
+                            double lo = (k == 0) ? -INFINITY : q - f * (q - SIGNED_GRID[k - 1]);
+                            double hi = (k == 14) ? INFINITY : q + f * (SIGNED_GRID[k + 1] - q);
+                            double sv = ldexp((double)v[i * 32 + j], -((int)byte - 127));
+                            if (sv > lo && sv < hi) *c = cp;
+                        }
+                        double now = oracle_decode(*c, byte), before = oracle_decode(cp, pbyte);
+                        if (!(now == before)) ++nflip;
+                    }
+                if (scales) scales[sidx] = byte;
+                if (scales_t) scales_t[bt * (rows / 32) * (cols / 32) + tc * (rows / 32) + tr] = byte;
+                if (flips) flips[sidx] = (uint16_t)nflip;
+                for (int i = 0; i < 32; ++i)
+                    for (int j = 0; j < 32; ++j) {
+                        int64_t r = tr * 32 + i, cc = tc * 32 + j;
+                        if (codes)
+                            put_nibble(codes + bt * rows * (cols / 2), r * cols + cc, code[i * 32 + j]);
+                        if (codes_t)
+                            put_nibble(codes_t + bt * rows * (cols / 2), cc * rows + r, code[i * 32 + j]);
+                    }
+            }
+        }
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
 /* Dequantize.                                                           */
 /* ------------------------------------------------------------------ */
 double oracle_decode(uint8_t code, uint8_t scale_byte)
