@@ -11,11 +11,19 @@ step runs, in order:
   Q1D(dY2) SR -> GEMM dh = dY2 W2^T ; Q1D(dY1) SR -> GEMM dX = dY1 W1^T
   Qcol(h), Qcol(dY2) RHT+SR -> GEMM dW2 = h^T dY2   (groups split K), fp32 out
   Qcol(X), Qcol(dY1) RHT+SR -> GEMM dW1 = X^T dY1   fp32 out
-The metric is BASELINE's pair: quantize GB/s and grouped-GEMM TFLOP/s, each
-as a fraction of its MI355X roofline; `value` is the whole step's algorithmic
-GEMM FLOPs divided by the step time.
+The metric is the pair quantize GB/s and grouped-GEMM TFLOP/s, each as a
+fraction of its MI355X roofline; `value` is the whole step's algorithmic GEMM
+FLOPs divided by the step time.
 
-Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+Every kernel instantiation is a role of its own, timed with HIP events on
+the launch stream, and set against its binding roofline: HBM bytes / 8 TB/s
+or FLOPs / 10.1 PFLOP/s, whichever floor is higher.  The line also carries
+the stand-alone workloads (1x32 RTNE of a 256x512 fp32 outlier matrix; RHT
++ SR of 16384x2880 bf16 activations; 2D quantize and dequantize of 32 expert
+weights 2880x5760; the grouped forward GEMM), with their round-trip error.
+
+Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--config {1,2,3,4,5}]
+                       [--no-cpu-baseline] [--no-standalone]
 """
 from __future__ import annotations
 
@@ -32,15 +40,26 @@ sys.path.insert(0, ROOT)
 import numpy as np  # noqa: E402
 
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic.txt")
-# kernel-name prefix (template arguments without spaces) of each GEMM role:
-# bf16 output with 2D weight scales, fp32 output with 1D scales
-# kernel-name prefixes of each role's launches (the last template argument,
-# the quantizing epilogue, is off in the step)
-ROLE_KERNEL = {"gemm": "gemm_kernel<true,true,", "gemm_wgrad": "gemm_kernel<false,false,true,"}
 PEAK_FP4_TFLOPS = 10100.0      # MI355X dense FP4 MFMA, TFLOP/s
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic.txt")
 E, D, F2, T, TOPK = 32, 2880, 5760, 16384, 4
 ROWS = T * TOPK
+BPE_1D = 2 + 0.5 + 1 / 32      # bf16 in, codes + 1x32 scales out, per element
+CS = 0.5 + 1 / 32              # 1x32 MXFP4 bytes per element
+WS = 0.5 + 1 / 1024            # 32x32 MXFP4 bytes per element (one layout)
+
+# role -> the kernel instantiation it launches (name without spaces)
+ROLE_KERNEL = {
+    "q2d": "q2d_kernel<true,false>",
+    "q1d_row_rtne": "q1d_row_kernel_w<true,false,false>",
+    "q1d_row_sr": "q1d_row_kernel_w<true,false,true>",
+    "q1d_col": "q1d_col_kernel<true,true,true>",
+    "gemm_fwd_gather": "gemm_kernel<true,true,false,true,true,false>",
+    "gemm_bf16": "gemm_kernel<true,true,false,false,true,false>",
+    "gemm_wgrad": "gemm_kernel<false,false,true,false,true,false>",
+}
+QUANT_ROLES = ("q2d", "q1d_row_rtne", "q1d_row_sr", "q1d_col")
+GEMM_ROLES = ("gemm_fwd_gather", "gemm_bf16", "gemm_wgrad")
 
 
 def build_inputs(torch, dev):
@@ -115,20 +134,20 @@ class Step:
         off, poff, idx = i["off"], i["poff"], i["idx"]
         self._t("q2d", lambda: mx.quantize_2d_into(i["W1"], b["w1c"], b["w1s"], b["w1tc"], b["w1ts"]))
         self._t("q2d", lambda: mx.quantize_2d_into(i["W2"], b["w2c"], b["w2s"], b["w2tc"], b["w2ts"]))
-        self._t("q1d_row", lambda: mx.quantize_1d(i["X"], codes=b["xc"], scales=b["xs"]))
-        self._t("gemm", lambda: mx.grouped_gemm(b["xc"], b["xs"], b["w1tc"], b["w1ts"], off, ROWS, F2, D,
-                                                a_row_index=idx, b_scale_2d=True, out=b["Y1"]))
-        self._t("q1d_row", lambda: mx.quantize_1d(i["h"], codes=b["hc"], scales=b["hs"]))
-        self._t("gemm", lambda: mx.grouped_gemm(b["hc"], b["hs"], b["w2tc"], b["w2ts"], off, ROWS, D, D,
-                                                b_scale_2d=True, out=b["Y2"]))
-        self._t("q1d_row", lambda: mx.quantize_1d(i["dY2"], rnd=mx.SR, seed=5, stream_id=1,
-                                                  codes=b["g2c"], scales=b["g2s"]))
-        self._t("gemm", lambda: mx.grouped_gemm(b["g2c"], b["g2s"], b["w2c"], b["w2s"], off, ROWS, D, D,
-                                                b_scale_2d=True, out=b["dh"]))
-        self._t("q1d_row", lambda: mx.quantize_1d(i["dY1"], rnd=mx.SR, seed=5, stream_id=0,
-                                                  codes=b["g1c"], scales=b["g1s"]))
-        self._t("gemm", lambda: mx.grouped_gemm(b["g1c"], b["g1s"], b["w1c"], b["w1s"], off, ROWS, D, F2,
-                                                b_scale_2d=True, out=b["dX"]))
+        self._t("q1d_row_rtne", lambda: mx.quantize_1d(i["X"], codes=b["xc"], scales=b["xs"]))
+        self._t("gemm_fwd_gather", lambda: mx.grouped_gemm(b["xc"], b["xs"], b["w1tc"], b["w1ts"], off, ROWS, F2,
+                                                           D, a_row_index=idx, b_scale_2d=True, out=b["Y1"]))
+        self._t("q1d_row_rtne", lambda: mx.quantize_1d(i["h"], codes=b["hc"], scales=b["hs"]))
+        self._t("gemm_bf16", lambda: mx.grouped_gemm(b["hc"], b["hs"], b["w2tc"], b["w2ts"], off, ROWS, D, D,
+                                                     b_scale_2d=True, out=b["Y2"]))
+        self._t("q1d_row_sr", lambda: mx.quantize_1d(i["dY2"], rnd=mx.SR, seed=5, stream_id=1,
+                                                     codes=b["g2c"], scales=b["g2s"]))
+        self._t("gemm_bf16", lambda: mx.grouped_gemm(b["g2c"], b["g2s"], b["w2c"], b["w2s"], off, ROWS, D, D,
+                                                     b_scale_2d=True, out=b["dh"]))
+        self._t("q1d_row_sr", lambda: mx.quantize_1d(i["dY1"], rnd=mx.SR, seed=5, stream_id=0,
+                                                     codes=b["g1c"], scales=b["g1s"]))
+        self._t("gemm_bf16", lambda: mx.grouped_gemm(b["g1c"], b["g1s"], b["w1c"], b["w1s"], off, ROWS, D, F2,
+                                                     b_scale_2d=True, out=b["dX"]))
         col = dict(block_axis=0, group_offsets=off, kp=self.kp, use_rht=True, sign_mask=m, rnd=mx.SR, seed=5)
         self._t("q1d_col", lambda: mx.quantize_1d(i["h"], stream_id=4, codes=b["hTc"], scales=b["hTs"], **col))
         self._t("q1d_col", lambda: mx.quantize_1d(i["dY2"], stream_id=5, codes=b["g2Tc"], scales=b["g2Ts"], **col))
@@ -144,28 +163,63 @@ class Step:
 
 
 def work_model():
-    """Algorithmic work per role in one step (bytes moved at minimum, or
-    FLOPs): 1D quantize from bf16 = 2 + 1/2 + 1/32 B per element; 2D with both
-    layouts = 2 + 1/2 + 1/2 + 2/1024 B per element; GEMM = 2 M N K with the
-    real (unpadded) token count."""
-    el_row = T * D + ROWS * D + ROWS * D + ROWS * F2
-    el_col = ROWS * D * 3 + ROWS * F2
-    el_2d = E * D * F2 + E * D * D
+    """Algorithmic work per role in one step: each input read once, each
+    output written once (padding and cache re-reads do not count), and
+    2 M N K FLOPs over the real (unpadded) token rows.
+
+    - 1D quantize from bf16: 2 B read + 0.5 + 1/32 B written per element;
+      the gathered X of the weight gradient is read once (16,384 token rows)
+      but written for every routed row (65,536).
+    - 2D quantize, both layouts: 2 B read + 2 x (0.5 + 1/1024) B written.
+    - GEMM: the A and B codes and scales read once, C written once (bf16, or
+      fp32 for the weight gradient)."""
+    gemm_fwd_gather = {
+        "flops": 2.0 * ROWS * D * F2,
+        "bytes": T * D * CS + E * F2 * D * WS + ROWS * F2 * 2,
+    }
+    # Y2 = h W2, dh = dY2 W2^T, dX = dY1 W1^T
+    gemm_bf16 = {
+        "flops": 2.0 * ROWS * (D * D + D * D + F2 * D),
+        "bytes": (ROWS * D * CS + E * D * D * WS + ROWS * D * 2) * 2 + (ROWS * F2 * CS + E * D * F2 * WS + ROWS * D * 2),
+    }
+    # dW2 = h^T dY2, dW1 = X^T dY1
+    gemm_wgrad = {
+        "flops": 2.0 * ROWS * (D * D + D * F2),
+        "bytes": (2 * ROWS * D * CS + E * D * D * 4) + (ROWS * D * CS + ROWS * F2 * CS + E * D * F2 * 4),
+    }
     return {
-        "q1d_row": {"bytes": el_row * (2 + 0.5 + 1 / 32), "launches": 4},
-        "q1d_col": {"bytes": el_col * (2 + 0.5 + 1 / 32), "launches": 4},
-        "q2d": {"bytes": el_2d * (2 + 0.5 + 0.5 + 2 / 1024), "launches": 2},
-        "gemm": {"flops": 2.0 * ROWS * (D * F2 + D * D + D * D + F2 * D), "launches": 4},
-        "gemm_wgrad": {"flops": 2.0 * ROWS * (D * D + D * F2), "launches": 2},
+        "q2d": {"bytes": (E * D * F2 + E * D * D) * (2 + 2 * WS), "launches": 2},
+        "q1d_row_rtne": {"bytes": (T * D + ROWS * D) * BPE_1D, "launches": 2},
+        "q1d_row_sr": {"bytes": (ROWS * D + ROWS * F2) * BPE_1D, "launches": 2},
+        "q1d_col": {"bytes": (T * D + 2 * ROWS * D + ROWS * F2) * 2 + (3 * ROWS * D + ROWS * F2) * CS,
+                    "launches": 4},
+        "gemm_fwd_gather": dict(gemm_fwd_gather, launches=1),
+        "gemm_bf16": dict(gemm_bf16, launches=3),
+        "gemm_wgrad": dict(gemm_wgrad, launches=2),
     }
 
 
+def roof(work, ms):
+    """The binding roofline of a kernel doing `work` in `ms`: the floor time
+    at HBM peak (bytes) or FP4 MFMA peak (flops), whichever is longer, and
+    the achieved rate in that roof's unit."""
+    s = ms / 1e3
+    t_hbm = work.get("bytes", 0.0) / (PEAK_HBM_GBS * 1e9)
+    t_mfma = work.get("flops", 0.0) / (PEAK_FP4_TFLOPS * 1e12)
+    if t_mfma >= t_hbm:
+        ach = work["flops"] / s / 1e12
+        return {"bound": "mfma", "achieved": ach, "peak": PEAK_FP4_TFLOPS, "unit": "TFLOP/s",
+                "frac": ach / PEAK_FP4_TFLOPS}
+    ach = work["bytes"] / s / 1e9
+    return {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": ach / PEAK_HBM_GBS}
+
+
 def kernel_source_hash():
-    """sha256 over the sources the GEMM kernel is compiled from."""
+    """sha256 over the device sources the GEMM kernel is compiled from."""
     import hashlib
     h = hashlib.sha256()
     for rel in ("mxfp4_precision_numerics_amd/csrc/mx_gemm.hip",
-                "mxfp4_precision_numerics_amd/csrc/mx_device.h", "include/mx.h"):
+                "mxfp4_precision_numerics_amd/csrc/mx_device.h"):
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
@@ -173,8 +227,8 @@ def kernel_source_hash():
 
 def measured_traffic(role):
     """HBM bytes per launch (scaled FETCH_SIZE + WRITE_SIZE) recorded for this
-    role's kernel, or None when no record exists or the kernel's sources have
-    changed since the counters were taken."""
+    role's kernel instantiation, or None when no record exists or the GEMM
+    sources have changed since the counters were taken."""
     if role not in ROLE_KERNEL or not os.path.exists(TRAFFIC_FILE):
         return None
     src, rec = None, {}
@@ -183,25 +237,117 @@ def measured_traffic(role):
         if len(f) >= 2 and f[0] == "source_sha256":
             src = f[1]
         elif len(f) >= 6 and f[0] == "kernel":
-            calls = float(f[7]) if len(f) >= 8 and f[6] == "calls" else 1.0
-            rec[f[1]] = (float(f[3]), float(f[5]), calls)
-    # a role may launch several instantiations (e.g. with and without a row
-    # gather): average over all of its dispatches
-    names = [k for k in rec if k.startswith(ROLE_KERNEL[role]) and k.endswith(",false>")]
-    if src != kernel_source_hash() or not names:
+            rec[f[1]] = (float(f[3]), float(f[5]))
+    name = ROLE_KERNEL[role]
+    if src != kernel_source_hash() or name not in rec:
         return None
-    n = sum(rec[k][2] for k in names)
-    rd = sum(rec[k][0] * rec[k][2] for k in names) / n
-    wr = sum(rec[k][1] * rec[k][2] for k in names) / n
+    rd, wr = rec[name]
     return {"read_bytes": rd, "write_bytes": wr, "bytes": rd + wr}
+
+
+def time_launches(torch, fns, reps, repeats=10):
+    """Median over `repeats` of the mean time of `reps` back-to-back launches
+    cycling through `fns` (ms per launch)."""
+    for f in fns:
+        f()
+    torch.cuda.synchronize()
+    out = []
+    for _ in range(repeats):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for k in range(reps):
+            fns[k % len(fns)]()
+        e.record()
+        torch.cuda.synchronize()
+        out.append(s.elapsed_time(e) / reps)
+    return float(np.median(out))
+
+
+def rel_err(torch, x, y):
+    """||x - y||_F / ||x||_F in float64 (round-trip error), and its SNR in dB."""
+    num = den = 0.0
+    for a, b in zip(x.reshape(-1).split(1 << 26), y.reshape(-1).split(1 << 26)):
+        a64 = a.double()
+        num += float(((a64 - b.double()) ** 2).sum())
+        den += float((a64 ** 2).sum())
+    r = math.sqrt(num / den)
+    return {"rel_err": r, "snr_db": -20 * math.log10(r) if r > 0 else float("inf")}
+
+
+# ---------------------------------------------------------------------------
+# Stand-alone workloads
+# ---------------------------------------------------------------------------
+def config1(torch, dev):
+    """1x32 RTNE of a 256x512 fp32 N(0,1) matrix with 131 entries (0.1%) x 50,
+    then dequantize to fp32: launch-latency bound (0.59 MB)."""
+    from mxfp4_precision_numerics_amd import mx
+    g = torch.Generator(device=dev).manual_seed(0)
+    x = torch.randn(256, 512, device=dev, generator=g)
+    pos = torch.randperm(256 * 512, device=dev, generator=g)[:131]
+    x.view(-1)[pos] *= 50.0
+    c, s = mx.quantize_1d(x)
+    y = mx.dequantize(c, s)
+    tq = time_launches(torch, [lambda: mx.quantize_1d(x, codes=c, scales=s)], 200)
+    td = time_launches(torch, [lambda: mx.dequantize(c, s, out=y)], 200)
+    nbytes = 256 * 512 * (4 + CS)
+    res = {"workload": "1x32 RTNE quantize + dequantize, fp32 256x512 N(0,1) with 0.1% outliers x50",
+           "quantize_ms": tq, "quantize_GBps": nbytes / tq / 1e6, "dequantize_ms": td,
+           "dequantize_GBps": nbytes / td / 1e6, "bound": "launch latency (0.59 MB)"}
+    res.update(rel_err(torch, x, y))
+    return res
+
+
+def config2(torch, dev):
+    """RHT + 1x32 SR of bf16 16384x2880 activations (N(0,1) x per-column
+    log-uniform[0.1, 10]); sign mask from seed 1, SR key 2.  Five input/output
+    sets (597 MB) rotate so the 256 MB Infinity Cache cannot hold the data."""
+    from mxfp4_precision_numerics_amd import mx
+    g = torch.Generator(device=dev).manual_seed(1)
+    c = torch.exp(torch.empty(D, device=dev).uniform_(math.log(0.1), math.log(10.0), generator=g))
+    sets = []
+    for _ in range(5):
+        x = (torch.randn(T, D, device=dev, generator=g) * c).to(torch.bfloat16)
+        sets.append((x, torch.empty(T, D // 2, dtype=torch.uint8, device=dev),
+                     torch.empty(T, D // 32, dtype=torch.uint8, device=dev)))
+    mask = mx.rht_sign_mask(1)
+    fns = [lambda s=s: mx.quantize_1d(s[0], use_rht=True, sign_mask=mask, rnd=mx.SR, seed=2,
+                                      codes=s[1], scales=s[2]) for s in sets]
+    t = time_launches(torch, fns, 50)
+    nbytes = T * D * BPE_1D
+    res = {"workload": "RHT + 1x32 SR quantize, bf16 16384x2880 activations (5 rotating sets, 597 MB)",
+           "ms": t, "GBps": nbytes / t / 1e6, "roofline": roof({"bytes": nbytes}, t)}
+    # round trip in the rotated basis: dequantized codes against RHT(x)
+    x, cc, ss = sets[0]
+    res.update(rel_err(torch, mx.rht(x, mask), mx.dequantize(cc, ss)))
+    return res
+
+
+def config3(torch, dev):
+    """2D (32x32) RTNE quantize of 32 expert weights bf16 2880x5760 N(0, 0.02)
+    (seed 3), both layouts, then dequantize the W layout to bf16."""
+    from mxfp4_precision_numerics_amd import mx
+    g = torch.Generator(device=dev).manual_seed(3)
+    w = (torch.randn(E, D, F2, device=dev, generator=g) * 0.02).to(torch.bfloat16)
+    c, s, ct, st = mx.quantize_2d(w)
+    y = mx.dequantize(c, s, block_rows=32, out_dtype=torch.bfloat16)
+    tq = time_launches(torch, [lambda: mx.quantize_2d_into(w, c, s, ct, st)], 5)
+    td = time_launches(torch, [lambda: mx.dequantize(c, s, block_rows=32, out=y)], 5)
+    n = E * D * F2
+    qb, db = n * (2 + 2 * WS), n * (WS + 2)
+    res = {"workload": "2D 32x32 RTNE quantize (both layouts) + bf16 dequantize, 32 x bf16 2880x5760 N(0,0.02)",
+           "quantize_ms": tq, "quantize_GBps": qb / tq / 1e6, "quantize_roofline": roof({"bytes": qb}, tq),
+           "dequantize_ms": td, "dequantize_GBps": db / td / 1e6, "dequantize_roofline": roof({"bytes": db}, td)}
+    res.update(rel_err(torch, w, y))
+    del w, c, s, ct, st, y
+    return res
 
 
 def fused_epilogue(torch, step, reps=5):
     """The quantizing epilogue on the second expert linear's forward GEMM
     (65536 x 2880 x 2880): its bf16 output quantized row-wise (1x32, RTNE) as
     the next MXFP4 GEMM's operand.  Times the GEMM followed by the 1D
-    quantizer against the fused call, with and without the bf16 output.
-    Measured after the timed steps, on the step's own buffers."""
+    quantizer against the fused call, with and without the bf16 output, on
+    the step's own buffers."""
     mx, b, i = step.mx, step.b, step.inp
     args = (b["hc"], b["hs"], b["w2tc"], b["w2ts"], i["off"], ROWS, D, D)
     runs = {
@@ -214,69 +360,108 @@ def fused_epilogue(torch, step, reps=5):
     }
     res = {"shape": "%dx%dx%d" % (ROWS, D, D)}
     for name, fn in runs.items():
-        for _ in range(2):
-            fn()
-        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        s.record()
-        for _ in range(reps):
-            fn()
-        e.record()
-        torch.cuda.synchronize()
-        res[name] = s.elapsed_time(e) / reps
+        res[name] = time_launches(torch, [fn], reps, repeats=5)
     return res
 
 
-def cpu_baseline(gemm_seconds=8.0):
+def cpu_baseline_config(k, gemm_seconds=8.0):
+    """The oracle on config k itself (configs 1-3 run whole; config 4 on
+    sampled output rows, extrapolated)."""
+    import oracle
+    from mxfp4_precision_numerics_amd import synth
+    threads = oracle.default_threads()
+    if k == 1:
+        x, _ = synth.outlier_matrix()
+        t0 = time.perf_counter()
+        reps = 0
+        while time.perf_counter() - t0 < 2.0:
+            c, s = oracle.quantize_1d(x)
+            oracle.dequantize(c, s)
+            reps += 1
+        dt = (time.perf_counter() - t0) / reps
+        return {"value": 256 * 512 * (4 + CS) / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+                "sample": "the whole 256x512 config, quantize + dequantize, %d repeats" % reps}
+    if k == 2:
+        x = synth.channel_scaled_activations()
+        t0 = time.perf_counter()
+        oracle.quantize_1d(x, use_rht=True, sign_mask=oracle.rht_sign_mask(1), rnd=oracle.SR, seed=2)
+        dt = time.perf_counter() - t0
+        return {"value": T * D * BPE_1D / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+                "sample": "the whole 16384x2880 config"}
+    if k == 3:
+        w = synth.normal_bf16((8, D, F2), 0.02, seed=3)
+        t0 = time.perf_counter()
+        oracle.quantize_2d(w)
+        dt = time.perf_counter() - t0
+        return {"value": w.size * (2 + 2 * WS) / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+                "sample": "8 of the 32 experts (2880x5760 each), both layouts"}
+    base = cpu_baseline(gemm_seconds)
+    return {"value": base["gemm_TFLOPs"], "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": base["gemm_sample"]}
+
+
+def cpu_baseline(gemm_seconds=8.0, single_thread=True):
     """The oracle, untuned, on a bounded sample of the same step; its rate per
     role is extrapolated to the full step.  The quantizers run on fixed
     slices; the FP64 GEMM runs batches of sampled output rows (full N, full K)
-    until about `gemm_seconds` have passed."""
+    until about `gemm_seconds` have passed.  With single_thread, a quarter of
+    the quantizer sample and 2 s of GEMM rows run again on one thread."""
     import oracle
     from mxfp4_precision_numerics_amd import synth
     threads = oracle.default_threads()
     rng = np.random.default_rng(0)
-    rows = 4096
-    xs = synth.channel_scaled_activations(rows=rows, cols=D, seed=1)
-    gs = synth.normal_bf16((rows, F2), 1e-3, seed=5)
     w = work_model()
-    per_el = 2 + 0.5 + 1 / 32
-    timings = {}
-    # row-wise RTNE and SR quantize: time per element
-    t0 = time.perf_counter()
-    oracle.quantize_1d(xs)
-    oracle.quantize_1d(gs, rnd=oracle.SR, seed=5)
-    dt = time.perf_counter() - t0
-    timings["q1d_row"] = dt / (rows * (D + F2)) * (w["q1d_row"]["bytes"] / per_el)
-    # column-wise RHT + SR over two ragged expert segments
-    off = np.array([0, 1500, rows], dtype=np.int32)
-    t0 = time.perf_counter()
-    oracle.quantize_1d(gs, block_axis=0, group_offsets=off, use_rht=True, sign_mask=1, rnd=oracle.SR, seed=5)
-    dt = time.perf_counter() - t0
-    timings["q1d_col"] = dt / (rows * F2) * (w["q1d_col"]["bytes"] / per_el)
-    # 2D, both layouts, on one full gate_up expert matrix
-    wsl = synth.normal_bf16((1, D, F2), 0.02, seed=5)
-    t0 = time.perf_counter()
-    oracle.quantize_2d(wsl)
-    dt = time.perf_counter() - t0
-    timings["q2d"] = dt / wsl.size * (E * D * F2 + E * D * D)
-    # GEMM: MAC rate on sampled output rows (full N, full K)
-    ac, asc = oracle.quantize_1d(synth.channel_scaled_activations(rows=256, cols=D, seed=1))
-    wb = synth.normal_bf16((1, F2, D), 0.02, seed=5)
-    bc, bs, _, _ = oracle.quantize_2d(wb)
-    done, dt = 0, 0.0
-    while dt < gemm_seconds and done < 4096:
-        sample_rows = [(0, int(m)) for m in rng.integers(0, 256, 2 * threads)]
+
+    def quant_rate(rows, nthreads):
+        """seconds per element of each quantizer role, on `rows` token rows"""
+        xs = synth.channel_scaled_activations(rows=rows, cols=D, seed=1)
+        gs = synth.normal_bf16((rows, F2), 1e-3, seed=5)
+        out = {}
         t0 = time.perf_counter()
-        oracle.grouped_gemm(ac, asc, bc, bs, [0, 256], 256, F2, D, b_scale_2d=True, rows=sample_rows)
-        dt += time.perf_counter() - t0
-        done += len(sample_rows)
-    mac_s = done * F2 * D / dt
-    timings["gemm"] = w["gemm"]["flops"] / 2 / mac_s
-    timings["gemm_wgrad"] = w["gemm_wgrad"]["flops"] / 2 / mac_s
-    t_total = sum(timings.values())
-    flops = w["gemm"]["flops"] + w["gemm_wgrad"]["flops"]
-    return {
+        oracle.quantize_1d(xs, threads=nthreads)
+        out["q1d_row_rtne"] = (time.perf_counter() - t0) / (rows * D)
+        t0 = time.perf_counter()
+        oracle.quantize_1d(gs, rnd=oracle.SR, seed=5, threads=nthreads)
+        out["q1d_row_sr"] = (time.perf_counter() - t0) / (rows * F2)
+        off = np.array([0, rows * 3 // 8, rows], dtype=np.int32)
+        t0 = time.perf_counter()
+        oracle.quantize_1d(gs, block_axis=0, group_offsets=off, use_rht=True, sign_mask=1, rnd=oracle.SR,
+                           seed=5, threads=nthreads)
+        out["q1d_col"] = (time.perf_counter() - t0) / (rows * F2)
+        wrows = D if rows >= 4096 else max(32, rows // 4 // 32 * 32)
+        wsl = synth.normal_bf16((1, wrows, F2), 0.02, seed=5)
+        t0 = time.perf_counter()
+        oracle.quantize_2d(wsl, threads=nthreads)
+        out["q2d"] = (time.perf_counter() - t0) / wsl.size
+        return out
+
+    def gemm_rate(seconds, nthreads):
+        ac, asc = oracle.quantize_1d(synth.channel_scaled_activations(rows=256, cols=D, seed=1))
+        wb = synth.normal_bf16((1, F2, D), 0.02, seed=5)
+        bc, bs, _, _ = oracle.quantize_2d(wb)
+        done, dt = 0, 0.0
+        while dt < seconds and done < 4096:
+            sample_rows = [(0, int(m)) for m in rng.integers(0, 256, 2 * nthreads)]
+            t0 = time.perf_counter()
+            oracle.grouped_gemm(ac, asc, bc, bs, [0, 256], 256, F2, D, b_scale_2d=True, rows=sample_rows,
+                                threads=nthreads)
+            dt += time.perf_counter() - t0
+            done += len(sample_rows)
+        return done * F2 * D / dt, done
+
+    def step_seconds(qr, mac_s):
+        el = {"q1d_row_rtne": T * D + ROWS * D, "q1d_row_sr": ROWS * D + ROWS * F2,
+              "q1d_col": 3 * ROWS * D + ROWS * F2, "q2d": E * D * F2 + E * D * D}
+        t = {k: qr[k] * el[k] for k in el}
+        t["gemm"] = sum(w[r]["flops"] for r in GEMM_ROLES) / 2 / mac_s
+        return t
+
+    qr = quant_rate(4096, threads)
+    mac_s, done = gemm_rate(gemm_seconds, threads)
+    t = step_seconds(qr, mac_s)
+    t_total = sum(t.values())
+    flops = sum(w[r]["flops"] for r in GEMM_ROLES)
+    res = {
         "value": flops / t_total / 1e12,
         "unit": "TFLOP/s",
         "cores": threads,
@@ -286,17 +471,59 @@ def cpu_baseline(gemm_seconds=8.0):
                    "GEMM of %d sampled output rows x 5760 x 2880; per-role rates extrapolated to the "
                    "full step (%.0f s extrapolated)" % (done, t_total)),
         "extrapolated_step_s": t_total,
+        "gemm_TFLOPs": 2 * mac_s / 1e12,
+        "gemm_sample": "FP64 GEMM of %d sampled output rows x 5760 x 2880" % done,
     }
+    if single_thread:
+        qr1 = quant_rate(1024, 1)
+        mac1, done1 = gemm_rate(2.0, 1)
+        t1 = sum(step_seconds(qr1, mac1).values())
+        res["single_thread"] = {"value": flops / t1 / 1e12, "unit": "TFLOP/s", "extrapolated_step_s": t1,
+                                "sample": "a quarter of the quantizer sample and %d GEMM rows, one thread"
+                                          % done1}
+    return res
+
+
+def run_step(torch, dev, args):
+    inp = build_inputs(torch, dev)
+    step = Step(torch, dev, inp)
+    for _ in range(args.warmup):
+        step.run()
+    torch.cuda.synchronize()
+    # timed region: K steps, per-launch events on the launch stream
+    step.events = []
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for _ in range(args.steps):
+        step.run()
+    t_end.record()
+    torch.cuda.synchronize()
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    # per role: its launches' summed time in each step (launches of one role
+    # may differ in size), then the median over the steps
+    n = len(step.events) // args.steps
+    per = {}
+    for k in range(args.steps):
+        tot = {}
+        for name, s, e in step.events[k * n:(k + 1) * n]:
+            tot[name] = tot.get(name, 0.0) + s.elapsed_time(e)
+        for name, v in tot.items():
+            per.setdefault(name, []).append(v)
+    return step, inp, ms_step, per
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=5, choices=[1, 2, 3, 4, 5],
+                    help="5 (default): the full expert step; 1-4: one stand-alone workload per line")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-fused-epilogue", action="store_true",
-                    help="skip the fused-epilogue comparison run after the timed steps (profiling runs)")
+    ap.add_argument("--no-standalone", action="store_true",
+                    help="skip the stand-alone workloads after the timed steps (profiling runs)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device copy of this many bytes (3 launches), to "
                          "calibrate the HBM byte counters against a kernel of known traffic")
@@ -320,69 +547,70 @@ def main():
         print(json.dumps({"copy_bytes": args.copy_bytes, "launches": 3}))
         return
     mx.lib()
-    inp = build_inputs(torch, dev)
-    step = Step(torch, dev, inp)
-    for _ in range(args.warmup):
-        step.run()
-    torch.cuda.synchronize()
-    # timed region: K steps, per-launch events on the launch stream
-    step.events = []
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record()
-    for _ in range(args.steps):
-        step.run()
-    t_end.record()
-    torch.cuda.synchronize()
-    ms_total = t_start.elapsed_time(t_end)
-    ms_step = ms_total / args.steps
-    per = {}
-    for name, s, e in step.events:
-        per.setdefault(name, []).append(s.elapsed_time(e))
+    common = {"n_gpus": 1, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+              "data": "synthetic"}
+    if args.config in (1, 2, 3):
+        res = {1: config1, 2: config2, 3: config3}[args.config](torch, dev)
+        r = res.get("roofline") or res.get("quantize_roofline") or roof({"bytes": 256 * 512 * (4 + CS)},
+                                                                       res["quantize_ms"])
+        out = dict(metric="quantize GB/s + MXFP4 grouped-GEMM TFLOPS (fraction of HBM / FP4 roofline)",
+                   value=r["achieved"], unit="GB/s", steps=10, warmup=1, ms_per_step=res.get("ms", res.get(
+                       "quantize_ms")), dtype="bf16 in, fp4-e2m1/ue8m0 out" if args.config > 1 else
+                   "fp32 in, fp4-e2m1/ue8m0 out", config={"workload": res["workload"]}, roofline=r, result=res,
+                   **common)
+        if not args.no_cpu_baseline:
+            out["cpu_baseline"] = cpu_baseline_config(args.config)
+        print(json.dumps(out))
+        return
+    step, inp, ms_step, per = run_step(torch, dev, args)
     w = work_model()
     kernels = {}
     for name, times in per.items():
-        avg = float(np.mean(times))
+        ms_role = float(np.median(times))
         launches = w[name]["launches"]
-        ms_role = avg * launches
-        k = {"launches_per_step": launches, "ms_per_step": ms_role, "avg_launch_ms": avg}
-        if "bytes" in w[name]:
-            gbs = w[name]["bytes"] / (ms_role / 1e3) / 1e9
-            k.update({"GB/s": gbs, "frac_hbm": gbs / PEAK_HBM_GBS})
-        else:
+        k = {"instantiation": ROLE_KERNEL[name], "launches_per_step": launches, "ms_per_step": ms_role,
+             "avg_launch_ms": ms_role / launches, "roofline": roof(w[name], ms_role)}
+        if "flops" in w[name]:
             tf = w[name]["flops"] / (ms_role / 1e3) / 1e12
             k.update({"TFLOP/s": tf, "frac_fp4": tf / PEAK_FP4_TFLOPS})
+        gbs = w[name]["bytes"] / (ms_role / 1e3) / 1e9
+        k.update({"GB/s": gbs, "frac_hbm": gbs / PEAK_HBM_GBS})
         kernels[name] = k
-    total_flops = w["gemm"]["flops"] + w["gemm_wgrad"]["flops"]
+    total_flops = sum(w[r]["flops"] for r in GEMM_ROLES)
     value = total_flops / (ms_step / 1e3) / 1e12
-    dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
+    if args.config == 4:
+        k = kernels["gemm_fwd_gather"]
+        out = dict(metric="quantize GB/s + MXFP4 grouped-GEMM TFLOPS (fraction of HBM / FP4 roofline)",
+                   value=k["TFLOP/s"], unit="TFLOP/s", steps=args.steps, warmup=args.warmup,
+                   ms_per_step=k["ms_per_step"], dtype="fp4-e2m1/ue8m0 operands, fp32 accumulate, bf16 out",
+                   config={"workload": "grouped MXFP4 GEMM forward, 32 experts, 65536 Zipf-routed rows gathered "
+                                       "from 16384 tokens, K 2880, N 5760"},
+                   roofline=dict(k["roofline"], kernel=k["instantiation"]), **common)
+        if not args.no_cpu_baseline:
+            out["cpu_baseline"] = cpu_baseline_config(4)
+        print(json.dumps(out))
+        return
+    dom = max(kernels, key=lambda r: kernels[r]["ms_per_step"])
     dk = kernels[dom]
+    rf = dict(dk["roofline"], kernel=dk["instantiation"], role=dom)
     tr = measured_traffic(dom)
-    if "TFLOP/s" in dk:
-        roof = {"kernel": dom, "bound": "mfma", "achieved": dk["TFLOP/s"], "peak": PEAK_FP4_TFLOPS,
-                "unit": "TFLOP/s", "frac": dk["TFLOP/s"] / PEAK_FP4_TFLOPS, "traffic": tr and tr["bytes"]}
-    else:
-        roof = {"kernel": dom, "bound": "hbm", "achieved": dk["GB/s"], "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": dk["GB/s"] / PEAK_HBM_GBS, "traffic": tr and tr["bytes"]}
+    rf["traffic"] = tr and tr["bytes"]
     if tr:
-        roof["traffic_read_write"] = [tr["read_bytes"], tr["write_bytes"]]
-    quant_bytes = sum(w[k]["bytes"] for k in ("q1d_row", "q1d_col", "q2d"))
-    quant_ms = sum(kernels[k]["ms_per_step"] for k in ("q1d_row", "q1d_col", "q2d"))
-    gemm_ms = kernels["gemm"]["ms_per_step"] + kernels["gemm_wgrad"]["ms_per_step"]
+        rf["traffic_read_write"] = [tr["read_bytes"], tr["write_bytes"]]
+        rf["algorithmic_bytes_per_launch"] = w[dom]["bytes"] / w[dom]["launches"]
+    if "flops" in w[dom]:
+        rf["mfma_frac"] = dk["frac_fp4"]
+    quant_bytes = sum(w[k]["bytes"] for k in QUANT_ROLES)
+    quant_ms = sum(kernels[k]["ms_per_step"] for k in QUANT_ROLES)
+    gemm_ms = sum(kernels[k]["ms_per_step"] for k in GEMM_ROLES)
     out = {
         "metric": "quantize GB/s + MXFP4 grouped-GEMM TFLOPS (fraction of HBM / FP4 roofline)",
         "value": value,
         "unit": "TFLOP/s",
-        "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
         "dtype": "fp4-e2m1/ue8m0 operands, fp32 accumulate",
-        "data": "synthetic",
         "config": {"workload": "quantized MoE expert step fwd+bwd: 32 experts, d_model 2880, ffn 2880 "
                                "(gate_up 5760), 16384 tokens top-4 Zipf(1.1)",
                    "experts": E, "d_model": D, "d_ff_gate_up": F2, "tokens": T, "top_k": TOPK},
@@ -391,10 +619,18 @@ def main():
         "gemm_TFLOPs": total_flops / (gemm_ms / 1e3) / 1e12,
         "gemm_frac_fp4": total_flops / (gemm_ms / 1e3) / 1e12 / PEAK_FP4_TFLOPS,
         "kernels": kernels,
-        "roofline": roof,
+        "roofline": rf,
+        **common,
     }
-    if not args.no_fused_epilogue:
+    if not args.no_standalone:
         out["fused_epilogue"] = fused_epilogue(torch, step)
+        del step, inp
+        torch.cuda.empty_cache()
+        out["standalone"] = {"config1": config1(torch, dev), "config2": config2(torch, dev),
+                             "config3": config3(torch, dev),
+                             "config4": {"workload": "grouped forward GEMM 65536x5760x2880 (the step's Y1 launch)",
+                                         **{k: kernels["gemm_fwd_gather"][k] for k in
+                                            ("avg_launch_ms", "TFLOP/s", "frac_fp4", "roofline")}}}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out))
