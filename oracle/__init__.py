@@ -66,6 +66,9 @@ def lib():
         L.oracle_quantize_2d.argtypes = [P, ctypes.c_int, i64, i64, i64, P, P, P, P, i64, i64]
         L.oracle_quantize_2d_deosc.argtypes = [P, ctypes.c_int, i64, i64, i64, P, P, ctypes.c_int,
                                                P, P, P, P, P, i64, i64]
+        L.oracle_quantize_1d_ex.argtypes = [P, ctypes.c_int, i64, i64, ctypes.c_int, u32, ctypes.c_int, u64,
+                                            u32, u64, ctypes.c_float, i64, P, P, P, i64, i64]
+        L.oracle_dequantize_1d_ex.argtypes = [P, P, P, i64, i64, i64, P, i64, i64]
         L.oracle_decode.argtypes = [ctypes.c_uint8, ctypes.c_uint8]
         L.oracle_decode.restype = ctypes.c_double
         L.oracle_dequantize.argtypes = [P, P, i64, i64, i64, ctypes.c_int, P, i64, i64]
@@ -201,6 +204,48 @@ def quantize_1d(x, block_axis: int = 1, group_offsets=None, kp: int | None = Non
 
     _run([job(a, b) for a, b in _split(qr, threads * 4)], threads)
     return codes, scales
+
+
+def quantize_1d_ex(x, use_rht: bool = False, sign_mask: int = 0, rnd: int = RNE, seed: int = 0,
+                   stream: int = 0, index_base: int = 0, clip_ratio: float = 1.0, macro_block: int = 0,
+                   threads: int | None = None):
+    """Row-wise 1x32 quantization with outlier clipping (clip_ratio) and
+    macro-block scaling (macro_block > 0), see oracle_quantize_1d_ex.
+    Returns (codes, scales, macro_r or None)."""
+    x = np.ascontiguousarray(x)
+    rows, cols = x.shape
+    codes = np.zeros((rows, cols // 2), dtype=np.uint8)
+    scales = np.zeros((rows, cols // 32), dtype=np.uint8)
+    mr = np.zeros((rows, cols // macro_block), dtype=np.float32) if macro_block else None
+    L = lib()
+    dt = _dtype_code(x)
+    threads = threads or default_threads()
+
+    def job(a, b):
+        return lambda: L.oracle_quantize_1d_ex(_ptr(x), dt, rows, cols, int(use_rht), sign_mask, rnd, seed,
+                                               stream, index_base, float(clip_ratio), int(macro_block),
+                                               _ptr(codes), _ptr(scales), _ptr(mr), a, b)
+
+    _run([job(a, b) for a, b in _split(rows, threads * 4)], threads)
+    return codes, scales, mr
+
+
+def dequantize_1d_ex(codes, scales, macro_r=None, macro_block: int = 0, threads: int | None = None):
+    """fp32 decode of quantize_1d_ex's output: deq(code, scale) / r."""
+    codes = np.ascontiguousarray(codes)
+    scales = np.ascontiguousarray(scales)
+    rows, half = codes.shape
+    mr = None if macro_r is None else np.ascontiguousarray(macro_r, dtype=np.float32)
+    y = np.zeros((rows, half * 2), dtype=np.float32)
+    L = lib()
+    threads = threads or default_threads()
+
+    def job(a, b):
+        return lambda: L.oracle_dequantize_1d_ex(_ptr(codes), _ptr(scales), _ptr(mr), rows, half * 2,
+                                                 int(macro_block), _ptr(y), a, b)
+
+    _run([job(a, b) for a, b in _split(rows, threads * 4)], threads)
+    return y
 
 
 def quantize_2d(w, threads: int | None = None):

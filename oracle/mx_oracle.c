@@ -58,6 +58,8 @@ static const double E2M1_MAG[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
 
 int oracle_version(void) { return 1; }
 
+double oracle_decode(uint8_t code, uint8_t scale_byte);
+
 /* ------------------------------------------------------------------ */
 /* Philox4x32-10 (Salmon et al., SC'11).                               */
 /* ------------------------------------------------------------------ */
@@ -320,6 +322,117 @@ int oracle_quantize_1d(const void* x, int dtype, int64_t rows, int64_t cols,
 }
 
 /* ------------------------------------------------------------------ */
+/* Study variants of the row-wise 1x32 quantizer: outlier clipping and   */
+/* macro-block scaling.                                                  */
+/*                                                                      */
+/* Both are named, without definitions, among the techniques that raised */
+/* operator-level SNR but failed end to end (Abstract of "Training an   */
+/* MoE LLM in MXFP4"; "The Numbers" in the news digest).  The readings: */
+/*   - outlier clipping with ratio rho in (0, 1]: a block's scale is    */
+/*     chosen for fl32(rho * amax) instead of amax, X = floor(log2(     */
+/*     fl32(rho * amax))) - 2, so the block's largest values saturate   */
+/*     at +-6 * 2^X (clipped) while the rest get a finer grid; rho = 1  */
+/*     is the plain quantizer;                                           */
+/*   - macro-block scaling with size Bm (a multiple of 32 dividing the  */
+/*     row, 0 = none): a second, fp32 scale per Bm consecutive elements */
+/*     of a row.  Its multiplier r = fl32(6 / amax_M) (1 when amax_M is */
+/*     0 or not finite, or when the quotient is not finite) maps the    */
+/*     macro-block's largest magnitude to 6 up to one rounding; the     */
+/*     elements y' = fl32(y * r) are then quantized in 1x32 blocks as   */
+/*     usual, and decode to deq(code, scale) / r.                       */
+/* The RHT (when on) comes first, so amax_M is over transformed values. */
+/* Element index for SR as in oracle_quantize_1d (row-wise).            */
+/* macro_r [rows x cols/Bm] (written when Bm > 0).                      */
+/* ------------------------------------------------------------------ */
+int oracle_quantize_1d_ex(const void* x, int dtype, int64_t rows, int64_t cols,
+                          int use_rht, uint32_t mask, int rnd, uint64_t seed, uint32_t stream,
+                          uint64_t index_base, float clip_ratio, int64_t macro_block,
+                          uint8_t* codes, uint8_t* scales, float* macro_r,
+                          int64_t r_begin, int64_t r_end)
+{
+    if (cols <= 0 || cols % 32 || rows < 0) return 2;
+    if (!(clip_ratio > 0.0f && clip_ratio <= 1.0f)) return 2;
+    if (macro_block < 0 || (macro_block > 0 && (macro_block % 32 || cols % macro_block))) return 2;
+    float y[32], t[32];
+    uint32_t r16[32];
+    uint8_t code[32];
+    for (int64_t row = r_begin; row < r_end; ++row) {
+        float r = 1.0f;
+        for (int64_t b = 0; b < cols / 32; ++b) {
+            /* a new macro-block starts: its multiplier from the transformed amax */
+            if (macro_block > 0 && (b * 32) % macro_block == 0) {
+                float amax = 0.0f;
+                int nonfinite = 0;
+                for (int64_t bb = b; bb < b + macro_block / 32; ++bb) {
+                    for (int j = 0; j < 32; ++j) t[j] = load_elem(x, dtype, row * cols + bb * 32 + j);
+                    if (use_rht) { oracle_rht_block(t, y, mask, 0); memcpy(t, y, sizeof(t)); }
+                    for (int j = 0; j < 32; ++j) {
+                        if (isnan(t[j]) || isinf(t[j])) nonfinite = 1;
+                        else if (fabsf(t[j]) > amax) amax = fabsf(t[j]);
+                    }
+                }
+                r = 1.0f;
+                if (!nonfinite && amax > 0.0f) {
+                    volatile float q = 6.0f / amax;          /* one fp32 rounding */
+                    if (!isinf(q)) r = q;
+                }
+                macro_r[row * (cols / macro_block) + (b * 32) / macro_block] = r;
+            }
+            for (int j = 0; j < 32; ++j) y[j] = load_elem(x, dtype, row * cols + b * 32 + j);
+            if (use_rht) { oracle_rht_block(y, t, mask, 0); memcpy(y, t, sizeof(y)); }
+            if (macro_block > 0)
+                for (int j = 0; j < 32; ++j) { volatile float p = y[j] * r; y[j] = p; }
+            if (rnd == 1)
+                for (int j = 0; j < 32; ++j)
+                    r16[j] = oracle_sr_bits(seed, stream, index_base + (uint64_t)(row * cols + b * 32 + j));
+            /* the block scale from the clipped amax */
+            double amax = 0.0;
+            int nonfinite = 0;
+            for (int j = 0; j < 32; ++j) {
+                if (isnan(y[j]) || isinf(y[j])) nonfinite = 1;
+                if (fabs((double)y[j]) > amax) amax = fabs((double)y[j]);
+            }
+            uint8_t byte;
+            if (nonfinite) {
+                byte = 0xFF;
+                for (int j = 0; j < 32; ++j) code[j] = 0;
+            } else {
+                volatile float ca = clip_ratio * (float)amax;   /* fl32(rho * amax) */
+                byte = oracle_scale_byte((double)ca);
+                int X = (int)byte - 127;
+                for (int j = 0; j < 32; ++j) {
+                    double A = fabs(ldexp((double)y[j], -X));
+                    int m = (rnd == 0) ? oracle_rtne_mag(A) : oracle_sr_mag(A, r16[j]);
+                    code[j] = (uint8_t)(((signbit(y[j]) ? 1 : 0) << 3) | m);
+                }
+            }
+            scales[row * (cols / 32) + b] = byte;
+            for (int j = 0; j < 16; ++j)
+                codes[row * (cols / 2) + b * 16 + j] = (uint8_t)(code[2 * j] | (code[2 * j + 1] << 4));
+        }
+    }
+    return 0;
+}
+
+/* Decode of oracle_quantize_1d_ex's output to fp32: deq(code, scale) / r,
+ * the division rounded once to fp32 (r = 1 without macro-blocks). */
+int oracle_dequantize_1d_ex(const uint8_t* codes, const uint8_t* scales, const float* macro_r,
+                            int64_t rows, int64_t cols, int64_t macro_block, float* y,
+                            int64_t r_begin, int64_t r_end)
+{
+    if (cols % 32 || (macro_block > 0 && (macro_block % 32 || cols % macro_block))) return 2;
+    for (int64_t row = r_begin; row < r_end; ++row)
+        for (int64_t c = 0; c < cols; ++c) {
+            uint8_t byte = codes[row * (cols / 2) + c / 2];
+            uint8_t code = (c % 2 == 0) ? (byte & 0xF) : (byte >> 4);
+            double v = oracle_decode(code, scales[row * (cols / 32) + c / 32]);
+            double r = macro_block > 0 ? (double)macro_r[row * (cols / macro_block) + c / macro_block] : 1.0;
+            y[row * cols + c] = (float)(v / r);    /* a double quotient of floats, rounded once */
+        }
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
 /* 2D quantize, 32x32 blocks, RTNE.  w [batch x rows x cols].           */
 /* codes [batch x rows x cols/2], scales [batch x rows/32 x cols/32];   */
 /* codes_t [batch x cols x rows/2], scales_t [batch x cols/32 x rows/32]*/
@@ -399,8 +512,6 @@ int oracle_quantize_2d(const void* w, int dtype, int64_t batch, int64_t rows, in
 /* cols/32] (the as-given layout of the previous call); outputs as in   */
 /* oracle_quantize_2d plus flips [batch x rows/32 x cols/32].           */
 /* ------------------------------------------------------------------ */
-double oracle_decode(uint8_t code, uint8_t scale_byte);
-
 static const double SIGNED_GRID[15] = {-6.0, -4.0, -3.0, -2.0, -1.5, -1.0, -0.5, 0.0,
                                        0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
 
