@@ -149,6 +149,81 @@ mx_status mx_quantize_2d(const void* w, mx_dtype wt, int64_t batch, int64_t rows
                          uint8_t* codes, int64_t codes_ld, uint8_t* scales, uint8_t* codes_t,
                          int64_t codes_t_ld, uint8_t* scales_t, mx_stream stream);
 
+/* Study variants of the row-wise 1x32 quantizer, for measuring
+ * operator-level SNR: outlier clipping and macro-block scaling.  Both are
+ * named among the techniques that improved operator-level SNR yet failed
+ * end to end (Abstract of "Training an MoE LLM in MXFP4"; "The Numbers" in
+ * the news digest "AMD's ALTO Gets 4-Bit MoE Training to Within 0.007 of
+ * BF16"); the pages define neither.  The readings:
+ *   - clip_ratio rho in (0, 1]: a block's scale is chosen for
+ *     fl32(rho * amax) instead of amax, X = floor(log2(fl32(rho * amax)))
+ *     - 2, so its largest values saturate at +-6 * 2^X while the others get
+ *     a finer grid; rho = 1 is mx_quantize_1d's rule;
+ *   - macro_block Bm (0 = none; else a multiple of 32 dividing cols): each
+ *     Bm consecutive elements of a row (after the RHT, when on) are
+ *     multiplied by r = fl32(6 / amax_M), their fp32 macro scale (r = 1
+ *     when amax_M is 0 or not finite, or 6 / amax_M is not finite), and the
+ *     products y' = fl32(y * r) are quantized in 1x32 blocks as usual.  A
+ *     decoded element is deq(code, scale) / r (mx_dequantize_1d_ex).
+ * x [rows x cols] (fp32 or bf16), row-major, 16-byte aligned; codes
+ * [rows x cols/2] (contiguous, 16-byte aligned), scales [rows x cols/32];
+ * macro_r [rows x cols/Bm] fp32 (written; required when Bm > 0).
+ * use_rht, sign_mask, rnd, seed, stream_id and index_base as in
+ * mx_quantize_1d (row-wise).  Device pointers owned by the caller.
+ * Errors: MX_ERR_DTYPE, MX_ERR_UNSUPPORTED (rnd), MX_ERR_SHAPE (sizes,
+ * clip_ratio outside (0, 1], macro_block), MX_ERR_NULL, MX_ERR_ALIGN,
+ * MX_ERR_LAUNCH.  rows == 0 launches nothing. */
+mx_status mx_quantize_1d_ex(const void* x, mx_dtype xt, int64_t rows, int64_t cols, int use_rht,
+                            uint32_t sign_mask, mx_round rnd, uint64_t seed, uint32_t stream_id,
+                            uint64_t index_base, float clip_ratio, int64_t macro_block, uint8_t* codes,
+                            uint8_t* scales, float* macro_r, mx_stream stream);
+
+/* Decode of mx_quantize_1d_ex's output to fp32: y = deq(code, scale) / r,
+ * the quotient rounded once (r = 1 when macro_block is 0; macro_r may then
+ * be NULL); a 0xFF scale decodes to NaN.  codes [rows x cols/2] contiguous,
+ * y [rows x cols] fp32, both 16-byte aligned.  Errors as
+ * mx_quantize_1d_ex. */
+mx_status mx_dequantize_1d_ex(const uint8_t* codes, const uint8_t* scales, const float* macro_r,
+                              int64_t rows, int64_t cols, int64_t macro_block, float* y,
+                              mx_stream stream);
+
+/* 32x32 quantization of a weight tensor with weight de-oscillation: a
+ * hysteresis band against the previous step's quantized weights.
+ * Pages: "What ALTO Actually Does" (news digest "AMD's ALTO Gets 4-Bit MoE
+ * Training to Within 0.007 of BF16") describes the oscillation: the
+ * optimizer moves a full-precision master weight while the GEMM consumes
+ * its quantized value, so a weight near a rounding boundary can alternate
+ * between two levels under updates much smaller than a level step; the
+ * Abstract of "Training an MoE LLM in MXFP4" names a simplified
+ * de-oscillation scheme without giving its rule.  The rule here: the tile's
+ * scale byte comes from its amax as in mx_quantize_2d; if it equals the
+ * previous byte (neither 0xFF), an element keeps its previous code c while
+ * its scaled value v = w / 2^X lies strictly inside
+ * (q - f (q - q_dn), q + f (q_up - q)), q the value of c on the signed E2M1
+ * grid {-6, ..., -0.5, 0, 0.5, ..., 6} (both zero codes are 0), q_dn / q_up
+ * its neighbours there (the band is open past +-6), f = 1/2 + margin64 / 64;
+ * otherwise it takes its round-to-nearest-even code, as does every element
+ * of a tile whose scale changed.  margin64 = 0 leaves every decoded value
+ * equal to mx_quantize_2d's.
+ * w: batch x [rows x cols] (fp32 master weights, or bf16), rows % 32 == 0,
+ * cols % 32 == 0; margin64 in [0, 31].
+ * prev_codes / prev_scales: the as-given layout written for the previous
+ * step (rows prev_codes_ld bytes apart, 0 = cols/2); they may be the very
+ * buffers codes / scales (in-place update, then with the same pitch).
+ * codes / scales: the as-given layout (required); codes_t / scales_t: the
+ * transposed layout (optional pair), as in mx_quantize_2d.
+ * flips (optional, uint16 [batch x rows/32 x cols/32], 2-byte aligned): per
+ * tile, the number of elements whose decoded value differs from the
+ * previous one (a 0xFF scale on either side counts all 1024).
+ * Device pointers owned by the caller; code pointers 16-byte aligned.
+ * Errors: MX_ERR_DTYPE, MX_ERR_SHAPE (sizes, margin64, pitches, an in-place
+ * call with a different pitch), MX_ERR_NULL, MX_ERR_ALIGN, MX_ERR_LAUNCH.
+ * An empty input returns MX_OK before any pointer is checked. */
+mx_status mx_quantize_2d_deosc(const void* w, mx_dtype wt, int64_t batch, int64_t rows, int64_t cols,
+                               const uint8_t* prev_codes, int64_t prev_codes_ld, const uint8_t* prev_scales,
+                               int margin64, uint8_t* codes, int64_t codes_ld, uint8_t* scales, uint8_t* codes_t,
+                               int64_t codes_t_ld, uint8_t* scales_t, uint16_t* flips, mx_stream stream);
+
 /* Exact decode of MXFP4: each E2M1 element times the UE8M0 power-of-two
  * scale its block shares (the format named in "What ALTO Actually Does",
  * news digest "AMD's ALTO Gets 4-Bit MoE Training to Within 0.007 of

@@ -580,15 +580,52 @@ __device__ __forceinline__ void transpose_nibbles_8x8(uint32_t* a) {
     }
 }
 
-template <bool BF16>
+// De-oscillation (DEOSC): a hysteresis band against the previous step's
+// codes.  While a tile's scale byte equals the previous one (neither 0xFF),
+// an element whose round-to-nearest-even code differs from its previous code
+// c keeps c while its scaled magnitude A = |w| / 2^X lies strictly inside
+// (lo[m], hi[m]), m = c & 7, and its sign is c's (any sign when m = 0):
+// the rounding interval of level m widened by f - 1/2 of a grid step on
+// each side, f = 1/2 + margin / 64 (lo[0] = -inf, hi[7] = +inf).  This is
+// the signed-grid band (q - f (q - q_dn), q + f (q_up - q)) of the previous
+// value q, written on magnitudes.  Every bound is a multiple of 2^-7, exact
+// in fp32, and A is exact (a power-of-two scaling), so each decision is
+// exact.
+struct DeoscArgs {
+    const uint8_t* prev_codes;   // as-given layout of the previous call (may alias codes)
+    int64_t prev_ld;
+    const uint8_t* prev_scales;  // [batch x rows/32 x cols/32] (may alias scales)
+    float f;                     // 1/2 + margin / 64
+    uint16_t* flips;             // per tile: elements whose decoded value changed (may be NULL)
+};
+
+// Decoded E2M1 value as (mantissa bit, exponent) for magnitude code m >= 1:
+// GRID[m] = (1 + mant / 2) 2^e.  Two nonzero codes under scale bytes s, t
+// decode to the same value iff their signs, mantissa bits and e + s agree.
+__device__ __forceinline__ uint32_t e2m1_value_key(uint32_t m, uint32_t sbyte) {
+    const uint32_t mant = m > 1u ? (m & 1u) : 0u;
+    return (mant << 16) | ((m >> 1) + sbyte);      // e + 1 + s, never negative
+}
+
+template <bool BF16, bool DEOSC>
 __global__ __launch_bounds__(256) void q2d_kernel(const void* __restrict__ w, int64_t rows, int64_t cols,
                                                   int64_t col_strips, int64_t row_strips, int64_t nsuper,
                                                   uint8_t* __restrict__ codes, int64_t ld,
                                                   uint8_t* __restrict__ scales,
                                                   uint8_t* __restrict__ codes_t, int64_t ld_t,
-                                                  uint8_t* __restrict__ scales_t) {
+                                                  uint8_t* __restrict__ scales_t, DeoscArgs dz) {
     __shared__ uint32_t wave_amax[4][8];
     __shared__ uint8_t tile_scale[Q2_TR][8];
+    __shared__ float2 band[8];                      // DEOSC: (lo, hi) per previous magnitude code
+    __shared__ uint32_t wave_flips[Q2_TR][4][8];    // DEOSC: flips per tile row, wave and tile
+    if (DEOSC && threadIdx.x < 8) {
+        const float grid[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
+        const int m = threadIdx.x;
+        const float lo = m == 0 ? -__builtin_inff() : grid[m] - dz.f * (grid[m] - grid[m - 1]);
+        const float hi = m == 7 ? __builtin_inff() : grid[m] + dz.f * (grid[m + 1] - grid[m]);
+        band[m] = make_float2(lo, hi);
+    }
+    if (DEOSC) __syncthreads();
     // [tile row][tile][row] 16 bytes of row codes; each tile row padded by one
     // entry so the 8 tile rows of one tile fall in different LDS banks
     constexpr int TC_TS = 8 * 32 + 1;
@@ -638,6 +675,15 @@ __global__ __launch_bounds__(256) void q2d_kernel(const void* __restrict__ w, in
                 }
             }
             if (ts + 1 < ntr) load_raw(ts + 1);
+            // DEOSC: this row's previous codes and the tile's previous scale,
+            // read before the new ones are written (the block-wide barriers
+            // below separate every thread's read from the scale's write)
+            uint4 pcw = make_uint4(0, 0, 0, 0);
+            uint32_t pbyte = 0xFFu;
+            if (DEOSC && valid) {
+                pcw = *(const uint4*)(dz.prev_codes + grow * dz.prev_ld + tile * 16);
+                pbyte = dz.prev_scales[(bt * row_tiles + tr) * tiles_per_row + tile];
+            }
             uint32_t am = 0;
 #pragma unroll
             for (int k = 0; k < 32; ++k) am = max(am, __float_as_uint(v[k]) & 0x7FFFFFFFu);
@@ -660,12 +706,55 @@ __global__ __launch_bounds__(256) void q2d_kernel(const void* __restrict__ w, in
             uint32_t cw[4];
 #pragma unroll
             for (int k = 0; k < 4; ++k) cw[k] = cvt8_rne(v + 8 * k, sc) & keep;
+            if (DEOSC) {
+                const bool hyst = byte == pbyte && byte != 0xFFu;
+                const bool nan_tile = byte == 0xFFu || pbyte == 0xFFu;
+                const float inv = __uint_as_float((254u - byte) << 23);   // 2^-X (byte <= 252 for finite w)
+                const uint32_t pw[4] = {pcw.x, pcw.y, pcw.z, pcw.w};
+                uint32_t nflip = 0;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    uint32_t out = 0;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float x = v[8 * k + e];
+                        const uint32_t cr = (cw[k] >> (4 * e)) & 0xFu, cp = (pw[k] >> (4 * e)) & 0xFu;
+                        const uint32_t m = cp & 7u;
+                        const float A = fabsf(x) * inv;
+                        const float2 b = band[m];
+                        const bool side = m == 0u || (cp >> 3) == (__float_as_uint(x) >> 31);
+                        const uint32_t c = (hyst && side && A > b.x && A < b.y) ? cp : cr;
+                        out |= c << (4 * e);
+                        const uint32_t mn = c & 7u;
+                        const bool differ = (mn == 0u) != (m == 0u) ||
+                                            (mn != 0u && ((c ^ cp) >> 3 || e2m1_value_key(mn, byte) !=
+                                                                               e2m1_value_key(m, pbyte)));
+                        nflip += (nan_tile || differ) ? 1u : 0u;
+                    }
+                    cw[k] = out;
+                }
+                if (!valid) nflip = 0;
+                // the tile's count: lanes with the same j (xor 8, 16, 32), then
+                // across the waves after the last tile row
+                nflip += (uint32_t)__shfl_xor((int)nflip, 8);
+                nflip += (uint32_t)__shfl_xor((int)nflip, 16);
+                nflip += (uint32_t)__shfl_xor((int)nflip, 32);
+                if (lane < 8) wave_flips[ts][wv][lane] = nflip;
+            }
             if (valid && codes)
                 store_b128(codes + grow * ld + tile * 16, make_uint4(cw[0], cw[1], cw[2], cw[3]));
             if (valid && r == 0 && scales) scales[(bt * row_tiles + tr) * tiles_per_row + tile] = (uint8_t)byte;
             tcodes[ts * TC_TS + j * 32 + r] = make_uint4(cw[0], cw[1], cw[2], cw[3]);
         }
         __syncthreads();
+        if (DEOSC && dz.flips && t < 64) {
+            const int jt = t >> 3, ts = t & 7;
+            const int64_t tile3 = cs * 8 + jt;
+            if (tile3 < tiles_per_row && ts < ntr)
+                dz.flips[(bt * row_tiles + tr0 + ts) * tiles_per_row + tile3] =
+                    (uint16_t)(wave_flips[ts][0][jt] + wave_flips[ts][1][jt] + wave_flips[ts][2][jt] +
+                               wave_flips[ts][3][jt]);
+        }
         if (codes_t) {
             // thread t: tile row ts = t % 8, code word w = (t / 8) % 4 (columns
             // 8w .. 8w+7) of tile jj = t / 32.  It reads that word of the
@@ -743,6 +832,134 @@ __global__ __launch_bounds__(256) void deq_kernel(const uint8_t* __restrict__ co
             p[0] = make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]), __float_as_uint(f[3]));
             p[1] = make_uint4(__float_as_uint(f[4]), __float_as_uint(f[5]), __float_as_uint(f[6]), __float_as_uint(f[7]));
         }
+    }
+}
+
+// ===========================================================================
+// Study variants of the row-wise quantizer (outlier clipping, macro-block
+// scaling).  Off the hot path: simple quad-per-block kernels.
+//   macro pass: one wave per macro-block of BM elements of a row; its quads
+//     walk the macro-block's 32-blocks 16 at a time (the RHT in registers
+//     when on), the wave reduces |max|, and r = fl32(6 / amax) (1 when the
+//     amax is 0 or not finite, or the quotient is not finite).
+//   quantize: a quad per 32-block; y' = fl32(y * r), block scale for
+//     fl32(rho * amax(y')), RTNE or SR as in the row quantizer.
+//   decode: a lane per 8 elements, deq / r rounded once.
+// ===========================================================================
+template <bool BF16, bool RHT>
+__device__ __forceinline__ void load_block_quad(const void* __restrict__ x, int64_t blk, int q, uint32_t m8,
+                                                float* t) {
+    if (BF16) {
+        const uint4 w = *((const uint4*)((const uint8_t*)x + blk * 64) + q);
+        t[0] = bf16lo(w.x); t[1] = bf16hi(w.x); t[2] = bf16lo(w.y); t[3] = bf16hi(w.y);
+        t[4] = bf16lo(w.z); t[5] = bf16hi(w.z); t[6] = bf16lo(w.w); t[7] = bf16hi(w.w);
+    } else {
+        const uint4* p = (const uint4*)((const uint8_t*)x + blk * 128) + 2 * q;
+        const uint4 a = p[0], b = p[1];
+        t[0] = __uint_as_float(a.x); t[1] = __uint_as_float(a.y); t[2] = __uint_as_float(a.z);
+        t[3] = __uint_as_float(a.w); t[4] = __uint_as_float(b.x); t[5] = __uint_as_float(b.y);
+        t[6] = __uint_as_float(b.z); t[7] = __uint_as_float(b.w);
+    }
+    if (RHT) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) t[e] = __uint_as_float(__float_as_uint(t[e]) ^ (((m8 >> e) & 1u) << 31));
+        rht32_quad(t, q);
+    }
+}
+
+template <bool BF16, bool RHT>
+__global__ __launch_bounds__(256) void q1d_ex_macro_kernel(const void* __restrict__ x, int64_t nmacro,
+                                                           int64_t mblocks, uint32_t mask,
+                                                           float* __restrict__ macro_r) {
+    const int lane = threadIdx.x & 63, q = lane & 3;
+    const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x >> 6);
+    const uint32_t m8 = (mask >> (8 * q)) & 0xFFu;
+    for (int64_t mb = wave; mb < nmacro; mb += nwaves) {
+        uint32_t am = 0;                              // |max| bit pattern (NaN above Inf)
+        for (int64_t k = lane >> 2; k < mblocks; k += 16) {
+            float t[8];
+            load_block_quad<BF16, RHT>(x, mb * mblocks + k, q, m8, t);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) am = max(am, __float_as_uint(t[e]) & 0x7FFFFFFFu);
+        }
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) am = max(am, (uint32_t)__shfl_xor((int)am, d));
+        if (lane == 0) {
+            float r = 1.0f;
+            if (am != 0u && am < 0x7F800000u) {
+                const float qt = __fdiv_rn(6.0f, __uint_as_float(am));
+                if (__float_as_uint(qt) < 0x7F800000u) r = qt;
+            }
+            macro_r[mb] = r;
+        }
+    }
+}
+
+template <bool BF16, bool RHT, bool SR>
+__global__ __launch_bounds__(256) void q1d_ex_kernel(const void* __restrict__ x, int64_t nblocks, int64_t mblocks,
+                                                     uint32_t mask, uint32_t k0, uint32_t k1, uint32_t stream_id,
+                                                     uint64_t index_base, float clip_ratio,
+                                                     const float* __restrict__ macro_r,
+                                                     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+    const int lane = threadIdx.x & 63, q = lane & 3;
+    const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x >> 6);
+    const uint32_t m8 = (mask >> (8 * q)) & 0xFFu;
+    for (int64_t base = wave * 16; base < nblocks; base += nwaves * 16) {
+        const int64_t blk = base + (lane >> 2);
+        const bool ok = blk < nblocks;
+        float t[8];
+        if (ok) load_block_quad<BF16, RHT>(x, blk, q, m8, t);
+        else
+#pragma unroll
+            for (int e = 0; e < 8; ++e) t[e] = 0.0f;
+        if (macro_r) {
+            // macro-blocks run along each row and divide it, so block blk
+            // lies in macro-block blk / mblocks
+            const float r = ok ? macro_r[blk / mblocks] : 1.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) t[e] = t[e] * r;
+        }
+        uint32_t am = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) am = max(am, __float_as_uint(t[e]) & 0x7FFFFFFFu);
+        am = quad_max_u(am);
+        // the scale for fl32(rho * amax); a NaN or Inf amax stays non-finite
+        const uint32_t byte = scale_byte_from_amax_bits(__float_as_uint(clip_ratio * __uint_as_float(am)) & 0x7FFFFFFFu);
+        const float sc = scale_operand(byte);
+        uint32_t packed;
+        if (SR) {
+            const uint64_t g = (index_base + (uint64_t)blk * 32 + (uint64_t)q * 8) >> 3;
+            const u32x4 rr = philox4x32_10((uint32_t)g, (uint32_t)(g >> 32), stream_id, 0u, k0, k1);
+            packed = cvt8_sr(t, sc, rr);
+        } else {
+            packed = cvt8_rne(t, sc);
+        }
+        if (byte == 0xFFu) packed = 0;
+        if (ok) {
+            *((uint32_t*)(codes + blk * 16) + q) = packed;
+            if (q == 0) scales[blk] = (uint8_t)byte;
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void deq_ex_kernel(const uint8_t* __restrict__ codes,
+                                                     const uint8_t* __restrict__ scales,
+                                                     const float* __restrict__ macro_r, int64_t munits,
+                                                     int64_t nunits, float* __restrict__ y) {
+    for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < nunits;
+         u += (int64_t)gridDim.x * blockDim.x) {
+        const uint32_t cw = *(const uint32_t*)(codes + u * 4);
+        const uint8_t sb = scales[u >> 2];
+        float f[8];
+        decode8(cw, scale_operand(sb), f);
+        const float r = macro_r ? macro_r[u / munits] : 1.0f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) f[k] = sb == 0xFF ? __uint_as_float(0x7FC00000u) : __fdiv_rn(f[k], r);
+        uint4* p = (uint4*)y + 2 * u;
+        p[0] = make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]), __float_as_uint(f[3]));
+        p[1] = make_uint4(__float_as_uint(f[4]), __float_as_uint(f[5]), __float_as_uint(f[6]), __float_as_uint(f[7]));
     }
 }
 
@@ -936,6 +1153,59 @@ mx_status mx_quantize_1d(const void* x, mx_dtype xt, int64_t rows, int64_t cols,
     return launched();
 }
 
+mx_status mx_quantize_1d_ex(const void* x, mx_dtype xt, int64_t rows, int64_t cols, int use_rht, uint32_t sign_mask,
+                            mx_round rnd, uint64_t seed, uint32_t stream_id, uint64_t index_base, float clip_ratio,
+                            int64_t macro_block, uint8_t* codes, uint8_t* scales, float* macro_r, mx_stream stream) {
+    if (xt != MX_F32 && xt != MX_BF16) return MX_ERR_DTYPE;
+    if (rnd != MX_RNE && rnd != MX_SR) return MX_ERR_UNSUPPORTED;
+    if (rows < 0 || cols <= 0 || cols % 32 || index_base % 32) return MX_ERR_SHAPE;
+    if (!(clip_ratio > 0.0f && clip_ratio <= 1.0f)) return MX_ERR_SHAPE;
+    if (macro_block < 0 || (macro_block > 0 && (macro_block % 32 || cols % macro_block))) return MX_ERR_SHAPE;
+    if (rows == 0) return MX_OK;
+    if (!x || !codes || !scales || (macro_block > 0 && !macro_r)) return MX_ERR_NULL;
+    if (!aligned16(x) || !aligned16(codes) || ((uintptr_t)macro_r & 3u)) return MX_ERR_ALIGN;
+    const bool bf = xt == MX_BF16, rh = use_rht != 0, sr = rnd == MX_SR;
+    const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+    const int64_t nblocks = rows * (cols / 32);
+    hipStream_t s = (hipStream_t)stream;
+    (void)hipGetLastError();
+    int64_t mblocks = 1;
+    const float* mr = nullptr;
+    if (macro_block > 0) {
+        mblocks = macro_block / 32;
+        const int64_t nmacro = rows * (cols / macro_block);
+        const int g = grid_for(nmacro, 4);
+        if (bf) {
+            if (rh) hipLaunchKernelGGL((q1d_ex_macro_kernel<true, true>), dim3(g), dim3(256), 0, s, x, nmacro, mblocks, sign_mask, macro_r);
+            else hipLaunchKernelGGL((q1d_ex_macro_kernel<true, false>), dim3(g), dim3(256), 0, s, x, nmacro, mblocks, sign_mask, macro_r);
+        } else {
+            if (rh) hipLaunchKernelGGL((q1d_ex_macro_kernel<false, true>), dim3(g), dim3(256), 0, s, x, nmacro, mblocks, sign_mask, macro_r);
+            else hipLaunchKernelGGL((q1d_ex_macro_kernel<false, false>), dim3(g), dim3(256), 0, s, x, nmacro, mblocks, sign_mask, macro_r);
+        }
+        mr = macro_r;
+    }
+    const int grid = grid_for(nblocks, 4 * 16);
+    MX_DISPATCH3(q1d_ex_kernel, bf, rh, sr, dim3(grid), s, x, nblocks, mblocks, sign_mask, k0, k1, stream_id,
+                 index_base, clip_ratio, mr, codes, scales);
+    return launched();
+}
+
+mx_status mx_dequantize_1d_ex(const uint8_t* codes, const uint8_t* scales, const float* macro_r, int64_t rows,
+                              int64_t cols, int64_t macro_block, float* y, mx_stream stream) {
+    if (rows < 0 || cols <= 0 || cols % 32) return MX_ERR_SHAPE;
+    if (macro_block < 0 || (macro_block > 0 && (macro_block % 32 || cols % macro_block))) return MX_ERR_SHAPE;
+    if (rows == 0) return MX_OK;
+    if (!codes || !scales || !y || (macro_block > 0 && !macro_r)) return MX_ERR_NULL;
+    if (!aligned16(codes) || !aligned16(y) || ((uintptr_t)macro_r & 3u)) return MX_ERR_ALIGN;
+    const int64_t nunits = rows * (cols / 8);
+    const int grid = grid_for(nunits, 256);
+    hipStream_t s = (hipStream_t)stream;
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(deq_ex_kernel, dim3(grid), dim3(256), 0, s, codes, scales, macro_block > 0 ? macro_r : nullptr,
+                       macro_block > 0 ? macro_block / 8 : 1, nunits, y);
+    return launched();
+}
+
 mx_status mx_quantize_2d(const void* w, mx_dtype wt, int64_t batch, int64_t rows, int64_t cols, uint8_t* codes,
                          int64_t codes_ld, uint8_t* scales, uint8_t* codes_t, int64_t codes_t_ld,
                          uint8_t* scales_t, mx_stream stream) {
@@ -956,13 +1226,48 @@ mx_status mx_quantize_2d(const void* w, mx_dtype wt, int64_t batch, int64_t rows
     const int64_t nsuper = batch * row_strips * col_strips;
     const int grid = grid_for(nsuper, 1);
     hipStream_t s = (hipStream_t)stream;
+    const DeoscArgs none{nullptr, 0, nullptr, 0.0f, nullptr};
     (void)hipGetLastError();
     if (wt == MX_BF16)
-        hipLaunchKernelGGL((q2d_kernel<true>), dim3(grid), dim3(256), 0, s, w, rows, cols, col_strips, row_strips,
-                           nsuper, codes, ld, scales, codes_t, ld_t, scales_t);
+        hipLaunchKernelGGL((q2d_kernel<true, false>), dim3(grid), dim3(256), 0, s, w, rows, cols, col_strips,
+                           row_strips, nsuper, codes, ld, scales, codes_t, ld_t, scales_t, none);
     else
-        hipLaunchKernelGGL((q2d_kernel<false>), dim3(grid), dim3(256), 0, s, w, rows, cols, col_strips, row_strips,
-                           nsuper, codes, ld, scales, codes_t, ld_t, scales_t);
+        hipLaunchKernelGGL((q2d_kernel<false, false>), dim3(grid), dim3(256), 0, s, w, rows, cols, col_strips,
+                           row_strips, nsuper, codes, ld, scales, codes_t, ld_t, scales_t, none);
+    return launched();
+}
+
+mx_status mx_quantize_2d_deosc(const void* w, mx_dtype wt, int64_t batch, int64_t rows, int64_t cols,
+                               const uint8_t* prev_codes, int64_t prev_codes_ld, const uint8_t* prev_scales,
+                               int margin64, uint8_t* codes, int64_t codes_ld, uint8_t* scales, uint8_t* codes_t,
+                               int64_t codes_t_ld, uint8_t* scales_t, uint16_t* flips, mx_stream stream) {
+    if (wt != MX_F32 && wt != MX_BF16) return MX_ERR_DTYPE;
+    if (batch < 0 || rows < 0 || cols < 0 || rows % 32 || cols % 32) return MX_ERR_SHAPE;
+    if (margin64 < 0 || margin64 > 31) return MX_ERR_SHAPE;
+    if (batch == 0 || rows == 0 || cols == 0) return MX_OK;     // (empty tensors may have null pointers)
+    if (!w || !prev_codes || !prev_scales || !codes || !scales) return MX_ERR_NULL;
+    if ((codes_t == nullptr) != (scales_t == nullptr)) return MX_ERR_NULL;
+    if (!aligned16(w) || !aligned16(codes) || !aligned16(prev_codes) || (codes_t && !aligned16(codes_t)) ||
+        ((uintptr_t)flips & 1u))
+        return MX_ERR_ALIGN;
+    const int64_t ld = codes_ld ? codes_ld : cols / 2, ld_t = codes_t_ld ? codes_t_ld : rows / 2;
+    const int64_t pld = prev_codes_ld ? prev_codes_ld : cols / 2;
+    if (ld < cols / 2 || ld % 16 || ld_t < rows / 2 || ld_t % 16 || pld < cols / 2 || pld % 16) return MX_ERR_SHAPE;
+    // in place: the previous codes may be the output itself, in the same layout
+    if (prev_codes == codes && pld != ld) return MX_ERR_SHAPE;
+    const int64_t col_strips = (cols / 32 + 7) / 8;
+    const int64_t row_strips = (rows / 32 + Q2_TR - 1) / Q2_TR;
+    const int64_t nsuper = batch * row_strips * col_strips;
+    const int grid = grid_for(nsuper, 1);
+    hipStream_t s = (hipStream_t)stream;
+    const DeoscArgs dz{prev_codes, pld, prev_scales, 0.5f + (float)margin64 / 64.0f, flips};
+    (void)hipGetLastError();
+    if (wt == MX_BF16)
+        hipLaunchKernelGGL((q2d_kernel<true, true>), dim3(grid), dim3(256), 0, s, w, rows, cols, col_strips,
+                           row_strips, nsuper, codes, ld, scales, codes_t, ld_t, scales_t, dz);
+    else
+        hipLaunchKernelGGL((q2d_kernel<false, true>), dim3(grid), dim3(256), 0, s, w, rows, cols, col_strips,
+                           row_strips, nsuper, codes, ld, scales, codes_t, ld_t, scales_t, dz);
     return launched();
 }
 

@@ -49,12 +49,18 @@ def lib():
         L.mx_quantize_1d.argtypes = [P, c_int, i64, i64, c_int, P, i32, i64, P, c_int, u32, c_int,
                                      u64, u32, u64, P, i64, P, P]
         L.mx_quantize_2d.argtypes = [P, c_int, i64, i64, i64, P, i64, P, P, i64, P, P]
+        L.mx_quantize_2d_deosc.argtypes = [P, c_int, i64, i64, i64, P, i64, P, c_int, P, i64, P, P, i64, P,
+                                           P, P]
         L.mx_dequantize.argtypes = [P, i64, P, i64, i64, i64, c_int, P, c_int, P]
+        L.mx_quantize_1d_ex.argtypes = [P, c_int, i64, i64, c_int, u32, c_int, u64, u32, u64,
+                                        ctypes.c_float, i64, P, P, P, P]
+        L.mx_dequantize_1d_ex.argtypes = [P, P, P, i64, i64, i64, P, P]
         L.mx_grouped_gemm.argtypes = [P, i64, P, P, P, i64, P, c_int, P, i32, c_int, i64, i64, i64,
                                       ctypes.c_float, P, c_int, P]
         L.mx_grouped_gemm_q.argtypes = [P, i64, P, P, P, i64, P, c_int, P, i32, i64, i64, i64,
                                         ctypes.c_float, P, P, i64, P, P]
-        for name in ("mx_rht", "mx_quantize_1d", "mx_quantize_2d", "mx_dequantize",
+        for name in ("mx_rht", "mx_quantize_1d", "mx_quantize_2d", "mx_quantize_2d_deosc", "mx_dequantize",
+                     "mx_quantize_1d_ex", "mx_dequantize_1d_ex",
                      "mx_grouped_gemm", "mx_grouped_gemm_q"):
             getattr(L, name).restype = c_int
         _lib = L
@@ -248,6 +254,94 @@ def quantize_2d_into(w, codes, scales, codes_t, scales_t):
         _ptr(w3), _dtype_code(w3), b, r, c, _ptr(codes), ld, _ptr(scales), _ptr(codes_t), ld_t,
         _ptr(scales_t), _stream()))
     out = [codes, scales, codes_t, scales_t]
+    if squeeze:
+        out = [t[0] if t is not None and t.dim() == 3 else t for t in out]
+    return tuple(out)
+
+
+def quantize_1d_ex(x, use_rht: bool = False, sign_mask: int = 0, rnd: int = RNE, seed: int = 0,
+                   stream_id: int = 0, index_base: int = 0, clip_ratio: float = 1.0, macro_block: int = 0,
+                   codes=None, scales=None, macro_r=None):
+    """Row-wise 1x32 quantization with outlier clipping and macro-block
+    scaling (see mx_quantize_1d_ex).  Returns (codes, scales, macro_r or
+    None)."""
+    torch = _torch()
+    _dev(x, "x")
+    rows, cols = x.shape
+    dev = x.device
+    codes = codes if codes is not None else torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
+    scales = scales if scales is not None else torch.empty((rows, cols // 32), dtype=torch.uint8, device=dev)
+    _shaped(codes, (rows, cols // 2), torch.uint8, "codes")
+    _shaped(scales, (rows, cols // 32), torch.uint8, "scales")
+    if macro_block:
+        if cols % macro_block:
+            raise ValueError("macro_block must divide cols")
+        macro_r = macro_r if macro_r is not None else torch.empty((rows, cols // macro_block),
+                                                                  dtype=torch.float32, device=dev)
+        _shaped(macro_r, (rows, cols // macro_block), torch.float32, "macro_r")
+    else:
+        macro_r = None
+    _check("mx_quantize_1d_ex", lib().mx_quantize_1d_ex(
+        _ptr(x), _dtype_code(x), rows, cols, int(use_rht), sign_mask, rnd, seed, stream_id, index_base,
+        float(clip_ratio), int(macro_block), _ptr(codes), _ptr(scales), _ptr(macro_r), _stream()))
+    return codes, scales, macro_r
+
+
+def dequantize_1d_ex(codes, scales, macro_r=None, macro_block: int = 0, out=None):
+    """fp32 decode of quantize_1d_ex's output: deq(code, scale) / r."""
+    torch = _torch()
+    _dev(codes, "codes")
+    rows, half = codes.shape
+    cols = half * 2
+    _shaped(scales, (rows, cols // 32), torch.uint8, "scales")
+    if macro_block:
+        _shaped(macro_r, (rows, cols // macro_block), torch.float32, "macro_r")
+    out = out if out is not None else torch.empty((rows, cols), dtype=torch.float32, device=codes.device)
+    _shaped(out, (rows, cols), torch.float32, "out")
+    _check("mx_dequantize_1d_ex", lib().mx_dequantize_1d_ex(
+        _ptr(codes), _ptr(scales), _ptr(macro_r) if macro_block else None, rows, cols, int(macro_block),
+        _ptr(out), _stream()))
+    return out
+
+
+def quantize_2d_deosc(w, prev_codes, prev_scales, margin64: int, codes=None, scales=None,
+                      codes_t=None, scales_t=None, transposed=True, flips=True):
+    """32x32 quantization with the de-oscillation band against the previous
+    step's as-given codes and scales (see mx_quantize_2d_deosc).  codes /
+    scales default to new tensors; passing prev_codes / prev_scales again
+    updates them in place.  Returns (codes, scales, codes_t, scales_t,
+    flips), None for what was not asked for."""
+    torch = _torch()
+    _dev(w, "w")
+    squeeze = w.dim() == 2
+    w3 = w.unsqueeze(0) if squeeze else w
+    b, r, c = w3.shape
+    u8, dev = torch.uint8, w.device
+
+    def as3(t):
+        return t.unsqueeze(0) if t is not None and t.dim() == 2 else t
+
+    prev_codes, prev_scales = as3(prev_codes), as3(prev_scales)
+    codes = as3(codes) if codes is not None else torch.empty((b, r, c // 2), dtype=u8, device=dev)
+    scales = as3(scales) if scales is not None else torch.empty((b, r // 32, c // 32), dtype=u8, device=dev)
+    if transposed:
+        codes_t = as3(codes_t) if codes_t is not None else torch.empty((b, c, r // 2), dtype=u8, device=dev)
+        scales_t = as3(scales_t) if scales_t is not None else torch.empty((b, c // 32, r // 32), dtype=u8,
+                                                                          device=dev)
+    else:
+        codes_t = scales_t = None
+    fl = torch.empty((b, r // 32, c // 32), dtype=torch.int16, device=dev) if flips else None
+    pld = _shaped(prev_codes, (b, r, c // 2), u8, "prev_codes", pitched=True)
+    _shaped(prev_scales, (b, r // 32, c // 32), u8, "prev_scales")
+    ld = _shaped(codes, (b, r, c // 2), u8, "codes", pitched=True)
+    _shaped(scales, (b, r // 32, c // 32), u8, "scales")
+    ld_t = 0 if codes_t is None else _shaped(codes_t, (b, c, r // 2), u8, "codes_t", pitched=True)
+    if scales_t is not None:
+        _shaped(scales_t, (b, c // 32, r // 32), u8, "scales_t")
+    _check("mx_quantize_2d_deosc", lib().mx_quantize_2d_deosc(
+        _ptr(w3), _dtype_code(w3), b, r, c, _ptr(prev_codes), pld, _ptr(prev_scales), int(margin64),
+        _ptr(codes), ld, _ptr(scales), _ptr(codes_t), ld_t, _ptr(scales_t), _ptr(fl), _stream()))
+    out = [codes, scales, codes_t, scales_t, fl]
     if squeeze:
         out = [t[0] if t is not None and t.dim() == 3 else t for t in out]
     return tuple(out)

@@ -15,7 +15,8 @@ def L():
 
 def test_every_declared_symbol_is_exported(L):
     names = mx.declared_functions()
-    assert set(names) >= {"mx_rht", "mx_quantize_1d", "mx_quantize_2d", "mx_dequantize",
+    assert set(names) >= {"mx_rht", "mx_quantize_1d", "mx_quantize_2d", "mx_quantize_2d_deosc", "mx_quantize_1d_ex",
+                          "mx_dequantize_1d_ex", "mx_dequantize",
                           "mx_grouped_gemm", "mx_grouped_gemm_q", "mx_rht_sign_mask", "mx_status_str",
                           "mx_version"}
     for n in names:
@@ -81,6 +82,49 @@ def test_quantize_2d_validation(L):
     assert q(FAKE, mx.MX_BF16, 0, 32, 32, FAKE, 0, FAKE, None, 0, None, None) == 0
     # empty: no pointer is looked at (zero-size tensors may have null pointers)
     assert q(None, mx.MX_BF16, 0, 32, 32, None, 0, None, None, 0, None, None) == 0
+
+
+def test_quantize_2d_deosc_validation(L):
+    q = L.mx_quantize_2d_deosc
+    ok = dict(w=FAKE, wt=mx.MX_F32, b=1, r=64, c=64, pc=FAKE, pld=0, ps=FAKE, m=8, cd=FAKE, ld=0,
+              sc=FAKE, ct=None, ldt=0, st=None, fl=FAKE, s=None)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return q(a["w"], a["wt"], a["b"], a["r"], a["c"], a["pc"], a["pld"], a["ps"], a["m"], a["cd"], a["ld"],
+                 a["sc"], a["ct"], a["ldt"], a["st"], a["fl"], a["s"])
+
+    assert call(r=48) == 2                       # rows not a multiple of 32
+    assert call(m=32) == 2 and call(m=-1) == 2   # margin outside [0, 31]
+    assert call(wt=3) == 4
+    assert call(pc=None) == 1 and call(ps=None) == 1 and call(cd=None) == 1 and call(sc=None) == 1
+    assert call(ct=FAKE) == 1                    # transposed codes without their scales
+    assert call(w=FAKE + 4) == 3 and call(pc=FAKE + 8) == 3 and call(fl=FAKE + 1) == 3
+    assert call(pld=16) == 2 and call(ld=40) == 2
+    assert call(pc=FAKE, cd=FAKE, pld=64, ld=0) == 2    # in place with another pitch
+    assert call(b=0, w=None, pc=None, ps=None, cd=None, sc=None) == 0
+
+
+def test_study_variant_validation(L):
+    q = L.mx_quantize_1d_ex
+    args = [FAKE, mx.MX_F32, 4, 256, 0, 0, 0, 0, 0, 0, 1.0, 128, FAKE, FAKE, FAKE, None]
+
+    def call(i_vals):
+        a = list(args)
+        for i, v in i_vals:
+            a[i] = v
+        return q(*a)
+
+    assert call([(10, 0.0)]) == 2 and call([(10, 1.5)]) == 2 and call([(10, float("nan"))]) == 2
+    assert call([(11, 96)]) == 2 and call([(11, 48)]) == 2 and call([(11, -32)]) == 2
+    assert call([(14, None)]) == 1 and call([(12, None)]) == 1
+    assert call([(14, FAKE + 2)]) == 3 and call([(0, FAKE + 4)]) == 3
+    assert call([(1, 5)]) == 4 and call([(6, 2)]) == 5 and call([(3, 48)]) == 2
+    assert call([(2, 0), (0, None), (12, None), (13, None), (14, None)]) == 0
+    d = L.mx_dequantize_1d_ex
+    assert d(FAKE, FAKE, None, 4, 256, 128, FAKE, None) == 1
+    assert d(FAKE, FAKE, FAKE, 4, 256, 96, FAKE, None) == 2
+    assert d(FAKE + 4, FAKE, None, 4, 256, 0, FAKE, None) == 3
 
 
 def test_dequantize_validation(L):
