@@ -52,8 +52,8 @@ WS = 0.5 + 1 / 1024            # 32x32 MXFP4 bytes per element (one layout)
 ROLE_KERNEL = {
     "q2d": "q2d_kernel<true,false>",
     "q1d_row_rtne": "q1d_row_kernel_w<true,false,false>",
+    "q1d_col": "q1d_col_kernel<true,true,true,0>",
     "q1d_row_sr": "q1d_row_kernel_w<true,false,true>",
-    "q1d_col": "q1d_col_kernel<true,true,true>",
     "gemm_fwd_gather": "gemm_kernel<true,true,false,true,true,false>",
     "gemm_bf16": "gemm_kernel<true,true,false,false,true,false>",
     "gemm_wgrad": "gemm_kernel<false,false,true,false,true,false>",
@@ -132,32 +132,38 @@ class Step:
         mx, b, i = self.mx, self.b, self.inp
         m = self.mask
         off, poff, idx = i["off"], i["poff"], i["idx"]
+        # Each tensor's row-wise and column-wise operands come from separate
+        # launches.  The column-wise RHT+SR quantizer is bound by arithmetic
+        # (Philox and the butterflies), so folding the row-wise pass into it
+        # (mx_quantize_1d_dual, one read) was measured slower: the row pass's
+        # work lands on the busy unit, and the read it saves was not the
+        # limit (see dual_quantize in the bench line).
+        col = dict(block_axis=0, group_offsets=off, kp=self.kp, use_rht=True, sign_mask=m, rnd=mx.SR, seed=5)
         self._t("q2d", lambda: mx.quantize_2d_into(i["W1"], b["w1c"], b["w1s"], b["w1tc"], b["w1ts"]))
         self._t("q2d", lambda: mx.quantize_2d_into(i["W2"], b["w2c"], b["w2s"], b["w2tc"], b["w2ts"]))
         self._t("q1d_row_rtne", lambda: mx.quantize_1d(i["X"], codes=b["xc"], scales=b["xs"]))
         self._t("gemm_fwd_gather", lambda: mx.grouped_gemm(b["xc"], b["xs"], b["w1tc"], b["w1ts"], off, ROWS, F2,
                                                            D, a_row_index=idx, b_scale_2d=True, out=b["Y1"]))
         self._t("q1d_row_rtne", lambda: mx.quantize_1d(i["h"], codes=b["hc"], scales=b["hs"]))
+        self._t("q1d_col", lambda: mx.quantize_1d(i["h"], stream_id=4, codes=b["hTc"], scales=b["hTs"], **col))
         self._t("gemm_bf16", lambda: mx.grouped_gemm(b["hc"], b["hs"], b["w2tc"], b["w2ts"], off, ROWS, D, D,
                                                      b_scale_2d=True, out=b["Y2"]))
         self._t("q1d_row_sr", lambda: mx.quantize_1d(i["dY2"], rnd=mx.SR, seed=5, stream_id=1,
                                                      codes=b["g2c"], scales=b["g2s"]))
+        self._t("q1d_col", lambda: mx.quantize_1d(i["dY2"], stream_id=5, codes=b["g2Tc"], scales=b["g2Ts"], **col))
         self._t("gemm_bf16", lambda: mx.grouped_gemm(b["g2c"], b["g2s"], b["w2c"], b["w2s"], off, ROWS, D, D,
                                                      b_scale_2d=True, out=b["dh"]))
-        self._t("q1d_row_sr", lambda: mx.quantize_1d(i["dY1"], rnd=mx.SR, seed=5, stream_id=0,
-                                                     codes=b["g1c"], scales=b["g1s"]))
-        self._t("gemm_bf16", lambda: mx.grouped_gemm(b["g1c"], b["g1s"], b["w1c"], b["w1s"], off, ROWS, D, F2,
-                                                     b_scale_2d=True, out=b["dX"]))
-        col = dict(block_axis=0, group_offsets=off, kp=self.kp, use_rht=True, sign_mask=m, rnd=mx.SR, seed=5)
-        self._t("q1d_col", lambda: mx.quantize_1d(i["h"], stream_id=4, codes=b["hTc"], scales=b["hTs"], **col))
-        self._t("q1d_col", lambda: mx.quantize_1d(i["dY2"], stream_id=5, codes=b["g2Tc"], scales=b["g2Ts"], **col))
         self._t("gemm_wgrad", lambda: mx.grouped_gemm(b["hTc"], b["hTs"], b["g2Tc"], b["g2Ts"], poff, D, D, self.kp,
                                                       group_dim_k=True, out=b["dW2"]))
+        self._t("q1d_row_sr", lambda: mx.quantize_1d(i["dY1"], rnd=mx.SR, seed=5, stream_id=0,
+                                                     codes=b["g1c"], scales=b["g1s"]))
+        self._t("q1d_col", lambda: mx.quantize_1d(i["dY1"], stream_id=3, codes=b["g1Tc"], scales=b["g1Ts"], **col))
+        self._t("gemm_bf16", lambda: mx.grouped_gemm(b["g1c"], b["g1s"], b["w1c"], b["w1s"], off, ROWS, D, F2,
+                                                     b_scale_2d=True, out=b["dX"]))
         # X^T: the routed rows are gathered from the 16384-token X inside the
         # quantizer (no permuted copy)
         self._t("q1d_col", lambda: mx.quantize_1d(i["X"], stream_id=2, codes=b["xTc"], scales=b["xTs"],
                                                   row_index=idx, **col))
-        self._t("q1d_col", lambda: mx.quantize_1d(i["dY1"], stream_id=3, codes=b["g1Tc"], scales=b["g1Ts"], **col))
         self._t("gemm_wgrad", lambda: mx.grouped_gemm(b["xTc"], b["xTs"], b["g1Tc"], b["g1Ts"], poff, D, F2, self.kp,
                                                       group_dim_k=True, out=b["dW1"]))
 
@@ -190,7 +196,7 @@ def work_model():
     return {
         "q2d": {"bytes": (E * D * F2 + E * D * D) * (2 + 2 * WS), "launches": 2},
         "q1d_row_rtne": {"bytes": (T * D + ROWS * D) * BPE_1D, "launches": 2},
-        "q1d_row_sr": {"bytes": (ROWS * D + ROWS * F2) * BPE_1D, "launches": 2},
+        "q1d_row_sr": {"bytes": ROWS * (D + F2) * BPE_1D, "launches": 2},
         "q1d_col": {"bytes": (T * D + 2 * ROWS * D + ROWS * F2) * 2 + (3 * ROWS * D + ROWS * F2) * CS,
                     "launches": 4},
         "gemm_fwd_gather": dict(gemm_fwd_gather, launches=1),
@@ -364,6 +370,104 @@ def fused_epilogue(torch, step, reps=5):
     return res
 
 
+def deosc_study(torch, dev, steps=10, sigma=1e-4, margins=(0, 4, 8, 16)):
+    """Weight de-oscillation on a synthetic master-weight trajectory: 32
+    expert weights fp32 2880x5760 N(0, 0.02) take `steps` zero-mean random
+    steps of `sigma` per element (the converged, noise-dominated regime in
+    which weights near a boundary oscillate).  The quantized state starts
+    from the plain 2D quantization and is updated in place by
+    mx_quantize_2d_deosc at each step.  Reports bin flips per step and the
+    final round-trip error against the master weights for each margin, and
+    the kernel's time and GB/s on this tensor."""
+    from mxfp4_precision_numerics_amd import mx
+    g = torch.Generator(device=dev).manual_seed(6)
+    w0 = torch.randn(E, D, F2, device=dev, generator=g) * 0.02
+    res = {"workload": "32 x fp32 2880x5760 master weights N(0,0.02), %d random-walk steps of %g" % (steps, sigma),
+           "margins": {}}
+    for m in margins:
+        w = w0.clone()
+        c, s, _, _ = mx.quantize_2d(w, transposed=False)
+        gs = torch.Generator(device=dev).manual_seed(7)
+        flips = []
+        for _ in range(steps):
+            w += torch.randn(w.shape, device=dev, generator=gs) * sigma
+            _, _, _, _, fl = mx.quantize_2d_deosc(w, c, s, m, codes=c, scales=s, transposed=False)
+            flips.append(int(fl.view(torch.int16).to(torch.int64).sum()))
+        y = mx.dequantize(c, s, block_rows=32)
+        r = rel_err(torch, w, y)
+        res["margins"][str(m)] = {"flips_per_step": float(np.mean(flips)), "flip_rate": float(np.mean(flips)) / w.numel(),
+                                  "rel_err": r["rel_err"], "snr_db": r["snr_db"]}
+        del w, y
+    # kernel time: fp32 master weights, both layouts, in place, margin 8
+    c, s, ct, st = mx.quantize_2d(w0)
+    t = time_launches(torch, [lambda: mx.quantize_2d_deosc(w0, c, s, 8, codes=c, scales=s, codes_t=ct,
+                                                           scales_t=st)], 5)
+    tp = time_launches(torch, [lambda: mx.quantize_2d_into(w0, c, s, ct, st)], 5)
+    n = E * D * F2
+    nbytes = n * (4 + WS + 2 * WS) + (n // 1024) * 2     # master weights, previous codes, both layouts, flips
+    res.update({"deosc_ms": t, "deosc_GBps": nbytes / t / 1e6, "deosc_roofline": roof({"bytes": nbytes}, t),
+                "plain_2d_fp32_ms": tp})
+    del w0, c, s, ct, st
+    return res
+
+
+def snr_study(torch, dev):
+    """Operator-level SNR (C26: -20 log10 of the relative Frobenius error) of
+    outlier clipping and macro-block scaling on synthetic tensors, with and
+    without the RHT, RTNE.  All quantization and decoding runs in the
+    library's kernels (mx_quantize_1d_ex / mx_dequantize_1d_ex); the error
+    sums are taken in float64 on the device."""
+    from mxfp4_precision_numerics_amd import mx
+    g = torch.Generator(device=dev).manual_seed(8)
+    c = torch.exp(torch.empty(D, device=dev).uniform_(math.log(0.1), math.log(10.0), generator=g))
+    act = (torch.randn(T, D, device=dev, generator=g) * c)
+    out = act.clone().view(-1)
+    pos = torch.randperm(out.numel(), device=dev, generator=g)[:out.numel() // 1000]
+    out[pos] *= 50.0
+    tensors = {
+        "activations 16384x2880 (N(0,1) x log-uniform channel scale)": act.to(torch.bfloat16),
+        "activations with 0.1% outliers x50": out.view(T, D).to(torch.bfloat16),
+        "gradients 16384x2880 N(0, 1e-3)": (torch.randn(T, D, device=dev, generator=g) * 1e-3).to(torch.bfloat16),
+        "heavy-tailed 16384x2880 (Student-t, 3 dof)": (torch.randn(T, D, device=dev, generator=g) / torch.sqrt(
+            sum(torch.randn(T, D, device=dev, generator=g) ** 2 for _ in range(3)) / 3)).to(torch.bfloat16),
+    }
+    variants = [("plain", 1.0, 0), ("clip 0.875", 0.875, 0), ("clip 0.75", 0.75, 0), ("clip 0.5", 0.5, 0),
+                ("clip search", 0.0, 0), ("macro 320", 1.0, 320), ("macro 2880 (row)", 1.0, 2880),
+                ("macro 320 + clip search", 0.0, 320)]
+    mask = mx.rht_sign_mask(1)
+    res = {}
+    for name, x in tensors.items():
+        row = {}
+        for use_rht in (False, True):
+            ref = mx.rht(x, mask) if use_rht else x.float()
+            for vname, clip, bm in variants:
+                cc, ss, mr = mx.quantize_1d_ex(x, use_rht=use_rht, sign_mask=mask, clip_ratio=clip, macro_block=bm)
+                y = mx.dequantize_1d_ex(cc, ss, mr, macro_block=bm)
+                row[("RHT, " if use_rht else "") + vname] = round(rel_err(torch, ref, y)["snr_db"], 3)
+        res[name] = row
+    return res
+
+
+def dual_vs_separate(torch, step, reps=5):
+    """The dual quantizer (one read, row-wise and column-wise RHT+SR codes)
+    against the two separate launches it replaces, on the step's buffers:
+    h (65536 x 2880, row RTNE) and dY1 (65536 x 5760, row SR)."""
+    mx, b, i = step.mx, step.b, step.inp
+    off, m, kp = i["off"], step.mask, step.kp
+    res = {}
+    for name, x, rnd, rs, cs_, rc, rsc, cc, csc in (("h_row_rtne", i["h"], mx.RNE, 0, 4, "hc", "hs", "hTc", "hTs"),
+                                                   ("dY1_row_sr", i["dY1"], mx.SR, 0, 3, "g1c", "g1s", "g1Tc", "g1Ts")):
+        sep = lambda: (mx.quantize_1d(x, rnd=rnd, seed=5, stream_id=rs, codes=b[rc], scales=b[rsc]),  # noqa
+                       mx.quantize_1d(x, block_axis=0, group_offsets=off, kp=kp, use_rht=True, sign_mask=m,
+                                      rnd=mx.SR, seed=5, stream_id=cs_, codes=b[cc], scales=b[csc]))
+        dual = lambda: mx.quantize_1d_dual(x, off, kp=kp, use_rht=True, sign_mask=m, col_rnd=mx.SR,  # noqa
+                                           col_stream_id=cs_, row_rnd=rnd, row_stream_id=rs, seed=5,
+                                           col_codes=b[cc], col_scales=b[csc], row_codes=b[rc], row_scales=b[rsc])
+        res[name] = {"shape": "%dx%d" % tuple(x.shape), "separate_ms": time_launches(torch, [sep], reps, repeats=5),
+                     "dual_ms": time_launches(torch, [dual], reps, repeats=5)}
+    return res
+
+
 def cpu_baseline_config(k, gemm_seconds=8.0):
     """The oracle on config k itself (configs 1-3 run whole; config 4 on
     sampled output rows, extrapolated)."""
@@ -451,7 +555,7 @@ def cpu_baseline(gemm_seconds=8.0, single_thread=True):
 
     def step_seconds(qr, mac_s):
         el = {"q1d_row_rtne": T * D + ROWS * D, "q1d_row_sr": ROWS * D + ROWS * F2,
-              "q1d_col": 3 * ROWS * D + ROWS * F2, "q2d": E * D * F2 + E * D * D}
+              "q1d_col": 3 * ROWS * D + ROWS * F2, "q2d": E * D * F2 + E * D * D}   # (the oracle runs each layout)
         t = {k: qr[k] * el[k] for k in el}
         t["gemm"] = sum(w[r]["flops"] for r in GEMM_ROLES) / 2 / mac_s
         return t
@@ -624,7 +728,12 @@ def main():
     }
     if not args.no_standalone:
         out["fused_epilogue"] = fused_epilogue(torch, step)
+        out["dual_quantize"] = dual_vs_separate(torch, step)
         del step, inp
+        torch.cuda.empty_cache()
+        out["deosc_study"] = deosc_study(torch, dev)
+        torch.cuda.empty_cache()
+        out["snr_study"] = snr_study(torch, dev)
         torch.cuda.empty_cache()
         out["standalone"] = {"config1": config1(torch, dev), "config2": config2(torch, dev),
                              "config3": config3(torch, dev),

@@ -131,6 +131,34 @@ mx_status mx_quantize_1d(const void* x, mx_dtype xt, int64_t rows, int64_t cols,
                          uint64_t seed, uint32_t stream_id, uint64_t index_base,
                          uint8_t* codes, int64_t codes_ld, uint8_t* scales, mx_stream stream);
 
+/* Both 1x32 quantizations of one token-major tensor from a single read: the
+ * column-wise, grouped layout (per-group padded, transposed, with the
+ * optional RHT; the weight-gradient operand) and the row-wise layout (1x32
+ * blocks along cols, never with the RHT; the data-gradient or forward
+ * operand).  The expert tensors dominate memory traffic as well as compute
+ * ("What ALTO Actually Does", news digest "AMD's ALTO Gets 4-Bit MoE
+ * Training to Within 0.007 of BF16"), and the recipe quantizes the same
+ * activation and gradient tensors once per GEMM that consumes them
+ * (Abstract of "Training an MoE LLM in MXFP4": 1D blocks, RHT and SR).
+ * The outputs are bit for bit those of
+ *   mx_quantize_1d(x, block_axis = 0, group_offsets, num_groups, kp, NULL,
+ *                  use_rht, sign_mask, col_rnd, seed, col_stream_id,
+ *                  col_index_base, col_codes, 0, col_scales) and
+ *   mx_quantize_1d(x, block_axis = 1, ..., use_rht = 0, row_rnd, seed,
+ *                  row_stream_id, row_index_base, row_codes, row_codes_ld,
+ *                  row_scales);
+ * the rows of x are the grouped positions (no row gather).  Row-wise codes
+ * [rows x cols/2] at pitch row_codes_ld (0 = cols/2), scales
+ * [rows x cols/32].  Arguments, layouts and errors otherwise as
+ * mx_quantize_1d. */
+mx_status mx_quantize_1d_dual(const void* x, mx_dtype xt, int64_t rows, int64_t cols,
+                              const int32_t* group_offsets, int32_t num_groups, int64_t kp, int use_rht,
+                              uint32_t sign_mask, mx_round col_rnd, uint32_t col_stream_id,
+                              uint64_t col_index_base, uint8_t* col_codes, uint8_t* col_scales,
+                              mx_round row_rnd, uint32_t row_stream_id, uint64_t row_index_base,
+                              uint8_t* row_codes, int64_t row_codes_ld, uint8_t* row_scales, uint64_t seed,
+                              mx_stream stream);
+
 /* 32x32 MXFP4 quantization, round to nearest even (the "2D" half of the
  * hybrid scheme, used for weights).  w: batch x [rows x cols], rows % 32 ==
  * 0, cols % 32 == 0.  One pass writes the as-given layout (codes
@@ -158,7 +186,12 @@ mx_status mx_quantize_2d(const void* w, mx_dtype wt, int64_t batch, int64_t rows
  *   - clip_ratio rho in (0, 1]: a block's scale is chosen for
  *     fl32(rho * amax) instead of amax, X = floor(log2(fl32(rho * amax)))
  *     - 2, so its largest values saturate at +-6 * 2^X while the others get
- *     a finer grid; rho = 1 is mx_quantize_1d's rule;
+ *     a finer grid; rho = 1 is mx_quantize_1d's rule; rho = 0 selects a
+ *     search instead: a block takes X - 1 rather than the rule's X when
+ *     that strictly lowers its squared round-to-nearest-even error, each
+ *     candidate's error summed in fp64 in its own units (eight elements in
+ *     order per quarter of the block, then the four quarters in order),
+ *     X - 1 winning iff S(X - 1) < 4 S(X);
  *   - macro_block Bm (0 = none; else a multiple of 32 dividing cols): each
  *     Bm consecutive elements of a row (after the RHT, when on) are
  *     multiplied by r = fl32(6 / amax_M), their fp32 macro scale (r = 1
@@ -171,7 +204,7 @@ mx_status mx_quantize_2d(const void* w, mx_dtype wt, int64_t batch, int64_t rows
  * use_rht, sign_mask, rnd, seed, stream_id and index_base as in
  * mx_quantize_1d (row-wise).  Device pointers owned by the caller.
  * Errors: MX_ERR_DTYPE, MX_ERR_UNSUPPORTED (rnd), MX_ERR_SHAPE (sizes,
- * clip_ratio outside (0, 1], macro_block), MX_ERR_NULL, MX_ERR_ALIGN,
+ * clip_ratio outside [0, 1], macro_block), MX_ERR_NULL, MX_ERR_ALIGN,
  * MX_ERR_LAUNCH.  rows == 0 launches nothing. */
 mx_status mx_quantize_1d_ex(const void* x, mx_dtype xt, int64_t rows, int64_t cols, int use_rht,
                             uint32_t sign_mask, mx_round rnd, uint64_t seed, uint32_t stream_id,
@@ -196,15 +229,20 @@ mx_status mx_dequantize_1d_ex(const uint8_t* codes, const uint8_t* scales, const
  * between two levels under updates much smaller than a level step; the
  * Abstract of "Training an MoE LLM in MXFP4" names a simplified
  * de-oscillation scheme without giving its rule.  The rule here: the tile's
- * scale byte comes from its amax as in mx_quantize_2d; if it equals the
- * previous byte (neither 0xFF), an element keeps its previous code c while
+ * scale byte comes from its amax as in mx_quantize_2d, except that when
+ * that is one below the previous byte p (p != 0xFF) and the amax is at
+ * least (4 - margin64 / 16) 2^(p - 127), the tile keeps p (its elements
+ * still fit without clipping; the digest's case of a block whose shared
+ * scale, set by an outlier, moves every value of the block); if the byte
+ * then equals the previous one (neither 0xFF), an element keeps its
+ * previous code c while
  * its scaled value v = w / 2^X lies strictly inside
  * (q - f (q - q_dn), q + f (q_up - q)), q the value of c on the signed E2M1
  * grid {-6, ..., -0.5, 0, 0.5, ..., 6} (both zero codes are 0), q_dn / q_up
  * its neighbours there (the band is open past +-6), f = 1/2 + margin64 / 64;
- * otherwise it takes its round-to-nearest-even code, as does every element
- * of a tile whose scale changed.  margin64 = 0 leaves every decoded value
- * equal to mx_quantize_2d's.
+ * otherwise it takes its round-to-nearest-even code (at the tile's byte),
+ * as does every element of a tile whose scale changed.  margin64 = 0
+ * leaves every decoded value equal to mx_quantize_2d's.
  * w: batch x [rows x cols] (fp32 master weights, or bf16), rows % 32 == 0,
  * cols % 32 == 0; margin64 in [0, 31].
  * prev_codes / prev_scales: the as-given layout written for the previous

@@ -279,15 +279,44 @@ struct ColTile {
     static constexpr int TILE = CT_BLOCKS * BSTRIDE;
 };
 
-template <bool BF16, bool RHT, bool SR>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BF16 ? 3 : 2))) void q1d_col_kernel(const void* __restrict__ x, int64_t cols,
-                                                      const int32_t* __restrict__ off, int num_groups,
-                                                      const int32_t* __restrict__ ridx, int64_t npos,
-                                                      int64_t kp, int64_t col_tiles, int vec,
-                                                      uint32_t mask, uint32_t k0, uint32_t k1,
-                                                      uint32_t stream_id, uint64_t index_base,
-                                                      uint8_t* __restrict__ codes,
-                                                      uint8_t* __restrict__ scales) {
+// ROWQ (the dual form): the same tile is also quantized row-wise (1x32
+// blocks along the columns, no RHT; 1 = RTNE, 2 = SR with its own stream
+// and index base), as mx_quantize_1d(block_axis = 1) would quantize the
+// grouped rows: one read of x feeds both layouts.
+struct ColArgs {
+    const void* x;
+    int64_t cols;
+    const int32_t* off;
+    int num_groups;
+    const int32_t* ridx;
+    int64_t npos;
+    int64_t kp, col_tiles;
+    int vec;
+    uint32_t mask, k0, k1, stream_id;
+    uint64_t index_base;
+    uint8_t* codes;
+    uint8_t* scales;
+    // ROWQ: the row-wise outputs
+    uint8_t* row_codes;
+    int64_t row_ld;
+    uint8_t* row_scales;
+    uint32_t row_stream_id;
+    uint64_t row_index_base;
+};
+
+template <bool BF16, bool RHT, bool SR, int ROWQ>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BF16 ? 3 : 2))) void q1d_col_kernel(ColArgs a) {
+    const void* __restrict__ x = a.x;
+    const int64_t cols = a.cols;
+    const int32_t* __restrict__ off = a.off;
+    const int num_groups = a.num_groups;
+    const int32_t* __restrict__ ridx = a.ridx;
+    const int64_t npos = a.npos, kp = a.kp, col_tiles = a.col_tiles;
+    const int vec = a.vec;
+    const uint32_t mask = a.mask, k0 = a.k0, k1 = a.k1, stream_id = a.stream_id;
+    const uint64_t index_base = a.index_base;
+    uint8_t* __restrict__ codes = a.codes;
+    uint8_t* __restrict__ scales = a.scales;
     using TL = ColTile<BF16>;
     constexpr int CH = TL::ROWB / 16;                       // 16-byte chunks per tile row
     constexpr int NLD = CT_BLOCKS * 32 * CH / 256;           // chunks per thread per tile
@@ -456,6 +485,70 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BF16 ? 3 : 
             load_regs(pre, pkb, nct * CT_COLS);
         }
 
+        // ---- ROWQ: the row-wise quantization of the tile's tokens.  Thread t
+        // takes token row t % 32 of block t / 32 and both 32-column blocks of
+        // it; rows past a group's end (padding) have no row-wise counterpart.
+        // The RHT's signs, applied as the tile entered LDS, are undone.
+        if (ROWQ) {
+            int64_t t0;
+            int32_t n;
+            block_info(pb0, t0, n);                      // lane b < 8 of each wave: block b
+            const int rb = tid >> 5, rj = tid & 31;
+            const int64_t tb = (int64_t)(((uint64_t)(uint32_t)__shfl((int)((uint64_t)t0 >> 32), rb) << 32) |
+                                         (uint32_t)__shfl((int)(uint32_t)t0, rb));
+            const int32_t nb = __shfl(n, rb);
+            const int64_t prow = tb + rj;                // the token's grouped row
+            const uint32_t sg = sign_word(rj);
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const int64_t c = c0 + 32 * half;
+                if (rj < nb && c < cols) {
+                    const uint8_t* src = tile + rb * TL::BSTRIDE + rj * TL::ROWB + half * 32 * TL::EB;
+                    float v[32];
+                    if (BF16) {
+#pragma unroll
+                        for (int k = 0; k < 4; ++k) {
+                            const uint4 w = *(const uint4*)(src + 16 * k);
+                            const uint32_t ww[4] = {w.x ^ sg, w.y ^ sg, w.z ^ sg, w.w ^ sg};
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                v[8 * k + 2 * e] = bf16lo(ww[e]);
+                                v[8 * k + 2 * e + 1] = bf16hi(ww[e]);
+                            }
+                        }
+                    } else {
+#pragma unroll
+                        for (int k = 0; k < 8; ++k) {
+                            const uint4 w = *(const uint4*)(src + 16 * k);
+                            v[4 * k + 0] = __uint_as_float(w.x ^ sg); v[4 * k + 1] = __uint_as_float(w.y ^ sg);
+                            v[4 * k + 2] = __uint_as_float(w.z ^ sg); v[4 * k + 3] = __uint_as_float(w.w ^ sg);
+                        }
+                    }
+                    uint32_t am = 0;
+#pragma unroll
+                    for (int e = 0; e < 32; ++e) am = max(am, __float_as_uint(v[e]) & 0x7FFFFFFFu);
+                    const uint32_t byte = scale_byte_from_amax_bits(am);
+                    const float sc = scale_operand(byte);
+                    uint32_t w4[4];
+                    const uint64_t ebase = a.row_index_base + (uint64_t)prow * (uint64_t)cols + (uint64_t)c;
+#pragma unroll
+                    for (int qq = 0; qq < 4; ++qq) {
+                        if (ROWQ == 2) {
+                            const uint64_t g8 = (ebase + qq * 8) >> 3;
+                            const u32x4 r = philox4x32_10((uint32_t)g8, (uint32_t)(g8 >> 32), a.row_stream_id, 0u,
+                                                          k0, k1);
+                            w4[qq] = cvt8_sr(v + 8 * qq, sc, r);
+                        } else {
+                            w4[qq] = cvt8_rne(v + 8 * qq, sc);
+                        }
+                    }
+                    if (byte == 0xFFu) w4[0] = w4[1] = w4[2] = w4[3] = 0;
+                    *(uint4*)(a.row_codes + prow * a.row_ld + (c >> 5) * 16) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+                    a.row_scales[prow * (cols >> 5) + (c >> 5)] = (uint8_t)byte;
+                }
+            }
+        }
+
         // ---- quantize: thread = (block b, column pair cp), one column at a time
         const int b = tid >> 5, cp = tid & 31;
         uint4 outc[2];
@@ -596,6 +689,8 @@ struct DeoscArgs {
     int64_t prev_ld;
     const uint8_t* prev_scales;  // [batch x rows/32 x cols/32] (may alias scales)
     float f;                     // 1/2 + margin / 64
+    float scale_keep;            // 4 - margin / 16: a one-binade drop of the tile amax above
+                                 // scale_keep * 2^X_prev keeps the previous scale byte
     uint16_t* flips;             // per tile: elements whose decoded value changed (may be NULL)
 };
 
@@ -695,7 +790,18 @@ __global__ __launch_bounds__(256) void q2d_kernel(const void* __restrict__ w, in
             __syncthreads();
             if (t < 8) {
                 const uint32_t m = max(max(wave_amax[0][t], wave_amax[1][t]), max(wave_amax[2][t], wave_amax[3][t]));
-                tile_scale[ts][t] = (uint8_t)scale_byte_from_amax_bits(m);
+                uint32_t sbyte = scale_byte_from_amax_bits(m);
+                // DEOSC: an amax that dropped just below the previous scale's
+                // range (the rule one byte below the previous byte p, amax >=
+                // (4 - margin / 16) 2^(p - 127)) keeps p; every element then
+                // fits without clipping
+                if (DEOSC && cs * 8 + t < tiles_per_row) {
+                    const uint32_t p = dz.prev_scales[(bt * row_tiles + tr) * tiles_per_row + cs * 8 + t];
+                    if (p != 0xFFu && sbyte != 0xFFu && sbyte + 1u == p &&
+                        __uint_as_float(m) >= dz.scale_keep * __uint_as_float(p << 23))
+                        sbyte = p;
+                }
+                tile_scale[ts][t] = (uint8_t)sbyte;
             }
             __syncthreads();
             const uint32_t byte = tile_scale[ts][j];
@@ -925,8 +1031,41 @@ __global__ __launch_bounds__(256) void q1d_ex_kernel(const void* __restrict__ x,
 #pragma unroll
         for (int e = 0; e < 8; ++e) am = max(am, __float_as_uint(t[e]) & 0x7FFFFFFFu);
         am = quad_max_u(am);
-        // the scale for fl32(rho * amax); a NaN or Inf amax stays non-finite
-        const uint32_t byte = scale_byte_from_amax_bits(__float_as_uint(clip_ratio * __uint_as_float(am)) & 0x7FFFFFFFu);
+        uint32_t byte;
+        if (clip_ratio > 0.0f) {
+            // the scale for fl32(rho * amax); a NaN or Inf amax stays non-finite
+            byte = scale_byte_from_amax_bits(__float_as_uint(clip_ratio * __uint_as_float(am)) & 0x7FFFFFFFu);
+        } else {
+            // search: X - 1 instead of X when it strictly lowers the block's
+            // squared RTNE error.  Each candidate's error is summed in its own
+            // units in fp64 (v = y / 2^X and the difference |v| - |q| are
+            // exact there, the square too): eight elements in order per lane,
+            // then the quad's four sums in lane order.  X - 1 wins iff
+            // S(X - 1) < 4 S(X).
+            byte = scale_byte_from_amax_bits(am);
+            if (byte != 0xFFu && byte > 0u) {
+                double S[2];
+#pragma unroll
+                for (int cand = 0; cand < 2; ++cand) {
+                    const uint32_t bc = byte - cand;
+                    const uint32_t cw = cvt8_rne(t, scale_operand(bc));
+                    float qv[8];
+                    decode8(cw, scale_operand(127u), qv);              // the RTNE grid values, unscaled
+                    const double inv = __longlong_as_double((long long)(1150u - bc) << 52);   // 2^-X, X = bc - 127
+                    double acc = 0.0;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const double d = fabs((double)t[e] * inv) - (double)fabsf(qv[e]);
+                        acc = acc + d * d;
+                    }
+                    const int l0 = lane & ~3;
+                    const double s0 = __shfl(acc, l0), s1 = __shfl(acc, l0 + 1), s2 = __shfl(acc, l0 + 2),
+                                 s3 = __shfl(acc, l0 + 3);
+                    S[cand] = ((s0 + s1) + s2) + s3;
+                }
+                if (S[1] < 4.0 * S[0]) byte -= 1u;
+            }
+        }
         const float sc = scale_operand(byte);
         uint32_t packed;
         if (SR) {
@@ -1007,6 +1146,47 @@ uint32_t host_philox_word0(uint32_t k0, uint32_t k1) {
         k1 += 0xBB67AE85u;
     }
     return c0;
+}
+
+// Column-wise launch: persistent grid sized to residency (the bf16 RHT+SR
+// variant needs ~150 VGPRs, 3 workgroups per CU; fp32 tiles take 66 KiB of
+// LDS and up to ~240 VGPRs, 2 per CU).  Fills a.col_tiles and a.vec.
+template <bool B, bool R, bool S, int Q>
+mx_status launch_col_t(ColArgs a, hipStream_t s) {
+    a.col_tiles = (a.cols + CT_COLS - 1) / CT_COLS;
+    const int64_t tiles = a.col_tiles * ((a.kp / 32 + CT_BLOCKS - 1) / CT_BLOCKS);
+    const int grid = (int)min(tiles, (int64_t)resident_blocks(B ? 3 : 2));
+    a.vec = (a.cols % (B ? 8 : 4)) == 0;
+    const size_t lds = (size_t)ColTile<B>::TILE + 4 * (size_t)(a.num_groups + 1);
+    if (!B) {
+        // fp32 tiles take more than 64 KiB of dynamic LDS: raise the limit of
+        // the instantiation about to run, on the current device, every call
+        // (the library keeps no state)
+        if (hipFuncSetAttribute((const void*)q1d_col_kernel<B, R, S, Q>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)lds) != hipSuccess) {
+            (void)hipGetLastError();
+            return MX_ERR_LAUNCH;
+        }
+    }
+    (void)hipGetLastError();
+    hipLaunchKernelGGL((q1d_col_kernel<B, R, S, Q>), dim3(grid), dim3(256), lds, s, a);
+    return hipGetLastError() == hipSuccess ? MX_OK : MX_ERR_LAUNCH;
+}
+
+template <bool B, bool R, bool S>
+mx_status launch_col_q(const ColArgs& a, int rowq, hipStream_t s) {
+    if (rowq == 0) return launch_col_t<B, R, S, 0>(a, s);
+    if (rowq == 1) return launch_col_t<B, R, S, 1>(a, s);
+    return launch_col_t<B, R, S, 2>(a, s);
+}
+
+mx_status launch_col(const ColArgs& a, bool bf, bool rh, bool sr, int rowq, hipStream_t s) {
+    if (bf) {
+        if (rh) return sr ? launch_col_q<true, true, true>(a, rowq, s) : launch_col_q<true, true, false>(a, rowq, s);
+        return sr ? launch_col_q<true, false, true>(a, rowq, s) : launch_col_q<true, false, false>(a, rowq, s);
+    }
+    if (rh) return sr ? launch_col_q<false, true, true>(a, rowq, s) : launch_col_q<false, true, false>(a, rowq, s);
+    return sr ? launch_col_q<false, false, true>(a, rowq, s) : launch_col_q<false, false, false>(a, rowq, s);
 }
 
 }  // namespace
@@ -1126,31 +1306,35 @@ mx_status mx_quantize_1d(const void* x, mx_dtype xt, int64_t rows, int64_t cols,
     if (!x || !codes || !scales) return MX_ERR_NULL;
     if (!aligned16(x) || !aligned16(codes)) return MX_ERR_ALIGN;
     if (cols > (int64_t)(0xFFFFFFFFu / (bf ? 2u : 4u))) return MX_ERR_SHAPE;   // one row of x within 4 GiB
-    const int64_t col_tiles = (cols + CT_COLS - 1) / CT_COLS;
-    const int64_t tiles = col_tiles * ((kp / 32 + CT_BLOCKS - 1) / CT_BLOCKS);
-    // persistent grid, sized to residency: the bf16 RHT+SR variant needs
-    // ~150 VGPRs (3 workgroups per CU); fp32 tiles take 66 KiB of LDS and
-    // up to ~240 VGPRs (2 per CU)
-    const int grid = (int)min(tiles, (int64_t)resident_blocks(bf ? 3 : 2));
-    const int vec = (cols % (bf ? 8 : 4)) == 0;
-    const size_t lds = (size_t)(bf ? ColTile<true>::TILE : ColTile<false>::TILE) + 4 * (size_t)(num_groups + 1);
-    if (!bf) {
-        // fp32 tiles take more than 64 KiB of dynamic LDS: raise the limit of
-        // the instantiation about to run, on the current device, every call
-        // (the library keeps no state)
-        const void* fn = rh ? (sr ? (const void*)q1d_col_kernel<false, true, true>
-                                  : (const void*)q1d_col_kernel<false, true, false>)
-                            : (sr ? (const void*)q1d_col_kernel<false, false, true>
-                                  : (const void*)q1d_col_kernel<false, false, false>);
-        if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess) {
-            (void)hipGetLastError();
-            return MX_ERR_LAUNCH;
-        }
-    }
-    (void)hipGetLastError();
-    MX_DISPATCH3_LDS(q1d_col_kernel, bf, rh, sr, dim3(grid), lds, s, x, cols, group_offsets, (int)num_groups, row_index, rows, kp,
-                     col_tiles, vec, sign_mask, k0, k1, stream_id, index_base, codes, scales);
-    return launched();
+    ColArgs a{x, cols, group_offsets, (int)num_groups, row_index, rows, kp, 0, 0, sign_mask, k0, k1, stream_id,
+              index_base, codes, scales, nullptr, 0, nullptr, 0, 0};
+    return launch_col(a, bf, rh, sr, 0, s);
+}
+
+mx_status mx_quantize_1d_dual(const void* x, mx_dtype xt, int64_t rows, int64_t cols, const int32_t* group_offsets,
+                              int32_t num_groups, int64_t kp, int use_rht, uint32_t sign_mask, mx_round col_rnd,
+                              uint32_t col_stream_id, uint64_t col_index_base, uint8_t* col_codes,
+                              uint8_t* col_scales, mx_round row_rnd, uint32_t row_stream_id,
+                              uint64_t row_index_base, uint8_t* row_codes, int64_t row_codes_ld,
+                              uint8_t* row_scales, uint64_t seed, mx_stream stream) {
+    if (xt != MX_F32 && xt != MX_BF16) return MX_ERR_DTYPE;
+    if ((col_rnd != MX_RNE && col_rnd != MX_SR) || (row_rnd != MX_RNE && row_rnd != MX_SR)) return MX_ERR_UNSUPPORTED;
+    if (rows < 0 || cols <= 0 || cols % 32) return MX_ERR_SHAPE;
+    if (col_index_base % 32 || row_index_base % 32) return MX_ERR_SHAPE;
+    if (num_groups < 1 || num_groups > COL_MAX_GROUPS) return MX_ERR_SHAPE;
+    if (kp < 0 || kp % 32) return MX_ERR_SHAPE;
+    const int64_t ld = row_codes_ld ? row_codes_ld : cols / 2;
+    if (ld < cols / 2 || ld % 16) return MX_ERR_SHAPE;
+    if (!group_offsets) return MX_ERR_NULL;
+    if (kp == 0 || rows == 0) return MX_OK;
+    if (!x || !col_codes || !col_scales || !row_codes || !row_scales) return MX_ERR_NULL;
+    if (!aligned16(x) || !aligned16(col_codes) || !aligned16(row_codes)) return MX_ERR_ALIGN;
+    const bool bf = xt == MX_BF16;
+    if (cols > (int64_t)(0xFFFFFFFFu / (bf ? 2u : 4u))) return MX_ERR_SHAPE;
+    ColArgs a{x, cols, group_offsets, (int)num_groups, nullptr, rows, kp, 0, 0, sign_mask, (uint32_t)seed,
+              (uint32_t)(seed >> 32), col_stream_id, col_index_base, col_codes, col_scales, row_codes, ld, row_scales,
+              row_stream_id, row_index_base};
+    return launch_col(a, bf, use_rht != 0, col_rnd == MX_SR, row_rnd == MX_SR ? 2 : 1, (hipStream_t)stream);
 }
 
 mx_status mx_quantize_1d_ex(const void* x, mx_dtype xt, int64_t rows, int64_t cols, int use_rht, uint32_t sign_mask,
@@ -1159,7 +1343,7 @@ mx_status mx_quantize_1d_ex(const void* x, mx_dtype xt, int64_t rows, int64_t co
     if (xt != MX_F32 && xt != MX_BF16) return MX_ERR_DTYPE;
     if (rnd != MX_RNE && rnd != MX_SR) return MX_ERR_UNSUPPORTED;
     if (rows < 0 || cols <= 0 || cols % 32 || index_base % 32) return MX_ERR_SHAPE;
-    if (!(clip_ratio > 0.0f && clip_ratio <= 1.0f)) return MX_ERR_SHAPE;
+    if (!(clip_ratio >= 0.0f && clip_ratio <= 1.0f)) return MX_ERR_SHAPE;
     if (macro_block < 0 || (macro_block > 0 && (macro_block % 32 || cols % macro_block))) return MX_ERR_SHAPE;
     if (rows == 0) return MX_OK;
     if (!x || !codes || !scales || (macro_block > 0 && !macro_r)) return MX_ERR_NULL;
@@ -1226,7 +1410,7 @@ mx_status mx_quantize_2d(const void* w, mx_dtype wt, int64_t batch, int64_t rows
     const int64_t nsuper = batch * row_strips * col_strips;
     const int grid = grid_for(nsuper, 1);
     hipStream_t s = (hipStream_t)stream;
-    const DeoscArgs none{nullptr, 0, nullptr, 0.0f, nullptr};
+    const DeoscArgs none{nullptr, 0, nullptr, 0.0f, 0.0f, nullptr};
     (void)hipGetLastError();
     if (wt == MX_BF16)
         hipLaunchKernelGGL((q2d_kernel<true, false>), dim3(grid), dim3(256), 0, s, w, rows, cols, col_strips,
@@ -1260,7 +1444,8 @@ mx_status mx_quantize_2d_deosc(const void* w, mx_dtype wt, int64_t batch, int64_
     const int64_t nsuper = batch * row_strips * col_strips;
     const int grid = grid_for(nsuper, 1);
     hipStream_t s = (hipStream_t)stream;
-    const DeoscArgs dz{prev_codes, pld, prev_scales, 0.5f + (float)margin64 / 64.0f, flips};
+    const DeoscArgs dz{prev_codes, pld, prev_scales, 0.5f + (float)margin64 / 64.0f, 4.0f - (float)margin64 / 16.0f,
+                       flips};
     (void)hipGetLastError();
     if (wt == MX_BF16)
         hipLaunchKernelGGL((q2d_kernel<true, true>), dim3(grid), dim3(256), 0, s, w, rows, cols, col_strips,

@@ -52,6 +52,8 @@ def lib():
         L.mx_quantize_2d_deosc.argtypes = [P, c_int, i64, i64, i64, P, i64, P, c_int, P, i64, P, P, i64, P,
                                            P, P]
         L.mx_dequantize.argtypes = [P, i64, P, i64, i64, i64, c_int, P, c_int, P]
+        L.mx_quantize_1d_dual.argtypes = [P, c_int, i64, i64, P, i32, i64, c_int, u32, c_int, u32, u64, P, P,
+                                          c_int, u32, u64, P, i64, P, u64, P]
         L.mx_quantize_1d_ex.argtypes = [P, c_int, i64, i64, c_int, u32, c_int, u64, u32, u64,
                                         ctypes.c_float, i64, P, P, P, P]
         L.mx_dequantize_1d_ex.argtypes = [P, P, P, i64, i64, i64, P, P]
@@ -60,7 +62,7 @@ def lib():
         L.mx_grouped_gemm_q.argtypes = [P, i64, P, P, P, i64, P, c_int, P, i32, i64, i64, i64,
                                         ctypes.c_float, P, P, i64, P, P]
         for name in ("mx_rht", "mx_quantize_1d", "mx_quantize_2d", "mx_quantize_2d_deosc", "mx_dequantize",
-                     "mx_quantize_1d_ex", "mx_dequantize_1d_ex",
+                     "mx_quantize_1d_ex", "mx_dequantize_1d_ex", "mx_quantize_1d_dual",
                      "mx_grouped_gemm", "mx_grouped_gemm_q"):
             getattr(L, name).restype = c_int
         _lib = L
@@ -219,6 +221,36 @@ def quantize_1d(x, block_axis: int = 1, group_offsets=None, kp: int = 0, use_rht
         _ptr(row_index), int(use_rht), sign_mask, rnd, seed, stream_id, index_base, _ptr(codes), codes_ld,
         _ptr(scales), _stream()))
     return codes, scales
+
+
+def quantize_1d_dual(x, group_offsets, kp: int = 0, use_rht: bool = False, sign_mask: int = 0,
+                     col_rnd: int = RNE, col_stream_id: int = 0, row_rnd: int = RNE, row_stream_id: int = 0,
+                     seed: int = 0, col_index_base: int = 0, row_index_base: int = 0, col_codes=None,
+                     col_scales=None, row_codes=None, row_scales=None):
+    """Column-wise (grouped, transposed, optional RHT) and row-wise (no RHT)
+    1x32 quantization of x from one read (see mx_quantize_1d_dual).
+    Returns (col_codes, col_scales, row_codes, row_scales); row_codes may
+    have padded rows (a row-slice view of a wider buffer)."""
+    torch = _torch()
+    _dev(x, "x")
+    rows, cols = x.shape
+    _index_vector(group_offsets, "group_offsets", min_numel=2)
+    ng = group_offsets.numel() - 1
+    kp = kp or padded_capacity(rows, ng)
+    u8, dev = torch.uint8, x.device
+    col_codes = col_codes if col_codes is not None else torch.empty((cols, kp // 2), dtype=u8, device=dev)
+    col_scales = col_scales if col_scales is not None else torch.empty((cols, kp // 32), dtype=u8, device=dev)
+    row_codes = row_codes if row_codes is not None else torch.empty((rows, cols // 2), dtype=u8, device=dev)
+    row_scales = row_scales if row_scales is not None else torch.empty((rows, cols // 32), dtype=u8, device=dev)
+    _shaped(col_codes, (cols, kp // 2), u8, "col_codes")
+    _shaped(col_scales, (cols, kp // 32), u8, "col_scales")
+    ld = _shaped(row_codes, (rows, cols // 2), u8, "row_codes", pitched=True)
+    _shaped(row_scales, (rows, cols // 32), u8, "row_scales")
+    _check("mx_quantize_1d_dual", lib().mx_quantize_1d_dual(
+        _ptr(x), _dtype_code(x), rows, cols, _ptr(group_offsets), ng, kp, int(use_rht), sign_mask, col_rnd,
+        col_stream_id, col_index_base, _ptr(col_codes), _ptr(col_scales), row_rnd, row_stream_id,
+        row_index_base, _ptr(row_codes), ld, _ptr(row_scales), seed, _stream()))
+    return col_codes, col_scales, row_codes, row_scales
 
 
 def quantize_2d(w, layout=True, transposed=True):

@@ -340,6 +340,17 @@ int oracle_quantize_1d(const void* x, int dtype, int64_t rows, int64_t cols,
 /*     macro-block's largest magnitude to 6 up to one rounding; the     */
 /*     elements y' = fl32(y * r) are then quantized in 1x32 blocks as   */
 /*     usual, and decode to deq(code, scale) / r.                       */
+/*   - clip_ratio = 0 selects a search instead of a fixed ratio: a block */
+/*     takes the exponent X - 1 (clipping its largest values) instead of */
+/*     the rule's X when that strictly lowers its squared round-to-     */
+/*     nearest-even error.  Each candidate's error is summed in its own */
+/*     units, sum (v_j - q_j)^2 with v_j = y_j / 2^X and q_j the RTNE    */
+/*     value: every difference is exact in fp32 and its square in fp64; */
+/*     the sum is taken in fp64 as s_k = ((d_8k^2 + d_8k+1^2) + ...) over */
+/*     the eight elements of each quarter k, then ((s_0 + s_1) + s_2) +  */
+/*     s_3.  X - 1 wins iff S(X - 1) < 4 S(X) (the same error in the     */
+/*     input's units; the factor 4 is exact).  Not taken when the rule   */
+/*     gives byte 0 (no lower exponent).                                 */
 /* The RHT (when on) comes first, so amax_M is over transformed values. */
 /* Element index for SR as in oracle_quantize_1d (row-wise).            */
 /* macro_r [rows x cols/Bm] (written when Bm > 0).                      */
@@ -351,7 +362,7 @@ int oracle_quantize_1d_ex(const void* x, int dtype, int64_t rows, int64_t cols,
                           int64_t r_begin, int64_t r_end)
 {
     if (cols <= 0 || cols % 32 || rows < 0) return 2;
-    if (!(clip_ratio > 0.0f && clip_ratio <= 1.0f)) return 2;
+    if (!(clip_ratio >= 0.0f && clip_ratio <= 1.0f)) return 2;
     if (macro_block < 0 || (macro_block > 0 && (macro_block % 32 || cols % macro_block))) return 2;
     float y[32], t[32];
     uint32_t r16[32];
@@ -397,8 +408,31 @@ int oracle_quantize_1d_ex(const void* x, int dtype, int64_t rows, int64_t cols,
                 byte = 0xFF;
                 for (int j = 0; j < 32; ++j) code[j] = 0;
             } else {
-                volatile float ca = clip_ratio * (float)amax;   /* fl32(rho * amax) */
-                byte = oracle_scale_byte((double)ca);
+                if (clip_ratio > 0.0f) {
+                    volatile float ca = clip_ratio * (float)amax;   /* fl32(rho * amax) */
+                    byte = oracle_scale_byte((double)ca);
+                } else {
+                    byte = oracle_scale_byte(amax);
+                    if (byte > 0) {
+                        double S[2];
+                        for (int cand = 0; cand < 2; ++cand) {
+                            int Xc = (int)byte - cand - 127;
+                            double part[4];
+                            for (int k = 0; k < 4; ++k) {
+                                double acc = 0.0;
+                                for (int e = 0; e < 8; ++e) {
+                                    double v = ldexp((double)y[8 * k + e], -Xc);
+                                    double q = E2M1_MAG[oracle_rtne_mag(fabs(v))];
+                                    double d = fabs(v) - q;           /* sign-free: |v - sign(v) q| */
+                                    acc = acc + d * d;
+                                }
+                                part[k] = acc;
+                            }
+                            S[cand] = ((part[0] + part[1]) + part[2]) + part[3];
+                        }
+                        if (S[1] < 4.0 * S[0]) byte = (uint8_t)(byte - 1);
+                    }
+                }
                 int X = (int)byte - 127;
                 for (int j = 0; j < 32; ++j) {
                     double A = fabs(ldexp((double)y[j], -X));
@@ -490,7 +524,14 @@ int oracle_quantize_2d(const void* w, int dtype, int64_t batch, int64_t rows, in
 /* in MXFP4") but give no formula; the reading implemented here is a   */
 /* hysteresis band:                                                    */
 /*   - the tile's scale byte comes from its amax as in                 */
-/*     oracle_quantize_2d;                                              */
+/*     oracle_quantize_2d, except that a tile whose amax has dropped    */
+/*     just below the previous scale's range keeps the previous byte:   */
+/*     when the rule gives exactly one less than the previous byte p    */
+/*     (p != 0xFF) and amax >= (4 - margin64/16) 2^(p - 127), the tile  */
+/*     keeps p.  Its elements then fit without clipping (amax / 2^X_p   */
+/*     < 4), and an amax that hovers around a power of two no longer    */
+/*     moves every value of the tile; upward crossings are never held   */
+/*     back (they would saturate the tile's largest values);            */
 /*   - if it equals the previous step's byte for that tile (and neither */
 /*     is 0xFF), each element keeps its previous code c_p while its     */
 /*     scaled value v = w / 2^X lies strictly inside                    */
@@ -543,6 +584,18 @@ int oracle_quantize_2d_deosc(const void* w, int dtype, int64_t batch, int64_t ro
                 uint8_t byte = quantize_block(v, 1024, 0, NULL, code);
                 int64_t sidx = bt * (rows / 32) * (cols / 32) + tr * (cols / 32) + tc;
                 uint8_t pbyte = prev_scales[sidx];
+                if (pbyte != 0xFF && byte != 0xFF && byte + 1 == pbyte) {
+                    double amax = 0.0;
+                    for (int k = 0; k < 1024; ++k)
+                        if (fabs((double)v[k]) > amax) amax = fabs((double)v[k]);
+                    if (amax >= ldexp(4.0 - margin64 / 16.0, (int)pbyte - 127)) {
+                        byte = pbyte;                       /* the previous scale is kept */
+                        for (int k = 0; k < 1024; ++k) {
+                            double A = fabs(ldexp((double)v[k], -((int)byte - 127)));
+                            code[k] = (uint8_t)(((signbit(v[k]) ? 1 : 0) << 3) | oracle_rtne_mag(A));
+                        }
+                    }
+                }
                 const uint8_t* pc = prev_codes + bt * rows * (cols / 2);
                 int hyst = (byte == pbyte && byte != 0xFF);
                 int nflip = 0;

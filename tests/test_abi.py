@@ -16,7 +16,7 @@ def L():
 def test_every_declared_symbol_is_exported(L):
     names = mx.declared_functions()
     assert set(names) >= {"mx_rht", "mx_quantize_1d", "mx_quantize_2d", "mx_quantize_2d_deosc", "mx_quantize_1d_ex",
-                          "mx_dequantize_1d_ex", "mx_dequantize",
+                          "mx_dequantize_1d_ex", "mx_quantize_1d_dual", "mx_dequantize",
                           "mx_grouped_gemm", "mx_grouped_gemm_q", "mx_rht_sign_mask", "mx_status_str",
                           "mx_version"}
     for n in names:
@@ -115,7 +115,7 @@ def test_study_variant_validation(L):
             a[i] = v
         return q(*a)
 
-    assert call([(10, 0.0)]) == 2 and call([(10, 1.5)]) == 2 and call([(10, float("nan"))]) == 2
+    assert call([(10, -0.5)]) == 2 and call([(10, 1.5)]) == 2 and call([(10, float("nan"))]) == 2
     assert call([(11, 96)]) == 2 and call([(11, 48)]) == 2 and call([(11, -32)]) == 2
     assert call([(14, None)]) == 1 and call([(12, None)]) == 1
     assert call([(14, FAKE + 2)]) == 3 and call([(0, FAKE + 4)]) == 3
@@ -125,6 +125,27 @@ def test_study_variant_validation(L):
     assert d(FAKE, FAKE, None, 4, 256, 128, FAKE, None) == 1
     assert d(FAKE, FAKE, FAKE, 4, 256, 96, FAKE, None) == 2
     assert d(FAKE + 4, FAKE, None, 4, 256, 0, FAKE, None) == 3
+
+
+def test_quantize_1d_dual_validation(L):
+    q = L.mx_quantize_1d_dual
+    args = [FAKE, mx.MX_BF16, 64, 96, FAKE, 2, 128, 1, 0, 1, 0, 0, FAKE, FAKE, 1, 0, 0, FAKE, 0, FAKE, 0, None]
+
+    def call(i_vals):
+        a = list(args)
+        for i, v in i_vals:
+            a[i] = v
+        return q(*a)
+
+    assert call([(3, 48)]) == 2                     # cols not a multiple of 32
+    assert call([(6, 40)]) == 2 and call([(5, 0)]) == 2
+    assert call([(11, 16)]) == 2 and call([(16, 8)]) == 2     # index bases
+    assert call([(18, 16)]) == 2 and call([(18, 40)]) == 2    # row pitch
+    assert call([(9, 3)]) == 5 and call([(14, 3)]) == 5       # rounding modes
+    assert call([(1, 2)]) == 4
+    assert call([(4, None)]) == 1 and call([(17, None)]) == 1 and call([(19, None)]) == 1
+    assert call([(0, FAKE + 2)]) == 3 and call([(17, FAKE + 8)]) == 3
+    assert call([(2, 0), (0, None), (12, None), (13, None), (17, None), (19, None)]) == 0
 
 
 def test_dequantize_validation(L):

@@ -109,3 +109,26 @@ def test_deosc_full_size_expert_weights():
         want = oracle.quantize_2d_deosc(w1[e], pc[e], ps[e], 8)
         for g, wnt, n in zip(got, want, ("codes", "scales", "codes_t", "scales_t", "flips")):
             _assert_same(g[e], wnt, "%s e%d" % (n, e))
+
+
+def test_deosc_scale_band_hovering_tiles():
+    """Tiles whose largest weight alternates just above and below a power of
+    two (the previous scale kept on the way down) on many tiles at once,
+    against the oracle carrying its own state; with margin 8 the flips stop
+    after the first step."""
+    rng = np.random.default_rng(19)
+    base = (rng.standard_normal((2, 256, 512)) * 0.02).astype(np.float32)
+    tiles = base.reshape(2, 8, 32, 16, 32)
+    tiles[:, :, 3, :, 9] = 4.01 * 2.0 ** -5            # one element per tile sets the amax
+    c, s, _, _ = oracle.quantize_2d(base)
+    dc, ds = dev(c), dev(s)
+    flips = []
+    for k in range(6):
+        w = base.copy()
+        w.reshape(2, 8, 32, 16, 32)[:, :, 3, :, 9] = (3.99 if k % 2 == 0 else 4.01) * 2.0 ** -5
+        want = oracle.quantize_2d_deosc(w, c, s, 8)
+        got = mx.quantize_2d_deosc(dev(w), dc, ds, 8, codes=dc, scales=ds)
+        _check(got, want, "step %d " % k)
+        c, s = want[0], want[1]
+        flips.append(int(want[4].sum()))
+    assert flips[1:] == [0] * 5, flips

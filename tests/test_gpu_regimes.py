@@ -265,3 +265,61 @@ def test_wgrad_offsets_past_k_are_clamped():
     for g in range(2):
         sel = rows[:, 0] == g
         assert rel_fro(got[g][rows[sel, 1]].astype(np.float64), want[sel]) <= 1e-5, g
+
+
+# ---------------------------------------------------------------------------
+# One read, both 1x32 layouts (mx_quantize_1d_dual)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dt,cols", [("bf16", 96), ("bf16", 160), ("f32", 96), ("bf16", 70 * 32)])
+@pytest.mark.parametrize("use_rht,col_rnd,row_rnd", [(True, 1, 1), (True, 1, 0), (False, 0, 1)])
+def test_dual_matches_oracle(dt, cols, use_rht, col_rnd, row_rnd):
+    """Both outputs of the dual call against the oracle's two quantizations
+    (row-wise without the RHT, column-wise with it), ragged groups."""
+    import torch
+    counts = [45, 0, 32, 7, 300, 1]
+    off = synth.offsets_from_counts(counts)
+    rows = int(off[-1])
+    rng = np.random.default_rng(cols + 3 * use_rht + col_rnd + 7 * row_rnd)
+    xf = (rng.standard_normal((rows, cols)) * np.exp2(rng.integers(-6, 6, (1, cols)))).astype(np.float32)
+    x = xf if dt == "f32" else synth.f32_to_bf16_bits(xf)
+    xd = dev(x) if dt == "f32" else dev_bf16(x)
+    mask = mx.rht_sign_mask(5)
+    kp = mx.padded_capacity(rows, len(counts))
+    buf, rcodes = _padded_codes(torch, rows, cols // 2, (cols // 2 + 127) // 128 * 128 + 16)
+    cc, cs, rc, rs = mx.quantize_1d_dual(xd, dev(off), kp=kp, use_rht=use_rht, sign_mask=mask, col_rnd=col_rnd,
+                                         col_stream_id=3, row_rnd=row_rnd, row_stream_id=0, seed=5,
+                                         row_index_base=64, row_codes=rcodes)
+    oc, os_ = oracle.quantize_1d(x, block_axis=0, group_offsets=off, kp=kp, use_rht=use_rht, sign_mask=mask,
+                                 rnd=col_rnd, seed=5, stream=3)
+    total = oracle.padded_total(off)
+    _assert_same(host(cs)[:, :total // 32], os_[:, :total // 32], "column scales")
+    _assert_same(host(cc)[:, :total // 2], oc[:, :total // 2], "column codes")
+    orc, ors = oracle.quantize_1d(x, rnd=row_rnd, seed=5, stream=0, index_base=64)
+    _assert_same(host(rs), ors, "row scales")
+    _assert_same(host(rc.contiguous()), orc, "row codes")
+    assert bool((buf[:, cols // 2:] == 0xA5).all()), "row padding was written"
+
+
+@pytest.mark.parametrize("cols,row_rnd", [(2880, 0), (2880, 1), (5760, 1)])
+def test_dual_full_size_equals_two_calls(cols, row_rnd):
+    """The expert step's h (row RTNE), dY2 and dY1 (row SR) at 65,536 routed
+    rows, 32 Zipf groups, padded code rows: the dual call equals the two
+    separate calls everywhere (compared on the device)."""
+    import torch
+    counts = synth.zipf_counts()
+    off = dev(synth.offsets_from_counts(counts))
+    rows = 65536
+    g = torch.Generator(device="cuda").manual_seed(cols + row_rnd)
+    x = (torch.randn(rows, cols, device="cuda", generator=g) * 1e-3).to(torch.bfloat16)
+    kp = mx.padded_capacity(rows, 32)
+    mask = mx.rht_sign_mask(5)
+    ldp = (cols // 2 + 127) // 128 * 128
+    rbuf = torch.zeros(rows, ldp, dtype=torch.uint8, device="cuda")
+    cc, cs, rc, rs = mx.quantize_1d_dual(x, off, kp=kp, use_rht=True, sign_mask=mask, col_rnd=1, col_stream_id=5,
+                                         row_rnd=row_rnd, row_stream_id=1, seed=5, row_codes=rbuf[:, :cols // 2])
+    cc2, cs2 = mx.quantize_1d(x, block_axis=0, group_offsets=off, kp=kp, use_rht=True, sign_mask=mask, rnd=1,
+                              seed=5, stream_id=5)
+    rc2, rs2 = mx.quantize_1d(x, rnd=row_rnd, seed=5, stream_id=1)
+    total = int(sum((int(n) + 31) // 32 * 32 for n in counts))
+    assert torch.equal(cc[:, :total // 2], cc2[:, :total // 2]) and torch.equal(cs[:, :total // 32], cs2[:, :total // 32])
+    assert torch.equal(rc.contiguous(), rc2) and torch.equal(rs, rs2)

@@ -32,7 +32,8 @@ def _data(rows, cols, seed, dt):
 
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
 @pytest.mark.parametrize("use_rht,rnd", [(False, 0), (True, 1)])
-@pytest.mark.parametrize("clip,bm", [(1.0, 0), (0.75, 0), (0.5, 0), (1.0, 128), (0.875, 256), (1.0, 2880)])
+@pytest.mark.parametrize("clip,bm", [(1.0, 0), (0.75, 0), (0.5, 0), (0.0, 0), (1.0, 160), (0.875, 320),
+                                     (1.0, 2880), (0.0, 320)])
 def test_study_variants_parity(dt, use_rht, rnd, clip, bm):
     rows, cols = 37, 2880
     xh, xd = _data(rows, cols, 7, dt)
@@ -49,6 +50,26 @@ def test_study_variants_parity(dt, use_rht, rnd, clip, bm):
     _assert_same(host(y), oracle.dequantize_1d_ex(oc, os_, omr, macro_block=bm), "decoded")
 
 
+def test_search_on_clippable_blocks():
+    """Blocks built so that clipping a binade pays (a lone maximum just above
+    a power of two) mixed with Gaussian ones: the search takes X - 1 on
+    some, bit for bit as the oracle."""
+    rng = np.random.default_rng(4)
+    x = (rng.standard_normal((256, 512)) * np.exp2(rng.integers(-8, 8, (256, 1)))).astype(np.float32)
+    blocks = x.reshape(-1, 32)
+    for b in range(0, blocks.shape[0], 2):
+        k = float(np.exp2(rng.integers(-6, 6)))
+        blocks[b] = rng.uniform(0.2, 0.35, 32).astype(np.float32) * k * rng.choice([-1, 1], 32)
+        blocks[b, rng.integers(0, 32)] = (4.0 + float(rng.uniform(0, 0.5))) * k
+    for rnd in (0, 1):
+        c, s, _ = mx.quantize_1d_ex(dev(x), rnd=rnd, seed=6, clip_ratio=0.0)
+        oc, os_, _ = oracle.quantize_1d_ex(x, rnd=rnd, seed=6, clip_ratio=0.0)
+        _assert_same(host(s), os_, "scales")
+        _assert_same(host(c), oc, "codes")
+    plain = oracle.quantize_1d_ex(x)[1]
+    assert np.any(os_ != plain)
+
+
 def test_study_plain_case_equals_the_row_quantizer():
     xh, xd = _data(64, 512, 9, "bf16")
     c, s, _ = mx.quantize_1d_ex(xd, rnd=1, seed=2)
@@ -59,13 +80,13 @@ def test_study_plain_case_equals_the_row_quantizer():
 
 def test_study_full_size_activations():
     """16384 x 2880 bf16 activations with 0.1% outliers, RHT + SR, rho 0.75,
-    macro-blocks of 128: the whole matrix against the oracle."""
+    macro-blocks of 320: the whole matrix against the oracle."""
     xh, xd = _data(16384, 2880, 1, "bf16")
     mask = mx.rht_sign_mask(1)
     c, s, mr = mx.quantize_1d_ex(xd, use_rht=True, sign_mask=mask, rnd=1, seed=2, clip_ratio=0.75,
-                                 macro_block=128)
+                                 macro_block=320)
     oc, os_, omr = oracle.quantize_1d_ex(xh, use_rht=True, sign_mask=mask, rnd=1, seed=2, clip_ratio=0.75,
-                                         macro_block=128)
+                                         macro_block=320)
     _assert_same(host(mr), omr, "macro_r")
     _assert_same(host(s), os_, "scales")
     _assert_same(host(c), oc, "codes")

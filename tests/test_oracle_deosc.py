@@ -201,3 +201,62 @@ def test_random_walk_flips_fall_with_the_margin():
     assert totals[0] > 0
     assert totals[0] > totals[4] > totals[16], totals
     assert totals[16] * 5 < totals[0], totals
+
+
+# (previous byte, margin64, tile amax, expected byte): the scale band keeps
+# the previous byte p when the rule gives p - 1 and amax >= (4 - m/16) 2^(p-127)
+SCALE_HAND = [
+    (127, 8, 3.9, 127),     # rule 126; 3.9 >= 3.5: kept
+    (127, 8, 3.5, 127),     # on the threshold: kept (>=)
+    (127, 8, 3.49, 126),    # below it
+    (127, 0, 3.99, 126),    # margin 0: no scale band
+    (127, 31, 2.0625, 127),  # the widest band: 4 - 31/16
+    (127, 31, 2.06, 126),
+    (126, 8, 4.5, 127),     # upward: never held back
+    (128, 31, 3.9, 126),    # two binades down: not held
+    (0xFF, 31, 3.9, 126),   # no previous scale
+]
+
+
+@pytest.mark.parametrize("pbyte,margin,amax,want", SCALE_HAND)
+def test_hand_worked_scale_band(pbyte, margin, amax, want):
+    w = _tile_with(0.3, amax=amax)
+    pc, ps = _prev_with(0x1, scale_byte=pbyte)
+    codes, scales, _, _, _ = oracle.quantize_2d_deosc(w, pc, ps, margin)
+    assert int(scales[0, 0, 0]) == want
+    # the tile's amax element, at the kept or the new scale: RTNE there
+    big = int(codes[0, 0, 0]) & 0xF
+    X = want - 127
+    assert GRID[big & 7] == GRID[oracle.rtne_mag(amax / 2.0 ** X)]
+
+
+def test_scale_band_improves_the_largest_value():
+    """amax 3.9 at a previous scale 2^0: the plain rule (2^-1) saturates it
+    to 6 * 2^-1 = 3 (error 0.9); the kept scale represents it as 4 (0.1)."""
+    w = _tile_with(0.3, amax=3.9)
+    pc, ps = _prev_with(0x1, scale_byte=127)
+    kept = oracle.quantize_2d_deosc(w, pc, ps, 8)
+    plain = oracle.quantize_2d(w)
+    assert oracle.dequantize(kept[0][0], kept[1][0], block_rows=32)[0, 0] == 4.0
+    assert oracle.dequantize(plain[0][0], plain[1][0], block_rows=32)[0, 0] == 3.0
+
+
+def test_amax_hovering_at_a_power_of_two_stops_flipping():
+    """A tile whose largest weight alternates 4.01 / 3.99 (times 2^-5) while
+    the rest stay put: without the band every element's value changes at
+    each crossing; with it, after the first step nothing changes."""
+    rng = np.random.default_rng(13)
+    base = (rng.standard_normal((1, 32, 32)) * 0.02).astype(np.float32)
+    base[0, 5, 7] = 4.01 * 2.0 ** -5
+    c, s, _, _ = oracle.quantize_2d(base)
+    totals = {}
+    for m in (0, 8):
+        cc, ss, tot = c, s, 0
+        for k in range(8):
+            w = base.copy()
+            w[0, 5, 7] = (3.99 if k % 2 == 0 else 4.01) * 2.0 ** -5
+            cc, ss, _, _, fl = oracle.quantize_2d_deosc(w, cc, ss, m)
+            tot += int(fl.sum())
+        totals[m] = tot
+    assert totals[0] > 8 * 300, totals       # hundreds of values move at every crossing
+    assert totals[8] == 0, totals

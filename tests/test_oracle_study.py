@@ -94,3 +94,45 @@ def test_zero_and_nonfinite_macro_blocks_take_multiplier_one():
     c, s, mr = oracle.quantize_1d_ex(x, macro_block=128)
     assert np.array_equal(mr, np.ones((1, 2), np.float32))
     assert int(s[0, 4]) == 0xFF and int(s[0, 0]) == 0
+
+
+def test_search_clips_when_it_lowers_the_block_error():
+    """Block [4, 0.3 x 31]: at X = 0 the 0.3s round to 0.5 (error 0.2 each,
+    squared sum ~1.24); at X = -1 they scale to 0.6 -> 0.5 (0.05 each in the
+    input's units) while 4 scales to 8 and saturates at 6 (error 1):
+    ~0.31 + 1 < 1.24, so the search takes X = -1 (byte 126)."""
+    x = np.full((1, 32), 0.3, dtype=np.float32)
+    x[0, 0] = 4.0
+    c, s, _ = oracle.quantize_1d_ex(x, clip_ratio=0.0)
+    assert int(s[0, 0]) == 126
+    assert int(c[0, 0]) & 0xF == 0x7 and int(c[0, 0]) >> 4 == 0x1
+    y = oracle.dequantize_1d_ex(c, s)
+    assert y[0, 0] == 3.0 and np.all(y[0, 1:] == 0.25)
+    # an outlier 50 among ones: clipping it would cost far more than it saves
+    x = np.ones((1, 32), dtype=np.float32)
+    x[0, 0] = 50.0
+    _, s, _ = oracle.quantize_1d_ex(x, clip_ratio=0.0)
+    assert int(s[0, 0]) == 130
+
+
+def test_search_never_raises_a_block_error():
+    """Gaussian blocks (where clipping a binade rarely pays: the block's max
+    saturates) mixed with blocks built to gain from it (a lone maximum just
+    above a power of two, the rest where the finer grid helps)."""
+    rng = np.random.default_rng(21)
+    x = (rng.standard_normal((128, 512)) * np.exp2(rng.integers(-8, 8, (128, 1)))).astype(np.float32)
+    x.reshape(-1)[rng.choice(x.size, 64, replace=False)] *= 30.0
+    blocks = x.reshape(-1, 32)
+    for b in range(0, blocks.shape[0], 3):
+        k = float(np.exp2(rng.integers(-6, 6)))
+        blocks[b] = rng.uniform(0.2, 0.35, 32).astype(np.float32) * k * rng.choice([-1, 1], 32)
+        blocks[b, rng.integers(0, 32)] = (4.0 + float(rng.uniform(0, 0.5))) * k
+    c0, s0, _ = oracle.quantize_1d_ex(x)
+    c1, s1, _ = oracle.quantize_1d_ex(x, clip_ratio=0.0)
+    e0 = ((oracle.dequantize_1d_ex(c0, s0).astype(np.float64) - x) ** 2).reshape(-1, 32).sum(axis=1)
+    e1 = ((oracle.dequantize_1d_ex(c1, s1).astype(np.float64) - x) ** 2).reshape(-1, 32).sum(axis=1)
+    low = s1.reshape(-1).astype(int) == s0.reshape(-1).astype(int) - 1
+    same = s1.reshape(-1) == s0.reshape(-1)
+    assert np.all(low | same) and low.any() and same.any()
+    assert np.all(e1[low] < e0[low])
+    assert np.array_equal(c1.reshape(-1, 16)[same], c0.reshape(-1, 16)[same])
