@@ -45,10 +45,13 @@
 // issues a fixed number of stores and the next tile's first barrier leaves
 // them in flight.
 //
-// LDS code tiles use an XOR swizzle of the eight 16-byte chunks of a row;
-// each row's 8 scale dwords are stored in the order (s0, s2, s4, s6, s1, s3,
-// s5, s7), so one 16-byte read gives a lane the scales of its four
-// K-quarters.  A chunk at or past the end of the K range is loaded from a
+// LDS code tiles use an XOR swizzle of the eight 16-byte chunks of a row.
+// K-quarter q of a stage takes chunk 4 h + q in lane half h, so a lane's four
+// scale bytes are adjacent in the row: moved one byte per lane, each scale
+// lands in a dword of its own (8 per row, one 16-byte read per lane); moved
+// in pairs, each pair does (4 per row, one 8-byte read).  Either way the
+// rows of an MFMA block sit consecutively, so a block's scale read is one
+// contiguous span of LDS, free of bank conflicts.  A chunk at or past the end of the K range is loaded from a
 // clamped (valid) address and its scale is forced to 2^-127 on both
 // operands, so its products (at most 36 * 2^-254) vanish in the fp32
 // accumulation.
@@ -297,11 +300,14 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
             if (decode(L, t)) return true;
         }
     };
-    // the A rows of this thread's DMA moves: r = t/8 + (NT/8) j
-    auto load_rows = [&](const Tile& t, int32_t (&arow)[NJ]) {
+    // The A rows of this thread's DMA moves: entry j < NJ is code move j,
+    // row t/8 + (NT/8) j; with pair moves (SA2) entry NJ + j is scale move
+    // j, row 16 (j NW + w) + l/4 (w: wave, l: lane).
+    constexpr int NR = SA2 ? NJ + 2 : NJ;
+    auto load_rows = [&](const Tile& t, int32_t (&arow)[NR]) {
 #pragma unroll
-        for (int jj = 0; jj < NJ; ++jj) {
-            int32_t m = t.m0 + (tid >> 3) + (NT / 8) * jj;
+        for (int jj = 0; jj < NR; ++jj) {
+            int32_t m = t.m0 + (jj < NJ ? (tid >> 3) + (NT / 8) * jj : 16 * ((jj - NJ) * NW + wave) + ((tid & 63) >> 2));
             if (m >= t.m1) m = t.m1 - 1;          // rows past the tile end are never stored
             arow[jj] = GATHER ? p.a_row_index[m] : m;
         }
@@ -320,13 +326,13 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
     // stage kt of tile t -> LDS buffer `buf`; chunks past the end are clamped
     // in range.  A stage's DMAs are numbered: A code rows (NJ), B code rows
     // (NJ), A scales (NJ / 2 pair moves or NJ byte moves), B scales (one 2D
-    // group move or NJ byte moves).  issue_slot(m) issues those with number
+    // group move, NJ / 2 pair moves or NJ byte moves).  issue_slot(m) issues those with number
     // p % 8 == m, so the main loop can spread a stage's DMAs over the eight
     // MFMA blocks of a K-quarter instead of issuing them in one burst.
     constexpr int NA_S = SA2 ? NJ / 2 : NJ, NB_S = B2D ? 1 : (SA2 ? NJ / 2 : NJ);
     constexpr int NPARTS = 2 * NJ + NA_S + NB_S;
     static_assert(NPARTS == dma_per_stage<B2D, SA2>(), "DMA count");
-    auto issue_slot = [&](const Tile& t, const int32_t (&arow)[NJ], int kt, int buf, int slot) {
+    auto issue_slot = [&](const Tile& t, const int32_t (&arow)[NR], int kt, int buf, int slot) {
         const uint32_t sb = lds_base + (uint32_t)buf * STAGE_BYTES;
         const uint8_t* bcodes = p.b_codes;
         const uint8_t* bscales = p.b_scales;
@@ -351,14 +357,14 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
             } else if (part < 2 * NJ + NA_S) {
                 const int j = part - 2 * NJ;
                 if (SA2) {
-                    // move j: lanes with pc < 4 take scale pair pc of row slot
-                    // 2 j, lanes with pc >= 4 pair pc - 4 of slot 2 j + 1 (the
-                    // rows of this thread's code moves); pairs past the end
-                    // repeat the pair that holds the last chunk
-                    const int half = pc >> 2;
+                    // move j of wave w fills tile rows 16 (j NW + w) .. + 15,
+                    // four lanes a row: lane l takes pair l % 4 of its row,
+                    // so tile row r lands at 16 r (pair p at + 4 p) and an
+                    // MFMA block's scale read is one contiguous 512-byte span;
+                    // pairs past the end repeat the pair that holds the last
+                    // chunk
                     const uint32_t kp = (uint32_t)(t.kc0 + min(kt * 8 + 2 * (pc & 3), t.kc_last & ~1));
-                    dma2(p.a_scales, (uint32_t)(half ? arow[2 * j + 1] : arow[2 * j]) * (uint32_t)KS + kp,
-                         sb + OFF_AS + (j * NW + wave) * 256);
+                    dma2(p.a_scales, (uint32_t)arow[NJ + j] * (uint32_t)KS + kp, sb + OFF_AS + (j * NW + wave) * 256);
                 } else {
                     const uint32_t ks = (uint32_t)(t.kc0 + min(kt * 8 + pc, t.kc_last));
                     dma1(p.a_scales, (uint32_t)arow[j] * (uint32_t)KS + ks, sb + OFF_AS + j * NT * 4 + wave * 256);
@@ -381,10 +387,10 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
                         dma1(bscales, (uint32_t)grp * (uint32_t)KS + ks, sb + OFF_BS + wave * 256);
                     }
                 } else if (SA2) {
-                    // as the A scales, for this thread's B rows
-                    const int half = pc >> 2;
+                    // as the A scales: tile row 16 (j NW + w) + l / 4
+                    const int32_t n = t.n0 + 16 * (j * NW + wave) + ((tid & 63) >> 2);
                     const uint32_t kp = (uint32_t)(t.kc0 + min(kt * 8 + 2 * (pc & 3), t.kc_last & ~1));
-                    dma2(bscales, (half ? nrow(2 * j + 1) : nrow(2 * j)) * (uint32_t)KS + kp,
+                    dma2(bscales, (uint32_t)(n < N32 ? n : N32 - 1) * (uint32_t)KS + kp,
                          sb + OFF_BS + (j * NW + wave) * 256);
                 } else {
                     const uint32_t ks = (uint32_t)(t.kc0 + min(kt * 8 + pc, t.kc_last));
@@ -393,7 +399,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
             }
         }
     };
-    auto issue = [&](const Tile& t, const int32_t (&arow)[NJ], int kt, int buf) {
+    auto issue = [&](const Tile& t, const int32_t (&arow)[NR], int kt, int buf) {
 #pragma unroll
         for (int slot = 0; slot < 8; ++slot) issue_slot(t, arow, kt, buf, slot);
     };
@@ -432,6 +438,9 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
     // Scale dword p of a row holds chunk p (one byte moves) or chunks 2 p
     // and 2 p + 1 (pair moves, SA2): lane half h takes dwords 4 h .. 4 h + 3
     // or 2 h, 2 h + 1.  B scales (1D or 2D) move in pairs along with A's.
+    // A row's dwords are adjacent and the rows of an MFMA block are
+    // consecutive, so each read below covers one contiguous span (no bank
+    // conflicts), except 2D B scales, which every lane reads alike.
     constexpr bool SB2 = SA2;
     using ARaw = typename std::conditional<SA2, uint2, uint4>::type;
     using BRaw = typename std::conditional<SB2, uint2, uint4>::type;
@@ -440,19 +449,12 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
         const uint8_t* sb = lds + buf * STAGE_BYTES;
 #pragma unroll
         for (int i = 0; i < FN; ++i)
-            // SB2, 1D: row r = wn WN + 32 i + lr was moved by wave (r % 64) / 8,
-            // lane 8 (r % 8) + 4 ((r / 64) % 2) of move r / 128 (as for A)
             s.b[i] = B2D ? *(const BRaw*)(sb + OFF_BS + (wn * FN + i) * 256 + lh * (int)sizeof(BRaw))
-                   : SB2 ? *(const BRaw*)(sb + OFF_BS + ((wn >> 1) * NW + 4 * i + (lr >> 3)) * 256 + (lr & 7) * 32 +
-                                          (wn & 1) * 16 + lh * 8)
+                   : SB2 ? *(const BRaw*)(sb + OFF_BS + (wn * WN + i * 32 + lr) * 16 + lh * 8)
                          : *(const BRaw*)(sb + OFF_BS + (wn * WN + i * 32 + lr) * 32 + lh * 16);
 #pragma unroll
         for (int i = 0; i < FM; ++i)
-            // SA2: row r = wm WM + 32 i + lr was moved by wave (r % 64) / 8,
-            // lane 8 (r % 8) + 4 ((r / 64) % 2) of move (r / 64) / 2 = wm:
-            // its four pair dwords are consecutive
-            s.a[i] = SA2 ? *(const ARaw*)(sb + OFF_AS + (wm * NW + (i & 1) * 4 + (lr >> 3)) * 256 + (lr & 7) * 32 +
-                                          (i >> 1) * 16 + lh * 8)
+            s.a[i] = SA2 ? *(const ARaw*)(sb + OFF_AS + (wm * WM + i * 32 + lr) * 16 + lh * 8)
                          : *(const ARaw*)(sb + OFF_AS + (wm * WM + i * 32 + lr) * 32 + lh * 16);
     };
     // byte q of the packed register: K-quarter q (a pair move leaves the
@@ -684,7 +686,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
     // tile's first fragments.  The epilogue then overlaps those loads, and the
     // next tile starts its MFMAs without a prologue.
     Tile cur, nxt;
-    int32_t arow[NJ], narow[NJ];
+    int32_t arow[NR], narow[NR];
     int32_t round = 0;
     if (!find_tile(round, cur)) return;
     load_rows(cur, arow);
@@ -757,9 +759,9 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
                 // gathered row indices are ordinary loads, and the
                 // compiler's wait for them lands before their first use.
                 const uint64_t sel = __builtin_amdgcn_readfirstlane((int)to_next) ? ~0ull : 0ull;
-                int32_t r2[NJ];
+                int32_t r2[NR];
 #pragma unroll
-                for (int jj = 0; jj < NJ; ++jj)
+                for (int jj = 0; jj < NR; ++jj)
                     asm volatile("v_cndmask_b32_e64 %0, %1, %2, %3"
                                  : "=v"(r2[jj]) : "v"(arow[jj]), "v"(narow[jj]), "s"(sel));
                 // the DMAs of stage kt + 2 go out between the last K-quarter's
@@ -797,9 +799,12 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
         par = chain ? par ^ (cur.nkt & 1) : 0;
         cur = nxt;
 #pragma unroll
-        for (int jj = 0; jj < NJ; ++jj) arow[jj] = narow[jj];
+        for (int jj = 0; jj < NR; ++jj) arow[jj] = narow[jj];
         round = nround;
     }
+    // the clamped stages issued by the last tile may still be landing in
+    // LDS: let them finish before the workgroup's LDS is released
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 inline bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
