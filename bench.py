@@ -54,9 +54,9 @@ ROLE_KERNEL = {
     "q1d_row_rtne": "q1d_row_kernel_w<true,false,false>",
     "q1d_col": "q1d_col_kernel<true,true,true,0>",
     "q1d_row_sr": "q1d_row_kernel_w<true,false,true>",
-    "gemm_fwd_gather": "gemm_kernel<true,true,false,true,true,false>",
-    "gemm_bf16": "gemm_kernel<true,true,false,false,true,false>",
-    "gemm_wgrad": "gemm_kernel<false,false,true,false,true,false>",
+    "gemm_fwd_gather": "gemm_kernel<true,true,false,true,true,false,false>",
+    "gemm_bf16": "gemm_kernel<true,true,false,false,true,false,true>",
+    "gemm_wgrad": "gemm_kernel<false,false,true,false,false,false,true>",
 }
 QUANT_ROLES = ("q2d", "q1d_row_rtne", "q1d_row_sr", "q1d_col")
 GEMM_ROLES = ("gemm_fwd_gather", "gemm_bf16", "gemm_wgrad")
@@ -115,6 +115,15 @@ class Step:
             Y1=z(ROWS, F2, dt=bf), Y2=z(ROWS, D, dt=bf), dh=z(ROWS, D, dt=bf), dX=z(ROWS, D, dt=bf),
             dW2=z(E, D, D, dt=f32), dW1=z(E, D, F2, dt=f32),
         )
+        # The step's GEMM operands carry their scales in the staged order
+        # (include/mx.h, MX_SCALES_STAGED): A of the three data-path GEMMs
+        # (row-wise, [ceil(K/256), rows, 8]) and both weight-gradient operands
+        # (column-wise, [kp/256 + E, cols, 8]).  The row-major buffers above
+        # serve the studies.
+        st_r = lambda k: z((k + 255) // 256, ROWS, 8)          # noqa: E731
+        st_c = lambda c: z(self.kp // 256 + E, c, 8)           # noqa: E731
+        self.b.update(hs_st=st_r(D), g2s_st=st_r(D), g1s_st=st_r(F2), hTs_st=st_c(D), g2Ts_st=st_c(D),
+                      xTs_st=st_c(D), g1Ts_st=st_c(F2))
         self.events = None
 
     def _t(self, name, fn):
@@ -144,28 +153,31 @@ class Step:
         self._t("q1d_row_rtne", lambda: mx.quantize_1d(i["X"], codes=b["xc"], scales=b["xs"]))
         self._t("gemm_fwd_gather", lambda: mx.grouped_gemm(b["xc"], b["xs"], b["w1tc"], b["w1ts"], off, ROWS, F2,
                                                            D, a_row_index=idx, b_scale_2d=True, out=b["Y1"]))
-        self._t("q1d_row_rtne", lambda: mx.quantize_1d(i["h"], codes=b["hc"], scales=b["hs"]))
-        self._t("q1d_col", lambda: mx.quantize_1d(i["h"], stream_id=4, codes=b["hTc"], scales=b["hTs"], **col))
-        self._t("gemm_bf16", lambda: mx.grouped_gemm(b["hc"], b["hs"], b["w2tc"], b["w2ts"], off, ROWS, D, D,
-                                                     b_scale_2d=True, out=b["Y2"]))
+        self._t("q1d_row_rtne", lambda: mx.quantize_1d(i["h"], codes=b["hc"], scales=b["hs_st"], staged=True))
+        self._t("q1d_col", lambda: mx.quantize_1d(i["h"], stream_id=4, codes=b["hTc"], scales=b["hTs_st"],
+                                                  staged=True, **col))
+        self._t("gemm_bf16", lambda: mx.grouped_gemm(b["hc"], b["hs_st"], b["w2tc"], b["w2ts"], off, ROWS, D, D,
+                                                     b_scale_2d=True, staged=True, out=b["Y2"]))
         self._t("q1d_row_sr", lambda: mx.quantize_1d(i["dY2"], rnd=mx.SR, seed=5, stream_id=1,
-                                                     codes=b["g2c"], scales=b["g2s"]))
-        self._t("q1d_col", lambda: mx.quantize_1d(i["dY2"], stream_id=5, codes=b["g2Tc"], scales=b["g2Ts"], **col))
-        self._t("gemm_bf16", lambda: mx.grouped_gemm(b["g2c"], b["g2s"], b["w2c"], b["w2s"], off, ROWS, D, D,
-                                                     b_scale_2d=True, out=b["dh"]))
-        self._t("gemm_wgrad", lambda: mx.grouped_gemm(b["hTc"], b["hTs"], b["g2Tc"], b["g2Ts"], poff, D, D, self.kp,
-                                                      group_dim_k=True, out=b["dW2"]))
+                                                     codes=b["g2c"], scales=b["g2s_st"], staged=True))
+        self._t("q1d_col", lambda: mx.quantize_1d(i["dY2"], stream_id=5, codes=b["g2Tc"], scales=b["g2Ts_st"],
+                                                  staged=True, **col))
+        self._t("gemm_bf16", lambda: mx.grouped_gemm(b["g2c"], b["g2s_st"], b["w2c"], b["w2s"], off, ROWS, D, D,
+                                                     b_scale_2d=True, staged=True, out=b["dh"]))
+        self._t("gemm_wgrad", lambda: mx.grouped_gemm(b["hTc"], b["hTs_st"], b["g2Tc"], b["g2Ts_st"], poff, D, D,
+                                                      self.kp, group_dim_k=True, staged=True, out=b["dW2"]))
         self._t("q1d_row_sr", lambda: mx.quantize_1d(i["dY1"], rnd=mx.SR, seed=5, stream_id=0,
-                                                     codes=b["g1c"], scales=b["g1s"]))
-        self._t("q1d_col", lambda: mx.quantize_1d(i["dY1"], stream_id=3, codes=b["g1Tc"], scales=b["g1Ts"], **col))
-        self._t("gemm_bf16", lambda: mx.grouped_gemm(b["g1c"], b["g1s"], b["w1c"], b["w1s"], off, ROWS, D, F2,
-                                                     b_scale_2d=True, out=b["dX"]))
+                                                     codes=b["g1c"], scales=b["g1s_st"], staged=True))
+        self._t("q1d_col", lambda: mx.quantize_1d(i["dY1"], stream_id=3, codes=b["g1Tc"], scales=b["g1Ts_st"],
+                                                  staged=True, **col))
+        self._t("gemm_bf16", lambda: mx.grouped_gemm(b["g1c"], b["g1s_st"], b["w1c"], b["w1s"], off, ROWS, D, F2,
+                                                     b_scale_2d=True, staged=True, out=b["dX"]))
         # X^T: the routed rows are gathered from the 16384-token X inside the
         # quantizer (no permuted copy)
-        self._t("q1d_col", lambda: mx.quantize_1d(i["X"], stream_id=2, codes=b["xTc"], scales=b["xTs"],
-                                                  row_index=idx, **col))
-        self._t("gemm_wgrad", lambda: mx.grouped_gemm(b["xTc"], b["xTs"], b["g1Tc"], b["g1Ts"], poff, D, F2, self.kp,
-                                                      group_dim_k=True, out=b["dW1"]))
+        self._t("q1d_col", lambda: mx.quantize_1d(i["X"], stream_id=2, codes=b["xTc"], scales=b["xTs_st"],
+                                                  row_index=idx, staged=True, **col))
+        self._t("gemm_wgrad", lambda: mx.grouped_gemm(b["xTc"], b["xTs_st"], b["g1Tc"], b["g1Ts_st"], poff, D, F2,
+                                                      self.kp, group_dim_k=True, staged=True, out=b["dW1"]))
 
 
 def work_model():
@@ -355,13 +367,13 @@ def fused_epilogue(torch, step, reps=5):
     quantizer against the fused call, with and without the bf16 output, on
     the step's own buffers."""
     mx, b, i = step.mx, step.b, step.inp
-    args = (b["hc"], b["hs"], b["w2tc"], b["w2ts"], i["off"], ROWS, D, D)
+    args = (b["hc"], b["hs_st"], b["w2tc"], b["w2ts"], i["off"], ROWS, D, D)
     runs = {
-        "gemm_then_quantize_ms": lambda: (mx.grouped_gemm(*args, b_scale_2d=True, out=b["Y2"]),
+        "gemm_then_quantize_ms": lambda: (mx.grouped_gemm(*args, b_scale_2d=True, staged=True, out=b["Y2"]),
                                           mx.quantize_1d(b["Y2"], codes=b["g2c"], scales=b["g2s"])),
-        "fused_ms": lambda: mx.grouped_gemm_q(*args, b_scale_2d=True, out=b["Y2"], codes=b["g2c"],
+        "fused_ms": lambda: mx.grouped_gemm_q(*args, b_scale_2d=True, staged=True, out=b["Y2"], codes=b["g2c"],
                                               scales=b["g2s"]),
-        "fused_mxfp4_only_ms": lambda: mx.grouped_gemm_q(*args, b_scale_2d=True, with_bf16=False,
+        "fused_mxfp4_only_ms": lambda: mx.grouped_gemm_q(*args, b_scale_2d=True, staged=True, with_bf16=False,
                                                          codes=b["g2c"], scales=b["g2s"]),
     }
     res = {"shape": "%dx%dx%d" % (ROWS, D, D)}

@@ -68,6 +68,25 @@ typedef enum {
 typedef enum { MX_F32 = 0, MX_BF16 = 1 } mx_dtype;
 typedef enum { MX_RNE = 0, MX_SR = 1 } mx_round;
 
+/* Scale storage orders (flags).
+ * Row-major, the default: the scale of block c of row r of an R x C grid of
+ *   32-element blocks is byte r*C + c.
+ * MX_SCALES_STAGED: the order the grouped GEMM's K loop consumes.  Blocks
+ *   8s .. 8s+7 of a row form stage s (256 elements of K); stages are stored
+ *   one after another, each holding 8 bytes for every row: the scale of
+ *   block 8s + j of row r is byte (s*R + r)*8 + j.  Slots of blocks past the
+ *   row's last block are padding, left unwritten by the quantizers and
+ *   ignored by the GEMM.  In the column-wise grouped layout each group's
+ *   padded blocks start a stage of their own: block j of group g is slot
+ *   j % 8 of stage S_g + j / 8, with S_g the sum over the groups before g of
+ *   ceil(B / 8) and B a group's padded block count (ceil32(n) / 32).
+ *   It holds the same bytes as the row-major order.  It exists so that one K
+ *   stage of a 256-row GEMM tile is 2 KiB of contiguous memory, read by a
+ *   few whole-line requests, instead of 256 separate 8-byte pieces, one
+ *   memory request each.
+ * MX_SCALES_B_2D: the GEMM's B operand has 2D (32x32) scales. */
+enum { MX_SCALES_B_2D = 1, MX_SCALES_STAGED = 2 };
+
 /* HIP stream handle (hipStream_t) passed as an opaque pointer. */
 typedef void* mx_stream;
 
@@ -119,6 +138,10 @@ mx_status mx_rht(const void* x, mx_dtype xt, float* y, int64_t rows, int64_t col
  *   permutation of tokens into expert order with the quantization: no
  *   permuted copy of x is written.  NULL: position p is x[p].
  *   One row of x must span at most 4 GiB - 1 bytes (else MX_ERR_SHAPE).
+ * block_axis | MX_SCALES_STAGED: the scales in the staged order.  Row-wise:
+ *   R = rows, scales holds ceil(cols/256) * rows * 8 bytes.  Column-wise:
+ *   per-group stages, R = cols, scales holds (kp/256 + num_groups) * cols * 8
+ *   bytes.  Padding slots are not written.
  * use_rht != 0 applies the RHT (sign_mask) to each block before quantizing.
  * rnd: MX_RNE or MX_SR (seed, stream_id, index_base as above; index_base %
  *   32 == 0).
@@ -294,11 +317,20 @@ mx_status mx_dequantize(const uint8_t* codes, int64_t codes_ld, const uint8_t* s
  * group_dim_k = 0 (forward / data gradient): groups split the M rows of C by
  *   group_offsets (DEVICE int32[num_groups+1], [0] = 0, [num_groups] = M).
  *   Row m of group g reads A row a_row_index[m] (DEVICE int32[M]; NULL = m)
- *   and multiplies B_g = b_codes + g*N*b_ld ([N x K]); b_scale_2d selects 2D
- *   scales [N/32 x K/32] per group (else 1D [N x K/32]).  C [M x N].
+ *   and multiplies B_g = b_codes + g*N*b_ld ([N x K]); MX_SCALES_B_2D in
+ *   scale_flags selects 2D scales [N/32 x K/32] per group (else 1D
+ *   [N x K/32]).  C [M x N].
  * group_dim_k = 1 (weight gradient): groups split K by group_offsets (DEVICE,
  *   multiples of 32, [num_groups] <= K); A [M x K], B [N x K], 1D scales;
  *   C [num_groups x M x N]; a group with an empty K range writes zeros.
+ * scale_flags: MX_SCALES_B_2D and/or MX_SCALES_STAGED.  Staged: with groups
+ *   along K, A's and B's scales are in the staged order with per-group
+ *   stages (R = M, resp. N; group g's blocks are those of its K range, as
+ *   mx_quantize_1d(block_axis = 0 | MX_SCALES_STAGED) writes them when
+ *   group_offsets are its padded group starts); needs num_groups < 64.  With
+ *   groups along M, A's scales are staged (R = M, one stage grid over K);
+ *   needs MX_SCALES_B_2D and no row index.  Staged scale pointers 4-byte
+ *   aligned, and (K/256 + num_groups + 1) * 8 * R below 4 GiB.
  * K % 32 == 0, N % 32 == 0, M >= 0; ct = MX_BF16 (round to nearest even) or
  * MX_F32.  Code and C pointers 16-byte aligned.  The kernel addresses each
  * operand with 32-bit byte offsets: N*b_ld (one B group) and, without a row
@@ -306,10 +338,11 @@ mx_status mx_dequantize(const uint8_t* codes, int64_t codes_ld, const uint8_t* s
  * index the indexed rows must lie within the first 4 GiB of a_codes.
  * Errors: MX_ERR_DTYPE (ct), MX_ERR_SHAPE (sizes, row pitches, num_groups
  * < 1, group_dim_k), MX_ERR_UNSUPPORTED (group_dim_k = 1 with 2D B scales or a row
- * index), MX_ERR_NULL, MX_ERR_ALIGN, MX_ERR_LAUNCH.  M == 0 launches nothing. */
+ * index; unknown scale_flags bits; staged scales outside the cases above),
+ * MX_ERR_NULL, MX_ERR_ALIGN, MX_ERR_LAUNCH.  M == 0 launches nothing. */
 mx_status mx_grouped_gemm(const uint8_t* a_codes, int64_t a_ld, const uint8_t* a_scales,
                           const int32_t* a_row_index,
-                          const uint8_t* b_codes, int64_t b_ld, const uint8_t* b_scales, int b_scale_2d,
+                          const uint8_t* b_codes, int64_t b_ld, const uint8_t* b_scales, int scale_flags,
                           const int32_t* group_offsets, int32_t num_groups, int group_dim_k,
                           int64_t M, int64_t N, int64_t K, float alpha,
                           void* c, mx_dtype ct, mx_stream stream);
@@ -333,7 +366,7 @@ mx_status mx_grouped_gemm(const uint8_t* a_codes, int64_t a_ld, const uint8_t* a
  * a multiple of 16). */
 mx_status mx_grouped_gemm_q(const uint8_t* a_codes, int64_t a_ld, const uint8_t* a_scales,
                             const int32_t* a_row_index,
-                            const uint8_t* b_codes, int64_t b_ld, const uint8_t* b_scales, int b_scale_2d,
+                            const uint8_t* b_codes, int64_t b_ld, const uint8_t* b_scales, int scale_flags,
                             const int32_t* group_offsets, int32_t num_groups,
                             int64_t M, int64_t N, int64_t K, float alpha,
                             void* c, uint8_t* c_codes, int64_t c_codes_ld, uint8_t* c_scales,

@@ -84,6 +84,7 @@ struct GemmArgs {
     int64_t lda, ldb;    // bytes from one code row to the next (A, B)
     int32_t G;
     int32_t b_scale_2d;
+    int32_t staged;      // scales in the staged layout (A; with groups along K also B)
     int32_t group_dim_k;
     int32_t tiles_n;
     int32_t tiles_m;     // group_dim_k = 1: tiles along M per group
@@ -131,6 +132,10 @@ __device__ __forceinline__ void dma2(const void* base, uint32_t voff, uint32_t l
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_ushort %0, %1"
                  :: "v"(voff), "s"(base), "s"(lds) : "memory");
 }
+__device__ __forceinline__ void dma4(const void* base, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+                 :: "v"(voff), "s"(base), "s"(lds) : "memory");
+}
 __device__ __forceinline__ void dma1(const void* base, uint32_t voff, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_ubyte %0, %1"
                  :: "v"(voff), "s"(base), "s"(lds) : "memory");
@@ -154,9 +159,10 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 // groups along K each tile's K window starts at an even chunk (Tile::head).
 // QOUT: the epilogue also quantizes the bf16 output row-wise (1x32 blocks
 // along N, round to nearest even), as the 1D quantizer would.
-template <bool OUT_BF16, bool B2D, bool GK, bool GATHER, bool SA2, bool QOUT>
+template <bool OUT_BF16, bool B2D, bool GK, bool GATHER, bool SA2, bool QOUT, bool STG>
 __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
     static_assert(!(GK && (B2D || GATHER)), "groups along K take 1D scales and no row index");
+    static_assert(!STG || (!GATHER && (GK || B2D)), "staged scales: A without a row index; B 2D or staged");
     static_assert(!QOUT || (OUT_BF16 && !GK), "the quantized output is the bf16 output of groups along M");
     // 2 x 4 waves of 128 x 64
     constexpr int WM = 128, WN = 64, FM = 4, FN = WN / 32;
@@ -195,6 +201,18 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
                 if (lane >= d) incl += v;
             }
             first_l = incl - t;                  // lane G: the total tile count
+        } else if (STG) {
+            // staged scales: group g's stages follow those of the groups
+            // before it; first_l = the first stage of group `lane`
+            const int32_t next = max(off_l, __shfl_down(off_l, 1));
+            const int32_t t = lane < p.G && next > off_l ? (next / 32 - off_l / 32 + 7) / 8 : 0;
+            int32_t incl = t;
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                const int32_t v = __shfl_up(incl, d);
+                if (lane >= d) incl += v;
+            }
+            first_l = incl - t;
         }
     }
 
@@ -204,6 +222,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
         int32_t kc0, kc_last;    // first K chunk (of 32); last valid chunk relative to it
         int32_t nkt;             // K stages
         int32_t head;            // 1: chunk kc0 lies before the group (groups along K, SA2)
+        int32_t sg;              // staged scales: the stage index of the tile's K stage 0
     };
     // (the host bounds M, N, K and the tile count to int32)
     const int32_t M32 = (int32_t)p.M, N32 = (int32_t)p.N, K32 = (int32_t)p.K;
@@ -213,7 +232,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
         // XCD-aware remap of the position: 32 consecutive ids per XCD turn
         const int32_t xcd = L % XCDS, j = L / XCDS;
         int32_t id = (j / XCD_BLOCK) * (XCDS * XCD_BLOCK) + xcd * XCD_BLOCK + (j % XCD_BLOCK);
-        int32_t g = -1, mb = 0, me = M32, kb = 0, ke = K32, mtiles;
+        int32_t g = -1, mb = 0, me = M32, kb = 0, ke = K32, mtiles, sg = 0;
         if (!GK) {
             if (table) {
                 if (id >= __builtin_amdgcn_readlane(first_l, p.G)) return false;
@@ -263,6 +282,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
             mtiles = p.tiles_m;
             kb = table ? __builtin_amdgcn_readlane(off_l, g) : clamp_off(p.off[g]);
             ke = max(kb, table ? __builtin_amdgcn_readlane(off_l, g + 1) : clamp_off(p.off[g + 1]));
+            if (STG) sg = __builtin_amdgcn_readlane(first_l, g);   // (staged: the host requires the table)
         }
         // grouped order inside the group: GROUP_M M-tiles x all N-tiles, m fastest
         const int32_t span = GROUP_M * p.tiles_n;
@@ -278,7 +298,8 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
         // groups along K with pair moves: the K window starts at the even
         // chunk at or below the group's first, so every scale pair is 2-byte
         // aligned; a chunk before the group (head) is masked like the tail
-        t.head = GK && SA2 ? (kb / 32) & 1 : 0;
+        t.head = GK && SA2 && !STG ? (kb / 32) & 1 : 0;
+        t.sg = sg;
         t.kc0 = kb / 32 - t.head;
         t.kc_last = ke / 32 - t.kc0 - 1;
         t.nkt = ke > kb ? (ke / 32 - t.kc0 + BK / 32 - 1) / (BK / 32) : 0;
@@ -329,9 +350,18 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
     // group move, NJ / 2 pair moves or NJ byte moves).  issue_slot(m) issues those with number
     // p % 8 == m, so the main loop can spread a stage's DMAs over the eight
     // MFMA blocks of a K-quarter instead of issuing them in one burst.
-    constexpr int NA_S = SA2 ? NJ / 2 : NJ, NB_S = B2D ? 1 : (SA2 ? NJ / 2 : NJ);
+    constexpr int NA_S = STG ? 1 : (SA2 ? NJ / 2 : NJ), NB_S = B2D || (STG && GK) ? 1 : (SA2 ? NJ / 2 : NJ);
     constexpr int NPARTS = 2 * NJ + NA_S + NB_S;
-    static_assert(NPARTS == dma_per_stage<B2D, SA2>(), "DMA count");
+    static_assert(STG || NPARTS == dma_per_stage<B2D, SA2>(), "DMA count");
+    static_assert(!STG || NPARTS == 2 * NJ + 2, "DMA count");
+    // staged scales: wave w moves tile rows 32 w .. 32 w + 31 of a stage's
+    // scales, two lanes a row (4 bytes each: one K half of the stage), from
+    // stage t.sg + kt of the staged layout ([stage][row][8 bytes]); tile row r
+    // lands at 8 r.  Stages past the tile's last repeat the last.
+    auto staged_off = [&](const Tile& t, int kt, int32_t row, int64_t rows) {
+        const uint32_t st = (uint32_t)(t.sg + min(kt, t.kc_last >> 3));
+        return (st * (uint32_t)rows + (uint32_t)row) * 8u + (uint32_t)(tid & 1) * 4u;
+    };
     auto issue_slot = [&](const Tile& t, const int32_t (&arow)[NR], int kt, int buf, int slot) {
         const uint32_t sb = lds_base + (uint32_t)buf * STAGE_BYTES;
         const uint8_t* bcodes = p.b_codes;
@@ -356,7 +386,11 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
                 dma16(bcodes, nrow(jj) * (uint32_t)KBB + kc * 16, sb + OFF_B + jj * NT * 16 + wave * 1024);
             } else if (part < 2 * NJ + NA_S) {
                 const int j = part - 2 * NJ;
-                if (SA2) {
+                if (STG) {
+                    int32_t m = t.m0 + 32 * wave + ((tid & 63) >> 1);
+                    if (m >= t.m1) m = t.m1 - 1;
+                    dma4(p.a_scales, staged_off(t, kt, m, p.M), sb + OFF_AS + wave * 256);
+                } else if (SA2) {
                     // move j of wave w fills tile rows 16 (j NW + w) .. + 15,
                     // four lanes a row: lane l takes pair l % 4 of its row,
                     // so tile row r lands at 16 r (pair p at + 4 p) and an
@@ -371,7 +405,10 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
                 }
             } else {
                 const int j = part - 2 * NJ - NA_S;
-                if (B2D) {
+                if (STG && GK) {
+                    const int32_t n = t.n0 + 32 * wave + ((tid & 63) >> 1);
+                    dma4(bscales, staged_off(t, kt, n < N32 ? n : N32 - 1, p.N), sb + OFF_BS + wave * 256);
+                } else if (B2D) {
                     // wave w fetches row group w of the tile (8 groups of 32
                     // rows): lane l takes scale position l % 8 (SA2: pair
                     // l % 4), so the copies of the same 8 bytes coalesce into
@@ -442,19 +479,22 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
     // consecutive, so each read below covers one contiguous span (no bank
     // conflicts), except 2D B scales, which every lane reads alike.
     constexpr bool SB2 = SA2;
-    using ARaw = typename std::conditional<SA2, uint2, uint4>::type;
-    using BRaw = typename std::conditional<SB2, uint2, uint4>::type;
+    using ARaw = typename std::conditional<STG, uint32_t, typename std::conditional<SA2, uint2, uint4>::type>::type;
+    using BRaw = typename std::conditional<STG && GK, uint32_t,
+                                           typename std::conditional<SB2, uint2, uint4>::type>::type;
     struct SclRaw { BRaw b[FN]; ARaw a[FM]; };
     auto read_scl = [&](SclRaw& s, int buf) {
         const uint8_t* sb = lds + buf * STAGE_BYTES;
 #pragma unroll
         for (int i = 0; i < FN; ++i)
             s.b[i] = B2D ? *(const BRaw*)(sb + OFF_BS + (wn * FN + i) * 256 + lh * (int)sizeof(BRaw))
+                   : STG ? *(const BRaw*)(sb + OFF_BS + (wn * WN + i * 32 + lr) * 8 + lh * 4)
                    : SB2 ? *(const BRaw*)(sb + OFF_BS + (wn * WN + i * 32 + lr) * 16 + lh * 8)
                          : *(const BRaw*)(sb + OFF_BS + (wn * WN + i * 32 + lr) * 32 + lh * 16);
 #pragma unroll
         for (int i = 0; i < FM; ++i)
-            s.a[i] = SA2 ? *(const ARaw*)(sb + OFF_AS + (wm * WM + i * 32 + lr) * 16 + lh * 8)
+            s.a[i] = STG ? *(const ARaw*)(sb + OFF_AS + (wm * WM + i * 32 + lr) * 8 + lh * 4)
+                   : SA2 ? *(const ARaw*)(sb + OFF_AS + (wm * WM + i * 32 + lr) * 16 + lh * 8)
                          : *(const ARaw*)(sb + OFF_AS + (wm * WM + i * 32 + lr) * 32 + lh * 16);
     };
     // byte q of the packed register: K-quarter q (a pair move leaves the
@@ -474,19 +514,22 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
     auto pack = [&](Scl& s, const SclRaw& r) {
 #pragma unroll
         for (int i = 0; i < FN; ++i) {
-            if constexpr (SB2) s.b[i] = pack2(r.b[i]);
+            if constexpr (STG && GK) s.b[i] = r.b[i];          // staged: the dword is the packed form
+            else if constexpr (SB2) s.b[i] = pack2(r.b[i]);
             else s.b[i] = pack4(r.b[i]);
         }
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
-            if constexpr (SA2) s.a[i] = pack2(r.a[i]);
+            if constexpr (STG) s.a[i] = r.a[i];
+            else if constexpr (SA2) s.a[i] = pack2(r.a[i]);
             else s.a[i] = pack4(r.a[i]);
         }
     };
 
     // "every DMA but the newest stage's has landed"
     auto wait_all_but_one_stage = [] {
-        if (B2D && SA2) asm volatile("s_waitcnt vmcnt(11)" ::: "memory");
+        if (STG) asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+        else if (B2D && SA2) asm volatile("s_waitcnt vmcnt(11)" ::: "memory");
         else if (B2D) asm volatile("s_waitcnt vmcnt(13)" ::: "memory");
         else if (SA2) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
         else asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
@@ -719,7 +762,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
                 read_frag(f0, par, 0);
                 read_scl(nsc, par);
                 pack(sc, nsc);
-                if (GK && SA2) head_mask(sc, cur.head);
+                if (GK && SA2 && !STG) head_mask(sc, cur.head);
             }
             // Stage kt+1's DMA was issued at stage kt-1's barrier, into the
             // buffer stage kt-1 had finished reading; at stage kt's barrier it
@@ -755,6 +798,11 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
                 t2.g = to_next ? nxt.g : cur.g;
                 t2.kc0 = to_next ? nxt.kc0 : cur.kc0;
                 t2.kc_last = to_next ? nxt.kc_last : cur.kc_last;
+                if (STG) {
+                    t2.m0 = to_next ? nxt.m0 : cur.m0;
+                    t2.m1 = to_next ? nxt.m1 : cur.m1;
+                    t2.sg = to_next ? nxt.sg : cur.sg;
+                }
                 // The row select is pinned here, after the barrier's wait:
                 // gathered row indices are ordinary loads, and the
                 // compiler's wait for them lands before their first use.
@@ -773,7 +821,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
                        [&](int m) { issue_slot(t2, r2, kt2, buf, m); });
                 pack(sc, nsc);
                 // the last stage packed the next tile's first scales (chained)
-                if (GK && SA2 && LAST) head_mask(sc, chain ? nxt.head : 0);
+                if (GK && SA2 && !STG && LAST) head_mask(sc, chain ? nxt.head : 0);
             };
             // At a chained tile's first barrier the previous tile's
             // EPI_STORES stores are the newest memory operations (without a
@@ -811,10 +859,13 @@ inline bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 
 // Validation shared by both entry points; fills everything but the outputs.
 mx_status gemm_setup(const uint8_t* a_codes, int64_t a_ld, const uint8_t* a_scales, const int32_t* a_row_index,
-                            const uint8_t* b_codes, int64_t b_ld, const uint8_t* b_scales, int b_scale_2d,
+                            const uint8_t* b_codes, int64_t b_ld, const uint8_t* b_scales, int scale_flags,
                             const int32_t* group_offsets, int32_t num_groups, int group_dim_k, int64_t M,
                             int64_t N, int64_t K, float alpha, GemmArgs& p, unsigned& grid) {
     if (M < 0 || N <= 0 || K <= 0 || N % 32 || K % 32) return MX_ERR_SHAPE;
+    if (scale_flags & ~(MX_SCALES_B_2D | MX_SCALES_STAGED)) return MX_ERR_UNSUPPORTED;
+    const int b_scale_2d = scale_flags & MX_SCALES_B_2D;
+    const bool staged = (scale_flags & MX_SCALES_STAGED) != 0;
     // code row pitch: 0 = K / 2 (contiguous rows); else at least K / 2 and
     // a multiple of 16 (every row starts 16-byte aligned)
     if (a_ld == 0) a_ld = K / 2;
@@ -823,10 +874,18 @@ mx_status gemm_setup(const uint8_t* a_codes, int64_t a_ld, const uint8_t* a_scal
     if (num_groups < 1) return MX_ERR_SHAPE;
     if (group_dim_k != 0 && group_dim_k != 1) return MX_ERR_SHAPE;
     if (group_dim_k == 1 && (b_scale_2d || a_row_index)) return MX_ERR_UNSUPPORTED;
+    // staged scales: groups along K need the in-register group table (fewer
+    // than 64 groups); groups along M take them for A with 2D B scales and
+    // no row index
+    if (staged && group_dim_k == 1 && num_groups >= 64) return MX_ERR_UNSUPPORTED;
+    if (staged && group_dim_k == 0 && (!b_scale_2d || a_row_index)) return MX_ERR_UNSUPPORTED;
     if (!group_offsets) return MX_ERR_NULL;
     if (M == 0) return MX_OK;
     if (!a_codes || !a_scales || !b_codes || !b_scales) return MX_ERR_NULL;
     if (!aligned16(a_codes) || !aligned16(b_codes)) return MX_ERR_ALIGN;
+    // staged scales move as dwords
+    if (staged && (((uintptr_t)a_scales & 3) || (group_dim_k == 1 && ((uintptr_t)b_scales & 3))))
+        return MX_ERR_ALIGN;
     // operand bytes are addressed by 32-bit offsets from the operand's (or
     // the B group's) base: each must span at most 4 GiB.  With a row index
     // the caller keeps the indexed rows within that range.
@@ -835,6 +894,9 @@ mx_status gemm_setup(const uint8_t* a_codes, int64_t a_ld, const uint8_t* a_scal
     if (!a_row_index && M * a_ld > lim) return MX_ERR_SHAPE;
     // tile coordinates are 32-bit
     if (M > 0x7FFFFF00LL || N > 0x7FFFFF00LL || K > 0x7FFFFF00LL) return MX_ERR_SHAPE;
+    // staged scales are addressed by 32-bit offsets too: at most K/256 + G
+    // stages of 8 bytes per row
+    if (staged && (K / 256 + num_groups + 1) * 8 * (group_dim_k == 1 ? max(M, N) : M) > lim) return MX_ERR_SHAPE;
 
     p = GemmArgs{};
     p.a_codes = a_codes;
@@ -850,6 +912,7 @@ mx_status gemm_setup(const uint8_t* a_codes, int64_t a_ld, const uint8_t* a_scal
     p.ldb = b_ld;
     p.G = num_groups;
     p.b_scale_2d = b_scale_2d ? 1 : 0;
+    p.staged = staged ? 1 : 0;
     p.group_dim_k = group_dim_k;
     p.tiles_n = (int32_t)((N + BN - 1) / BN);
     p.tiles_m = (int32_t)((M + BM - 1) / BM);
@@ -881,13 +944,20 @@ void launch_m(const GemmArgs& p, unsigned grid, hipStream_t s) {
     const dim3 gd(grid), bd(NT);
     const bool gather = p.a_row_index != nullptr;
     const bool sa2 = (p.K / 32) % 2 == 0 && ((uintptr_t)p.a_scales & 1) == 0 && ((uintptr_t)p.b_scales & 1) == 0;
-#define MX_GEMM_LAUNCH(B2, GA, S2) hipLaunchKernelGGL((gemm_kernel<BF, B2, false, GA, S2, QOUT>), gd, bd, 0, s, p)
+#define MX_GEMM_LAUNCH(B2, GA, S2) hipLaunchKernelGGL((gemm_kernel<BF, B2, false, GA, S2, QOUT, false>), gd, bd, 0, s, p)
 #define MX_GEMM_S(B2, GA) \
     do { if (sa2) MX_GEMM_LAUNCH(B2, GA, true); else MX_GEMM_LAUNCH(B2, GA, false); } while (0)
 #define MX_GEMM_G(B2) \
     do { if (gather) MX_GEMM_S(B2, true); else MX_GEMM_S(B2, false); } while (0)
-    if (p.b_scale_2d) MX_GEMM_G(true);
-    else MX_GEMM_G(false);
+    if (p.staged) {
+        // staged A scales (2D B, no row index)
+        if (sa2) hipLaunchKernelGGL((gemm_kernel<BF, true, false, false, true, QOUT, true>), gd, bd, 0, s, p);
+        else hipLaunchKernelGGL((gemm_kernel<BF, true, false, false, false, QOUT, true>), gd, bd, 0, s, p);
+    } else if (p.b_scale_2d) {
+        MX_GEMM_G(true);
+    } else {
+        MX_GEMM_G(false);
+    }
 #undef MX_GEMM_G
 #undef MX_GEMM_S
 #undef MX_GEMM_LAUNCH
@@ -914,12 +984,15 @@ extern "C" mx_status mx_grouped_gemm(const uint8_t* a_codes, int64_t a_ld, const
     if (group_dim_k == 1) {
         const dim3 gd(grid), bd(NT);
         const bool sa2 = (p.K / 32) % 2 == 0 && ((uintptr_t)p.a_scales & 1) == 0 && ((uintptr_t)p.b_scales & 1) == 0;
-        if (ct == MX_BF16) {
-            if (sa2) hipLaunchKernelGGL((gemm_kernel<true, false, true, false, true, false>), gd, bd, 0, s, p);
-            else hipLaunchKernelGGL((gemm_kernel<true, false, true, false, false, false>), gd, bd, 0, s, p);
+        if (p.staged) {
+            if (ct == MX_BF16) hipLaunchKernelGGL((gemm_kernel<true, false, true, false, false, false, true>), gd, bd, 0, s, p);
+            else hipLaunchKernelGGL((gemm_kernel<false, false, true, false, false, false, true>), gd, bd, 0, s, p);
+        } else if (ct == MX_BF16) {
+            if (sa2) hipLaunchKernelGGL((gemm_kernel<true, false, true, false, true, false, false>), gd, bd, 0, s, p);
+            else hipLaunchKernelGGL((gemm_kernel<true, false, true, false, false, false, false>), gd, bd, 0, s, p);
         } else {
-            if (sa2) hipLaunchKernelGGL((gemm_kernel<false, false, true, false, true, false>), gd, bd, 0, s, p);
-            else hipLaunchKernelGGL((gemm_kernel<false, false, true, false, false, false>), gd, bd, 0, s, p);
+            if (sa2) hipLaunchKernelGGL((gemm_kernel<false, false, true, false, true, false, false>), gd, bd, 0, s, p);
+            else hipLaunchKernelGGL((gemm_kernel<false, false, true, false, false, false, false>), gd, bd, 0, s, p);
         }
     } else if (ct == MX_BF16) {
         launch_m<true, false>(p, grid, s);

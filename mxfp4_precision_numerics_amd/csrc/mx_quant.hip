@@ -42,6 +42,9 @@ struct RowPitch {
     int64_t ld;         // bytes from one code row to the next
     int64_t step_rows;  // PITCH 2: the grid stride in blocks, as whole rows
     int64_t step_rem;   //          and the blocks left over
+    uint32_t srows;     // 0: row-major scales; else the staged order with srows rows:
+                        // block b of row r -> byte ((b / 8) srows + r) 8 + b % 8 (the host
+                        // keeps the staged array below 4 GiB, so 32-bit offsets)
 };
 
 // row = floor(blk / bpr) from the double quotient, which is within one of it
@@ -155,15 +158,24 @@ __device__ __forceinline__ void q1d_row_body(const void* __restrict__ x, int64_t
             }
             if (byte == 0xFFu) packed = 0;   // non-finite block: codes are 0
             if (blk < nblocks) {
+                int64_t srow = 0, sb = 0;     // staged scales: the block's row and its block in the row
                 if (PITCH == 2) {
                     const int32_t o = u * 16 + (lane >> 2);
                     const uint32_t rel = (uint32_t)o * 16u + (o >= thr ? (uint32_t)rp.pad : 0u);
                     *((uint32_t*)(cbase + rel) + q) = packed;
+                    srow = row0 + (o >= thr ? 1 : 0);
+                    sb = o >= thr ? o - thr : b0 + o;
                 } else {
                     const int64_t cofs = PITCH ? pofs : blk * 16;
                     *((uint32_t*)(codes + cofs) + q) = packed;
+                    if (rp.srows) split_block(blk, rp, srow, sb);
                 }
-                if (q == 0) scales[blk] = (uint8_t)byte;
+                if (q == 0) {
+                    if (rp.srows)
+                        scales[((uint32_t)(sb >> 3) * rp.srows + (uint32_t)srow) * 8u + (uint32_t)(sb & 7)] = (uint8_t)byte;
+                    else
+                        scales[blk] = (uint8_t)byte;
+                }
             }
         }
         if (PITCH == 2) {
@@ -302,6 +314,8 @@ struct ColArgs {
     uint8_t* row_scales;
     uint32_t row_stream_id;
     uint64_t row_index_base;
+    // scales in the staged layout (each group's blocks start a new stage of 8)
+    int staged;
 };
 
 template <bool BF16, bool RHT, bool SR, int ROWQ>
@@ -323,31 +337,54 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BF16 ? 3 : 
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     uint8_t* tile = smem;                                          // TL::TILE bytes
     int32_t* pstart = (int32_t*)(smem + TL::TILE);                 // num_groups + 1
-    __shared__ int32_t wave_sum[4];
+    int32_t* sstart = pstart + num_groups + 1;                     // staged: num_groups + 1
+    __shared__ int32_t wave_sum[4], wave_ssum[4];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
     // padded start (in 32-token blocks) of every group: block-wide scan of
-    // ceil32(n_g) / 32, each thread summing a contiguous chunk of groups
+    // ceil32(n_g) / 32, each thread summing a contiguous chunk of groups;
+    // staged scales also need each group's first stage (a scan of
+    // ceil(blocks / 8))
+    const bool staged = a.staged != 0;
     {
         const int chunk = (num_groups + 255) / 256;
         const int g0 = min(num_groups, tid * chunk), g1 = min(num_groups, g0 + chunk);
-        int32_t local = 0;
-        for (int g = g0; g < g1; ++g) local += (off[g + 1] - off[g] + 31) >> 5;
-        int32_t incl = local;
+        int32_t local = 0, slocal = 0;
+        for (int g = g0; g < g1; ++g) {
+            const int32_t nb = (off[g + 1] - off[g] + 31) >> 5;
+            local += nb;
+            slocal += (nb + 7) >> 3;
+        }
+        int32_t incl = local, sincl = slocal;
 #pragma unroll
         for (int d = 1; d < 64; d <<= 1) {
-            const int32_t v = __shfl_up(incl, d);
-            if (lane >= d) incl += v;
+            const int32_t v = __shfl_up(incl, d), sv = __shfl_up(sincl, d);
+            if (lane >= d) {
+                incl += v;
+                sincl += sv;
+            }
         }
-        if (lane == 63) wave_sum[wave] = incl;
+        if (lane == 63) {
+            wave_sum[wave] = incl;
+            wave_ssum[wave] = sincl;
+        }
         __syncthreads();
-        int32_t run = incl - local;
-        for (int w = 0; w < wave; ++w) run += wave_sum[w];
-        for (int g = g0; g < g1; ++g) {
-            pstart[g] = run;
-            run += (off[g + 1] - off[g] + 31) >> 5;
+        int32_t run = incl - local, srun = sincl - slocal;
+        for (int w = 0; w < wave; ++w) {
+            run += wave_sum[w];
+            srun += wave_ssum[w];
         }
-        if (tid == 255) pstart[num_groups] = run;
+        for (int g = g0; g < g1; ++g) {
+            const int32_t nb = (off[g + 1] - off[g] + 31) >> 5;
+            pstart[g] = run;
+            run += nb;
+            if (staged) sstart[g] = srun;
+            srun += (nb + 7) >> 3;
+        }
+        if (tid == 255) {
+            pstart[num_groups] = run;
+            if (staged) sstart[num_groups] = srun;
+        }
         __syncthreads();
     }
     // The offsets come from the device and are trusted only this far: the
@@ -454,6 +491,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BF16 ? 3 : 
     for (int64_t tl = tbeg; tl < tend; ++tl) {
         const int64_t pb0 = br * CT_BLOCKS;
         const int64_t c0 = ct * CT_COLS;
+        // staged scales: lane b < 8 of every wave places block pb0 + b
+        // (stage << 3 | slot; the last group starting at or before it)
+        int32_t splace = 0;
+        if (staged && lane < CT_BLOCKS && pb0 + lane < nblk_total) {
+            const int64_t pb = pb0 + lane;
+            int lo = 0, hi = num_groups - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (pstart[mid] <= pb) lo = mid; else hi = mid - 1;
+            }
+            const int32_t rel = (int32_t)(pb - pstart[lo]);
+            splace = ((sstart[lo] + (rel >> 3)) << 3) | (rel & 7);
+        }
 
         // ---- the tile into LDS (rows past a group's end, columns past cols: 0)
         if (vec) {
@@ -617,6 +667,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BF16 ? 3 : 
         __syncthreads();
         // ---- store: 8 lanes write one column's 8 blocks (128 contiguous bytes)
         const int64_t nv = min((int64_t)CT_BLOCKS, nblk_total - pb0);
+        // staged: this thread's block ch = tid % 8 (the same for both k), from
+        // lane ch, read with every lane active
+        const int32_t pl = staged ? __shfl(splace, tid & 7) : 0;
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
             const int q = tid + 256 * k;
@@ -624,7 +677,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BF16 ? 3 : 
             if (c0 + col < cols && ch < nv) {
                 *(uint4*)(codes + (c0 + col) * (kp >> 1) + (pb0 + ch) * 16) =
                     *(const uint4*)(oc + col * CT_OUT_PITCH + ch * 16);
-                scales[(c0 + col) * kp_blocks + pb0 + ch] = os[col * CT_BLOCKS + ch];
+                int64_t si = (c0 + col) * kp_blocks + pb0 + ch;
+                if (staged) si = ((int64_t)(pl >> 3) * cols + c0 + col) * 8 + (pl & 7);
+                scales[si] = os[col * CT_BLOCKS + ch];
             }
         }
         __syncthreads();                                     // LDS is reused by the next tile
@@ -1157,7 +1212,7 @@ mx_status launch_col_t(ColArgs a, hipStream_t s) {
     const int64_t tiles = a.col_tiles * ((a.kp / 32 + CT_BLOCKS - 1) / CT_BLOCKS);
     const int grid = (int)min(tiles, (int64_t)resident_blocks(B ? 3 : 2));
     a.vec = (a.cols % (B ? 8 : 4)) == 0;
-    const size_t lds = (size_t)ColTile<B>::TILE + 4 * (size_t)(a.num_groups + 1);
+    const size_t lds = (size_t)ColTile<B>::TILE + 4 * (size_t)(a.num_groups + 1) * (a.staged ? 2 : 1);
     if (!B) {
         // fp32 tiles take more than 64 KiB of dynamic LDS: raise the limit of
         // the instantiation about to run, on the current device, every call
@@ -1266,6 +1321,8 @@ mx_status mx_quantize_1d(const void* x, mx_dtype xt, int64_t rows, int64_t cols,
     const bool bf = xt == MX_BF16, rh = use_rht != 0, sr = rnd == MX_SR;
     const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
     hipStream_t s = (hipStream_t)stream;
+    const bool staged = (block_axis & MX_SCALES_STAGED) != 0;
+    block_axis &= ~MX_SCALES_STAGED;
     if (block_axis == 1) {
         if (cols % 32) return MX_ERR_SHAPE;
         if (group_offsets || num_groups || kp) return MX_ERR_SHAPE;
@@ -1283,7 +1340,10 @@ mx_status mx_quantize_1d(const void* x, mx_dtype xt, int64_t rows, int64_t cols,
         // wave per unrolled step
         const int64_t stride = (int64_t)grid * 4 * 16 * ROW_UNROLL;
         const int64_t bpr = cols / 32;
-        const RowPitch rp{bpr, 1.0 / (double)bpr, ld - cols / 2, ld, stride / bpr, stride % bpr};
+        // staged scales: ceil(cols / 256) stages of rows x 8 bytes, 32-bit offsets
+        if (staged && (cols + 255) / 256 * rows * 8 > (int64_t)0xFFFFFFFFu) return MX_ERR_SHAPE;
+        const RowPitch rp{bpr, 1.0 / (double)bpr, ld - cols / 2, ld, stride / bpr, stride % bpr,
+                          staged ? (uint32_t)rows : 0u};
         (void)hipGetLastError();
         if (ld == cols / 2) {
             MX_DISPATCH3(q1d_row_kernel, bf, rh, sr, dim3(grid), s, x, nblocks, sign_mask, k0, k1, stream_id,
@@ -1307,7 +1367,7 @@ mx_status mx_quantize_1d(const void* x, mx_dtype xt, int64_t rows, int64_t cols,
     if (!aligned16(x) || !aligned16(codes)) return MX_ERR_ALIGN;
     if (cols > (int64_t)(0xFFFFFFFFu / (bf ? 2u : 4u))) return MX_ERR_SHAPE;   // one row of x within 4 GiB
     ColArgs a{x, cols, group_offsets, (int)num_groups, row_index, rows, kp, 0, 0, sign_mask, k0, k1, stream_id,
-              index_base, codes, scales, nullptr, 0, nullptr, 0, 0};
+              index_base, codes, scales, nullptr, 0, nullptr, 0, 0, staged ? 1 : 0};
     return launch_col(a, bf, rh, sr, 0, s);
 }
 

@@ -17,6 +17,8 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "mx.h")
 
 MX_F32, MX_BF16 = 0, 1
 RNE, SR = 0, 1
+# scale storage orders (include/mx.h): 2D B scales; staged ([stage][row][8 bytes])
+SCALES_B_2D, SCALES_STAGED = 1, 2
 STATUS = {0: "MX_OK", 1: "MX_ERR_NULL", 2: "MX_ERR_SHAPE", 3: "MX_ERR_ALIGN",
           4: "MX_ERR_DTYPE", 5: "MX_ERR_UNSUPPORTED", 6: "MX_ERR_LAUNCH"}
 
@@ -176,6 +178,10 @@ def rht(x, sign_mask: int, inverse: bool = False, out=None):
     return out
 
 
+def _scale_flags(b_scale_2d, staged):
+    return (SCALES_B_2D if b_scale_2d else 0) | (SCALES_STAGED if staged else 0)
+
+
 def padded_capacity(rows: int, num_groups: int) -> int:
     """A token capacity that holds any grouping of `rows` tokens into
     `num_groups` groups each padded to a multiple of 32, rounded up to a
@@ -187,13 +193,14 @@ def padded_capacity(rows: int, num_groups: int) -> int:
 
 def quantize_1d(x, block_axis: int = 1, group_offsets=None, kp: int = 0, use_rht: bool = False,
                 sign_mask: int = 0, rnd: int = RNE, seed: int = 0, stream_id: int = 0,
-                index_base: int = 0, codes=None, scales=None, row_index=None):
+                index_base: int = 0, codes=None, scales=None, row_index=None, staged: bool = False):
     """Returns (codes, scales) uint8 device tensors; see mx_quantize_1d.
     row_index (column-wise only): gather x's rows through it; the grouped
     positions then number row_index.numel().  A row-wise codes output may
     have padded rows, e.g. buf[:, :cols // 2] of a wider buffer (its row
     stride, a multiple of 16, is passed as the pitch; the padding is not
-    written)."""
+    written).  staged: scales in the staged order (include/mx.h), row-wise
+    [ceil(cols / 256), rows, 8], column-wise [kp // 256 + groups, cols, 8]."""
     torch = _torch()
     _dev(x, "x")
     rows, cols = x.shape
@@ -203,12 +210,16 @@ def quantize_1d(x, block_axis: int = 1, group_offsets=None, kp: int = 0, use_rht
     ng = 0
     if block_axis == 1:
         shape_c, shape_s = (rows, cols // 2), (rows, cols // 32)
+        if staged:
+            shape_s = ((cols + 255) // 256, rows, 8)
     else:
         _index_vector(group_offsets, "group_offsets", min_numel=2)
         ng = group_offsets.numel() - 1
         if not kp:
             kp = padded_capacity(rows, ng)
         shape_c, shape_s = (cols, kp // 2), (cols, kp // 32)
+        if staged:
+            shape_s = (kp // 256 + ng, cols, 8)
     if codes is None:
         codes = torch.empty(shape_c, dtype=torch.uint8, device=x.device)
     if scales is None:
@@ -217,7 +228,7 @@ def quantize_1d(x, block_axis: int = 1, group_offsets=None, kp: int = 0, use_rht
     codes_ld = _shaped(codes, shape_c, torch.uint8, "codes", pitched=True)
     _shaped(scales, shape_s, torch.uint8, "scales")
     _check("mx_quantize_1d", lib().mx_quantize_1d(
-        _ptr(x), _dtype_code(x), rows, cols, block_axis, _ptr(group_offsets), ng, kp,
+        _ptr(x), _dtype_code(x), rows, cols, block_axis | (SCALES_STAGED if staged else 0), _ptr(group_offsets), ng, kp,
         _ptr(row_index), int(use_rht), sign_mask, rnd, seed, stream_id, index_base, _ptr(codes), codes_ld,
         _ptr(scales), _stream()))
     return codes, scales
@@ -399,9 +410,11 @@ def dequantize(codes, scales, block_rows: int = 1, out_dtype=None, out=None):
 
 
 def _gemm_operands(a_codes, a_scales, a_row_index, b_codes, b_scales, group_offsets, M, N, K,
-                   b_scale_2d, group_dim_k):
+                   b_scale_2d, group_dim_k, staged=False):
     """Check A, B and their scales against M, N, K and the group count (the
-    extents the kernel reads); returns (a_ld, b_ld, G)."""
+    extents the kernel reads); returns (a_ld, b_ld, G).  Staged scales are
+    [stages, rows, 8]: K // 256 + G stages with groups along K, ceil(K / 256)
+    along M."""
     torch = _torch()
     u8 = torch.uint8
     _index_vector(group_offsets, "group_offsets", min_numel=2)
@@ -413,10 +426,11 @@ def _gemm_operands(a_codes, a_scales, a_row_index, b_codes, b_scales, group_offs
             raise ValueError("a_row_index must be int32 [M]")
         a_rows = a_codes.shape[0]
     a_ld = _shaped(a_codes, (a_rows, K // 2), u8, "a_codes", pitched=True)
-    _shaped(a_scales, (a_rows, K // 32), u8, "a_scales")
+    stages = (K // 256 + G) if group_dim_k else (K + 255) // 256
+    _shaped(a_scales, (stages, a_rows, 8) if staged else (a_rows, K // 32), u8, "a_scales")
     if group_dim_k:
         b_ld = _shaped(b_codes, (N, K // 2), u8, "b_codes", pitched=True)
-        _shaped(b_scales, (N, K // 32), u8, "b_scales")
+        _shaped(b_scales, (stages, N, 8) if staged else (N, K // 32), u8, "b_scales")
     else:
         b_ld = _shaped(b_codes, (G, N, K // 2), u8, "b_codes", pitched=True)
         _shaped(b_scales, (G, N // 32, K // 32) if b_scale_2d else (G, N, K // 32), u8, "b_scales")
@@ -425,13 +439,13 @@ def _gemm_operands(a_codes, a_scales, a_row_index, b_codes, b_scales, group_offs
 
 def grouped_gemm(a_codes, a_scales, b_codes, b_scales, group_offsets, M, N, K,
                  a_row_index=None, b_scale_2d=False, group_dim_k=False, alpha=1.0,
-                 out_dtype=None, out=None):
+                 out_dtype=None, out=None, staged=False):
     """C (bf16 by default, or out_dtype float32) per mx_grouped_gemm.  a_codes
     and b_codes may have padded rows (row-slice views of wider buffers); rows
     padded to whole 128-byte lines are read fastest."""
     torch = _torch()
     a_ld, b_ld, G = _gemm_operands(a_codes, a_scales, a_row_index, b_codes, b_scales, group_offsets,
-                                   M, N, K, b_scale_2d, group_dim_k)
+                                   M, N, K, b_scale_2d, group_dim_k, staged)
     shape = (G, M, N) if group_dim_k else (M, N)
     if out is None:
         out = torch.empty(shape, dtype=out_dtype or torch.bfloat16, device=a_codes.device)
@@ -439,21 +453,21 @@ def grouped_gemm(a_codes, a_scales, b_codes, b_scales, group_offsets, M, N, K,
         _shaped(out, shape, out_dtype or out.dtype, "out")
     _check("mx_grouped_gemm", lib().mx_grouped_gemm(
         _ptr(a_codes), a_ld, _ptr(a_scales), _ptr(a_row_index), _ptr(b_codes), b_ld, _ptr(b_scales),
-        int(bool(b_scale_2d)), _ptr(group_offsets), G, int(bool(group_dim_k)), M, N, K,
+        _scale_flags(b_scale_2d, staged), _ptr(group_offsets), G, int(bool(group_dim_k)), M, N, K,
         float(alpha), _ptr(out), _dtype_code(out), _stream()))
     return out
 
 
 def grouped_gemm_q(a_codes, a_scales, b_codes, b_scales, group_offsets, M, N, K,
                    a_row_index=None, b_scale_2d=False, alpha=1.0, with_bf16=True,
-                   out=None, codes=None, scales=None):
+                   out=None, codes=None, scales=None, staged=False):
     """Grouped GEMM (groups split M) whose bf16 output is also written as
     row-wise MXFP4 (1x32 along N, RTNE) by the GEMM's epilogue.  Returns
     (c or None, codes [M x N/2], scales [M x N/32]); out / codes / scales
     are optional preallocated outputs."""
     torch = _torch()
     a_ld, b_ld, G = _gemm_operands(a_codes, a_scales, a_row_index, b_codes, b_scales, group_offsets,
-                                   M, N, K, b_scale_2d, False)
+                                   M, N, K, b_scale_2d, False, staged)
     dev = a_codes.device
     c = None
     if with_bf16:
@@ -465,6 +479,6 @@ def grouped_gemm_q(a_codes, a_scales, b_codes, b_scales, group_offsets, M, N, K,
     _shaped(scales, (M, N // 32), torch.uint8, "scales")
     _check("mx_grouped_gemm_q", lib().mx_grouped_gemm_q(
         _ptr(a_codes), a_ld, _ptr(a_scales), _ptr(a_row_index), _ptr(b_codes), b_ld, _ptr(b_scales),
-        int(bool(b_scale_2d)), _ptr(group_offsets), G, M, N, K, float(alpha),
+        _scale_flags(b_scale_2d, staged), _ptr(group_offsets), G, M, N, K, float(alpha),
         _ptr(c), _ptr(codes), c_ld, _ptr(scales), _stream()))
     return c, codes, scales

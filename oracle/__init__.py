@@ -56,6 +56,8 @@ def lib():
         L.oracle_sr_bits.argtypes = [u64, u32, u64]
         L.oracle_sr_bits.restype = u32
         L.oracle_rht_block.argtypes = [P, P, u32, ctypes.c_int]
+        L.oracle_stage_scales.argtypes = [P, i64, i64, P, i32, P]
+        L.oracle_stage_scales.restype = i64
         L.oracle_scale_byte.argtypes = [ctypes.c_double]
         L.oracle_scale_byte.restype = ctypes.c_uint8
         L.oracle_rtne_mag.argtypes = [ctypes.c_double]
@@ -204,6 +206,32 @@ def quantize_1d(x, block_axis: int = 1, group_offsets=None, kp: int | None = Non
 
     _run([job(a, b) for a, b in _split(qr, threads * 4)], threads)
     return codes, scales
+
+
+def stage_scales(scales, group_offsets=None, stages: int | None = None, fill: int = 0):
+    """The staged storage order of a row-major scale matrix (mx_oracle.c,
+    oracle_stage_scales): [stages, rows, 8].  group_offsets: token offsets
+    of the column-wise grouped layout (each group padded to 32 tokens, so
+    group g's blocks start at its padded start / 32); None: one group per
+    row.  stages: the array's stage count (default: the number the mapping
+    uses); slots no block maps to hold `fill`."""
+    sc = np.ascontiguousarray(scales, dtype=np.uint8)
+    rows, nblk = sc.shape
+    if group_offsets is None:
+        gb, ng = None, 0
+        used = (nblk + 7) // 8
+    else:
+        n = np.diff(np.asarray(group_offsets, dtype=np.int64))
+        gb = np.ascontiguousarray(np.concatenate([[0], np.cumsum((n + 31) // 32)]).astype(np.int64))
+        ng = len(n)
+        used = int(np.sum((np.diff(gb) + 7) // 8))
+    st = used if stages is None else int(stages)
+    if st < used:
+        raise ValueError("stages below the %d the mapping uses" % used)
+    out = np.full((st, rows, 8), fill, dtype=np.uint8)
+    got = lib().oracle_stage_scales(_ptr(sc), rows, nblk, _ptr(gb), ng, _ptr(out))
+    assert got == used
+    return out
 
 
 def quantize_1d_ex(x, use_rht: bool = False, sign_mask: int = 0, rnd: int = RNE, seed: int = 0,

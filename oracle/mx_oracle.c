@@ -757,3 +757,37 @@ int oracle_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
     }
     return 0;
 }
+
+/* ------------------------------------------------------------------------
+ * Staged storage order of a scale matrix (no arithmetic: a permutation of
+ * bytes).  This order is not from the pages; it is the order the library's
+ * grouped GEMM reads one K stage of 256 elements in (include/mx.h,
+ * MX_SCALES_STAGED), written here from that definition so the tests can
+ * compare the library's staged output with the row-major oracle output.
+ *
+ * scales: rows x nblk, row-major (block b of row r at r * nblk + b).
+ * gb: num_groups + 1 block offsets (non-decreasing, gb[0] = 0, gb[G] <=
+ * nblk) splitting the blocks of every row into groups; num_groups = 0
+ * means a single group of all nblk blocks.  Group g's blocks fill stages
+ * of 8 of their own, numbered after those of the groups before it: block
+ * gb[g] + i goes to slot i % 8 of stage S_g + i / 8, S_g = sum over g' < g
+ * of ceil((gb[g'+1] - gb[g']) / 8), i.e. to out[((S_g + i/8) * rows + r) * 8
+ * + i % 8].  Bytes of out no block maps to are left untouched.  Returns the
+ * number of stages. */
+int64_t oracle_stage_scales(const uint8_t* scales, int64_t rows, int64_t nblk, const int64_t* gb,
+                            int32_t num_groups, uint8_t* out) {
+    int64_t one[2] = {0, nblk};
+    if (num_groups == 0) {
+        gb = one;
+        num_groups = 1;
+    }
+    int64_t stage0 = 0;
+    for (int32_t g = 0; g < num_groups; ++g) {
+        const int64_t n = gb[g + 1] - gb[g];
+        for (int64_t r = 0; r < rows; ++r)
+            for (int64_t i = 0; i < n; ++i)
+                out[((stage0 + i / 8) * rows + r) * 8 + i % 8] = scales[r * nblk + gb[g] + i];
+        stage0 += (n + 7) / 8;
+    }
+    return stage0;
+}

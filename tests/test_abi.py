@@ -65,6 +65,14 @@ def test_quantize_1d_validation(L):
     assert q(FAKE, mx.MX_BF16, 4, 64, 1, None, 0, 0, None, 0, 0, 0, 0, 0, 0, FAKE, 16, FAKE, None) == 2
     assert q(FAKE, mx.MX_BF16, 4, 64, 1, None, 0, 0, None, 0, 0, 0, 0, 0, 0, FAKE, 40, FAKE, None) == 2
     assert q(FAKE, mx.MX_BF16, 4, 32, 0, FAKE, 2, 64, None, 0, 0, 0, 0, 0, 0, FAKE, 48, FAKE, None) == 2
+    # staged scales keep the axis checks; an unknown axis value stays a shape error
+    assert q(FAKE, mx.MX_BF16, 4, 32, 1 | mx.SCALES_STAGED, FAKE, 2, 0, None, 0, 0, 0, 0, 0, 0, FAKE, 0, FAKE,
+             None) == 2
+    assert q(FAKE, mx.MX_BF16, 4, 33, 1 | mx.SCALES_STAGED, None, 0, 0, None, 0, 0, 0, 0, 0, 0, FAKE, 0, FAKE,
+             None) == 2
+    assert q(FAKE, mx.MX_BF16, 4, 32, 4, None, 0, 0, None, 0, 0, 0, 0, 0, 0, FAKE, 0, FAKE, None) == 2
+    assert q(FAKE, mx.MX_BF16, 4, 32, 0 | mx.SCALES_STAGED, FAKE, 2, 40, None, 0, 0, 0, 0, 0, 0, FAKE, 0, FAKE,
+             None) == 2
     # empty input is a no-op that launches nothing
     assert q(None, mx.MX_BF16, 0, 32, 1, None, 0, 0, None, 0, 0, 0, 0, 0, 0, None, 0, None, None) == 0
 
@@ -195,6 +203,19 @@ def test_gemm_validation(L):
     assert call(b_ld=40) == 2
     # B group of N rows at the pitch beyond 4 GiB - 1
     assert call(N=2**20, K=64, b_ld=2**13) == 2
+    # scale flags: unknown bits; staged scales with groups along K need
+    # fewer than 64 groups and 4-byte aligned scales; along M they need 2D
+    # B scales and no row index
+    S, B2 = mx.SCALES_STAGED, mx.SCALES_B_2D
+    assert call(b_scale_2d=4) == 5
+    assert call(gk=1, b_scale_2d=S, G=64) == 5
+    assert call(gk=1, b_scale_2d=S, a_scales=FAKE + 2) == 3
+    assert call(gk=1, b_scale_2d=S, b_scales=FAKE + 1) == 3
+    assert call(b_scale_2d=S) == 5
+    assert call(b_scale_2d=S | B2, a_row_index=FAKE) == 5
+    assert call(b_scale_2d=S | B2, a_scales=FAKE + 2) == 3
+    # staged scales addressed past 4 GiB: (K/256 + G + 1) * 8 * rows
+    assert call(gk=1, b_scale_2d=S, M=64, N=2**23, K=64, G=63) == 2
     assert call(M=0) == 0
 
 
@@ -224,6 +245,9 @@ def test_gemm_q_validation(L):
     assert call(qc_ld=16) == 2
     assert call(qc_ld=40) == 3
     assert call(M=2**20, N=64, qc_ld=2**12) == 2
+    # staged A scales need 2D B scales; unknown flag bits
+    assert call(b_scale_2d=mx.SCALES_STAGED) == 5
+    assert call(b_scale_2d=8) == 5
     assert call(M=0) == 0
 
 
