@@ -560,12 +560,13 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
     // read of the next quarter's fragment piece whose last use it was, into
     // the same registers (B piece i is last used by block i FM + FM - 1, A
     // piece jj by block FM + jj), so a single fragment set suffices and every
-    // read still has at least three MFMAs to land.
+    // read still has at least three MFMAs to land.  skip (wave-uniform): the
+    // quarter lies wholly past the end of K, its MFMAs would add only zeros.
     auto no_extra = [](int) {};
-    auto mma_rd = [&](Frag& f, const Scl& s, int q, bool tail, int nbuf, int nq, auto&& extra) {
+    auto mma_rd = [&](Frag& f, const Scl& s, int q, bool tail, bool skip, int nbuf, int nq, auto&& extra) {
 #pragma unroll
         for (int m = 0; m < FN * FM; ++m) {
-            mma1(f, s, q, tail, m);
+            if (!skip) mma1(f, s, q, tail, m);
             extra(m);
             if (m == FM - 1) read_piece(f, nbuf, nq, 0);                 // B 0
             if (m >= FM) read_piece(f, nbuf, nq, FN + (m - FM));         // A m - FM
@@ -711,11 +712,27 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
                         swap16(Y[0][e], Y[1][e]);
                         swap16(Y[2][e], Y[3][e]);
                     }
-                    const int32_t col = col0 + i * 32 + 8 * rh + 4 * elh;
-                    put(r0, col, Y[0][0], Y[0][1], Y[0][2], Y[0][3]);
-                    put(r0 + 16, col, Y[1][0], Y[1][1], Y[1][2], Y[1][3]);
-                    put(r0, col + 16, Y[2][0], Y[2][1], Y[2][2], Y[2][3]);
-                    put(r0 + 16, col + 16, Y[3][0], Y[3][1], Y[3][2], Y[3][3]);
+                    // -> whole 128-byte row lines: lanes with bit 3 set trade
+                    // their rows 0..7 of the left half (Y[2h]) for rows 8..15
+                    // of the right half held 8 lanes away (a row rotate by 8,
+                    // DPP), so one store writes 8 rows x 32 columns:
+                    // Z[k]: row 8 k + (lane % 8), columns 16 b3 + 8 rh + 4 lh
+                    const bool b3 = (ln & 8) != 0;
+                    uint32_t Z[4][4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+#pragma unroll
+                        for (int h = 0; h < 2; ++h) {
+                            const uint32_t l8 = (uint32_t)__builtin_amdgcn_mov_dpp((int)Y[h][e], 0x128, 0xF, 0xF, false);
+                            const uint32_t r8 = (uint32_t)__builtin_amdgcn_mov_dpp((int)Y[2 + h][e], 0x128, 0xF, 0xF, false);
+                            Z[2 * h][e] = b3 ? r8 : Y[h][e];
+                            Z[2 * h + 1][e] = b3 ? Y[2 + h][e] : l8;
+                        }
+                    }
+                    const int32_t rb = wm * WM + jj * 32 + (ln & 7);
+                    const int32_t col = col0 + i * 32 + (b3 ? 16 : 0) + 8 * rh + 4 * elh;
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) put(rb + 8 * k, col, Z[k][0], Z[k][1], Z[k][2], Z[k][3]);
                 }
             }
         }
@@ -778,9 +795,14 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
                 constexpr bool LAST = decltype(last_c)::value;
                 const int buf = (kt & 1) ^ par;
                 const int kcl = kt * 8 + 4 * lh;          // this lane's chunk in K-quarter 0
-                mma_rd(f0, sc, 0, LAST && kcl > cur.kc_last, buf, 1, no_extra);
-                mma_rd(f0, sc, 1, LAST && kcl + 1 > cur.kc_last, buf, 2, no_extra);
-                mma_rd(f0, sc, 2, LAST && kcl + 2 > cur.kc_last, buf, 3, no_extra);
+                // K-quarter q holds chunks kt 8 + q (lane half 0) and + 4: it
+                // is all tail once the first is past the last chunk
+                auto past = [&](int q) {
+                    return LAST && __builtin_amdgcn_readfirstlane(kt * 8 + q - cur.kc_last) > 0;
+                };
+                mma_rd(f0, sc, 0, LAST && kcl > cur.kc_last, false, buf, 1, no_extra);
+                mma_rd(f0, sc, 1, LAST && kcl + 1 > cur.kc_last, past(1), buf, 2, no_extra);
+                mma_rd(f0, sc, 2, LAST && kcl + 2 > cur.kc_last, past(2), buf, 3, no_extra);
                 if (FIRST) {
                     if (EPI_STORES == 16) asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)" ::: "memory");
                     else asm volatile("s_waitcnt vmcnt(32) lgkmcnt(0)" ::: "memory");
@@ -817,7 +839,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
                 // full memory pipeline stalls one block, not the whole burst
                 const int kt2 = to_next ? kt + 2 - cur.nkt : kt + 2;
                 read_scl(nsc, buf ^ 1);
-                mma_rd(f0, sc, 3, LAST && kcl + 3 > cur.kc_last, buf ^ 1, 0,
+                mma_rd(f0, sc, 3, LAST && kcl + 3 > cur.kc_last, past(3), buf ^ 1, 0,
                        [&](int m) { issue_slot(t2, r2, kt2, buf, m); });
                 pack(sc, nsc);
                 // the last stage packed the next tile's first scales (chained)
