@@ -624,7 +624,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
         int ln = lane;
         asm volatile("" : "+v"(ln));
         const int elr = ln & 31, elh = ln >> 5;
-        const int rr = elr & 15, rh = elr >> 4;
+        const int rh = elr >> 4;                        // (lane bits 0..3: the row rr within 16)
         const int32_t nrows = t.m1 - t.m0;
         typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
         auto put = [&](int32_t row, int32_t col, uint32_t v0, uint32_t v1, uint32_t v2, uint32_t v3) {
@@ -632,9 +632,10 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
             const uint32_t off = row < nrows && col < N32 ? (uint32_t)(row * N32 + col) * EB : 0x80000000u;
             __builtin_amdgcn_raw_buffer_store_b128((u32x4){v0, v1, v2, v3}, rsrc, off, 0, 0);
         };
+        static_assert(FN == 2, "the bf16 stores pair the wave's two 32-column blocks");
 #pragma unroll
         for (int jj = 0; jj < FM; ++jj) {
-            const int32_t r0 = wm * WM + jj * 32 + rr;     // rows r0 and r0 + 16 of the tile
+            uint32_t G[FN][2][4];                          // bf16: block i, rows 16 h + rr, as stored
 #pragma unroll
             for (int i = 0; i < FN; ++i) {
                 const v16f& c = acc[i][jj];
@@ -696,9 +697,9 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
                         swap16(P[0][d], P[2][d]);
                         swap16(P[1][d], P[3][d]);
                     }
-                    const int32_t col = col0 + i * 32 + 16 * rh + 8 * elh;
-                    put(r0, col, P[0][0], P[0][1], P[1][0], P[1][1]);
-                    put(r0 + 16, col, P[2][0], P[2][1], P[3][0], P[3][1]);
+                    // G[i][h]: row 16 h + rr, columns 32 i + 16 rh + 8 lh + (0..7)
+                    G[i][0][0] = P[0][0]; G[i][0][1] = P[0][1]; G[i][0][2] = P[1][0]; G[i][0][3] = P[1][1];
+                    G[i][1][0] = P[2][0]; G[i][1][1] = P[2][1]; G[i][1][2] = P[3][0]; G[i][1][3] = P[3][1];
                 } else {
                     // Y[q]: columns 8 q + 4 lh + (0..3)
                     uint32_t Y[4][4];
@@ -733,6 +734,28 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
                     const int32_t col = col0 + i * 32 + (b3 ? 16 : 0) + 8 * rh + 4 * elh;
 #pragma unroll
                     for (int k = 0; k < 4; ++k) put(rb + 8 * k, col, Z[k][0], Z[k][1], Z[k][2], Z[k][3]);
+                }
+            }
+            if (OUT_BF16) {
+                // whole 128-byte row lines from the wave's two blocks (64
+                // bf16 columns): lanes with bit 3 set trade rows 0..7 of block
+                // 0 for rows 8..15 of block 1 held 8 lanes away (DPP row
+                // rotate by 8), so one store writes 8 rows x 64 columns
+                const bool b3 = (ln & 8) != 0;
+                const int32_t rb = wm * WM + jj * 32 + (ln & 7);
+                const int32_t col = col0 + (b3 ? 32 : 0) + 16 * rh + 8 * elh;
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    uint32_t A[4], B[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const uint32_t l8 = (uint32_t)__builtin_amdgcn_mov_dpp((int)G[0][h][e], 0x128, 0xF, 0xF, false);
+                        const uint32_t r8 = (uint32_t)__builtin_amdgcn_mov_dpp((int)G[1][h][e], 0x128, 0xF, 0xF, false);
+                        A[e] = b3 ? r8 : G[0][h][e];
+                        B[e] = b3 ? G[1][h][e] : l8;
+                    }
+                    put(rb + 16 * h, col, A[0], A[1], A[2], A[3]);
+                    put(rb + 16 * h + 8, col, B[0], B[1], B[2], B[3]);
                 }
             }
         }
