@@ -27,17 +27,27 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC] + FLAGS + [os.path.join(CSRC, s) for s in SOURCES] + ["-o", tmp]
-    res = subprocess.run(cmd, capture_output=True, text=True)
+PROBE = os.path.join(HERE, "hbm_probe")
+
+
+def _hipcc(cmd, out, verbose):
+    tmp = out + ".tmp%d" % os.getpid()
+    res = subprocess.run([HIPCC] + cmd + ["-o", tmp], capture_output=True, text=True)
     # the host pass does not know the packed-fp32 feature name and says so
     err = "\n".join(l for l in res.stderr.splitlines() if "not a recognized feature" not in l)
     if res.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + err)
     if verbose and err.strip():
         print(err, file=sys.stderr)
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    _hipcc(FLAGS + [os.path.join(CSRC, s) for s in SOURCES], LIB, verbose)
+    # the HBM-rate probe the quantizers' rooflines are read against (an
+    # executable, not part of the library; bench.py --hbm-ceiling runs it)
+    probe_flags = [f for f in FLAGS if f not in ("-fPIC", "-shared")]
+    _hipcc(probe_flags + [os.path.join(CSRC, "hbm_probe.hip")], PROBE, verbose)
     return LIB
 
 

@@ -1,0 +1,130 @@
+// hbm_probe.hip -- measurement helper, not part of libmx355: the HBM rate
+// this part reaches for the quantizers' memory access patterns, with no
+// arithmetic in the way, as the ceiling their roofline fractions are read
+// against.  Built by build.py into an executable; bench.py --hbm-ceiling
+// runs it.  Each pattern streams a 755 MB bf16 tensor (65536 x 5760, three
+// times the 256 MB Infinity Cache), 10 launches back to back, best of 3.
+//
+//   row1d   per 32-element block: 64 bytes read, 16 code bytes + 1 scale
+//           byte written (the row-wise quantizer's lane mapping: four lanes
+//           a block, 16 bytes each)
+//   two2d   per 32 x 32 tile: 2 KiB read, two 512-byte code layouts and
+//           two scale bytes written (the 2D quantizer's byte mix)
+//   read    read only (16-byte loads)
+//   copy    1:1 copy (16-byte loads and stores)
+//
+// Output: one JSON line per pattern, bytes counted as read + written.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdio.h>
+
+namespace {
+
+constexpr double PEAK_GBS = 8000.0;   // MI355X HBM3E
+
+__global__ __launch_bounds__(256) void row1d(const uint4* __restrict__ x, int64_t nblocks,
+                                             uint32_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+    const int lane = threadIdx.x & 63, q = lane & 3;
+    const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6), nwaves = (int64_t)gridDim.x * 4;
+    for (int64_t base = wave * 64; base < nblocks; base += nwaves * 64) {
+        uint4 w[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int64_t blk = base + u * 16 + (lane >> 2);
+            w[u] = blk < nblocks ? x[blk * 4 + q] : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int64_t blk = base + u * 16 + (lane >> 2);
+            if (blk < nblocks) {
+                codes[blk * 4 + q] = w[u].x ^ w[u].y ^ w[u].z ^ w[u].w;
+                if (q == 0) scales[blk] = (uint8_t)(w[u].x >> 23);
+            }
+        }
+    }
+}
+
+// one thread per 32-element row of a tile: 64 bytes in, 16 bytes to each
+// code layout; lane 0 of every 32 writes the two scale bytes
+__global__ __launch_bounds__(256) void two2d(const uint4* __restrict__ x, int64_t nrows32,
+                                             uint4* __restrict__ codes, uint4* __restrict__ codes_t,
+                                             uint8_t* __restrict__ scales) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < nrows32; i += (int64_t)gridDim.x * 256) {
+        const uint4 a = x[4 * i], b = x[4 * i + 1], c = x[4 * i + 2], d = x[4 * i + 3];
+        const uint4 v = make_uint4(a.x ^ b.y, c.z ^ d.w, a.y ^ c.x, b.z ^ d.x);
+        codes[i] = v;
+        codes_t[i] = make_uint4(v.y, v.x, v.w, v.z);
+        if ((threadIdx.x & 31) == 0) {
+            scales[2 * (i >> 5)] = (uint8_t)v.x;
+            scales[2 * (i >> 5) + 1] = (uint8_t)v.y;
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void read_only(const uint4* __restrict__ x, int64_t n16, uint32_t* __restrict__ sink) {
+    uint32_t acc = 0;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (int64_t)gridDim.x * 256) {
+        const uint4 w = x[i];
+        acc ^= w.x ^ w.y ^ w.z ^ w.w;
+    }
+    if (acc == 0x9E3779B9u) sink[0] = acc;     // keeps the loads; never true for the fill below
+}
+
+__global__ __launch_bounds__(256) void copy16(const uint4* __restrict__ x, int64_t n16, uint4* __restrict__ y) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (int64_t)gridDim.x * 256) y[i] = x[i];
+}
+
+#define CHECK(call)                                                             \
+    do {                                                                        \
+        if ((call) != hipSuccess) {                                             \
+            fprintf(stderr, "hbm_probe: %s failed\n", #call);                   \
+            return 1;                                                           \
+        }                                                                       \
+    } while (0)
+
+}  // namespace
+
+int main() {
+    const int64_t elems = 65536LL * 5760;
+    const int64_t nblocks = elems / 32, n16 = elems * 2 / 16;
+    uint4 *x = nullptr, *y = nullptr, *c2 = nullptr;
+    uint32_t* codes = nullptr;
+    uint8_t* scales = nullptr;
+    CHECK(hipMalloc(&x, elems * 2));
+    CHECK(hipMalloc(&y, elems * 2));
+    CHECK(hipMalloc(&c2, elems / 2));
+    CHECK(hipMalloc(&codes, elems / 2));
+    CHECK(hipMalloc(&scales, nblocks));
+    CHECK(hipMemset(x, 0x3C, elems * 2));      // bf16 1.18 everywhere
+    hipEvent_t s, e;
+    CHECK(hipEventCreate(&s));
+    CHECK(hipEventCreate(&e));
+    const int grid = 8192;
+    const char* names[4] = {"row1d", "two2d", "read", "copy"};
+    const double bytes[4] = {elems * (2.0 + 0.5 + 1.0 / 32), elems * (2.0 + 1.0 + 2.0 / 1024), elems * 2.0,
+                             elems * 4.0};
+    for (int p = 0; p < 4; ++p) {
+        float best = 1e30f;
+        for (int rep = 0; rep < 3; ++rep) {
+            CHECK(hipEventRecord(s));
+            for (int k = 0; k < 10; ++k) {
+                if (p == 0) hipLaunchKernelGGL(row1d, dim3(grid), dim3(256), 0, 0, x, nblocks, codes, scales);
+                if (p == 1)
+                    hipLaunchKernelGGL(two2d, dim3(grid), dim3(256), 0, 0, x, nblocks, (uint4*)codes, c2, scales);
+                if (p == 2) hipLaunchKernelGGL(read_only, dim3(grid), dim3(256), 0, 0, x, n16, codes);
+                if (p == 3) hipLaunchKernelGGL(copy16, dim3(grid), dim3(256), 0, 0, x, n16, y);
+            }
+            CHECK(hipGetLastError());
+            CHECK(hipEventRecord(e));
+            CHECK(hipEventSynchronize(e));
+            float ms = 0;
+            CHECK(hipEventElapsedTime(&ms, s, e));
+            if (ms < best) best = ms;
+        }
+        const double sec = best / 10 / 1e3, gbs = bytes[p] / sec / 1e9;
+        printf("{\"pattern\": \"%s\", \"bytes\": %.0f, \"us\": %.1f, \"GBps\": %.0f, \"frac_hbm\": %.3f}\n", names[p],
+               bytes[p], sec * 1e6, gbs, gbs / PEAK_GBS);
+    }
+    CHECK(hipDeviceSynchronize());
+    return 0;
+}

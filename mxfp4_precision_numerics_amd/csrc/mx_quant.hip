@@ -125,6 +125,10 @@ __device__ __forceinline__ void q1d_row_body(const void* __restrict__ x, int64_t
                 for (int e = 0; e < 8; ++e) v[u][e] = 0.0f;
             }
         }
+        // every lane of a quad holds its block's scale byte; after the trip,
+        // lane q stores the byte of step u = q (64 consecutive blocks per wave)
+        static_assert(ROW_UNROLL == 4, "one scale store per quad lane");
+        uint32_t sbyte[ROW_UNROLL];
 #pragma unroll
         for (int u = 0; u < ROW_UNROLL; ++u) {
             const int64_t blk = base + u * 16 + (lane >> 2);
@@ -157,24 +161,35 @@ __device__ __forceinline__ void q1d_row_body(const void* __restrict__ x, int64_t
                 packed = cvt8_rne(t, sc);
             }
             if (byte == 0xFFu) packed = 0;   // non-finite block: codes are 0
+            sbyte[u] = byte;
             if (blk < nblocks) {
-                int64_t srow = 0, sb = 0;     // staged scales: the block's row and its block in the row
                 if (PITCH == 2) {
                     const int32_t o = u * 16 + (lane >> 2);
                     const uint32_t rel = (uint32_t)o * 16u + (o >= thr ? (uint32_t)rp.pad : 0u);
                     *((uint32_t*)(cbase + rel) + q) = packed;
-                    srow = row0 + (o >= thr ? 1 : 0);
-                    sb = o >= thr ? o - thr : b0 + o;
                 } else {
                     const int64_t cofs = PITCH ? pofs : blk * 16;
                     *((uint32_t*)(codes + cofs) + q) = packed;
-                    if (rp.srows) split_block(blk, rp, srow, sb);
                 }
-                if (q == 0) {
-                    if (rp.srows)
-                        scales[((uint32_t)(sb >> 3) * rp.srows + (uint32_t)srow) * 8u + (uint32_t)(sb & 7)] = (uint8_t)byte;
-                    else
-                        scales[blk] = (uint8_t)byte;
+            }
+        }
+        {
+            const int64_t blk = base + q * 16 + (lane >> 2);
+            const uint32_t byte = q == 0 ? sbyte[0] : q == 1 ? sbyte[1] : q == 2 ? sbyte[2] : sbyte[3];
+            if (blk < nblocks) {
+                if (rp.srows) {
+                    // staged scales: the block's row and its block in the row
+                    int64_t srow, sb;
+                    if (PITCH == 2) {
+                        const int32_t o = q * 16 + (lane >> 2);
+                        srow = row0 + (o >= thr ? 1 : 0);
+                        sb = o >= thr ? o - thr : b0 + o;
+                    } else {
+                        split_block(blk, rp, srow, sb);
+                    }
+                    scales[((uint32_t)(sb >> 3) * rp.srows + (uint32_t)srow) * 8u + (uint32_t)(sb & 7)] = (uint8_t)byte;
+                } else {
+                    scales[blk] = (uint8_t)byte;
                 }
             }
         }
