@@ -82,7 +82,9 @@ def build_inputs(torch, dev):
     dY1 = (torch.randn(ROWS, F2, device=dev, generator=g5) * 1e-3).to(torch.bfloat16)
     dY2 = (torch.randn(ROWS, D, device=dev, generator=g5) * 1e-3).to(torch.bfloat16)
     idx_d = torch.from_numpy(idx).to(dev)
-    pad = (counts + 31) // 32 * 32
+    # the weight gradient's K segments: each expert's tokens padded to 256, so
+    # every K stage of its GEMM starts on whole 128-byte code lines
+    pad = (counts + 255) // 256 * 256
     poff = np.concatenate([[0], np.cumsum(pad)]).astype(np.int32)
     return dict(X=X, W1=W1, W2=W2, h=h, dY1=dY1, dY2=dY2, counts=counts,
                 off=torch.from_numpy(off).to(dev), idx=idx_d,
@@ -103,7 +105,7 @@ class Step:
             # operand row as whole lines); a view of the row's bytes
             return z(*s[:-1], (s[-1] + 127) // 128 * 128)[..., :s[-1]]
 
-        self.kp = mx.padded_capacity(ROWS, E)
+        self.kp = mx.padded_capacity(ROWS, E, 256)
         self.mask = mx.rht_sign_mask(5)
         self.b = dict(
             w1c=zc(E, D, F2 // 2), w1s=z(E, D // 32, F2 // 32), w1tc=zc(E, F2, D // 2),
@@ -148,7 +150,8 @@ class Step:
         # (mx_quantize_1d_dual, one read) was measured slower: the row pass's
         # work lands on the busy unit, and the read it saves was not the
         # limit (see dual_quantize in the bench line).
-        col = dict(block_axis=0, group_offsets=off, kp=self.kp, use_rht=True, sign_mask=m, rnd=mx.SR, seed=5)
+        col = dict(block_axis=0, group_offsets=off, kp=self.kp, use_rht=True, sign_mask=m, rnd=mx.SR, seed=5,
+                   group_pad=256)
         self._t("q2d", lambda: mx.quantize_2d_into(i["W1"], b["w1c"], b["w1s"], b["w1tc"], b["w1ts"]))
         self._t("q2d", lambda: mx.quantize_2d_into(i["W2"], b["w2c"], b["w2s"], b["w2tc"], b["w2ts"]))
         self._t("q1d_row_rtne", lambda: mx.quantize_1d(i["X"], codes=b["xc"], scales=b["xs"]))

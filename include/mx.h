@@ -84,8 +84,12 @@ typedef enum { MX_RNE = 0, MX_SR = 1 } mx_round;
  *   stage of a 256-row GEMM tile is 2 KiB of contiguous memory, read by a
  *   few whole-line requests, instead of 256 separate 8-byte pieces, one
  *   memory request each.
- * MX_SCALES_B_2D: the GEMM's B operand has 2D (32x32) scales. */
-enum { MX_SCALES_B_2D = 1, MX_SCALES_STAGED = 2 };
+ * MX_SCALES_B_2D: the GEMM's B operand has 2D (32x32) scales.
+ * MX_GROUPS_PAD256 (column-wise quantize only): each group's token segment
+ *   is zero-padded to a multiple of 256 tokens instead of 32, so every K
+ *   stage of the weight-gradient GEMM starts on a whole 128-byte line of
+ *   codes (its group offsets are then the 256-padded starts). */
+enum { MX_SCALES_B_2D = 1, MX_SCALES_STAGED = 2, MX_GROUPS_PAD256 = 4 };
 
 /* HIP stream handle (hipStream_t) passed as an opaque pointer. */
 typedef void* mx_stream;
@@ -142,6 +146,10 @@ mx_status mx_rht(const void* x, mx_dtype xt, float* y, int64_t rows, int64_t col
  *   R = rows, scales holds ceil(cols/256) * rows * 8 bytes.  Column-wise:
  *   per-group stages, R = cols, scales holds (kp/256 + num_groups) * cols * 8
  *   bytes.  Padding slots are not written.
+ * block_axis = 0 | MX_GROUPS_PAD256 (may be combined with the staged flag):
+ *   groups padded to multiples of 256 tokens (ceil256 in place of ceil32
+ *   above; kp >= sum_g ceil256(n_g), rows + 255 * num_groups always
+ *   suffices).  Row-wise: MX_ERR_SHAPE.
  * use_rht != 0 applies the RHT (sign_mask) to each block before quantizing.
  * rnd: MX_RNE or MX_SR (seed, stream_id, index_base as above; index_base %
  *   32 == 0).

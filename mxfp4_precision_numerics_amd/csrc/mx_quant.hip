@@ -331,6 +331,8 @@ struct ColArgs {
     uint64_t row_index_base;
     // scales in the staged layout (each group's blocks start a new stage of 8)
     int staged;
+    // blocks per group padding unit: 1 (groups padded to 32 tokens) or 8 (256)
+    int pad_blocks;
 };
 
 template <bool BF16, bool RHT, bool SR, int ROWQ>
@@ -365,8 +367,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BF16 ? 3 : 
         const int chunk = (num_groups + 255) / 256;
         const int g0 = min(num_groups, tid * chunk), g1 = min(num_groups, g0 + chunk);
         int32_t local = 0, slocal = 0;
-        for (int g = g0; g < g1; ++g) {
+        const int32_t pu = a.pad_blocks;
+        auto padded_blocks = [&](int g) {
             const int32_t nb = (off[g + 1] - off[g] + 31) >> 5;
+            return pu == 8 ? (nb + 7) & ~7 : nb;
+        };
+        for (int g = g0; g < g1; ++g) {
+            const int32_t nb = padded_blocks(g);
             local += nb;
             slocal += (nb + 7) >> 3;
         }
@@ -390,7 +397,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BF16 ? 3 : 
             srun += wave_ssum[w];
         }
         for (int g = g0; g < g1; ++g) {
-            const int32_t nb = (off[g + 1] - off[g] + 31) >> 5;
+            const int32_t nb = padded_blocks(g);
             pstart[g] = run;
             run += nb;
             if (staged) sstart[g] = srun;
@@ -1337,7 +1344,9 @@ mx_status mx_quantize_1d(const void* x, mx_dtype xt, int64_t rows, int64_t cols,
     const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
     hipStream_t s = (hipStream_t)stream;
     const bool staged = (block_axis & MX_SCALES_STAGED) != 0;
-    block_axis &= ~MX_SCALES_STAGED;
+    const bool pad256 = (block_axis & MX_GROUPS_PAD256) != 0;
+    block_axis &= ~(MX_SCALES_STAGED | MX_GROUPS_PAD256);
+    if (pad256 && block_axis != 0) return MX_ERR_SHAPE;
     if (block_axis == 1) {
         if (cols % 32) return MX_ERR_SHAPE;
         if (group_offsets || num_groups || kp) return MX_ERR_SHAPE;
@@ -1382,7 +1391,7 @@ mx_status mx_quantize_1d(const void* x, mx_dtype xt, int64_t rows, int64_t cols,
     if (!aligned16(x) || !aligned16(codes)) return MX_ERR_ALIGN;
     if (cols > (int64_t)(0xFFFFFFFFu / (bf ? 2u : 4u))) return MX_ERR_SHAPE;   // one row of x within 4 GiB
     ColArgs a{x, cols, group_offsets, (int)num_groups, row_index, rows, kp, 0, 0, sign_mask, k0, k1, stream_id,
-              index_base, codes, scales, nullptr, 0, nullptr, 0, 0, staged ? 1 : 0};
+              index_base, codes, scales, nullptr, 0, nullptr, 0, 0, staged ? 1 : 0, pad256 ? 8 : 1};
     return launch_col(a, bf, rh, sr, 0, s);
 }
 
@@ -1408,7 +1417,7 @@ mx_status mx_quantize_1d_dual(const void* x, mx_dtype xt, int64_t rows, int64_t 
     if (cols > (int64_t)(0xFFFFFFFFu / (bf ? 2u : 4u))) return MX_ERR_SHAPE;
     ColArgs a{x, cols, group_offsets, (int)num_groups, nullptr, rows, kp, 0, 0, sign_mask, (uint32_t)seed,
               (uint32_t)(seed >> 32), col_stream_id, col_index_base, col_codes, col_scales, row_codes, ld, row_scales,
-              row_stream_id, row_index_base};
+              row_stream_id, row_index_base, 0, 1};
     return launch_col(a, bf, use_rht != 0, col_rnd == MX_SR, row_rnd == MX_SR ? 2 : 1, (hipStream_t)stream);
 }
 

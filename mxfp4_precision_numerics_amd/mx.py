@@ -17,8 +17,9 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "mx.h")
 
 MX_F32, MX_BF16 = 0, 1
 RNE, SR = 0, 1
-# scale storage orders (include/mx.h): 2D B scales; staged ([stage][row][8 bytes])
-SCALES_B_2D, SCALES_STAGED = 1, 2
+# scale storage orders (include/mx.h): 2D B scales; staged ([stage][row][8 bytes]);
+# column-wise groups padded to 256 tokens
+SCALES_B_2D, SCALES_STAGED, GROUPS_PAD256 = 1, 2, 4
 STATUS = {0: "MX_OK", 1: "MX_ERR_NULL", 2: "MX_ERR_SHAPE", 3: "MX_ERR_ALIGN",
           4: "MX_ERR_DTYPE", 5: "MX_ERR_UNSUPPORTED", 6: "MX_ERR_LAUNCH"}
 
@@ -182,25 +183,28 @@ def _scale_flags(b_scale_2d, staged):
     return (SCALES_B_2D if b_scale_2d else 0) | (SCALES_STAGED if staged else 0)
 
 
-def padded_capacity(rows: int, num_groups: int) -> int:
+def padded_capacity(rows: int, num_groups: int, group_pad: int = 32) -> int:
     """A token capacity that holds any grouping of `rows` tokens into
-    `num_groups` groups each padded to a multiple of 32, rounded up to a
-    multiple of 256 tokens: every row of the column-wise codes is then a
-    whole number of 128-byte lines, and the number of 32-token blocks is even
-    (the grouped GEMM moves scale bytes in pairs)."""
-    return (rows + 31 * num_groups + 255) // 256 * 256
+    `num_groups` groups each padded to a multiple of group_pad (32 or 256),
+    rounded up to a multiple of 256 tokens: every row of the column-wise
+    codes is then a whole number of 128-byte lines, and the number of
+    32-token blocks is even (the grouped GEMM moves scale bytes in pairs)."""
+    return (rows + (group_pad - 1) * num_groups + 255) // 256 * 256
 
 
 def quantize_1d(x, block_axis: int = 1, group_offsets=None, kp: int = 0, use_rht: bool = False,
                 sign_mask: int = 0, rnd: int = RNE, seed: int = 0, stream_id: int = 0,
-                index_base: int = 0, codes=None, scales=None, row_index=None, staged: bool = False):
+                index_base: int = 0, codes=None, scales=None, row_index=None, staged: bool = False,
+                group_pad: int = 32):
     """Returns (codes, scales) uint8 device tensors; see mx_quantize_1d.
     row_index (column-wise only): gather x's rows through it; the grouped
     positions then number row_index.numel().  A row-wise codes output may
     have padded rows, e.g. buf[:, :cols // 2] of a wider buffer (its row
     stride, a multiple of 16, is passed as the pitch; the padding is not
     written).  staged: scales in the staged order (include/mx.h), row-wise
-    [ceil(cols / 256), rows, 8], column-wise [kp // 256 + groups, cols, 8]."""
+    [ceil(cols / 256), rows, 8], column-wise [kp // 256 + groups, cols, 8].
+    group_pad (column-wise): 32, or 256 to start every group on a whole K
+    stage of the weight-gradient GEMM."""
     torch = _torch()
     _dev(x, "x")
     rows, cols = x.shape
@@ -215,8 +219,10 @@ def quantize_1d(x, block_axis: int = 1, group_offsets=None, kp: int = 0, use_rht
     else:
         _index_vector(group_offsets, "group_offsets", min_numel=2)
         ng = group_offsets.numel() - 1
+        if group_pad not in (32, 256):
+            raise ValueError("group_pad is 32 or 256")
         if not kp:
-            kp = padded_capacity(rows, ng)
+            kp = padded_capacity(rows, ng, group_pad)
         shape_c, shape_s = (cols, kp // 2), (cols, kp // 32)
         if staged:
             shape_s = (kp // 256 + ng, cols, 8)
@@ -228,7 +234,9 @@ def quantize_1d(x, block_axis: int = 1, group_offsets=None, kp: int = 0, use_rht
     codes_ld = _shaped(codes, shape_c, torch.uint8, "codes", pitched=True)
     _shaped(scales, shape_s, torch.uint8, "scales")
     _check("mx_quantize_1d", lib().mx_quantize_1d(
-        _ptr(x), _dtype_code(x), rows, cols, block_axis | (SCALES_STAGED if staged else 0), _ptr(group_offsets), ng, kp,
+        _ptr(x), _dtype_code(x), rows, cols,
+        block_axis | (SCALES_STAGED if staged else 0) | (GROUPS_PAD256 if group_pad == 256 else 0),
+        _ptr(group_offsets), ng, kp,
         _ptr(row_index), int(use_rht), sign_mask, rnd, seed, stream_id, index_base, _ptr(codes), codes_ld,
         _ptr(scales), _stream()))
     return codes, scales

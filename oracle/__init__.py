@@ -62,7 +62,7 @@ def lib():
         L.oracle_scale_byte.restype = ctypes.c_uint8
         L.oracle_rtne_mag.argtypes = [ctypes.c_double]
         L.oracle_sr_mag.argtypes = [ctypes.c_double, u32]
-        L.oracle_quantize_1d.argtypes = [P, ctypes.c_int, i64, i64, ctypes.c_int, P, i32, i64,
+        L.oracle_quantize_1d.argtypes = [P, ctypes.c_int, i64, i64, ctypes.c_int, P, i32, i64, i32,
                                          ctypes.c_int, u32, ctypes.c_int, u64, u32, u64,
                                          P, P, i64, i64]
         L.oracle_quantize_2d.argtypes = [P, ctypes.c_int, i64, i64, i64, P, P, P, P, i64, i64]
@@ -165,20 +165,21 @@ def _dtype_code(x):
 # --------------------------------------------------------------------------
 # Quantizers
 # --------------------------------------------------------------------------
-def padded_total(group_offsets) -> int:
+def padded_total(group_offsets, group_pad: int = 32) -> int:
     off = np.asarray(group_offsets, dtype=np.int64)
     n = np.diff(off)
-    return int(np.sum((n + 31) // 32 * 32))
+    return int(np.sum((n + group_pad - 1) // group_pad * group_pad))
 
 
 def quantize_1d(x, block_axis: int = 1, group_offsets=None, kp: int | None = None,
                 use_rht: bool = False, sign_mask: int = 0, rnd: int = RNE,
                 seed: int = 0, stream: int = 0, index_base: int = 0,
-                threads: int | None = None):
+                threads: int | None = None, group_pad: int = 32):
     """1x32 quantization (see mx_oracle.c, oracle_quantize_1d).
 
     Returns (codes uint8, scales uint8).  For block_axis=0 the outputs are the
-    transposed, per-group padded layout [cols x kp/2] and [cols x kp/32];
+    transposed, per-group padded layout [cols x kp/2] and [cols x kp/32],
+    each group padded to a multiple of group_pad tokens (32 or 256);
     entries beyond the padded total stay 0 here."""
     x = np.ascontiguousarray(x)
     rows, cols = x.shape
@@ -192,7 +193,7 @@ def quantize_1d(x, block_axis: int = 1, group_offsets=None, kp: int | None = Non
         off = np.ascontiguousarray(
             np.asarray(group_offsets if group_offsets is not None else [0, rows], dtype=np.int32))
         ng = len(off) - 1
-        kp_ = padded_total(off) if kp is None else int(kp)
+        kp_ = padded_total(off, group_pad) if kp is None else int(kp)
         qr, qc = cols, kp_
     codes = np.zeros((qr, qc // 2), dtype=np.uint8)
     scales = np.zeros((qr, qc // 32), dtype=np.uint8)
@@ -201,18 +202,18 @@ def quantize_1d(x, block_axis: int = 1, group_offsets=None, kp: int | None = Non
 
     def job(a, b):
         return lambda: L.oracle_quantize_1d(
-            _ptr(x), dt, rows, cols, block_axis, _ptr(off), ng, kp_, int(use_rht),
+            _ptr(x), dt, rows, cols, block_axis, _ptr(off), ng, kp_, group_pad, int(use_rht),
             sign_mask, rnd, seed, stream, index_base, _ptr(codes), _ptr(scales), a, b)
 
     _run([job(a, b) for a, b in _split(qr, threads * 4)], threads)
     return codes, scales
 
 
-def stage_scales(scales, group_offsets=None, stages: int | None = None, fill: int = 0):
+def stage_scales(scales, group_offsets=None, stages: int | None = None, fill: int = 0, group_pad: int = 32):
     """The staged storage order of a row-major scale matrix (mx_oracle.c,
     oracle_stage_scales): [stages, rows, 8].  group_offsets: token offsets
-    of the column-wise grouped layout (each group padded to 32 tokens, so
-    group g's blocks start at its padded start / 32); None: one group per
+    of the column-wise grouped layout (each group padded to group_pad
+    tokens, so group g's blocks start at its padded start / 32); None: one group per
     row.  stages: the array's stage count (default: the number the mapping
     uses); slots no block maps to hold `fill`."""
     sc = np.ascontiguousarray(scales, dtype=np.uint8)
@@ -222,7 +223,8 @@ def stage_scales(scales, group_offsets=None, stages: int | None = None, fill: in
         used = (nblk + 7) // 8
     else:
         n = np.diff(np.asarray(group_offsets, dtype=np.int64))
-        gb = np.ascontiguousarray(np.concatenate([[0], np.cumsum((n + 31) // 32)]).astype(np.int64))
+        gb = np.ascontiguousarray(np.concatenate(
+            [[0], np.cumsum((n + group_pad - 1) // group_pad * (group_pad // 32))]).astype(np.int64))
         ng = len(n)
         used = int(np.sum((np.diff(gb) + 7) // 8))
     st = used if stages is None else int(stages)

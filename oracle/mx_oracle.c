@@ -248,7 +248,9 @@ static uint8_t quantize_block(const float* v, int n, int rnd, const uint32_t* r1
 /*   [rows x cols/32].                                                  */
 /* block_axis = 0: the rows of x are split into groups by offsets       */
 /*   off[0..G] (off[0] = 0, off[G] = rows); each group is zero-padded   */
-/*   to a multiple of 32 rows; Q = [cols x kp] with Q[c][P_g + r] =     */
+/*   to a multiple of group_pad rows (32, or 256 so that every 256-     */
+/*   token K stage of the weight gradient starts a group's segment on a  */
+/*   whole 128-byte line of codes); Q = [cols x kp] with Q[c][P_g + r] = */
 /*   x[off[g] + r][c], P_g the padded start of group g; 32-blocks run   */
 /*   along Q's rows (i.e. down the token axis of one group).  codes     */
 /*   [cols x kp/2], scales [cols x kp/32]; positions of Q beyond the    */
@@ -259,7 +261,7 @@ static uint8_t quantize_block(const float* v, int n, int rnd, const uint32_t* r1
 /* ------------------------------------------------------------------ */
 int oracle_quantize_1d(const void* x, int dtype, int64_t rows, int64_t cols,
                        int block_axis, const int32_t* off, int32_t num_groups,
-                       int64_t kp, int use_rht, uint32_t mask, int rnd,
+                       int64_t kp, int32_t group_pad, int use_rht, uint32_t mask, int rnd,
                        uint64_t seed, uint32_t stream, uint64_t index_base,
                        uint8_t* codes, uint8_t* scales,
                        int64_t q_row_begin, int64_t q_row_end)
@@ -271,7 +273,7 @@ int oracle_quantize_1d(const void* x, int dtype, int64_t rows, int64_t cols,
         q_cols = cols;
     } else {
         q_cols = kp;
-        if (kp % 32) return 2;
+        if (kp % 32 || group_pad <= 0 || group_pad % 32) return 2;
     }
     float v[32], t[32];
     uint32_t r16[32];
@@ -288,7 +290,7 @@ int oracle_quantize_1d(const void* x, int dtype, int64_t rows, int64_t cols,
                 int g = -1;
                 for (int gg = 0; gg < num_groups; ++gg) {
                     int64_t n = (int64_t)off[gg + 1] - off[gg];
-                    int64_t np = (n + 31) / 32 * 32;
+                    int64_t np = (n + group_pad - 1) / group_pad * group_pad;
                     if (b * 32 >= p && b * 32 < p + np) { g = gg; break; }
                     p += np;
                 }

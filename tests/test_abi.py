@@ -70,7 +70,10 @@ def test_quantize_1d_validation(L):
              None) == 2
     assert q(FAKE, mx.MX_BF16, 4, 33, 1 | mx.SCALES_STAGED, None, 0, 0, None, 0, 0, 0, 0, 0, 0, FAKE, 0, FAKE,
              None) == 2
-    assert q(FAKE, mx.MX_BF16, 4, 32, 4, None, 0, 0, None, 0, 0, 0, 0, 0, 0, FAKE, 0, FAKE, None) == 2
+    assert q(FAKE, mx.MX_BF16, 4, 32, 8, None, 0, 0, None, 0, 0, 0, 0, 0, 0, FAKE, 0, FAKE, None) == 2
+    # groups padded to 256 tokens: column-wise only
+    assert q(FAKE, mx.MX_BF16, 4, 32, 1 | mx.GROUPS_PAD256, None, 0, 0, None, 0, 0, 0, 0, 0, 0, FAKE, 0, FAKE,
+             None) == 2
     assert q(FAKE, mx.MX_BF16, 4, 32, 0 | mx.SCALES_STAGED, FAKE, 2, 40, None, 0, 0, 0, 0, 0, 0, FAKE, 0, FAKE,
              None) == 2
     # empty input is a no-op that launches nothing

@@ -288,3 +288,65 @@ def test_step_chain_staged_rowwise_then_dgrad():
         gc, gs = mx.quantize_1d(dy, rnd=mx.SR, seed=5, stream_id=1, staged=staged, codes=wide[:, :K // 2])
         outs.append(mx.grouped_gemm(gc, gs, bcd, bsd, off, M, N, K, b_scale_2d=True, staged=staged))
     assert torch.equal(outs[0], outs[1])
+
+
+@pytest.mark.parametrize("staged,rnd,gather", [(True, mx.SR, True), (False, mx.SR, False), (True, mx.RNE, False)])
+def test_colwise_groups_padded_to_256_match_oracle(staged, rnd, gather):
+    """Column-wise quantize with every group padded to 256 tokens (the
+    layout the step's weight gradient reads): codes and scales against the
+    oracle with the same padding, ragged and empty groups."""
+    import torch
+    rng = np.random.default_rng(31 + int(staged))
+    counts = [300, 0, 17, 700, 256, 1]
+    off = synth.offsets_from_counts(counts)
+    rows, cols, G = int(off[-1]), 96, len(counts)
+    src_rows = rows + 5
+    xb = synth.f32_to_bf16_bits(rng.standard_normal((src_rows, cols)).astype(np.float32))
+    idx = rng.permutation(src_rows)[:rows].astype(np.int32) if gather else None
+    kp = mx.padded_capacity(rows, G, 256)
+    mask = mx.rht_sign_mask(7)
+    S = kp // 256 + G
+    sbuf = torch.full((S, cols, 8) if staged else (cols, kp // 32), JUNK, dtype=torch.uint8, device="cuda")
+    c, s = mx.quantize_1d(dev_bf16(xb), block_axis=0, group_offsets=dev(off), kp=kp, use_rht=True, sign_mask=mask,
+                          rnd=rnd, seed=4, stream_id=3, row_index=None if idx is None else dev(idx), staged=staged,
+                          group_pad=256, scales=sbuf)
+    xg = xb if idx is None else xb[idx]
+    oc, os_ = oracle.quantize_1d(xg, block_axis=0, group_offsets=off, kp=kp, use_rht=True, sign_mask=mask, rnd=rnd,
+                                 seed=4, stream=3, group_pad=256)
+    tot = oracle.padded_total(off, 256)
+    assert np.array_equal(host(c)[:, :tot // 2], oc[:, :tot // 2])
+    if staged:
+        want = oracle.stage_scales(os_, off, stages=S, fill=JUNK, group_pad=256)
+        m = oracle.stage_scales(np.ones_like(os_), off, stages=S, fill=0, group_pad=256).astype(bool)
+        got = host(s)
+        assert np.array_equal(got[m], want[m]) and np.all(got[~m] == JUNK)
+    else:
+        assert np.array_equal(host(s)[:, :tot // 32], os_[:, :tot // 32])
+
+
+def test_step_chain_groups_padded_to_256():
+    """The weight-gradient chain with groups padded to 256 tokens and staged
+    scales equals, bit for bit, the chain with 32-token padding and row-major
+    scales moved one byte at a time: the same products over the same K
+    stages (every group starts a stage in both), only placed differently."""
+    import torch
+    rng = np.random.default_rng(9)
+    counts = np.array([700, 0, 45, 300, 1200, 33])
+    off = synth.offsets_from_counts(counts)
+    rows, G = int(off[-1]), len(counts)
+    T, D, F = 900, 160, 224
+    x = dev_bf16(synth.f32_to_bf16_bits(rng.standard_normal((T, D)).astype(np.float32)))
+    dy = dev_bf16(synth.f32_to_bf16_bits((rng.standard_normal((rows, F)) * 1e-3).astype(np.float32)))
+    idx = dev(synth.routing_row_index(counts, n_tokens=T))
+    outs = []
+    for pad, staged in ((256, True), (32, False)):
+        kp = mx.padded_capacity(rows, G, pad)
+        poff = dev(np.concatenate([[0], np.cumsum((counts + pad - 1) // pad * pad)]).astype(np.int32))
+        col = dict(block_axis=0, group_offsets=dev(off), kp=kp, rnd=mx.RNE, group_pad=pad, staged=staged)
+        xc, xs = mx.quantize_1d(x, row_index=idx, **col)
+        gc, gs = mx.quantize_1d(dy, **col)
+        if not staged:
+            xs, gs = _at_odd_address(xs), _at_odd_address(gs)
+        outs.append(mx.grouped_gemm(xc, xs, gc, gs, poff, D, F, kp, group_dim_k=True, staged=staged,
+                                    out_dtype=torch.float32))
+    assert torch.equal(outs[0], outs[1])

@@ -10,6 +10,11 @@ pages'; it permutes bytes and does no arithmetic.
   appended to fresh stages of 8, stage after stage), computed here by a
   different route: walking the blocks one by one with a running cursor;
 - every input byte lands exactly once and no two blocks share a slot.
+
+Also the column-wise layout with groups padded to 256 tokens: RTNE blocks
+equal those of the 32-token padding at the new starts with zero-filled
+padding blocks, and SR draws at the padded position (rebuilt element by
+element from the generator and the SR magnitude rule).
 """
 import os
 
@@ -104,3 +109,50 @@ def test_row_wise_is_one_group_per_row_and_extra_stages_stay_filled():
     assert np.array_equal(a, b[:3]) and np.all(b[3:] == 7)
     for r in range(3):
         assert np.array_equal(a[:, r, :].reshape(-1)[:19], sc[r])
+
+
+def test_group_pad_256_places_blocks_and_zero_fills():
+    """Groups padded to 256 tokens (the layout whose weight-gradient K stages
+    start on whole code lines): with RTNE, which does not depend on position,
+    each group's blocks equal those of the 32-token padding at the group's
+    new start, and the blocks between a group's 32-padded and 256-padded ends
+    are all-zero codes with scale byte 0 (amax 0)."""
+    rng = np.random.default_rng(11)
+    counts = [100, 0, 257, 31]
+    off = np.concatenate([[0], np.cumsum(counts)])
+    x = rng.standard_normal((int(off[-1]), 40)).astype(np.float32)
+    c32, s32 = oracle.quantize_1d(x, block_axis=0, group_offsets=off)
+    c256, s256 = oracle.quantize_1d(x, block_axis=0, group_offsets=off, group_pad=256)
+    assert s256.shape == (40, (256 + 0 + 512 + 256) // 32)
+    p32 = p256 = 0
+    for n in counts:
+        b32, b256 = (n + 31) // 32, (n + 255) // 256 * 8
+        assert np.array_equal(s256[:, p256:p256 + b32], s32[:, p32:p32 + b32])
+        assert np.array_equal(c256[:, 16 * p256:16 * (p256 + b32)], c32[:, 16 * p32:16 * (p32 + b32)])
+        assert np.all(s256[:, p256 + b32:p256 + b256] == 0)
+        assert np.all(c256[:, 16 * (p256 + b32):16 * (p256 + b256)] == 0)
+        p32 += b32
+        p256 += b256
+
+
+def test_group_pad_256_sr_uses_the_padded_position():
+    """With SR each element draws its 16 bits at index c * kp + its padded
+    position: rebuilt here for a few elements from the generator and the SR
+    magnitude rule, for the third group (which starts at 512 when groups are
+    padded to 256, at 160 when padded to 32)."""
+    rng = np.random.default_rng(12)
+    counts = [100, 60, 300]
+    off = np.concatenate([[0], np.cumsum(counts)])
+    x = rng.standard_normal((int(off[-1]), 8)).astype(np.float32)
+    c, s = oracle.quantize_1d(x, block_axis=0, group_offsets=off, group_pad=256, rnd=oracle.SR, seed=7, stream=3)
+    kp = c.shape[1] * 2
+    assert kp == 256 + 256 + 512
+    for col, r in ((0, 0), (5, 37), (7, 299)):
+        pos = 512 + r
+        v = float(x[off[2] + r, col])
+        byte = int(s[col, pos // 32])
+        a = abs(v) / 2.0 ** (byte - 127)
+        mag = oracle.sr_mag(a, oracle.sr_bits(7, 3, col * kp + pos))
+        code = (c[col, pos // 2] >> (4 * (pos % 2))) & 0xF
+        assert code & 7 == mag
+        assert (code >> 3) == (1 if v < 0 else 0) or mag == 0
