@@ -506,6 +506,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BF16 ? 3 : 
     int64_t br = tbeg / col_tiles, ct = tbeg % col_tiles;
     uint4 pre[NLD];
     uint32_t pkb = 0;
+    int32_t splace = 0;          // staged scales: this lane's block placement (lanes 0..7)
+    int64_t splace_br = -1;      // the block row it was computed for
     if (vec && tbeg < tend) {
         rows_for(br * CT_BLOCKS);
         load_regs(pre, pkb, ct * CT_COLS);
@@ -514,17 +516,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BF16 ? 3 : 
         const int64_t pb0 = br * CT_BLOCKS;
         const int64_t c0 = ct * CT_COLS;
         // staged scales: lane b < 8 of every wave places block pb0 + b
-        // (stage << 3 | slot; the last group starting at or before it)
-        int32_t splace = 0;
-        if (staged && lane < CT_BLOCKS && pb0 + lane < nblk_total) {
-            const int64_t pb = pb0 + lane;
-            int lo = 0, hi = num_groups - 1;
-            while (lo < hi) {
-                const int mid = (lo + hi + 1) >> 1;
-                if (pstart[mid] <= pb) lo = mid; else hi = mid - 1;
+        // (stage << 3 | slot; the last group starting at or before it),
+        // once per block row (its column tiles share it)
+        if (staged && br != splace_br) {
+            splace_br = br;
+            splace = 0;
+            if (lane < CT_BLOCKS && pb0 + lane < nblk_total) {
+                const int64_t pb = pb0 + lane;
+                int lo = 0, hi = num_groups - 1;
+                while (lo < hi) {
+                    const int mid = (lo + hi + 1) >> 1;
+                    if (pstart[mid] <= pb) lo = mid; else hi = mid - 1;
+                }
+                const int32_t rel = (int32_t)(pb - pstart[lo]);
+                splace = ((sstart[lo] + (rel >> 3)) << 3) | (rel & 7);
             }
-            const int32_t rel = (int32_t)(pb - pstart[lo]);
-            splace = ((sstart[lo] + (rel >> 3)) << 3) | (rel & 7);
         }
 
         // ---- the tile into LDS (rows past a group's end, columns past cols: 0)
@@ -700,7 +706,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BF16 ? 3 : 
                 *(uint4*)(codes + (c0 + col) * (kp >> 1) + (pb0 + ch) * 16) =
                     *(const uint4*)(oc + col * CT_OUT_PITCH + ch * 16);
                 int64_t si = (c0 + col) * kp_blocks + pb0 + ch;
-                if (staged) si = ((int64_t)(pl >> 3) * cols + c0 + col) * 8 + (pl & 7);
+                // (the host keeps the staged array below 4 GiB: 32-bit offsets)
+                if (staged) si = (uint32_t)(((uint32_t)(pl >> 3) * (uint32_t)cols + (uint32_t)(c0 + col)) * 8u +
+                                            (uint32_t)(pl & 7));
                 scales[si] = os[col * CT_BLOCKS + ch];
             }
         }
@@ -1390,6 +1398,8 @@ mx_status mx_quantize_1d(const void* x, mx_dtype xt, int64_t rows, int64_t cols,
     if (!x || !codes || !scales) return MX_ERR_NULL;
     if (!aligned16(x) || !aligned16(codes)) return MX_ERR_ALIGN;
     if (cols > (int64_t)(0xFFFFFFFFu / (bf ? 2u : 4u))) return MX_ERR_SHAPE;   // one row of x within 4 GiB
+    // staged scales: at most kp/256 + num_groups stages of cols x 8 bytes, 32-bit offsets
+    if (staged && (kp / 256 + num_groups) * cols * 8 > (int64_t)0xFFFFFFFFu) return MX_ERR_SHAPE;
     ColArgs a{x, cols, group_offsets, (int)num_groups, row_index, rows, kp, 0, 0, sign_mask, k0, k1, stream_id,
               index_base, codes, scales, nullptr, 0, nullptr, 0, 0, staged ? 1 : 0, pad256 ? 8 : 1};
     return launch_col(a, bf, rh, sr, 0, s);
