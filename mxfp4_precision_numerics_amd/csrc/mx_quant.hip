@@ -794,7 +794,7 @@ __global__ __launch_bounds__(256) void q2d_kernel(const void* __restrict__ w, in
                                                   uint8_t* __restrict__ scales,
                                                   uint8_t* __restrict__ codes_t, int64_t ld_t,
                                                   uint8_t* __restrict__ scales_t, DeoscArgs dz) {
-    __shared__ uint32_t wave_amax[4][8];
+    __shared__ uint32_t wave_amax[Q2_TR][4][8];    // per tile row: each wave's maximum per tile
     __shared__ uint8_t tile_scale[Q2_TR][8];
     __shared__ float2 band[8];                      // DEOSC: (lo, hi) per previous magnitude code
     __shared__ uint32_t wave_flips[Q2_TR][4][8];    // DEOSC: flips per tile row, wave and tile
@@ -871,25 +871,22 @@ __global__ __launch_bounds__(256) void q2d_kernel(const void* __restrict__ w, in
             am = max(am, (uint32_t)__shfl_xor((int)am, 8));
             am = max(am, (uint32_t)__shfl_xor((int)am, 16));
             am = max(am, (uint32_t)__shfl_xor((int)am, 32));
-            if (lane < 8) wave_amax[wv][lane] = am;
+            if (lane < 8) wave_amax[ts][wv][lane] = am;
             __syncthreads();
-            if (t < 8) {
-                const uint32_t m = max(max(wave_amax[0][t], wave_amax[1][t]), max(wave_amax[2][t], wave_amax[3][t]));
-                uint32_t sbyte = scale_byte_from_amax_bits(m);
-                // DEOSC: an amax that dropped just below the previous scale's
-                // range (the rule one byte below the previous byte p, amax >=
-                // (4 - margin / 16) 2^(p - 127)) keeps p; every element then
-                // fits without clipping
-                if (DEOSC && cs * 8 + t < tiles_per_row) {
-                    const uint32_t p = dz.prev_scales[(bt * row_tiles + tr) * tiles_per_row + cs * 8 + t];
-                    if (p != 0xFFu && sbyte != 0xFFu && sbyte + 1u == p &&
-                        __uint_as_float(m) >= dz.scale_keep * __uint_as_float(p << 23))
-                        sbyte = p;
-                }
-                tile_scale[ts][t] = (uint8_t)sbyte;
-            }
-            __syncthreads();
-            const uint32_t byte = tile_scale[ts][j];
+            // Every thread forms its tile's scale from the four waves' maxima.
+            // Each tile row has its own slots, so no wave overwrites maxima
+            // another is still reading: one barrier per tile row.
+            const uint32_t m = max(max(wave_amax[ts][0][j], wave_amax[ts][1][j]),
+                                   max(wave_amax[ts][2][j], wave_amax[ts][3][j]));
+            uint32_t byte = scale_byte_from_amax_bits(m);
+            // DEOSC: an amax that dropped just below the previous scale's
+            // range (the rule one byte below the previous byte p, amax >=
+            // (4 - margin / 16) 2^(p - 127)) keeps p; every element then fits
+            // without clipping
+            if (DEOSC && valid && pbyte != 0xFFu && byte != 0xFFu && byte + 1u == pbyte &&
+                __uint_as_float(m) >= dz.scale_keep * __uint_as_float(pbyte << 23))
+                byte = pbyte;
+            if (t < 8) tile_scale[ts][t] = (uint8_t)byte;      // (r = 0, j = t) for the transposed scales
             const float sc = scale_operand(byte);
             // non-finite tile: codes are 0 (a mask, so the four converts stay
             // branch-free and the row's 16 code bytes go out as one store)
