@@ -104,13 +104,15 @@ constexpr int GROUP_M = 4;         // M-tiles per tile-order group
 constexpr int XCDS = 8;
 constexpr int XCD_BLOCK = 32;      // consecutive tile ids per XCD turn
 // one stage in LDS: A codes, B codes (256 rows x 128 bytes each), A and B
-// scales (256 rows x 8 dwords each; scales moved in pairs take 4 dwords)
+// scales (256 rows x 8 dwords each; scales moved in pairs take 4 dwords a
+// row, staged scales 2)
 constexpr int OFF_A = 0, OFF_B = 32768, OFF_AS = 65536, OFF_BS = 73728;
 constexpr int STAGE_BYTES = 81920;
 // DMA ops per thread per stage: 8 code moves (4 rows of each operand), 4
 // A-scale moves (one byte each) or 2 (SA2: two bytes each), and 4 or 2
 // (SA2) B-scale moves for 1D B scales, or 1 for 2D B scales (8 row groups
-// of 32 per tile).
+// of 32 per tile).  Staged scales (STG) take one dword move per operand
+// whose scales are staged: 10 in all (the other operand's being 2D).
 template <bool B2D, bool SA2>
 constexpr int dma_per_stage() { return 8 + (SA2 ? 2 : 4) + (B2D ? 1 : (SA2 ? 2 : 4)); }
 
@@ -322,9 +324,9 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs p) {
         }
     };
     // The A rows of this thread's DMA moves: entry j < NJ is code move j,
-    // row t/8 + (NT/8) j; with pair moves (SA2) entry NJ + j is scale move
-    // j, row 16 (j NW + w) + l/4 (w: wave, l: lane).
-    constexpr int NR = SA2 ? NJ + 2 : NJ;
+    // row t/8 + (NT/8) j; with A's scales moved in pairs (SA2, not staged)
+    // entry NJ + j is scale move j, row 16 (j NW + w) + l/4 (w: wave, l: lane).
+    constexpr int NR = SA2 && !STG ? NJ + 2 : NJ;
     auto load_rows = [&](const Tile& t, int32_t (&arow)[NR]) {
 #pragma unroll
         for (int jj = 0; jj < NR; ++jj) {
