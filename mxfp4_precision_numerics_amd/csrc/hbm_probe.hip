@@ -12,6 +12,9 @@
 //           two scale bytes written (the 2D quantizer's byte mix)
 //   read    read only (16-byte loads)
 //   copy    1:1 copy (16-byte loads and stores)
+//   write   write only (16-byte stores)
+//   w6r1    six bytes written per byte read (the fp32-output weight
+//           gradient's mix: about 1.6 GB written per 0.25 GB of operands)
 //
 // Output: one JSON line per pattern, bytes counted as read + written.
 #include <hip/hip_runtime.h>
@@ -70,6 +73,21 @@ __global__ __launch_bounds__(256) void read_only(const uint4* __restrict__ x, in
     if (acc == 0x9E3779B9u) sink[0] = acc;     // keeps the loads; never true for the fill below
 }
 
+__global__ __launch_bounds__(256) void write16(int64_t n16, uint4* __restrict__ y) {
+    const uint4 v = make_uint4(threadIdx.x, blockIdx.x, 1u, 2u);
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (int64_t)gridDim.x * 256) y[i] = v;
+}
+
+// thread i reads x[i] and writes slab k of y at i for k = 0..5 (every store
+// instruction covers consecutive 16-byte pieces)
+__global__ __launch_bounds__(256) void w6r1(const uint4* __restrict__ x, int64_t nr16, uint4* __restrict__ y) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < nr16; i += (int64_t)gridDim.x * 256) {
+        const uint4 v = x[i];
+#pragma unroll
+        for (int k = 0; k < 6; ++k) y[k * nr16 + i] = make_uint4(v.x + k, v.y, v.z, v.w);
+    }
+}
+
 __global__ __launch_bounds__(256) void copy16(const uint4* __restrict__ x, int64_t n16, uint4* __restrict__ y) {
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (int64_t)gridDim.x * 256) y[i] = x[i];
 }
@@ -100,10 +118,11 @@ int main() {
     CHECK(hipEventCreate(&s));
     CHECK(hipEventCreate(&e));
     const int grid = 8192;
-    const char* names[4] = {"row1d", "two2d", "read", "copy"};
-    const double bytes[4] = {elems * (2.0 + 0.5 + 1.0 / 32), elems * (2.0 + 1.0 + 2.0 / 1024), elems * 2.0,
-                             elems * 4.0};
-    for (int p = 0; p < 4; ++p) {
+    const int64_t nr16 = n16 / 6;     // w6r1: y holds six slabs of nr16 pieces
+    const char* names[6] = {"row1d", "two2d", "read", "copy", "write", "w6r1"};
+    const double bytes[6] = {elems * (2.0 + 0.5 + 1.0 / 32), elems * (2.0 + 1.0 + 2.0 / 1024), elems * 2.0,
+                             elems * 4.0, elems * 2.0, nr16 * 16.0 * 7};
+    for (int p = 0; p < 6; ++p) {
         float best = 1e30f;
         for (int rep = 0; rep < 3; ++rep) {
             CHECK(hipEventRecord(s));
@@ -113,6 +132,8 @@ int main() {
                     hipLaunchKernelGGL(two2d, dim3(grid), dim3(256), 0, 0, x, nblocks, (uint4*)codes, c2, scales);
                 if (p == 2) hipLaunchKernelGGL(read_only, dim3(grid), dim3(256), 0, 0, x, n16, codes);
                 if (p == 3) hipLaunchKernelGGL(copy16, dim3(grid), dim3(256), 0, 0, x, n16, y);
+                if (p == 4) hipLaunchKernelGGL(write16, dim3(grid), dim3(256), 0, 0, n16, y);
+                if (p == 5) hipLaunchKernelGGL(w6r1, dim3(grid), dim3(256), 0, 0, x, nr16, y);
             }
             CHECK(hipGetLastError());
             CHECK(hipEventRecord(e));

@@ -62,10 +62,6 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-// ---------------------------------------------------------------------------
-// Block scale from the amax bit pattern (sign already cleared):
-//   exponent field E; byte = max(E - 2, 0); E == 255 (NaN/Inf) -> 0xFF.
-// ---------------------------------------------------------------------------
 // One 16-byte vector store to a 16-byte-aligned global address.  Used where
 // the compiler's address strength reduction would otherwise split the store
 // into four dword stores.  The trailing s_nop covers the one wait state a
@@ -76,10 +72,14 @@ __device__ __forceinline__ void store_b128(void* p, uint4 v) {
     asm volatile("global_store_dwordx4 %0, %1, off\n\ts_nop 1" :: "v"(p), "v"(d) : "memory");
 }
 
+// ---------------------------------------------------------------------------
+// Block scale from the amax bit pattern (sign already cleared):
+//   exponent field E; byte = max(E - 2, 0); E == 255 (NaN/Inf) -> 0xFF.
+// ---------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t scale_byte_from_amax_bits(uint32_t amax_bits) {
     const uint32_t E = amax_bits >> 23;
-    if (E >= 255u) return 0xFFu;
-    return E > 2u ? E - 2u : 0u;
+    const uint32_t b = __builtin_elementwise_sub_sat(E, 2u);     // max(E - 2, 0)
+    return E >= 255u ? 0xFFu : b;
 }
 
 // fp32 whose exponent field is the UE8M0 byte: the conversion instructions'
@@ -117,22 +117,39 @@ __device__ __forceinline__ uint32_t cvt_sr_fp4_byte(uint32_t old, v2f src, uint3
     return old;
 }
 
+// The two random words of one Philox word w, one multiply-add each:
+//   even: (0xFFFF - lo16) << 16 = lo24(w) * -2^16 + 0xFFFF0000 (mod 2^32);
+//   odd:  (0xFFFF - hi16) << 15 in bits 30..15, bits 14..0 zero, from the
+//         signed high half: hi16 * -2^15 + 0x7FFF8000 (mod 2^32).  Bit 31 is
+//         then set for hi16 >= 2^15; the second slot sees the word shifted
+//         left by one, so that bit never reaches it.
+__device__ __forceinline__ uint32_t sr_word_even(uint32_t w) {
+    uint32_t r;
+    asm("v_mad_i32_i24 %0, %1, %2, %3" : "=v"(r) : "v"(w), "s"(-65536), "v"(0xFFFF0000u));
+    return r;
+}
+__device__ __forceinline__ uint32_t sr_word_odd(uint32_t w) {
+    uint32_t r;
+    asm("v_mad_i32_i16 %0, %1, %2, %3 op_sel:[1,0,0,0]" : "=v"(r) : "v"(w), "s"(-32768), "v"(0x7FFF8000u));
+    return r;
+}
+
 // SR: r = the 4 Philox words for these 8 elements (element e uses word e>>1,
 // low half for even e, high half for odd e).  The instruction converts a
 // pair of values; its first slot rounds with the random word as given and
 // its second slot with the word shifted left by one bit.  So the pair
 // (v[2j], v[2j+1]) is converted twice: once with (~lo16) << 16, keeping the
-// first slot's nibble (the even element), and once with (~hi16) << 15,
-// which the second slot sees as (~hi16) << 16, keeping its nibble (the odd
-// element).  Both words have their low 16 bits zero.  The two results are
-// merged nibble by nibble.
+// first slot's nibble (the even element), and once with ~hi16 in bits
+// 30..15, which the second slot sees as (~hi16) << 16, keeping its nibble
+// (the odd element).  Both words seen have their low 16 bits zero.  The two
+// results are merged nibble by nibble.
 __device__ __forceinline__ uint32_t cvt8_sr(const float* v, float sc, const u32x4& r) {
     const uint32_t w[4] = {r.x, r.y, r.z, r.w};
     uint32_t we[4], wo[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        we[j] = ~w[j] << 16;
-        wo[j] = (~w[j] >> 1) & 0x7FFF8000u;
+        we[j] = sr_word_even(w[j]);
+        wo[j] = sr_word_odd(w[j]);
     }
     // byte 0 starts each dword: the builtin form (its destination not tied to
     // "old") leaves the other bytes unspecified, and they are written next
