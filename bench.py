@@ -610,8 +610,7 @@ def run_step(torch, dev, args):
     for _ in range(args.warmup):
         step.run()
     torch.cuda.synchronize()
-    # timed region: K steps, per-launch events on the launch stream
-    step.events = []
+    # timed region: K steps and nothing else on the launch stream
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -621,6 +620,13 @@ def run_step(torch, dev, args):
     t_end.record()
     torch.cuda.synchronize()
     ms_step = t_start.elapsed_time(t_end) / args.steps
+    # K more steps with an event pair around every launch, for the per-kernel
+    # times (the events cost about 0.1 ms per step, so they stay out of the
+    # timed region above)
+    step.events = []
+    for _ in range(args.steps):
+        step.run()
+    torch.cuda.synchronize()
     # per role: its launches' summed time in each step (launches of one role
     # may differ in size), then the median over the steps
     n = len(step.events) // args.steps
