@@ -1,7 +1,8 @@
 // mx_quant.hip -- RHT, 1x32 / 32x32 MXFP4 quantization and dequantization
 // kernels for gfx950, and their C-ABI entry points (include/mx.h).
 //
-// The kernels are HBM-bound streams.  Lane mappings are chosen so that every
+// The kernels stream HBM (the RTNE ones are bound by it; with SR or the RHT
+// the arithmetic binds first).  Lane mappings are chosen so that every
 // global load and store of a wave is a contiguous run:
 //   row-wise 1D / RHT: a quad of lanes owns one 32-block (8 elements per
 //     lane, one 16-byte bf16 load), a wave covers 16 consecutive blocks; the
