@@ -54,12 +54,13 @@ ROLE_KERNEL = {
     "q2d": "q2d_kernel<true,false>",
     "q1d_row_rtne": "q1d_row_kernel_w<true,false,false>",
     "q1d_col": "q1d_col_kernel<true,true,true,0>",
-    "q1d_row_sr": "q1d_row_kernel_w<true,false,true>",
+    "q1d_dual_rtne": "q1d_col_kernel<true,true,true,1>",
+    "q1d_dual_sr": "q1d_col_kernel<true,true,true,2>",
     "gemm_fwd_gather": "gemm_kernel<true,true,false,true,true,false,false>",
     "gemm_bf16": "gemm_kernel<true,true,false,false,true,false,true>",
     "gemm_wgrad": "gemm_kernel<false,false,true,false,false,false,true>",
 }
-QUANT_ROLES = ("q2d", "q1d_row_rtne", "q1d_row_sr", "q1d_col")
+QUANT_ROLES = ("q2d", "q1d_row_rtne", "q1d_col", "q1d_dual_rtne", "q1d_dual_sr")
 GEMM_ROLES = ("gemm_fwd_gather", "gemm_bf16", "gemm_wgrad")
 
 
@@ -144,36 +145,33 @@ class Step:
         mx, b, i = self.mx, self.b, self.inp
         m = self.mask
         off, poff, idx = i["off"], i["poff"], i["idx"]
-        # Each tensor's row-wise and column-wise operands come from separate
-        # launches.  The column-wise RHT+SR quantizer is bound by arithmetic
-        # (Philox and the butterflies), so folding the row-wise pass into it
-        # (mx_quantize_1d_dual, one read) was measured slower: the row pass's
-        # work lands on the busy unit, and the read it saves was not the
-        # limit (see dual_quantize in the bench line).
+        # h, dY2 and dY1 feed a row-wise GEMM operand and a column-wise
+        # weight-gradient operand: one dual launch reads each tensor once and
+        # writes both (mx_quantize_1d_dual).  X's row-wise operand is of the
+        # 16,384 tokens, its column-wise one of the 65,536 routed rows, so it
+        # keeps two launches.
         col = dict(block_axis=0, group_offsets=off, kp=self.kp, use_rht=True, sign_mask=m, rnd=mx.SR, seed=5,
                    group_pad=256)
+
+        def dual(x, row_rnd, row_sid, col_sid, rc, rs, cc, cs):
+            return mx.quantize_1d_dual(x, off, kp=self.kp, use_rht=True, sign_mask=m, col_rnd=mx.SR,
+                                       col_stream_id=col_sid, row_rnd=row_rnd, row_stream_id=row_sid, seed=5,
+                                       col_codes=b[cc], col_scales=b[cs], row_codes=b[rc], row_scales=b[rs],
+                                       staged=True, group_pad=256)
         self._t("q2d", lambda: mx.quantize_2d_into(i["W1"], b["w1c"], b["w1s"], b["w1tc"], b["w1ts"]))
         self._t("q2d", lambda: mx.quantize_2d_into(i["W2"], b["w2c"], b["w2s"], b["w2tc"], b["w2ts"]))
         self._t("q1d_row_rtne", lambda: mx.quantize_1d(i["X"], codes=b["xc"], scales=b["xs"]))
         self._t("gemm_fwd_gather", lambda: mx.grouped_gemm(b["xc"], b["xs"], b["w1tc"], b["w1ts"], off, ROWS, F2,
                                                            D, a_row_index=idx, b_scale_2d=True, out=b["Y1"]))
-        self._t("q1d_row_rtne", lambda: mx.quantize_1d(i["h"], codes=b["hc"], scales=b["hs_st"], staged=True))
-        self._t("q1d_col", lambda: mx.quantize_1d(i["h"], stream_id=4, codes=b["hTc"], scales=b["hTs_st"],
-                                                  staged=True, **col))
+        self._t("q1d_dual_rtne", lambda: dual(i["h"], mx.RNE, 0, 4, "hc", "hs_st", "hTc", "hTs_st"))
         self._t("gemm_bf16", lambda: mx.grouped_gemm(b["hc"], b["hs_st"], b["w2tc"], b["w2ts"], off, ROWS, D, D,
                                                      b_scale_2d=True, staged=True, out=b["Y2"]))
-        self._t("q1d_row_sr", lambda: mx.quantize_1d(i["dY2"], rnd=mx.SR, seed=5, stream_id=1,
-                                                     codes=b["g2c"], scales=b["g2s_st"], staged=True))
-        self._t("q1d_col", lambda: mx.quantize_1d(i["dY2"], stream_id=5, codes=b["g2Tc"], scales=b["g2Ts_st"],
-                                                  staged=True, **col))
+        self._t("q1d_dual_sr", lambda: dual(i["dY2"], mx.SR, 1, 5, "g2c", "g2s_st", "g2Tc", "g2Ts_st"))
         self._t("gemm_bf16", lambda: mx.grouped_gemm(b["g2c"], b["g2s_st"], b["w2c"], b["w2s"], off, ROWS, D, D,
                                                      b_scale_2d=True, staged=True, out=b["dh"]))
         self._t("gemm_wgrad", lambda: mx.grouped_gemm(b["hTc"], b["hTs_st"], b["g2Tc"], b["g2Ts_st"], poff, D, D,
                                                       self.kp, group_dim_k=True, staged=True, out=b["dW2"]))
-        self._t("q1d_row_sr", lambda: mx.quantize_1d(i["dY1"], rnd=mx.SR, seed=5, stream_id=0,
-                                                     codes=b["g1c"], scales=b["g1s_st"], staged=True))
-        self._t("q1d_col", lambda: mx.quantize_1d(i["dY1"], stream_id=3, codes=b["g1Tc"], scales=b["g1Ts_st"],
-                                                  staged=True, **col))
+        self._t("q1d_dual_sr", lambda: dual(i["dY1"], mx.SR, 0, 3, "g1c", "g1s_st", "g1Tc", "g1Ts_st"))
         self._t("gemm_bf16", lambda: mx.grouped_gemm(b["g1c"], b["g1s_st"], b["w1c"], b["w1s"], off, ROWS, D, F2,
                                                      b_scale_2d=True, staged=True, out=b["dX"]))
         # X^T: the routed rows are gathered from the 16384-token X inside the
@@ -191,7 +189,9 @@ def work_model():
 
     - 1D quantize from bf16: 2 B read + 0.5 + 1/32 B written per element;
       the gathered X of the weight gradient is read once (16,384 token rows)
-      but written for every routed row (65,536).
+      but written for every routed row (65,536).  Both 1x32 layouts of one
+      tensor from one read (h, dY2, dY1): 2 B read + 2 x (0.5 + 1/32) B
+      written per element.
     - 2D quantize, both layouts: 2 B read + 2 x (0.5 + 1/1024) B written.
     - GEMM: the A and B codes and scales read once, C written once (bf16, or
       fp32 for the weight gradient)."""
@@ -211,10 +211,10 @@ def work_model():
     }
     return {
         "q2d": {"bytes": (E * D * F2 + E * D * D) * (2 + 2 * WS), "launches": 2},
-        "q1d_row_rtne": {"bytes": (T * D + ROWS * D) * BPE_1D, "launches": 2},
-        "q1d_row_sr": {"bytes": ROWS * (D + F2) * BPE_1D, "launches": 2},
-        "q1d_col": {"bytes": (T * D + 2 * ROWS * D + ROWS * F2) * 2 + (3 * ROWS * D + ROWS * F2) * CS,
-                    "launches": 4},
+        "q1d_row_rtne": {"bytes": T * D * BPE_1D, "launches": 1},
+        "q1d_col": {"bytes": T * D * 2 + ROWS * D * CS, "launches": 1},
+        "q1d_dual_rtne": {"bytes": ROWS * D * (2 + 2 * CS), "launches": 1},
+        "q1d_dual_sr": {"bytes": ROWS * (D + F2) * (2 + 2 * CS), "launches": 2},
         "gemm_fwd_gather": dict(gemm_fwd_gather, launches=1),
         "gemm_bf16": dict(gemm_bf16, launches=3),
         "gemm_wgrad": dict(gemm_wgrad, launches=2),
@@ -466,19 +466,25 @@ def snr_study(torch, dev):
 
 def dual_vs_separate(torch, step, reps=5):
     """The dual quantizer (one read, row-wise and column-wise RHT+SR codes)
-    against the two separate launches it replaces, on the step's buffers:
-    h (65536 x 2880, row RTNE) and dY1 (65536 x 5760, row SR)."""
+    against the two launches it replaces, on the step's buffers and layouts
+    (staged scales, groups padded to 256 tokens): h (65536 x 2880, row RTNE),
+    dY2 (65536 x 2880, row SR) and dY1 (65536 x 5760, row SR)."""
     mx, b, i = step.mx, step.b, step.inp
     off, m, kp = i["off"], step.mask, step.kp
+    col = dict(block_axis=0, group_offsets=off, kp=kp, use_rht=True, sign_mask=m, rnd=mx.SR, seed=5,
+               group_pad=256, staged=True)
     res = {}
-    for name, x, rnd, rs, cs_, rc, rsc, cc, csc in (("h_row_rtne", i["h"], mx.RNE, 0, 4, "hc", "hs", "hTc", "hTs"),
-                                                   ("dY1_row_sr", i["dY1"], mx.SR, 0, 3, "g1c", "g1s", "g1Tc", "g1Ts")):
-        sep = lambda: (mx.quantize_1d(x, rnd=rnd, seed=5, stream_id=rs, codes=b[rc], scales=b[rsc]),  # noqa
-                       mx.quantize_1d(x, block_axis=0, group_offsets=off, kp=kp, use_rht=True, sign_mask=m,
-                                      rnd=mx.SR, seed=5, stream_id=cs_, codes=b[cc], scales=b[csc]))
+    for name, x, rnd, rs, cs_, rc, rsc, cc, csc in (
+            ("h_row_rtne", i["h"], mx.RNE, 0, 4, "hc", "hs_st", "hTc", "hTs_st"),
+            ("dY2_row_sr", i["dY2"], mx.SR, 1, 5, "g2c", "g2s_st", "g2Tc", "g2Ts_st"),
+            ("dY1_row_sr", i["dY1"], mx.SR, 0, 3, "g1c", "g1s_st", "g1Tc", "g1Ts_st")):
+        sep = lambda: (mx.quantize_1d(x, rnd=rnd, seed=5, stream_id=rs, codes=b[rc], scales=b[rsc],  # noqa
+                                      staged=True),
+                       mx.quantize_1d(x, stream_id=cs_, codes=b[cc], scales=b[csc], **col))
         dual = lambda: mx.quantize_1d_dual(x, off, kp=kp, use_rht=True, sign_mask=m, col_rnd=mx.SR,  # noqa
                                            col_stream_id=cs_, row_rnd=rnd, row_stream_id=rs, seed=5,
-                                           col_codes=b[cc], col_scales=b[csc], row_codes=b[rc], row_scales=b[rsc])
+                                           col_codes=b[cc], col_scales=b[csc], row_codes=b[rc], row_scales=b[rsc],
+                                           staged=True, group_pad=256)
         res[name] = {"shape": "%dx%d" % tuple(x.shape), "separate_ms": time_launches(torch, [sep], reps, repeats=5),
                      "dual_ms": time_launches(torch, [dual], reps, repeats=5)}
     return res

@@ -180,7 +180,12 @@ mx_status mx_quantize_1d(const void* x, mx_dtype xt, int64_t rows, int64_t cols,
  *                  row_scales);
  * the rows of x are the grouped positions (no row gather).  Row-wise codes
  * [rows x cols/2] at pitch row_codes_ld (0 = cols/2), scales
- * [rows x cols/32].  Arguments, layouts and errors otherwise as
+ * [rows x cols/32].  layout_flags: 0, or MX_SCALES_STAGED (both outputs'
+ * scales in the staged order: column-wise [kp/256 + num_groups][cols][8],
+ * row-wise [ceil(cols/256)][rows][8]) and/or MX_GROUPS_PAD256 (the
+ * column-wise output's groups padded to 256 tokens), exactly as those flags
+ * act in the two mx_quantize_1d calls above; other bits:
+ * MX_ERR_UNSUPPORTED.  Arguments, layouts and errors otherwise as
  * mx_quantize_1d. */
 mx_status mx_quantize_1d_dual(const void* x, mx_dtype xt, int64_t rows, int64_t cols,
                               const int32_t* group_offsets, int32_t num_groups, int64_t kp, int use_rht,
@@ -188,7 +193,7 @@ mx_status mx_quantize_1d_dual(const void* x, mx_dtype xt, int64_t rows, int64_t 
                               uint64_t col_index_base, uint8_t* col_codes, uint8_t* col_scales,
                               mx_round row_rnd, uint32_t row_stream_id, uint64_t row_index_base,
                               uint8_t* row_codes, int64_t row_codes_ld, uint8_t* row_scales, uint64_t seed,
-                              mx_stream stream);
+                              int layout_flags, mx_stream stream);
 
 /* 32x32 MXFP4 quantization, round to nearest even (the "2D" half of the
  * hybrid scheme, used for weights).  w: batch x [rows x cols], rows % 32 ==

@@ -343,6 +343,9 @@ struct ColArgs {
     int staged;
     // blocks per group padding unit: 1 (groups padded to 32 tokens) or 8 (256)
     int pad_blocks;
+    // ROWQ: 0, row-major row-wise scales; else staged with this many rows
+    // (block b of grouped row r at byte ((b / 8) row_srows + r) 8 + b % 8)
+    uint32_t row_srows;
 };
 
 template <bool BF16, bool RHT, bool SR, int ROWQ>
@@ -517,6 +520,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BF16 ? 3 : 
     uint4 pre[NLD];
     uint32_t pkb = 0;
     int32_t splace = 0;          // staged scales: this lane's block placement (lanes 0..7)
+    int64_t rq_tb = 0;           // ROWQ: first grouped row of this thread's block, its
+    int32_t rq_nb = 0;           //       token count, and the block row they are for
+    int64_t rq_br = -1;
     int64_t splace_br = -1;      // the block row it was computed for
     if (vec && tbeg < tend) {
         rows_for(br * CT_BLOCKS);
@@ -578,15 +584,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BF16 ? 3 : 
         // it; rows past a group's end (padding) have no row-wise counterpart.
         // The RHT's signs, applied as the tile entered LDS, are undone.
         if (ROWQ) {
-            int64_t t0;
-            int32_t n;
-            block_info(pb0, t0, n);                      // lane b < 8 of each wave: block b
             const int rb = tid >> 5, rj = tid & 31;
-            const int64_t tb = (int64_t)(((uint64_t)(uint32_t)__shfl((int)((uint64_t)t0 >> 32), rb) << 32) |
-                                         (uint32_t)__shfl((int)(uint32_t)t0, rb));
-            const int32_t nb = __shfl(n, rb);
-            const int64_t prow = tb + rj;                // the token's grouped row
-            const uint32_t sg = sign_word(rj);
+            if (br != rq_br) {
+                // once per block row (its column tiles share it): block rb's
+                // first grouped row and its token count
+                rq_br = br;
+                int64_t t0;
+                int32_t n;
+                block_info(pb0, t0, n);                  // lane b < 8 of each wave: block b
+                rq_tb = (int64_t)(((uint64_t)(uint32_t)__shfl((int)((uint64_t)t0 >> 32), rb) << 32) |
+                                  (uint32_t)__shfl((int)(uint32_t)t0, rb));
+                rq_nb = __shfl(n, rb);
+            }
+            const int32_t nb = rq_nb;
+            const int64_t prow = rq_tb + rj;             // the token's grouped row
+            // The RHT's signs, flipped on the way into LDS, are undone on the
+            // codes: rounding is symmetric, so the codes of -x are those of x
+            // with every nibble's sign bit flipped (zeros included), and the
+            // block amax does not see signs.
+            const uint32_t cflip = sign_word(rj) ? 0x88888888u : 0u;
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
                 const int64_t c = c0 + 32 * half;
@@ -597,7 +613,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BF16 ? 3 : 
 #pragma unroll
                         for (int k = 0; k < 4; ++k) {
                             const uint4 w = *(const uint4*)(src + 16 * k);
-                            const uint32_t ww[4] = {w.x ^ sg, w.y ^ sg, w.z ^ sg, w.w ^ sg};
+                            const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
                             for (int e = 0; e < 4; ++e) {
                                 v[8 * k + 2 * e] = bf16lo(ww[e]);
@@ -608,8 +624,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BF16 ? 3 : 
 #pragma unroll
                         for (int k = 0; k < 8; ++k) {
                             const uint4 w = *(const uint4*)(src + 16 * k);
-                            v[4 * k + 0] = __uint_as_float(w.x ^ sg); v[4 * k + 1] = __uint_as_float(w.y ^ sg);
-                            v[4 * k + 2] = __uint_as_float(w.z ^ sg); v[4 * k + 3] = __uint_as_float(w.w ^ sg);
+                            v[4 * k + 0] = __uint_as_float(w.x); v[4 * k + 1] = __uint_as_float(w.y);
+                            v[4 * k + 2] = __uint_as_float(w.z); v[4 * k + 3] = __uint_as_float(w.w);
                         }
                     }
                     uint32_t am = 0;
@@ -618,21 +634,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BF16 ? 3 : 
                     const uint32_t byte = scale_byte_from_amax_bits(am);
                     const float sc = scale_operand(byte);
                     uint32_t w4[4];
-                    const uint64_t ebase = a.row_index_base + (uint64_t)prow * (uint64_t)cols + (uint64_t)c;
+                    // counter of elements 8 qq .. 8 qq + 7 of the block: (ebase + 8 qq) / 8
+                    const uint64_t e8 = (a.row_index_base + (uint64_t)prow * (uint64_t)cols + (uint64_t)c) >> 3;
 #pragma unroll
                     for (int qq = 0; qq < 4; ++qq) {
                         if (ROWQ == 2) {
-                            const uint64_t g8 = (ebase + qq * 8) >> 3;
+                            const uint64_t g8 = e8 + (uint64_t)qq;
                             const u32x4 r = philox4x32_10((uint32_t)g8, (uint32_t)(g8 >> 32), a.row_stream_id, 0u,
                                                           k0, k1);
                             w4[qq] = cvt8_sr(v + 8 * qq, sc, r);
                         } else {
                             w4[qq] = cvt8_rne(v + 8 * qq, sc);
                         }
+                        w4[qq] ^= cflip;
                     }
                     if (byte == 0xFFu) w4[0] = w4[1] = w4[2] = w4[3] = 0;
                     *(uint4*)(a.row_codes + prow * a.row_ld + (c >> 5) * 16) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
-                    a.row_scales[prow * (cols >> 5) + (c >> 5)] = (uint8_t)byte;
+                    const uint32_t rcb = (uint32_t)(c >> 5);
+                    if (a.row_srows)
+                        a.row_scales[((rcb >> 3) * a.row_srows + (uint32_t)prow) * 8u + (rcb & 7u)] = (uint8_t)byte;
+                    else
+                        a.row_scales[prow * (cols >> 5) + (c >> 5)] = (uint8_t)byte;
                 }
             }
         }
@@ -1418,9 +1440,12 @@ mx_status mx_quantize_1d_dual(const void* x, mx_dtype xt, int64_t rows, int64_t 
                               uint32_t col_stream_id, uint64_t col_index_base, uint8_t* col_codes,
                               uint8_t* col_scales, mx_round row_rnd, uint32_t row_stream_id,
                               uint64_t row_index_base, uint8_t* row_codes, int64_t row_codes_ld,
-                              uint8_t* row_scales, uint64_t seed, mx_stream stream) {
+                              uint8_t* row_scales, uint64_t seed, int layout_flags, mx_stream stream) {
     if (xt != MX_F32 && xt != MX_BF16) return MX_ERR_DTYPE;
     if ((col_rnd != MX_RNE && col_rnd != MX_SR) || (row_rnd != MX_RNE && row_rnd != MX_SR)) return MX_ERR_UNSUPPORTED;
+    if (layout_flags & ~(MX_SCALES_STAGED | MX_GROUPS_PAD256)) return MX_ERR_UNSUPPORTED;
+    const bool staged = (layout_flags & MX_SCALES_STAGED) != 0;
+    const bool pad256 = (layout_flags & MX_GROUPS_PAD256) != 0;
     if (rows < 0 || cols <= 0 || cols % 32) return MX_ERR_SHAPE;
     if (col_index_base % 32 || row_index_base % 32) return MX_ERR_SHAPE;
     if (num_groups < 1 || num_groups > COL_MAX_GROUPS) return MX_ERR_SHAPE;
@@ -1433,9 +1458,13 @@ mx_status mx_quantize_1d_dual(const void* x, mx_dtype xt, int64_t rows, int64_t 
     if (!aligned16(x) || !aligned16(col_codes) || !aligned16(row_codes)) return MX_ERR_ALIGN;
     const bool bf = xt == MX_BF16;
     if (cols > (int64_t)(0xFFFFFFFFu / (bf ? 2u : 4u))) return MX_ERR_SHAPE;
+    // staged scales: 32-bit offsets in both orders
+    if (staged && ((kp / 256 + num_groups) * cols * 8 > (int64_t)0xFFFFFFFFu ||
+                   (cols + 255) / 256 * rows * 8 > (int64_t)0xFFFFFFFFu))
+        return MX_ERR_SHAPE;
     ColArgs a{x, cols, group_offsets, (int)num_groups, nullptr, rows, kp, 0, 0, sign_mask, (uint32_t)seed,
               (uint32_t)(seed >> 32), col_stream_id, col_index_base, col_codes, col_scales, row_codes, ld, row_scales,
-              row_stream_id, row_index_base, 0, 1};
+              row_stream_id, row_index_base, staged ? 1 : 0, pad256 ? 8 : 1, staged ? (uint32_t)rows : 0u};
     return launch_col(a, bf, use_rht != 0, col_rnd == MX_SR, row_rnd == MX_SR ? 2 : 1, (hipStream_t)stream);
 }
 

@@ -56,7 +56,7 @@ def lib():
                                            P, P]
         L.mx_dequantize.argtypes = [P, i64, P, i64, i64, i64, c_int, P, c_int, P]
         L.mx_quantize_1d_dual.argtypes = [P, c_int, i64, i64, P, i32, i64, c_int, u32, c_int, u32, u64, P, P,
-                                          c_int, u32, u64, P, i64, P, u64, P]
+                                          c_int, u32, u64, P, i64, P, u64, c_int, P]
         L.mx_quantize_1d_ex.argtypes = [P, c_int, i64, i64, c_int, u32, c_int, u64, u32, u64,
                                         ctypes.c_float, i64, P, P, P, P]
         L.mx_dequantize_1d_ex.argtypes = [P, P, P, i64, i64, i64, P, P]
@@ -245,30 +245,38 @@ def quantize_1d(x, block_axis: int = 1, group_offsets=None, kp: int = 0, use_rht
 def quantize_1d_dual(x, group_offsets, kp: int = 0, use_rht: bool = False, sign_mask: int = 0,
                      col_rnd: int = RNE, col_stream_id: int = 0, row_rnd: int = RNE, row_stream_id: int = 0,
                      seed: int = 0, col_index_base: int = 0, row_index_base: int = 0, col_codes=None,
-                     col_scales=None, row_codes=None, row_scales=None):
+                     col_scales=None, row_codes=None, row_scales=None, staged: bool = False, group_pad: int = 32):
     """Column-wise (grouped, transposed, optional RHT) and row-wise (no RHT)
     1x32 quantization of x from one read (see mx_quantize_1d_dual).
     Returns (col_codes, col_scales, row_codes, row_scales); row_codes may
-    have padded rows (a row-slice view of a wider buffer)."""
+    have padded rows (a row-slice view of a wider buffer).  staged: both
+    outputs' scales in the staged order (column-wise [kp // 256 + groups,
+    cols, 8], row-wise [ceil(cols / 256), rows, 8]); group_pad: the
+    column-wise output's group padding, 32 or 256 tokens."""
     torch = _torch()
     _dev(x, "x")
     rows, cols = x.shape
     _index_vector(group_offsets, "group_offsets", min_numel=2)
     ng = group_offsets.numel() - 1
-    kp = kp or padded_capacity(rows, ng)
+    if group_pad not in (32, 256):
+        raise ValueError("group_pad is 32 or 256")
+    kp = kp or padded_capacity(rows, ng, group_pad)
     u8, dev = torch.uint8, x.device
+    shape_cs = (kp // 256 + ng, cols, 8) if staged else (cols, kp // 32)
+    shape_rs = ((cols + 255) // 256, rows, 8) if staged else (rows, cols // 32)
     col_codes = col_codes if col_codes is not None else torch.empty((cols, kp // 2), dtype=u8, device=dev)
-    col_scales = col_scales if col_scales is not None else torch.empty((cols, kp // 32), dtype=u8, device=dev)
+    col_scales = col_scales if col_scales is not None else torch.empty(shape_cs, dtype=u8, device=dev)
     row_codes = row_codes if row_codes is not None else torch.empty((rows, cols // 2), dtype=u8, device=dev)
-    row_scales = row_scales if row_scales is not None else torch.empty((rows, cols // 32), dtype=u8, device=dev)
+    row_scales = row_scales if row_scales is not None else torch.empty(shape_rs, dtype=u8, device=dev)
     _shaped(col_codes, (cols, kp // 2), u8, "col_codes")
-    _shaped(col_scales, (cols, kp // 32), u8, "col_scales")
+    _shaped(col_scales, shape_cs, u8, "col_scales")
     ld = _shaped(row_codes, (rows, cols // 2), u8, "row_codes", pitched=True)
-    _shaped(row_scales, (rows, cols // 32), u8, "row_scales")
+    _shaped(row_scales, shape_rs, u8, "row_scales")
+    flags = (SCALES_STAGED if staged else 0) | (GROUPS_PAD256 if group_pad == 256 else 0)
     _check("mx_quantize_1d_dual", lib().mx_quantize_1d_dual(
         _ptr(x), _dtype_code(x), rows, cols, _ptr(group_offsets), ng, kp, int(use_rht), sign_mask, col_rnd,
         col_stream_id, col_index_base, _ptr(col_codes), _ptr(col_scales), row_rnd, row_stream_id,
-        row_index_base, _ptr(row_codes), ld, _ptr(row_scales), seed, _stream()))
+        row_index_base, _ptr(row_codes), ld, _ptr(row_scales), seed, flags, _stream()))
     return col_codes, col_scales, row_codes, row_scales
 
 

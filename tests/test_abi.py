@@ -140,7 +140,7 @@ def test_study_variant_validation(L):
 
 def test_quantize_1d_dual_validation(L):
     q = L.mx_quantize_1d_dual
-    args = [FAKE, mx.MX_BF16, 64, 96, FAKE, 2, 128, 1, 0, 1, 0, 0, FAKE, FAKE, 1, 0, 0, FAKE, 0, FAKE, 0, None]
+    args = [FAKE, mx.MX_BF16, 64, 96, FAKE, 2, 128, 1, 0, 1, 0, 0, FAKE, FAKE, 1, 0, 0, FAKE, 0, FAKE, 0, 0, None]
 
     def call(i_vals):
         a = list(args)
@@ -157,6 +157,11 @@ def test_quantize_1d_dual_validation(L):
     assert call([(4, None)]) == 1 and call([(17, None)]) == 1 and call([(19, None)]) == 1
     assert call([(0, FAKE + 2)]) == 3 and call([(17, FAKE + 8)]) == 3
     assert call([(2, 0), (0, None), (12, None), (13, None), (17, None), (19, None)]) == 0
+    assert call([(21, 8)]) == 5 and call([(21, 1)]) == 5      # layout flags: staged and pad256 only
+    assert call([(21, mx.SCALES_STAGED | mx.GROUPS_PAD256), (2, 0), (0, None), (12, None), (13, None),
+                 (17, None), (19, None)]) == 0
+    # staged: the row-wise order's 32-bit offsets (ceil(cols / 256) * rows * 8 bytes)
+    assert call([(21, mx.SCALES_STAGED), (2, 2 ** 31), (3, 256)]) == 2
 
 
 def test_dequantize_validation(L):

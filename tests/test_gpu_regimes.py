@@ -323,3 +323,86 @@ def test_dual_full_size_equals_two_calls(cols, row_rnd):
     total = int(sum((int(n) + 31) // 32 * 32 for n in counts))
     assert torch.equal(cc[:, :total // 2], cc2[:, :total // 2]) and torch.equal(cs[:, :total // 32], cs2[:, :total // 32])
     assert torch.equal(rc.contiguous(), rc2) and torch.equal(rs, rs2)
+
+
+JUNK = 0xA7
+
+
+@pytest.mark.parametrize("dt,cols,row_rnd", [("bf16", 96, 1), ("bf16", 352, 0), ("f32", 160, 1)])
+def test_dual_staged_pad256_matches_oracle(dt, cols, row_rnd):
+    """The dual call with both outputs' scales in the staged order and the
+    column-wise groups padded to 256 tokens (the layouts the expert step's
+    GEMMs read), against the oracle: codes bit for bit, every staged scale
+    slot the oracle maps equal to its byte, the others untouched."""
+    import torch
+    counts = [300, 0, 17, 700, 256, 1]
+    off = synth.offsets_from_counts(counts)
+    rows, G = int(off[-1]), len(counts)
+    rng = np.random.default_rng(cols + 11 * row_rnd)
+    xf = (rng.standard_normal((rows, cols)) * np.exp2(rng.integers(-6, 6, (1, cols)))).astype(np.float32)
+    x = xf if dt == "f32" else synth.f32_to_bf16_bits(xf)
+    xd = dev(x) if dt == "f32" else dev_bf16(x)
+    mask = mx.rht_sign_mask(6)
+    kp = mx.padded_capacity(rows, G, 256)
+    Sc, Sr = kp // 256 + G, (cols + 255) // 256
+    csb = torch.full((Sc, cols, 8), JUNK, dtype=torch.uint8, device="cuda")
+    rsb = torch.full((Sr, rows, 8), JUNK, dtype=torch.uint8, device="cuda")
+    buf, rcodes = _padded_codes(torch, rows, cols // 2, (cols // 2 + 127) // 128 * 128 + 16)
+    cc, cs, rc, rs = mx.quantize_1d_dual(xd, dev(off), kp=kp, use_rht=True, sign_mask=mask, col_rnd=1,
+                                         col_stream_id=2, row_rnd=row_rnd, row_stream_id=1, seed=9,
+                                         row_codes=rcodes, col_scales=csb, row_scales=rsb, staged=True,
+                                         group_pad=256)
+    oc, os_ = oracle.quantize_1d(x, block_axis=0, group_offsets=off, kp=kp, use_rht=True, sign_mask=mask, rnd=1,
+                                 seed=9, stream=2, group_pad=256)
+    tot = oracle.padded_total(off, 256)
+    _assert_same(host(cc)[:, :tot // 2], oc[:, :tot // 2], "column codes")
+    want = oracle.stage_scales(os_, off, stages=Sc, fill=JUNK, group_pad=256)
+    m = oracle.stage_scales(np.ones_like(os_), off, stages=Sc, fill=0, group_pad=256).astype(bool)
+    got = host(cs)
+    assert np.array_equal(got[m], want[m]) and np.all(got[~m] == JUNK), "column scales"
+    orc, ors = oracle.quantize_1d(x, rnd=row_rnd, seed=9, stream=1)
+    _assert_same(host(rc.contiguous()), orc, "row codes")
+    want = oracle.stage_scales(ors, stages=Sr, fill=JUNK)
+    m = oracle.stage_scales(np.ones_like(ors), stages=Sr, fill=0).astype(bool)
+    got = host(rs)
+    assert np.array_equal(got[m], want[m]) and np.all(got[~m] == JUNK), "row scales"
+    assert bool((buf[:, cols // 2:] == 0xA5).all()), "row padding was written"
+
+
+@pytest.mark.parametrize("cols,row_rnd", [(2880, 0), (5760, 1)])
+def test_dual_full_size_staged_pad256_equals_two_calls(cols, row_rnd):
+    """The expert step's layouts at full size (65,536 routed rows, 32 Zipf
+    groups padded to 256 tokens, staged scales, padded code rows): the dual
+    call equals the two separate calls the step would otherwise make."""
+    import torch
+    counts = synth.zipf_counts()
+    off = dev(synth.offsets_from_counts(counts))
+    rows = 65536
+    g = torch.Generator(device="cuda").manual_seed(cols + 7 * row_rnd)
+    x = (torch.randn(rows, cols, device="cuda", generator=g) * 1e-3).to(torch.bfloat16)
+    kp = mx.padded_capacity(rows, 32, 256)
+    mask = mx.rht_sign_mask(5)
+    ldp = (cols // 2 + 127) // 128 * 128
+    rbuf = torch.zeros(rows, ldp, dtype=torch.uint8, device="cuda")
+    # staged row scales: the slots past a row's last block are never written
+    Sr = (cols + 255) // 256
+    rsb = torch.full((Sr, rows, 8), JUNK, dtype=torch.uint8, device="cuda")
+    rsb2 = torch.full((Sr, rows, 8), JUNK, dtype=torch.uint8, device="cuda")
+    cc, cs, rc, rs = mx.quantize_1d_dual(x, off, kp=kp, use_rht=True, sign_mask=mask, col_rnd=1, col_stream_id=5,
+                                         row_rnd=row_rnd, row_stream_id=1, seed=5, row_codes=rbuf[:, :cols // 2],
+                                         row_scales=rsb, staged=True, group_pad=256)
+    cc2, cs2 = mx.quantize_1d(x, block_axis=0, group_offsets=off, kp=kp, use_rht=True, sign_mask=mask, rnd=1,
+                              seed=5, stream_id=5, staged=True, group_pad=256)
+    rbuf2 = torch.zeros(rows, ldp, dtype=torch.uint8, device="cuda")
+    rc2, rs2 = mx.quantize_1d(x, rnd=row_rnd, seed=5, stream_id=1, staged=True, codes=rbuf2[:, :cols // 2],
+                              scales=rsb2)
+    pad = (np.asarray(counts) + 255) // 256 * 256
+    total = int(pad.sum())
+    assert torch.equal(cc[:, :total // 2], cc2[:, :total // 2])
+    # staged column scales: compare the slots the groups' blocks occupy
+    S = kp // 256 + 32
+    m = torch.from_numpy(oracle.stage_scales(np.ones((cols, total // 32), np.uint8),
+                                             synth.offsets_from_counts(counts), stages=S, fill=0,
+                                             group_pad=256).astype(bool)).cuda()
+    assert torch.equal(cs[m], cs2[m])
+    assert torch.equal(rbuf, rbuf2) and torch.equal(rs, rs2)

@@ -91,7 +91,7 @@ assert L.mx_grouped_gemm(F, i64(0), F, None, F, i64(0), F, 0, F, 0, 0, i64(64), 
 assert L.mx_grouped_gemm_q(F, i64(0), F, None, F, i64(0), F, 0, F, 1, i64(64), i64(64), i64(64), ctypes.c_float(1.0), F, None, i64(0), F, None) == 1
 assert L.mx_quantize_1d_ex(F, 0, i64(4), i64(256), 0, 0, 0, u64(0), 0, u64(0), ctypes.c_float(2.0), i64(0), F, F, None, None) == 2
 assert L.mx_dequantize_1d_ex(F, F, None, i64(4), i64(256), i64(128), F, None) == 1
-assert L.mx_quantize_1d_dual(F, 1, i64(64), i64(48), F, 2, i64(128), 1, 0, 1, 0, u64(0), F, F, 1, 0, u64(0), F, i64(0), F, u64(0), None) == 2
+assert L.mx_quantize_1d_dual(F, 1, i64(64), i64(48), F, 2, i64(128), 1, 0, 1, 0, u64(0), F, F, 1, 0, u64(0), F, i64(0), F, u64(0), 0, None) == 2
 # empty inputs return before looking at any pointer
 assert L.mx_quantize_2d(None, 1, i64(0), i64(32), i64(32), None, i64(0), None, None, i64(0), None, None) == 0
 assert L.mx_grouped_gemm(F, i64(0), F, None, F, i64(0), F, 0, F, 1, 0, i64(0), i64(64), i64(64), ctypes.c_float(1.0), None, 1, None) == 0
