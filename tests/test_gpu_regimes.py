@@ -406,3 +406,36 @@ def test_dual_full_size_staged_pad256_equals_two_calls(cols, row_rnd):
                                              group_pad=256).astype(bool)).cuda()
     assert torch.equal(cs[m], cs2[m])
     assert torch.equal(rbuf, rbuf2) and torch.equal(rs, rs2)
+
+
+@pytest.mark.parametrize("dt,row_rnd", [("f32", 0), ("bf16", 1)])
+def test_dual_nonfinite_blocks_match_oracle(dt, row_rnd):
+    """Blocks holding Inf, -Inf or NaN (and finite values whose RHT sums
+    overflow) in the dual call: both outputs take scale 0xFF and zero codes
+    exactly where the oracle does.  The row pass undoes the RHT's signs on
+    its codes, so this checks that a non-finite block's codes are zeroed
+    after that flip."""
+    rng = np.random.default_rng(21)
+    counts = [64, 40, 96]
+    off = synth.offsets_from_counts(counts)
+    rows, cols = int(off[-1]), 96
+    x = rng.standard_normal((rows, cols)).astype(np.float32)
+    x[3, 0] = np.inf
+    x[40, 5] = -np.inf
+    x[70, 33] = np.nan
+    x[100:104, 64] = 3.0e38
+    x = synth.f32_to_bf16_bits(x) if dt == "bf16" else x
+    xd = dev_bf16(x) if dt == "bf16" else dev(x)
+    kp = mx.padded_capacity(rows, len(counts))
+    mask = 0xFFFFFFFF          # every sign flipped: every row-wise code goes through the flip
+    cc, cs, rc, rs = mx.quantize_1d_dual(xd, dev(off), kp=kp, use_rht=True, sign_mask=mask, col_rnd=1,
+                                         col_stream_id=2, row_rnd=row_rnd, row_stream_id=0, seed=4)
+    oc, os_ = oracle.quantize_1d(x, block_axis=0, group_offsets=off, kp=kp, use_rht=True, sign_mask=mask, rnd=1,
+                                 seed=4, stream=2)
+    total = oracle.padded_total(off)
+    _assert_same(host(cs)[:, :total // 32], os_[:, :total // 32], "column scales")
+    _assert_same(host(cc)[:, :total // 2], oc[:, :total // 2], "column codes")
+    orc, ors = oracle.quantize_1d(x, rnd=row_rnd, seed=4, stream=0)
+    assert np.count_nonzero(ors == 0xFF) >= 3
+    _assert_same(host(rs), ors, "row scales")
+    _assert_same(host(rc), orc, "row codes")
