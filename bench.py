@@ -755,8 +755,11 @@ def main():
         "config": {"workload": "quantized MoE expert step fwd+bwd: 32 experts, d_model 2880, ffn 2880 "
                                "(gate_up 5760), 16384 tokens top-4 Zipf(1.1)",
                    "experts": E, "d_model": D, "d_ff_gate_up": F2, "tokens": T, "top_k": TOPK},
+        "quantize_ms_per_step": quant_ms,
+        "quantize_GB_per_step": quant_bytes / 1e9,
         "quantize_GBps": quant_bytes / (quant_ms / 1e3) / 1e9,
         "quantize_frac_hbm": quant_bytes / (quant_ms / 1e3) / 1e9 / PEAK_HBM_GBS,
+        "gemm_ms_per_step": gemm_ms,
         "gemm_TFLOPs": total_flops / (gemm_ms / 1e3) / 1e12,
         "gemm_frac_fp4": total_flops / (gemm_ms / 1e3) / 1e12 / PEAK_FP4_TFLOPS,
         "kernels": kernels,
